@@ -1,0 +1,43 @@
+"""CPU oracle for block-sparse video attention -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, obviously correct NumPy code that states what the hot path
+computes, in float64, for checking the HIP library against.  Only the test
+suite, the smoke check and the benchmark's CPU-baseline leg may import it; the
+library never does, and nothing here imports the library.
+
+Sources (page title, then section):
+  * "LVSA: Training-Free Sparse Attention for Long Video Diffusion",
+    Meccanismo Core: the frame set A(t) = G u W(t) of a query frame t, the
+    rotating periodic global anchors G and the local window W(t).
+  * "Accelerating Text-to-Video Generation with Calibrated Sparse Attention",
+    A. Fase di Calibrazione / B. Fase di Inferenza: 128x128 attention blocks,
+    a static per-(timestep, layer, head) block mask, attention computed only
+    over the selected blocks.
+  * Softmax attention itself (all pages assume full softmax attention inside
+    the selected blocks), written as its textbook definition.
+
+Modules:
+  masks      frame rule, tile lift, static (SplitMix64) and dense tile masks
+  csr        per-query-tile lists of active key tiles
+  attention  dense float64 softmax attention with masked blocks set to -inf
+
+Every function here is pinned by tests/test_oracle_*.py against values and
+properties fixed by the pages or by mathematics (hand-enumerated masks,
+brute-force token-level masks, a published SplitMix64 test vector, textbook
+full attention, single-block brute force, convex-combination bounds).  The
+attention output itself has no printed worked example on the pages; it is
+pinned only through those definitions and invariants.
+"""
+from .masks import (anchor_frames, window_frames, frame_set, frame_mask,
+                    tile_frame_range, tile_mask_window_anchor,
+                    splitmix64_stream, static_hash24, tile_mask_static,
+                    tile_mask_dense, tile_mask)
+from .csr import tile_csr
+from .attention import block_sparse_attention, block_sparse_attention_rows
+
+__all__ = [
+    "anchor_frames", "window_frames", "frame_set", "frame_mask",
+    "tile_frame_range", "tile_mask_window_anchor", "splitmix64_stream",
+    "static_hash24", "tile_mask_static", "tile_mask_dense", "tile_mask",
+    "tile_csr", "block_sparse_attention", "block_sparse_attention_rows",
+]

@@ -1,0 +1,139 @@
+"""Seeded synthetic workloads for block-sparse video attention.
+
+This module holds only shapes, mask parameters and seeded random inputs.  It
+does none of the method's arithmetic: no masks, no tile lists, no attention.
+Both the CPU oracle's tests and the HIP path's tests and benchmark draw their
+inputs from here, so the two sides always see identical values.
+
+The shapes follow the video diffusion transformers the pages study (a 21-frame
+latent horizon for Wan 2.1, LVSA page, "Meccanismo Core"; 128x128 attention
+blocks, CalibAtt page, "A. Fase di Calibrazione").  Real activations and model
+weights are not available, so Q, K and V are i.i.d. N(0, 1) draws at those
+shapes; VBench-style quality suites are out of scope entirely.
+
+Token order is frame-major: token n = f*P + y*grid_w + x with P = grid_h*grid_w.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import torch
+
+# Mask kinds, numbered as in include/bsattn.h.
+MASK_WINDOW_ANCHOR = 0
+MASK_STATIC_RANDOM = 1
+MASK_DENSE = 2
+
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+
+
+def thresh24_for_density(p: float) -> int:
+    """24-bit threshold of the static random mask: a tile is drawn active when
+    the top 24 bits of its hash are below floor(p * 2**24)."""
+    if not (0.0 <= p <= 1.0):
+        raise ValueError("density must lie in [0, 1]")
+    return min(int(p * (1 << 24)), 1 << 24)
+
+
+@dataclass(frozen=True)
+class MaskSpec:
+    kind: int
+    window: int = 0          # half-width w, in frames
+    num_anchors: int = 0     # n_a global anchor frames
+    rotation: int = 0        # r, reduced mod T by the mask builder
+    seed: int = 0            # static mode
+    thresh24: int = 0        # static mode
+    force_diagonal: int = 0  # static mode
+    mask_heads: int = 1      # Hm: 1 (shared by all heads) or H
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    d: int
+    frames: int
+    grid_h: int
+    grid_w: int
+    tile: int
+    dtype: int
+    mask: MaskSpec
+    seed: int
+    # rotations a run sweeps through (the step index for the tiny case,
+    # (layer + step) mod T for the video shapes)
+    rotations: tuple = field(default=(0,))
+
+    @property
+    def P(self) -> int:
+        return self.grid_h * self.grid_w
+
+    @property
+    def N(self) -> int:
+        return self.frames * self.P
+
+    @property
+    def num_tiles(self) -> int:
+        return -(-self.N // self.tile)
+
+    def with_rotation(self, r: int) -> "Workload":
+        return replace(self, mask=replace(self.mask, rotation=r))
+
+    def with_mask(self, **kw) -> "Workload":
+        return replace(self, mask=replace(self.mask, **kw))
+
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == DTYPE_F32 else torch.bfloat16
+
+
+# The five workloads.  Index 1 is the small case the oracle finishes in
+# seconds; index 2 is the 32 760-token video shape the headline metric uses.
+WORKLOADS = {
+    1: Workload("tiny_4x8x8_tile64", B=1, H=2, d=64, frames=4, grid_h=8, grid_w=8,
+                tile=64, dtype=DTYPE_F32,
+                mask=MaskSpec(MASK_WINDOW_ANCHOR, window=1, num_anchors=1),
+                seed=1001, rotations=(0, 1, 2, 3)),
+    2: Workload("video_21x30x52_window_anchor", B=1, H=12, d=128, frames=21,
+                grid_h=30, grid_w=52, tile=128, dtype=DTYPE_BF16,
+                mask=MaskSpec(MASK_WINDOW_ANCHOR, window=1, num_anchors=2),
+                seed=1002, rotations=tuple(range(21))),
+    3: Workload("video_21x30x52_static_p30", B=1, H=12, d=128, frames=21,
+                grid_h=30, grid_w=52, tile=128, dtype=DTYPE_BF16,
+                mask=MaskSpec(MASK_STATIC_RANDOM, seed=3,
+                              thresh24=thresh24_for_density(0.3),
+                              force_diagonal=1, mask_heads=12),
+                seed=1003),
+    4: Workload("long_84x30x52_window_anchor", B=1, H=12, d=128, frames=84,
+                grid_h=30, grid_w=52, tile=128, dtype=DTYPE_BF16,
+                mask=MaskSpec(MASK_WINDOW_ANCHOR, window=2, num_anchors=4),
+                seed=1004, rotations=tuple(range(84))),
+    5: Workload("dense_21x30x52_h40", B=1, H=40, d=128, frames=21, grid_h=30,
+                grid_w=52, tile=128, dtype=DTYPE_BF16,
+                mask=MaskSpec(MASK_DENSE), seed=1005),
+}
+
+
+def make_qkv(w: Workload, seed: Optional[int] = None, device: str = "cpu"):
+    """Q, K, V of shape [B, H, N, d] drawn i.i.d. N(0, 1) in float32 from a CPU
+    generator (seeded, in the order Q, K, V), then rounded to the workload's
+    dtype (round-to-nearest-even for bf16)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    shape = (w.B, w.H, w.N, w.d)
+    out = []
+    for _ in range(3):
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        out.append(x.to(w.torch_dtype()).to(device))
+    return tuple(out)
+
+
+def small_workload(frames=3, grid_h=5, grid_w=9, tile=64, d=64, H=2, B=1,
+                   dtype=DTYPE_BF16, mask: Optional[MaskSpec] = None,
+                   seed=77, name="small") -> Workload:
+    """A reduced workload for tests: several tiles and a ragged last tile."""
+    if mask is None:
+        mask = MaskSpec(MASK_WINDOW_ANCHOR, window=1, num_anchors=1)
+    return Workload(name, B=B, H=H, d=d, frames=frames, grid_h=grid_h,
+                    grid_w=grid_w, tile=tile, dtype=dtype, mask=mask, seed=seed)
