@@ -1,0 +1,244 @@
+"""Python binding of libbsattn (block-sparse video attention for MI355X).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the computation runs in the library's HIP kernels.
+The calls mirror include/bsattn.h:
+
+    build_mask(layout, params, mask)                    -> bsattn_build_mask
+    compact(mask, row_ptr, col_idx)                     -> bsattn_compact
+    fwd(q, k, v, o, row_ptr, col_idx, tile, ...)        -> bsattn_fwd
+
+plus small helpers that allocate the outputs with torch (make_mask,
+make_csr, attention).  There is no fallback: if libbsattn.so is missing or a
+call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbsattn.so")
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED = -2
+ERR_HIP = -3
+
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+
+MASK_WINDOW_ANCHOR = 0
+MASK_STATIC_RANDOM = 1
+MASK_DENSE = 2
+
+# Every symbol include/bsattn.h exports.
+EXPORTS = ("bsattn_version", "bsattn_status_string", "bsattn_last_error",
+           "bsattn_num_tiles", "bsattn_build_mask", "bsattn_compact",
+           "bsattn_fwd")
+
+
+class BsattnError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {detail or 'error'} (status {status})")
+        self.status = status
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("frames", ctypes.c_int32), ("grid_h", ctypes.c_int32),
+                ("grid_w", ctypes.c_int32), ("tile", ctypes.c_int32)]
+
+
+class MaskParams(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("num_anchors", ctypes.c_int32), ("rotation", ctypes.c_int32),
+                ("seed", ctypes.c_uint64), ("thresh24", ctypes.c_uint32),
+                ("force_diagonal", ctypes.c_int32),
+                ("mask_heads", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use; raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python __graft_entry__.py build` "
+            "(or block_sparse_attention_bsattn_amd/_build.py) first")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, u8p, i32p, vp = (ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                          ctypes.c_void_p)
+    L.bsattn_version.restype = ctypes.c_int
+    L.bsattn_version.argtypes = []
+    L.bsattn_status_string.restype = ctypes.c_char_p
+    L.bsattn_status_string.argtypes = [ctypes.c_int]
+    L.bsattn_last_error.restype = ctypes.c_char_p
+    L.bsattn_last_error.argtypes = []
+    L.bsattn_num_tiles.restype = i32
+    L.bsattn_num_tiles.argtypes = [ctypes.c_int64, i32]
+    L.bsattn_build_mask.restype = ctypes.c_int
+    L.bsattn_build_mask.argtypes = [ctypes.POINTER(Layout),
+                                    ctypes.POINTER(MaskParams), u8p, vp]
+    L.bsattn_compact.restype = ctypes.c_int
+    L.bsattn_compact.argtypes = [i32, i32, u8p, i32p, i32p, vp]
+    L.bsattn_fwd.restype = ctypes.c_int
+    L.bsattn_fwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                             i32, i32p, i32p, ctypes.c_float, vp]
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        detail = lib().bsattn_last_error().decode()
+        raise BsattnError(status, where, detail)
+
+
+def _stream(stream):
+    """hipStream_t handle: an int, a torch stream, or the current stream."""
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t, name, dtype=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, not {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def version() -> int:
+    return lib().bsattn_version()
+
+
+def num_tiles(tokens: int, tile: int) -> int:
+    return lib().bsattn_num_tiles(tokens, tile)
+
+
+def _params(kind, window=0, num_anchors=0, rotation=0, seed=0, thresh24=0,
+            force_diagonal=0, mask_heads=1) -> MaskParams:
+    return MaskParams(kind, window, num_anchors, rotation,
+                      seed & 0xFFFFFFFFFFFFFFFF, thresh24, int(force_diagonal),
+                      mask_heads)
+
+
+def build_mask(layout: Sequence[int], mask, stream=None, **params):
+    """bsattn_build_mask into the uint8 tensor `mask` [Hm, Tq, Tk].
+
+    layout = (frames, grid_h, grid_w, tile); params are the fields of
+    bsattn_mask_params (kind, window, num_anchors, rotation, seed, thresh24,
+    force_diagonal, mask_heads)."""
+    import torch
+    L = Layout(*[int(x) for x in layout])
+    P = _params(**params)
+    tiles = num_tiles(L.frames * L.grid_h * L.grid_w, L.tile)
+    if tuple(mask.shape) != (P.mask_heads, tiles, tiles):
+        raise ValueError(f"mask must have shape {(P.mask_heads, tiles, tiles)}")
+    st = lib().bsattn_build_mask(ctypes.byref(L), ctypes.byref(P),
+                                 _ptr(mask, "mask", torch.uint8), _stream(stream))
+    _check(st, "bsattn_build_mask")
+    return mask
+
+
+def compact(mask, row_ptr, col_idx, stream=None):
+    """bsattn_compact of mask [Hm, Tq, Tk] into row_ptr [Hm*Tq+1] and col_idx."""
+    import torch
+    Hm, Tq, Tk = mask.shape
+    rows = Hm * Tq
+    if row_ptr.numel() != rows + 1:
+        raise ValueError("row_ptr must hold Hm*Tq + 1 entries")
+    if col_idx.numel() < rows * Tk:
+        raise ValueError("col_idx must hold at least Hm*Tq*Tk entries")
+    st = lib().bsattn_compact(rows, Tk, _ptr(mask, "mask", torch.uint8),
+                              _ptr(row_ptr, "row_ptr", torch.int32),
+                              _ptr(col_idx, "col_idx", torch.int32),
+                              _stream(stream))
+    _check(st, "bsattn_compact")
+    return row_ptr, col_idx
+
+
+def fwd(q, k, v, o, row_ptr, col_idx, tile: int, mask_heads: int = 1,
+        lse=None, scale: float = 0.0, stream=None):
+    """bsattn_fwd: o = block-sparse attention of q, k, v ([B, H, N, d])."""
+    import torch
+    if q.dtype == torch.bfloat16:
+        dt = DTYPE_BF16
+    elif q.dtype == torch.float32:
+        dt = DTYPE_F32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if q.dim() != 4:
+        raise ValueError("q must have shape [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{name} must have the shape of q")
+    if lse is not None and tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must have shape [B, H, N]")
+    st = lib().bsattn_fwd(B, H, N, d, tile, dt, _ptr(q, "q", q.dtype),
+                          _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype),
+                          _ptr(o, "o", q.dtype),
+                          _ptr(lse, "lse", torch.float32, allow_none=True),
+                          mask_heads, _ptr(row_ptr, "row_ptr", torch.int32),
+                          _ptr(col_idx, "col_idx", torch.int32), float(scale),
+                          _stream(stream))
+    _check(st, "bsattn_fwd")
+    return o
+
+
+# ------------------------------------------------------- allocating helpers
+def make_mask(frames, grid_h, grid_w, tile, device="cuda", stream=None,
+              **params):
+    import torch
+    hm = params.get("mask_heads", 1)
+    t = num_tiles(frames * grid_h * grid_w, tile)
+    mask = torch.empty((hm, t, t), dtype=torch.uint8, device=device)
+    return build_mask((frames, grid_h, grid_w, tile), mask, stream=stream,
+                      **params)
+
+
+def make_csr(mask, stream=None):
+    import torch
+    Hm, Tq, Tk = mask.shape
+    row_ptr = torch.empty(Hm * Tq + 1, dtype=torch.int32, device=mask.device)
+    col_idx = torch.empty(max(Hm * Tq * Tk, 1), dtype=torch.int32,
+                          device=mask.device)
+    return compact(mask, row_ptr, col_idx, stream=stream)
+
+
+def attention(q, k, v, row_ptr, col_idx, tile, mask_heads=1, want_lse=False,
+              scale=0.0, stream=None):
+    import torch
+    o = torch.empty_like(q)
+    lse = None
+    if want_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fwd(q, k, v, o, row_ptr, col_idx, tile, mask_heads=mask_heads, lse=lse,
+        scale=scale, stream=stream)
+    return (o, lse) if want_lse else o
+
+
+def mask_params_of(spec) -> dict:
+    """Keyword parameters of build_mask from an object with the fields of
+    bsattn_mask_params (e.g. a workload's mask spec)."""
+    return dict(kind=spec.kind, window=spec.window,
+                num_anchors=spec.num_anchors, rotation=spec.rotation,
+                seed=spec.seed, thresh24=spec.thresh24,
+                force_diagonal=spec.force_diagonal,
+                mask_heads=spec.mask_heads)

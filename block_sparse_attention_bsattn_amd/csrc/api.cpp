@@ -1,0 +1,181 @@
+// Host side of the C ABI declared in include/bsattn.h: argument validation,
+// error reporting and dispatch to the kernel launchers.  Nothing is enqueued
+// unless every check passes; no device memory is allocated here.
+#include "bsattn.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "bsattn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return BSATTN_OK;
+}
+
+int hip_status(int err, const char* what) {
+  if (err == 0) return ok();
+  return fail(BSATTN_ERR_HIP, "%s: HIP error %d", what, err);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxCells = (int64_t)1 << 31;
+
+}  // namespace
+
+extern "C" {
+
+BSATTN_API int bsattn_version(void) { return 100; }
+
+BSATTN_API const char* bsattn_status_string(int status) {
+  switch (status) {
+    case BSATTN_OK: return "ok";
+    case BSATTN_ERR_INVALID_ARG: return "invalid argument";
+    case BSATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case BSATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+BSATTN_API const char* bsattn_last_error(void) { return g_last_error.c_str(); }
+
+BSATTN_API int32_t bsattn_num_tiles(int64_t tokens, int32_t tile) {
+  if (tokens < 0 || tile <= 0) return -1;
+  const int64_t t = (tokens + tile - 1) / tile;
+  return t > INT32_MAX ? -1 : (int32_t)t;
+}
+
+BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
+                                 const bsattn_mask_params* params,
+                                 uint8_t* mask, void* stream) {
+  if (!layout || !params || !mask)
+    return fail(BSATTN_ERR_INVALID_ARG, "build_mask: null pointer");
+  const bsattn_layout L = *layout;
+  const bsattn_mask_params M = *params;
+  if (L.frames < 1 || L.grid_h < 1 || L.grid_w < 1 || L.tile < 1)
+    return fail(BSATTN_ERR_INVALID_ARG,
+                "build_mask: frames, grid_h, grid_w and tile must be >= 1");
+  const int64_t per_frame = (int64_t)L.grid_h * L.grid_w;
+  const int64_t tokens = per_frame * L.frames;
+  if (tokens > INT32_MAX)
+    return fail(BSATTN_ERR_INVALID_ARG, "build_mask: more than 2^31-1 tokens");
+  if (M.kind < BSATTN_MASK_WINDOW_ANCHOR || M.kind > BSATTN_MASK_DENSE)
+    return fail(BSATTN_ERR_INVALID_ARG, "build_mask: unknown mask kind %d", M.kind);
+  if (M.mask_heads < 1)
+    return fail(BSATTN_ERR_INVALID_ARG, "build_mask: mask_heads must be >= 1");
+  if (M.kind == BSATTN_MASK_WINDOW_ANCHOR) {
+    if (M.window < 0)
+      return fail(BSATTN_ERR_INVALID_ARG, "build_mask: window must be >= 0");
+    if (M.num_anchors < 0 || M.num_anchors > L.frames)
+      return fail(BSATTN_ERR_INVALID_ARG,
+                  "build_mask: num_anchors must lie in [0, frames]");
+  }
+  if (M.kind == BSATTN_MASK_STATIC_RANDOM && M.thresh24 > (1u << 24))
+    return fail(BSATTN_ERR_INVALID_ARG, "build_mask: thresh24 exceeds 2^24");
+  const int32_t tiles = bsattn_num_tiles(tokens, L.tile);
+  const int64_t cells = (int64_t)M.mask_heads * tiles * tiles;
+  if (cells >= kMaxCells)
+    return fail(BSATTN_ERR_INVALID_ARG, "build_mask: mask has >= 2^31 cells");
+
+  bsattn::MaskLaunch a;
+  a.kind = M.kind;
+  a.frames = L.frames;
+  a.tokens_per_frame = (int32_t)per_frame;
+  a.tokens = (int32_t)tokens;
+  a.tile = L.tile;
+  a.tq = tiles;
+  a.tk = tiles;
+  a.mask_heads = M.mask_heads;
+  a.window = M.window;
+  a.num_anchors = M.num_anchors;
+  a.rotation = ((M.rotation % L.frames) + L.frames) % L.frames;
+  a.seed = M.seed;
+  a.thresh24 = M.thresh24;
+  a.force_diagonal = M.force_diagonal != 0;
+  return hip_status(bsattn::launch_build_mask(a, mask, stream), "build_mask");
+}
+
+BSATTN_API int bsattn_compact(int32_t rows, int32_t Tk, const uint8_t* mask,
+                              int32_t* row_ptr, int32_t* col_idx, void* stream) {
+  if (rows < 0 || Tk < 0)
+    return fail(BSATTN_ERR_INVALID_ARG, "compact: rows and Tk must be >= 0");
+  if ((int64_t)rows * Tk >= kMaxCells)
+    return fail(BSATTN_ERR_INVALID_ARG, "compact: mask has >= 2^31 cells");
+  if (!row_ptr) return fail(BSATTN_ERR_INVALID_ARG, "compact: null row_ptr");
+  if ((int64_t)rows * Tk > 0 && (!mask || !col_idx))
+    return fail(BSATTN_ERR_INVALID_ARG, "compact: null mask or col_idx");
+  return hip_status(bsattn::launch_compact(rows, Tk, mask, row_ptr, col_idx, stream),
+                    "compact");
+}
+
+BSATTN_API int bsattn_fwd(int32_t B, int32_t H, int32_t N, int32_t d,
+                          int32_t tile, int32_t dtype, const void* q,
+                          const void* k, const void* v, void* o, float* lse,
+                          int32_t mask_heads, const int32_t* row_ptr,
+                          const int32_t* col_idx, float scale, void* stream) {
+  if (B < 0 || H < 0 || N < 0 || d < 0)
+    return fail(BSATTN_ERR_INVALID_ARG, "fwd: B, H, N and d must be >= 0");
+  if (d != 64 && d != 128)
+    return fail(BSATTN_ERR_UNSUPPORTED, "fwd: head dim %d (supported: 64, 128)", d);
+  if (tile != 64 && tile != 128)
+    return fail(BSATTN_ERR_UNSUPPORTED, "fwd: tile %d (supported: 64, 128)", tile);
+  if (dtype != BSATTN_DTYPE_BF16 && dtype != BSATTN_DTYPE_F32)
+    return fail(BSATTN_ERR_UNSUPPORTED, "fwd: dtype %d", dtype);
+  if ((int64_t)B * H * N == 0) return ok();
+  if (B > 65535 || H > 65535)
+    return fail(BSATTN_ERR_INVALID_ARG, "fwd: B and H must be <= 65535");
+  if (mask_heads != 1 && mask_heads != H)
+    return fail(BSATTN_ERR_INVALID_ARG, "fwd: mask_heads %d must be 1 or H=%d",
+                mask_heads, H);
+  if (!q || !k || !v || !o || !row_ptr || !col_idx)
+    return fail(BSATTN_ERR_INVALID_ARG, "fwd: null pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(BSATTN_ERR_INVALID_ARG, "fwd: q, k, v, o must be 16-byte aligned");
+  if (!(scale == scale) || isinf(scale))
+    return fail(BSATTN_ERR_INVALID_ARG, "fwd: scale must be finite");
+  const int32_t tiles = bsattn_num_tiles(N, tile);
+  const int64_t cells = (int64_t)mask_heads * tiles * tiles;
+  if (cells >= kMaxCells)
+    return fail(BSATTN_ERR_INVALID_ARG, "fwd: tile mask has >= 2^31 cells");
+
+  bsattn::FwdLaunch a;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.tile = tile;
+  a.dtype = dtype;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.mask_heads = mask_heads;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.tiles = tiles;
+  a.col_cap = cells;
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  return hip_status(bsattn::launch_fwd(a, stream), "fwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Internal launch entry points shared by the host API layer and the kernel
+// translation units.  Arguments are already validated by the caller.
+#pragma once
+
+#include <stdint.h>
+
+namespace bsattn {
+
+struct MaskLaunch {
+  int32_t kind;
+  int32_t frames, tokens_per_frame, tokens, tile;
+  int32_t tq, tk, mask_heads;
+  int32_t window, num_anchors, rotation;  // rotation already in [0, frames)
+  uint64_t seed;
+  uint32_t thresh24;
+  int32_t force_diagonal;
+};
+
+struct FwdLaunch {
+  int32_t B, H, N, d, tile, dtype;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int32_t mask_heads;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int32_t tiles;      // Tq = Tk
+  int64_t col_cap;    // entries of col_idx that may be read
+  float scale_log2;   // softmax scale * log2(e)
+};
+
+// Each returns a hipError_t value (0 = success).
+int launch_build_mask(const MaskLaunch& a, uint8_t* mask, void* stream);
+int launch_compact(int32_t rows, int32_t tk, const uint8_t* mask,
+                   int32_t* row_ptr, int32_t* col_idx, void* stream);
+int launch_fwd(const FwdLaunch& a, void* stream);
+
+}  // namespace bsattn

@@ -1,0 +1,85 @@
+// Tile-mask builder.
+//
+// LVSA page, "Meccanismo Core": a query frame t attends to A(t) = G u W(t),
+// the local window W(t) plus the rotating global anchor frames G.  The mask is
+// built at tile granularity: tile pair (i, j) is active when some frame
+// covered by query tile i may attend to some frame covered by key tile j.
+//
+// The frames a tile covers form a contiguous range [lo, hi], so the window
+// part reduces to the gap between two integer intervals:
+//   exists t in [a, b], f in [c, e] with |f - t| <= w
+//   <=>  max(0, c - b, a - e) <= w.
+// The anchor part is independent of the query tile: some anchor frame
+// g_k = (r + floor(k*T/n_a)) mod T lies in the key tile's range.
+//
+// Static mode (CalibAtt page, "B. Fase di Inferenza": the block lists are
+// precomputed and deterministic) draws one SplitMix64 value per cell
+// c = (h*Tq + i)*Tk + j: the (c+1)-th output of the generator seeded with
+// `seed` (Steele, Lea and Flood, OOPSLA 2014).  The cell is active when the
+// output's top 24 bits are below thresh24, or on the diagonal when forced.
+#include <hip/hip_runtime.h>
+
+#include "bsattn_internal.h"
+
+namespace bsattn {
+namespace {
+
+__device__ __forceinline__ uint64_t splitmix64_at(uint64_t seed, uint64_t n) {
+  uint64_t z = seed + n * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__device__ __forceinline__ void frame_range(int tile_idx, int tile, int tokens,
+                                            int per_frame, int& lo, int& hi) {
+  const int first = tile_idx * tile;
+  const int last = min(first + tile, tokens) - 1;
+  lo = first / per_frame;
+  hi = last / per_frame;
+}
+
+__global__ void build_mask_kernel(MaskLaunch a, uint8_t* __restrict__ mask) {
+  const int64_t total = (int64_t)a.mask_heads * a.tq * a.tk;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
+       c += stride) {
+    const int j = (int)(c % a.tk);
+    const int64_t hi_row = c / a.tk;
+    const int i = (int)(hi_row % a.tq);
+    uint8_t on = 0;
+    if (a.kind == 0) {
+      int qa, qb, ka, kb;
+      frame_range(i, a.tile, a.tokens, a.tokens_per_frame, qa, qb);
+      frame_range(j, a.tile, a.tokens, a.tokens_per_frame, ka, kb);
+      const int gap = max(0, max(ka - qb, qa - kb));
+      on = gap <= a.window;
+      for (int k = 0; k < a.num_anchors && !on; ++k) {
+        const int g = (int)((a.rotation + ((int64_t)k * a.frames) / a.num_anchors) %
+                            a.frames);
+        on = (g >= ka) && (g <= kb);
+      }
+    } else if (a.kind == 1) {
+      const uint64_t z = splitmix64_at(a.seed, (uint64_t)c + 1);
+      on = ((uint32_t)(z >> 40) < a.thresh24) || (a.force_diagonal && i == j);
+    } else {
+      on = 1;
+    }
+    mask[c] = on;
+  }
+}
+
+}  // namespace
+
+int launch_build_mask(const MaskLaunch& a, uint8_t* mask, void* stream) {
+  const int64_t total = (int64_t)a.mask_heads * a.tq * a.tk;
+  if (total == 0) return hipSuccess;
+  const int block = 256;
+  int64_t grid = (total + block - 1) / block;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(build_mask_kernel, dim3((unsigned)grid), dim3(block), 0,
+                     (hipStream_t)stream, a, mask);
+  return hipGetLastError();
+}
+
+}  // namespace bsattn

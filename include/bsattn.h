@@ -1,0 +1,155 @@
+/*
+ * bsattn -- block-sparse softmax self-attention over video tokens, for
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The problem (LVSA page, "Meccanismo Core"; CalibAtt page, "A. Fase di
+ * Calibrazione" and "B. Fase di Inferenza"): Q, K, V of shape [B, H, N, d]
+ * hold the tokens of a video latent of T frames on a grid_h x grid_w grid,
+ * flattened frame-major (token n = f*P + y*grid_w + x, P = grid_h*grid_w,
+ * N = T*P).  The attention matrix is cut into square tiles of `tile` tokens;
+ * a tile mask says which key tiles each query tile reads, and only those
+ * tiles are computed.  The output O has the shape of Q.
+ *
+ * Pipeline: bsattn_build_mask -> bsattn_compact -> bsattn_fwd.
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument named "device" is device memory on the current
+ *     HIP device, owned by the caller.  The library never allocates, frees or
+ *     copies caller memory and never synchronises.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued asynchronously; results are valid in stream order.
+ *   - Every call validates its arguments on the host first.  On error it
+ *     enqueues nothing and returns a negative bsattn_status; the detail is
+ *     available from bsattn_last_error() (per thread).
+ *   - Results are deterministic: repeated calls on the same inputs give
+ *     bitwise-identical outputs.
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSATTN_API __attribute__((visibility("default")))
+
+typedef enum {
+  BSATTN_OK = 0,
+  BSATTN_ERR_INVALID_ARG = -1, /* null pointer, inconsistent sizes, Hm not in {1,H} */
+  BSATTN_ERR_UNSUPPORTED = -2, /* head dim, tile or dtype outside the built set */
+  BSATTN_ERR_HIP = -3          /* the HIP runtime rejected a launch */
+} bsattn_status;
+
+typedef enum { BSATTN_DTYPE_BF16 = 0, BSATTN_DTYPE_F32 = 1 } bsattn_dtype;
+
+typedef enum {
+  BSATTN_MASK_WINDOW_ANCHOR = 0, /* LVSA local window + rotating global anchors */
+  BSATTN_MASK_STATIC_RANDOM = 1, /* seeded stand-in for a calibrated static mask */
+  BSATTN_MASK_DENSE = 2          /* all tiles active (full attention) */
+} bsattn_mask_kind;
+
+/* Token geometry of the video latent.  N = frames*grid_h*grid_w; the number
+ * of query tiles and of key tiles is Tq = Tk = ceil(N / tile). */
+typedef struct {
+  int32_t frames; /* T >= 1 */
+  int32_t grid_h; /* >= 1 */
+  int32_t grid_w; /* >= 1 */
+  int32_t tile;   /* BT, in tokens, >= 1 (bsattn_fwd supports 64 and 128) */
+} bsattn_layout;
+
+/* Mask parameters; fields a mode does not use are ignored.
+ *
+ * WINDOW_ANCHOR (LVSA page, "Meccanismo Core"): query frame t attends to
+ *   A(t) = G u W(t), W(t) = {f in [0,T) : |f - t| <= window} and
+ *   G = {(r + floor(k*T/num_anchors)) mod T : 0 <= k < num_anchors}, with
+ *   r = rotation reduced mod T (the caller picks r per denoising step and
+ *   layer; the page shifts the anchors with the step).  Tile pair (i, j) is
+ *   active when some frame covered by query tile i attends to some frame
+ *   covered by key tile j.  All mask_heads slices are identical.
+ * STATIC_RANDOM (CalibAtt page, "B. Fase di Inferenza": a precomputed,
+ *   deterministic per-head block list): cell c = (h*Tq + i)*Tk + j is active
+ *   when the top 24 bits of the (c+1)-th SplitMix64 output for `seed` are
+ *   below thresh24 (thresh24 = floor(p * 2^24) for density p), or when i == j
+ *   and force_diagonal != 0.
+ * DENSE: every cell active. */
+typedef struct {
+  int32_t kind;           /* bsattn_mask_kind */
+  int32_t window;         /* w >= 0, in frames */
+  int32_t num_anchors;    /* 0 <= n_a <= T */
+  int32_t rotation;       /* any integer; reduced mod T */
+  uint64_t seed;          /* STATIC_RANDOM */
+  uint32_t thresh24;      /* STATIC_RANDOM, <= 2^24 */
+  int32_t force_diagonal; /* STATIC_RANDOM */
+  int32_t mask_heads;     /* Hm >= 1: number of mask slices (1 = shared by all heads) */
+} bsattn_mask_params;
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+BSATTN_API int bsattn_version(void);
+
+/* Short static text for a status code. */
+BSATTN_API const char* bsattn_status_string(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+BSATTN_API const char* bsattn_last_error(void);
+
+/* Number of tiles along one side: ceil(tokens / tile); -1 on bad input. */
+BSATTN_API int32_t bsattn_num_tiles(int64_t tokens, int32_t tile);
+
+/* Build the tile mask.
+ *   layout, params: host structs (read during the call only).
+ *   mask: device uint8 [Hm, Tq, Tk], row-major, Hm = params->mask_heads;
+ *         every byte is written (0 or 1).
+ * Errors: INVALID_ARG on null pointers, non-positive sizes, window < 0,
+ * num_anchors outside [0, T], thresh24 > 2^24, mask_heads < 1, an unknown
+ * kind, or Hm*Tq*Tk >= 2^31. */
+BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
+                                 const bsattn_mask_params* params,
+                                 uint8_t* mask, void* stream);
+
+/* Turn a tile mask into per-query-tile lists of active key tiles (CSR over
+ * the mask viewed as a [rows, Tk] matrix, rows = Hm*Tq, row r = h*Tq + i).
+ *   mask:    device uint8 [rows, Tk]; any nonzero byte counts as active.
+ *   row_ptr: device int32 [rows + 1]; row_ptr[0] = 0, row_ptr[r+1] =
+ *            row_ptr[r] + (active tiles of row r); row_ptr[rows] = nnz.
+ *   col_idx: device int32, capacity >= nnz (rows*Tk always suffices);
+ *            entries row_ptr[r] .. row_ptr[r+1]-1 hold row r's active key
+ *            tiles in ascending order.
+ * CalibAtt page, "B. Fase di Inferenza" (precomputed block lists); the list
+ * stores the active tiles, the complement of the page's skip list.
+ * Errors: INVALID_ARG on null pointers, rows < 0, Tk < 0, rows*Tk >= 2^31. */
+BSATTN_API int bsattn_compact(int32_t rows, int32_t Tk, const uint8_t* mask,
+                              int32_t* row_ptr, int32_t* col_idx, void* stream);
+
+/* Block-sparse attention forward.
+ *   q, k, v: device [B, H, N, d] contiguous, element type `dtype`
+ *            (BF16 or F32; F32 inputs are rounded to bf16 for the matrix
+ *            products, which accumulate in fp32).
+ *   o:       device [B, H, N, d] of the same dtype (written).
+ *   lse:     device float [B, H, N] or NULL; natural-log sum of exp of the
+ *            scaled scores over the active keys (-inf for a row with none).
+ *   mask_heads: Hm, 1 or H; head h reads CSR slice (Hm == H ? h : 0).  All
+ *            batch entries share the CSR.
+ *   row_ptr, col_idx: device CSR from bsattn_compact for rows = Hm*Tq,
+ *            Tk = Tq = ceil(N/tile).  Key-tile indices outside [0, Tk) are
+ *            skipped; row_ptr values are read as written by bsattn_compact.
+ *   scale:   softmax scale; <= 0 selects 1/sqrt(d).
+ * For each query row n: O[n] = softmax(scale * q_n K_A^T) V_A over the keys A
+ * of its active tiles (keys >= N never enter); O[n] = 0 when A is empty.
+ * Supported: d in {64, 128}, tile in {64, 128}.  B*H*N == 0 is a no-op.
+ * Errors: INVALID_ARG (null pointers, negative sizes, Hm not in {1, H},
+ * B*H*N*d >= 2^31 elements per tensor), UNSUPPORTED (d, tile, dtype),
+ * HIP (launch failure). */
+BSATTN_API int bsattn_fwd(int32_t B, int32_t H, int32_t N, int32_t d,
+                          int32_t tile, int32_t dtype, const void* q,
+                          const void* k, const void* v, void* o, float* lse,
+                          int32_t mask_heads, const int32_t* row_ptr,
+                          const int32_t* col_idx, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H */

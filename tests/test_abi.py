@@ -1,0 +1,123 @@
+"""The C-ABI library loads, exports every declared symbol and rejects bad
+arguments on the host before touching a GPU (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_bsattn_amd as bs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bs.LIB_PATH),
+                                reason="libbsattn.so not built")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"BSATTN_API\s+[\w\s\*]+?\b(bsattn_\w+)\s*\(",
+                                 text)))
+
+
+def test_header_lists_the_pipeline():
+    syms = declared_symbols()
+    for name in ("bsattn_build_mask", "bsattn_compact", "bsattn_fwd"):
+        assert name in syms
+    assert sorted(bs.EXPORTS) == syms
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(bs.LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+
+
+def test_version_and_strings():
+    assert bs.version() >= 100
+    L = bs.lib()
+    assert L.bsattn_status_string(0) == b"ok"
+    assert L.bsattn_status_string(-1) == b"invalid argument"
+    assert L.bsattn_status_string(-2) == b"unsupported configuration"
+    assert L.bsattn_status_string(-3) == b"HIP runtime error"
+    assert L.bsattn_status_string(7) == b"unknown status"
+
+
+def test_num_tiles():
+    assert bs.num_tiles(32760, 128) == 256
+    assert bs.num_tiles(131040, 128) == 1024
+    assert bs.num_tiles(256, 64) == 4
+    assert bs.num_tiles(0, 64) == 0
+    assert bs.num_tiles(1, 128) == 1
+    assert bs.num_tiles(10, 0) == -1
+    assert bs.num_tiles(-1, 64) == -1
+
+
+def _fwd(**kw):
+    args = dict(B=1, H=2, N=100, d=64, tile=64, dtype=0, q=8, k=8, v=8, o=8,
+                lse=None, mask_heads=1, row_ptr=8, col_idx=8, scale=0.0,
+                stream=None)
+    args.update(kw)
+    L = bs.lib()
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.bsattn_fwd(args["B"], args["H"], args["N"], args["d"], args["tile"],
+                        args["dtype"], p(args["q"]), p(args["k"]), p(args["v"]),
+                        p(args["o"]), p(args["lse"]), args["mask_heads"],
+                        p(args["row_ptr"]), p(args["col_idx"]), args["scale"],
+                        None)
+
+
+def test_fwd_rejects_bad_arguments_without_launching():
+    assert _fwd(d=96) == bs.ERR_UNSUPPORTED
+    assert b"head dim" in bs.lib().bsattn_last_error()
+    assert _fwd(tile=32) == bs.ERR_UNSUPPORTED
+    assert _fwd(dtype=5) == bs.ERR_UNSUPPORTED
+    assert _fwd(N=-1) == bs.ERR_INVALID_ARG
+    assert _fwd(mask_heads=3) == bs.ERR_INVALID_ARG
+    assert _fwd(q=None) == bs.ERR_INVALID_ARG
+    assert _fwd(col_idx=None) == bs.ERR_INVALID_ARG
+    assert _fwd(q=9) == bs.ERR_INVALID_ARG       # misaligned
+    assert b"aligned" in bs.lib().bsattn_last_error()
+    assert _fwd(scale=float("nan")) == bs.ERR_INVALID_ARG
+    assert _fwd(H=70000) == bs.ERR_INVALID_ARG
+    # empty problems are a successful no-op, even with null pointers
+    assert _fwd(N=0, q=None, k=None, v=None, o=None) == bs.OK
+    assert _fwd(B=0) == bs.OK
+    assert bs.lib().bsattn_last_error() == b""
+
+
+def test_build_mask_rejects_bad_arguments():
+    L = bs.lib()
+    ok_layout = bs.Layout(4, 8, 8, 64)
+    ok_params = bs.MaskParams(0, 1, 1, 0, 0, 0, 0, 1)
+    m = ctypes.c_void_p(64)
+
+    def call(layout=ok_layout, params=ok_params, mask=m):
+        return L.bsattn_build_mask(None if layout is None else ctypes.byref(layout),
+                                   None if params is None else ctypes.byref(params),
+                                   mask, None)
+
+    assert call(layout=None) == bs.ERR_INVALID_ARG
+    assert call(params=None) == bs.ERR_INVALID_ARG
+    assert call(mask=None) == bs.ERR_INVALID_ARG
+    assert call(layout=bs.Layout(0, 8, 8, 64)) == bs.ERR_INVALID_ARG
+    assert call(layout=bs.Layout(4, 8, 8, 0)) == bs.ERR_INVALID_ARG
+    assert call(params=bs.MaskParams(3, 1, 1, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
+    assert call(params=bs.MaskParams(0, -1, 1, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
+    assert call(params=bs.MaskParams(0, 1, 5, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
+    assert call(params=bs.MaskParams(1, 0, 0, 0, 0, (1 << 24) + 1, 0, 1)) == \
+        bs.ERR_INVALID_ARG
+    assert call(params=bs.MaskParams(2, 0, 0, 0, 0, 0, 0, 0)) == bs.ERR_INVALID_ARG
+    assert call(layout=bs.Layout(1 << 20, 64, 64, 64)) == bs.ERR_INVALID_ARG
+
+
+def test_compact_rejects_bad_arguments():
+    L = bs.lib()
+    p = ctypes.c_void_p(64)
+    assert L.bsattn_compact(-1, 4, p, p, p, None) == bs.ERR_INVALID_ARG
+    assert L.bsattn_compact(4, -1, p, p, p, None) == bs.ERR_INVALID_ARG
+    assert L.bsattn_compact(4, 4, p, None, p, None) == bs.ERR_INVALID_ARG
+    assert L.bsattn_compact(4, 4, None, p, p, None) == bs.ERR_INVALID_ARG
+    assert L.bsattn_compact(1 << 16, 1 << 16, p, p, p, None) == bs.ERR_INVALID_ARG

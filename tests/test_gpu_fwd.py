@@ -1,0 +1,196 @@
+"""GPU forward against the float64 oracle.
+
+Small workloads are compared on every output element; the full-size video
+workloads, in the launch configuration the benchmark times, on sampled query
+rows that the oracle computes one by one (every query tile's first and last
+row plus seeded random rows, for every head)."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_bsattn_amd as bs
+import oracle
+import workloads as W
+from parity_util import (assert_close, check_mask_csr, gpu_mask_csr,
+                         oracle_mask, to64)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(w, q=None, k=None, v=None, want_lse=True):
+    mask, rp, ci = gpu_mask_csr(w)
+    if q is None:
+        q, k, v = W.make_qkv(w, device="cuda")
+    out = bs.attention(q, k, v, rp, ci, w.tile, mask_heads=w.mask.mask_heads,
+                       want_lse=want_lse)
+    torch.cuda.synchronize()
+    return (q, k, v, mask, rp, ci) + (out if want_lse else (out, None))
+
+
+def full_parity(w, lse_tol=1e-3):
+    q, k, v, mask, rp, ci, o, lse = run_gpu(w)
+    m_ref = check_mask_csr(w, mask, rp, ci)
+    o_ref, lse_ref = oracle.block_sparse_attention(q.cpu(), k.cpu(), v.cpu(),
+                                                   m_ref, w.tile, workers=8)
+    assert_close(w.name, to64(o), o_ref, to64(lse), lse_ref, lse_tol=lse_tol)
+    return o, lse
+
+
+@pytest.mark.parametrize("r", [0, 1, 2, 3])
+def test_tiny_config_every_step(r):
+    # fp32 inputs are rounded to bf16 for the matrix products, so the scores
+    # (and the log-sum-exp) carry bf16 input rounding: |dS| ~ 2^-8 |q||k|/sqrt(d)
+    full_parity(W.WORKLOADS[1].with_rotation(r), lse_tol=2e-2)
+
+
+SMALL = [
+    # name, frames, gh, gw, tile, d, H, B, dtype, mask
+    ("ragged_t64_d64", 3, 5, 9, 64, 64, 2, 1, W.DTYPE_BF16,
+     W.MaskSpec(W.MASK_WINDOW_ANCHOR, window=1, num_anchors=1, rotation=2)),
+    ("ragged_t64_d128", 5, 7, 11, 64, 128, 3, 2, W.DTYPE_BF16,
+     W.MaskSpec(W.MASK_WINDOW_ANCHOR, window=0, num_anchors=2, rotation=1)),
+    ("ragged_t128_d128", 5, 9, 13, 128, 128, 2, 1, W.DTYPE_BF16,
+     W.MaskSpec(W.MASK_WINDOW_ANCHOR, window=1, num_anchors=1, rotation=4)),
+    ("ragged_t128_d64", 7, 9, 13, 128, 64, 2, 2, W.DTYPE_BF16,
+     W.MaskSpec(W.MASK_WINDOW_ANCHOR, window=1, num_anchors=2, rotation=3)),
+    ("static_perhead_t128", 6, 10, 13, 128, 128, 3, 2, W.DTYPE_BF16,
+     W.MaskSpec(W.MASK_STATIC_RANDOM, seed=9, thresh24=W.thresh24_for_density(0.4),
+                force_diagonal=1, mask_heads=3)),
+    ("static_shared_t64", 6, 10, 13, 64, 64, 2, 1, W.DTYPE_BF16,
+     W.MaskSpec(W.MASK_STATIC_RANDOM, seed=10, thresh24=W.thresh24_for_density(0.3),
+                force_diagonal=1, mask_heads=1)),
+    ("dense_f32_t128_d128", 4, 8, 9, 128, 128, 2, 1, W.DTYPE_F32,
+     W.MaskSpec(W.MASK_DENSE)),
+    ("dense_f32_t64_d128", 4, 8, 9, 64, 128, 1, 1, W.DTYPE_F32,
+     W.MaskSpec(W.MASK_DENSE)),
+    ("exact_tiles_t128", 4, 8, 16, 128, 128, 2, 1, W.DTYPE_BF16,
+     W.MaskSpec(W.MASK_WINDOW_ANCHOR, window=1, num_anchors=1)),
+    ("single_token", 1, 1, 1, 128, 128, 1, 1, W.DTYPE_BF16,
+     W.MaskSpec(W.MASK_DENSE)),
+    ("one_partial_tile", 1, 5, 7, 64, 64, 2, 1, W.DTYPE_BF16,
+     W.MaskSpec(W.MASK_DENSE)),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_full_parity(case):
+    name, T, gh, gw, tile, d, H, B, dt, mask = case
+    w = W.small_workload(frames=T, grid_h=gh, grid_w=gw, tile=tile, d=d, H=H,
+                         B=B, dtype=dt, mask=mask, name=name,
+                         seed=zlib.crc32(name.encode()) & 0xFFFF)
+    full_parity(w, lse_tol=2e-2 if dt == W.DTYPE_F32 else 1e-3)
+
+
+def test_empty_rows():
+    """Rows whose active list is empty give O = 0 and lse = -inf."""
+    w = W.small_workload(frames=6, grid_h=10, grid_w=13, tile=64, d=64, H=2,
+                         mask=W.MaskSpec(W.MASK_STATIC_RANDOM, seed=4,
+                                         thresh24=W.thresh24_for_density(0.15),
+                                         force_diagonal=0, mask_heads=2))
+    q, k, v, mask, rp, ci, o, lse = run_gpu(w)
+    m_ref = check_mask_csr(w, mask, rp, ci)
+    assert (m_ref.sum(axis=2) == 0).any(), "case needs an empty row"
+    o_ref, lse_ref = oracle.block_sparse_attention(q.cpu(), k.cpu(), v.cpu(),
+                                                   m_ref, w.tile)
+    assert_close(w.name, to64(o), o_ref, to64(lse), lse_ref)
+    w0 = w.with_mask(thresh24=0)
+    q, k, v, mask, rp, ci, o, lse = run_gpu(w0, q, k, v)
+    assert int(rp[-1]) == 0
+    assert (o == 0).all() and torch.isneginf(lse).all()
+
+
+def test_scale_argument():
+    w = W.small_workload(frames=3, grid_h=8, grid_w=9, tile=64, d=128, H=2)
+    mask, rp, ci = gpu_mask_csr(w)
+    q, k, v = W.make_qkv(w, device="cuda")
+    o = bs.attention(q, k, v, rp, ci, w.tile, scale=0.21)
+    torch.cuda.synchronize()
+    o_ref, _ = oracle.block_sparse_attention(q.cpu(), k.cpu(), v.cpu(),
+                                             oracle_mask(w), w.tile, scale=0.21)
+    assert_close("scale=0.21", to64(o), o_ref)
+
+
+def test_skipped_tiles_are_never_read():
+    """K/V tiles that no query tile reads are filled with NaN; the output must
+    stay finite and bitwise equal to the unpoisoned run."""
+    T, gh, gw, tile = 9, 10, 13, 64
+    w = W.small_workload(frames=T, grid_h=gh, grid_w=gw, tile=tile, d=128, H=2,
+                         mask=W.MaskSpec(W.MASK_WINDOW_ANCHOR, window=0,
+                                         num_anchors=0))
+    q, k, v, mask, rp, ci, o, lse = run_gpu(w)
+    m_ref = oracle_mask(w)
+    # keep only tiles 0..3 active as keys for every query tile
+    m_ref[:, :, 4:] = 0
+    m_dev = torch.from_numpy(m_ref).cuda()
+    rp, ci = bs.make_csr(m_dev)
+    o1, lse1 = bs.attention(q, k, v, rp, ci, tile, want_lse=True)
+    kp, vp = k.clone(), v.clone()
+    kp[:, :, 4 * tile:] = float("nan")
+    vp[:, :, 4 * tile:] = float("nan")
+    o2, lse2 = bs.attention(q, kp, vp, rp, ci, tile, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o2.float()).all()
+    assert torch.equal(o1, o2) and torch.equal(lse1, lse2)
+    o_ref, _ = oracle.block_sparse_attention(q.cpu(), k.cpu(), v.cpu(), m_ref,
+                                             tile)
+    assert_close("poisoned", to64(o2), o_ref)
+
+
+def test_constant_and_tile_id_values():
+    w = W.small_workload(frames=5, grid_h=9, grid_w=13, tile=128, d=128, H=2,
+                         mask=W.MaskSpec(W.MASK_WINDOW_ANCHOR, window=1,
+                                         num_anchors=1, rotation=3))
+    q, k, _ = W.make_qkv(w, device="cuda")
+    v1 = torch.ones_like(q)
+    _, _, _, mask, rp, ci, o, _ = run_gpu(w, q, k, v1)
+    assert torch.allclose(o.float(), torch.ones_like(o, dtype=torch.float32),
+                          atol=1e-2, rtol=0)
+    tid = (torch.arange(w.N, device="cuda") // w.tile).to(q.dtype)
+    vt = tid[None, None, :, None].expand_as(q).contiguous()
+    o = bs.attention(q, k, vt, rp, ci, w.tile)
+    torch.cuda.synchronize()
+    m = mask.cpu().numpy()[0]
+    of = o.float().cpu().numpy()
+    for n in range(w.N):
+        act = np.nonzero(m[n // w.tile])[0]
+        assert act.min() - 0.05 <= of[0, 0, n, 0] <= act.max() + 0.05
+
+
+def test_deterministic():
+    w = W.WORKLOADS[3]
+    q, k, v, mask, rp, ci, o1, l1 = run_gpu(w)
+    o2, l2 = bs.attention(q, k, v, rp, ci, w.tile, mask_heads=w.mask.mask_heads,
+                          want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def sample_rows(w, per_tile_random=1, seed=0):
+    g = np.random.default_rng(seed)
+    rows = set()
+    for i in range(w.num_tiles):
+        lo = i * w.tile
+        hi = min(lo + w.tile, w.N) - 1
+        rows.update((lo, hi))
+        rows.update(int(x) for x in g.integers(lo, hi + 1, per_tile_random))
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("cfg,stride", [(2, 1), (3, 1), (4, 4), (5, 2)])
+def test_full_size_sampled_rows(cfg, stride):
+    """Full-size workload on the GPU; the oracle computes sampled rows (every
+    `stride`-th query tile's first and last row plus one random row)."""
+    w = W.WORKLOADS[cfg]
+    q, k, v, mask, rp, ci, o, lse = run_gpu(w)
+    m_ref = check_mask_csr(w, mask, rp, ci)
+    rows = sample_rows(w)
+    keep = (rows // w.tile) % stride == 0
+    keep |= rows >= (w.num_tiles - 1) * w.tile       # always the ragged tail
+    rows = rows[keep]
+    o_ref, lse_ref = oracle.block_sparse_attention_rows(
+        q.cpu(), k.cpu(), v.cpu(), m_ref, w.tile, rows, workers=16)
+    idx = torch.from_numpy(rows).cuda()
+    assert_close(f"{w.name} ({len(rows)} rows x {w.B * w.H} heads)",
+                 to64(o[:, :, idx]), o_ref, to64(lse[:, :, idx]), lse_ref)

@@ -1,0 +1,91 @@
+"""GPU mask builder and compaction against the oracle, bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_bsattn_amd as bs
+import oracle
+import workloads as W
+from conftest import read_golden
+from parity_util import check_mask_csr, gpu_mask_csr
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_configs_every_rotation(cfg):
+    w = W.WORKLOADS[cfg]
+    for r in w.rotations:
+        wr = w.with_rotation(r)
+        mask, rp, ci = gpu_mask_csr(wr)
+        check_mask_csr(wr, mask, rp, ci)
+
+
+def test_rotation_reduced_mod_T():
+    w = W.WORKLOADS[2]
+    for r in (-1, 21, 21 * 5 + 4, -22):
+        wr = w.with_rotation(r)
+        mask, rp, ci = gpu_mask_csr(wr)
+        check_mask_csr(wr, mask, rp, ci)
+
+
+def test_hand_enumerated_misaligned_layout():
+    lines = read_golden("misaligned_window_anchor_mask.txt")
+    hdr = lines[0].split()
+    kv = dict(zip(hdr[0::2], map(int, hdr[1::2])))
+    want = np.array([[int(c) for c in ln] for ln in lines[1:]], dtype=np.uint8)
+    mask = bs.make_mask(kv["frames"], kv["grid_h"], kv["grid_w"], kv["tile"],
+                        kind=0, window=kv["window"], num_anchors=kv["anchors"],
+                        rotation=kv["rotation"])
+    assert np.array_equal(mask.cpu().numpy()[0], want)
+
+
+@pytest.mark.parametrize("T,gh,gw,BT,w,na,r,hm", [
+    (5, 1, 3, 2, 1, 2, 3, 1), (7, 1, 5, 4, 0, 2, 6, 2), (9, 3, 3, 5, 2, 3, 7, 1),
+    (3, 1, 7, 3, 0, 0, 0, 1), (8, 1, 3, 16, 1, 2, 5, 3), (33, 4, 5, 64, 3, 5, 11, 1),
+    (13, 30, 52, 128, 0, 13, 2, 1), (40, 2, 2, 1, 2, 4, 9, 1),
+])
+def test_window_anchor_odd_layouts(T, gh, gw, BT, w, na, r, hm):
+    wl = W.small_workload(frames=T, grid_h=gh, grid_w=gw, tile=BT,
+                          mask=W.MaskSpec(W.MASK_WINDOW_ANCHOR, window=w,
+                                          num_anchors=na, rotation=r,
+                                          mask_heads=hm))
+    mask, rp, ci = gpu_mask_csr(wl)
+    check_mask_csr(wl, mask, rp, ci)
+
+
+@pytest.mark.parametrize("hm,seed,p,diag", [(1, 0, 0.5, 0), (3, 12345, 0.1, 1),
+                                            (2, 2**64 - 1, 0.9, 1), (4, 7, 0.0, 0),
+                                            (1, 7, 1.0, 0)])
+def test_static_masks(hm, seed, p, diag):
+    wl = W.small_workload(frames=11, grid_h=10, grid_w=13, tile=64,
+                          mask=W.MaskSpec(W.MASK_STATIC_RANDOM, seed=seed,
+                                          thresh24=W.thresh24_for_density(p),
+                                          force_diagonal=diag, mask_heads=hm))
+    mask, rp, ci = gpu_mask_csr(wl)
+    check_mask_csr(wl, mask, rp, ci)
+
+
+def test_compact_on_arbitrary_masks():
+    """Compaction of masks the builder cannot produce (any nonzero byte is
+    active; wide rows spanning several 64-column chunks; empty rows)."""
+    g = torch.Generator().manual_seed(5)
+    for rows, tk in [(1, 1), (3, 63), (5, 64), (7, 65), (130, 200), (2, 1024),
+                     (1025, 3), (4000, 17)]:
+        m = (torch.randint(0, 4, (rows, tk), generator=g) *
+             torch.randint(0, 2, (rows, tk), generator=g)).to(torch.uint8)
+        m[rows // 2] = 0
+        dev = m.cuda().reshape(1, rows, tk)
+        rp, ci = bs.make_csr(dev)
+        rp_ref, ci_ref = oracle.tile_csr(m.numpy().reshape(1, rows, tk))
+        assert np.array_equal(rp.cpu().numpy(), rp_ref)
+        assert np.array_equal(ci[:int(rp_ref[-1])].cpu().numpy(), ci_ref)
+
+
+def test_mask_and_csr_repeatable():
+    w = W.WORKLOADS[3]
+    m1, rp1, ci1 = gpu_mask_csr(w)
+    m2, rp2, ci2 = gpu_mask_csr(w)
+    assert torch.equal(m1, m2) and torch.equal(rp1, rp2)
+    n = int(rp1[-1])
+    assert torch.equal(ci1[:n], ci2[:n])
