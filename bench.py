@@ -1,0 +1,217 @@
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+One step = one pass of the whole path over one synthetic batch at the
+32 760-token video shape (B=1, H=12, d=128, 21 frames of 30x52 latents, bf16,
+128x128 tiles): build the window(+-1 frame) + 2 rotating-anchor mask for
+rotation r = (layer + step) mod 21 (layer 0), compact it into active-tile
+lists, run the fused forward.  Inputs are resident in HBM before timing.
+
+Printed: ONE JSON line with
+  value        active-block TFLOP/s of the whole step (mask + lists + forward),
+  ms_per_step  wall time per step,
+  roofline     the forward kernel's active TFLOP/s per launch (HIP events on
+               the launch stream) against the bf16 dense MFMA peak,
+  cpu_baseline the float64 CPU oracle on a bounded row sample,
+plus the forward-only time, the same kernel at density 1.0 and the speedup.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn fwd TFLOP/s (active blocks) + ms/call at 32760 tokens"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (no sparsity)
+HEADLINE = 2                # the 32 760-token video workload
+
+
+def active_flops(mask_np: np.ndarray, w) -> float:
+    """4*d*rows(i)*cols(j) summed over active tiles, real (unpadded) token
+    counts, over every batch entry and head."""
+    Hm, Tq, Tk = mask_np.shape
+    sizes = np.minimum(w.tile, w.N - np.arange(Tq) * w.tile).astype(np.float64)
+    per_slice = np.einsum("hij,i,j->h", mask_np.astype(np.float64), sizes, sizes)
+    heads_per_slice = w.H if Hm == 1 else 1
+    return float(4.0 * w.d * w.B * heads_per_slice * per_slice.sum())
+
+
+def cpu_baseline(w, q, k, v, mask_np, tiles: int, workers: int):
+    """The oracle as it stands, on `tiles` evenly spaced query tiles (every
+    row of them, every head) at rotation 0; TFLOP/s credited like the GPU
+    (active blocks only)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    pick = np.linspace(0, w.num_tiles - 1, tiles).round().astype(int)
+    rows = np.concatenate([np.arange(i * w.tile, min((i + 1) * w.tile, w.N))
+                           for i in pick])
+    sizes = np.minimum(w.tile, w.N - np.arange(w.num_tiles) * w.tile)
+    flops = 0.0
+    for i in pick:
+        act = mask_np[0, i].astype(bool)
+        flops += 4.0 * w.d * sizes[i] * sizes[act].sum()
+    flops *= w.B * w.H
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    t0 = time.perf_counter()
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            oracle.block_sparse_attention_rows(qc, kc, vc, mask_np, w.tile, rows,
+                                               workers=workers)
+    else:
+        oracle.block_sparse_attention_rows(qc, kc, vc, mask_np, w.tile, rows,
+                                           workers=workers)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"{len(rows)} query rows ({tiles} of {w.num_tiles} query "
+                      f"tiles) x {w.B * w.H} heads at rotation 0, float64 NumPy, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-tiles", type=int, default=24,
+                    help="query tiles in the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--dense-calls", type=int, default=5)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the block-sparse path here has no "
+              "multi-GPU implementation (heads would shard with no exchange); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_bsattn_amd as bs
+    import workloads as W
+
+    bs.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.WORKLOADS[HEADLINE]
+    q, k, v = W.make_qkv(w, device=dev)
+    o = torch.empty_like(q)
+    Tn = w.num_tiles
+    Hm = w.mask.mask_heads
+    mask = torch.empty((Hm, Tn, Tn), dtype=torch.uint8, device=dev)
+    row_ptr = torch.empty(Hm * Tn + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(Hm * Tn * Tn, dtype=torch.int32, device=dev)
+    layout = (w.frames, w.grid_h, w.grid_w, w.tile)
+    stream = torch.cuda.current_stream()
+    T = w.frames
+
+    # active FLOPs for every rotation the run visits
+    flops_by_r = {}
+    for r in range(T):
+        bs.build_mask(layout, mask, **bs.mask_params_of(w.with_rotation(r).mask))
+        flops_by_r[r] = active_flops(mask.cpu().numpy(), w)
+
+    def step(s, ev=None):
+        r = s % T  # (layer + step) mod T with layer 0
+        bs.build_mask(layout, mask, stream=stream,
+                      **bs.mask_params_of(w.with_rotation(r).mask))
+        bs.compact(mask, row_ptr, col_idx, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, mask_heads=Hm,
+               stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        return flops_by_r[r]
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    total_flops = 0.0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        total_flops += step(args.warmup + s, events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fwd_ms = np.array([a.elapsed_time(b) for a, b in events])
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = total_flops / elapsed / 1e12
+    fwd_flops_mean = total_flops / args.steps
+    fwd_tflops = fwd_flops_mean / (fwd_ms.mean() * 1e-3) / 1e12
+
+    # the same kernel at density 1.0 on the same shape
+    bs.build_mask(layout, mask, kind=W.MASK_DENSE, mask_heads=Hm)
+    bs.compact(mask, row_ptr, col_idx)
+    dense_flops = active_flops(mask.cpu().numpy(), w)
+    bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, mask_heads=Hm)
+    dev_ev = [(torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True))
+              for _ in range(args.dense_calls)]
+    for a, b in dev_ev:
+        a.record(stream)
+        bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, mask_heads=Hm)
+        b.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = float(np.median([a.elapsed_time(b) for a, b in dev_ev]))
+
+    cpu = None
+    if args.cpu_tiles > 0:
+        bs.build_mask(layout, mask, **bs.mask_params_of(w.with_rotation(0).mask))
+        torch.cuda.synchronize()
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        cpu = cpu_baseline(w, q, k, v, mask.cpu().numpy(), args.cpu_tiles, workers)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+            "tile": w.tile, "frames": w.frames, "grid": [w.grid_h, w.grid_w],
+            "mask": "window +-1 frame + 2 anchors rotating (layer+step) mod 21",
+            "step": "build_mask + compact + fwd",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(fwd_tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "fwd_kernel<128,128,bf16>",
+            "fwd_ms_mean": round(float(fwd_ms.mean()), 4),
+            "active_tflop_per_launch": round(fwd_flops_mean / 1e12, 4),
+        },
+        "fwd_ms_per_call": round(float(fwd_ms.mean()), 4),
+        "density": round(fwd_flops_mean / dense_flops, 4),
+        "dense_fwd_ms": round(dense_ms, 4),
+        "dense_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 3),
+        "speedup_vs_density_1": round(dense_ms / float(fwd_ms.mean()), 3),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -36,5 +36,7 @@ int launch_build_mask(const MaskLaunch& a, uint8_t* mask, void* stream);
 int launch_compact(int32_t rows, int32_t tk, const uint8_t* mask,
                    int32_t* row_ptr, int32_t* col_idx, void* stream);
 int launch_fwd(const FwdLaunch& a, void* stream);
+// tuned instance: bf16, head dim 128, 128x128 tiles, N * 256 < 2^31
+int launch_fwd_bf16_t128_d128(const FwdLaunch& a, void* stream);
 
 }  // namespace bsattn

@@ -244,6 +244,9 @@ int launch_d(const FwdLaunch& a, hipStream_t s) {
 }  // namespace
 
 int launch_fwd(const FwdLaunch& a, void* stream) {
+  if (a.tile == 128 && a.d == 128 && a.dtype == 0 &&
+      (int64_t)a.N * 256 < ((int64_t)1 << 31))
+    return launch_fwd_bf16_t128_d128(a, stream);
   hipStream_t s = (hipStream_t)stream;
   return a.tile == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
 }
