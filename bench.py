@@ -86,6 +86,9 @@ def main():
     ap.add_argument("--cpu-tiles", type=int, default=24,
                     help="query tiles in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--dense-calls", type=int, default=5)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB "
+                         "(byte-counter calibration under a profiler)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -165,6 +168,15 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     dense_ms = float(np.median([a.elapsed_time(b) for a, b in dev_ev]))
+
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if args.cpu_tiles > 0:
