@@ -23,11 +23,24 @@
 //     S_t = K_t Q^T: 64 MFMAs per wave) while the other runs its vector phase
 //     (the online softmax of S_t); the roles swap at each barrier, so every
 //     SIMD always has one MFMA wave and one VALU wave.
-//   * each group owns one K and one V buffer in LDS (4 x 32 KB = 128 KB).
-//     At the start of its vector phase a group fetches K_{t+1} and V_t with
-//     buffer_load ... lds (16 B per lane, no VGPR staging; rows past the
-//     sequence end are outside the buffer range and arrive as zeros), and
-//     waits for them at the end of that phase.
+//   * the two groups share their K/V tiles: they walk the union of their
+//     two active lists (key tiles ascending; a tile only one group needs is
+//     skipped by the other), so each staged tile serves 256 query rows.
+//     Neighbouring query tiles of a window mask need nearly the same key
+//     tiles, and L2 -> LDS staging traffic per flop halves.
+//   * K and V tiles are double-buffered in LDS (2 x 2 x 32 KB).  Entry w's
+//     K is read in phases 2w (group 0) and 2w+1 (group 1), its V in phases
+//     2w+2 and 2w+3, so K_{w+1} and V_w are fetched during phases 2w and
+//     2w+1, two phases ahead of use.  Each wave issues its share of one
+//     fetch (8 loads of 1 KB) at the start of its vector phase and waits for
+//     it at the end: group 1 fetches K_{w+1} in phase 2w, group 0 fetches
+//     V_w in phase 2w+1.  Matrix phases issue no global-memory instruction,
+//     so the MFMA stream never stalls on the memory-address queue.  Loads
+//     are buffer_load ... lds (16 B per lane, no VGPR staging; rows past the
+//     sequence end are outside the buffer range and arrive as zeros).  The
+//     lines of the tile one entry further ahead are touched in the same
+//     phase (4 B per 128-byte line into a scratch LDS area), so the real
+//     fetches hit L2.
 //   * LDS layout: row-major, 256 B per row, 16-byte chunk c of row R at chunk
 //     position c ^ S(R), S(R) = 4*(R % 4) + (R / 4) % 4: conflict-free for the
 //     K reader (16 consecutive rows, one chunk column) and for the
@@ -39,7 +52,8 @@
 //   * O^T += V^T P^T on the same MFMA, P straight from the score registers
 //     with the reduction index permuted to the keys the lane holds.  The V^T
 //     operand comes from row-major V via ds_read_b64_tr_b16 (lane i of each
-//     16-lane group receives element i % 4 of source lane 4e + i / 4).
+//     16-lane group receives element i % 4 of source lane 4e + i / 4).  MFMA
+//     operands are read from LDS four MFMAs ahead of use.
 //   * Row sums use v_dot2 on the bf16-rounded P, the values PV consumes.
 //   * Workgroups are remapped so each XCD (own L2) walks a contiguous range
 //     of (head, query-tile pair); neighbouring query tiles share most of
@@ -58,6 +72,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
@@ -73,11 +88,16 @@ constexpr int ROW_BYTES = D * 2;            // 256
 constexpr int TILE_BYTES = BT * ROW_BYTES;  // 32 KB
 constexpr float TAU = 8.0f;                 // lazy-rescale threshold (log2 units)
 constexpr int NXCD = 8;
+constexpr int PF = 4;                       // MFMA operand read-ahead (steps)
 
-// Workgroup barrier that first drains this wave's LDS reads: a buffer that a
-// barrier releases for refilling must have no read of it still queued.
+// Lambdas are forced inline: an outlined lambda would reach its captures
+// through memory and turn every buffer resource into a waterfall loop.
+#define INLINE __attribute__((always_inline))
+
+// Workgroup barrier that first drains this wave's LDS reads (a buffer a
+// barrier releases for refilling must have no read of it still queued) and
+// scalar loads.
 #define BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
-#define WAIT_VM0() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
@@ -96,14 +116,51 @@ __device__ __forceinline__ int list_len(sconst_i32 row_ptr, int64_t cap, int mro
   return e0 > b0 ? (int)(e0 - b0) : 0;
 }
 
+// Load i (0..7) of a tile fetch: 1 KB of the tile into LDS; the immediate
+// offset 1024 (i % 4) applies to both the global and the LDS address.
+template <int I>
+__device__ __forceinline__ void fetch_load(__amdgpu_buffer_rsrc_t rs, lds_char_t* buf, int wg,
+                                           uint32_t voff, uint32_t toff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(buf + (8 * wg + 4 * (I >> 2)) * 1024),
+                                           16, voff, toff + 4096 * (I >> 2), 1024 * (I & 3), 0);
+}
+__device__ __forceinline__ void fetch_load_i(int i, __amdgpu_buffer_rsrc_t rs, lds_char_t* buf,
+                                             int wg, const uint32_t* ld_off, uint32_t toff) {
+  switch (i) {  // resolved at compile time: every caller's loop is unrolled
+    case 0: fetch_load<0>(rs, buf, wg, ld_off[0], toff); break;
+    case 1: fetch_load<1>(rs, buf, wg, ld_off[1], toff); break;
+    case 2: fetch_load<2>(rs, buf, wg, ld_off[2], toff); break;
+    case 3: fetch_load<3>(rs, buf, wg, ld_off[3], toff); break;
+    case 4: fetch_load<4>(rs, buf, wg, ld_off[0], toff); break;
+    case 5: fetch_load<5>(rs, buf, wg, ld_off[1], toff); break;
+    case 6: fetch_load<6>(rs, buf, wg, ld_off[2], toff); break;
+    default: fetch_load<7>(rs, buf, wg, ld_off[3], toff); break;
+  }
+}
+
+__device__ __forceinline__ lds_char_t* uniform_lds(lds_char_t* p) {
+  return (lds_char_t*)(uintptr_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+// One entry of the merged list of the two groups: key tile index in bits
+// 0..28 (BAD_TILE for an index outside [0, Tk)), bit 30 set when group 0
+// needs it, bit 29 when group 1 does; NONE past the end of both lists.
+constexpr int NONE = -1;
+constexpr int BAD_TILE = 0x0FFFFFFE;  // sorts after every real tile
+constexpr int LIST_END = 0x0FFFFFFF;  // head of an exhausted list
+__device__ __forceinline__ int ent_tile(int e) { return e < 0 ? -1 : (e & 0x1FFFFFFF); }
+__device__ __forceinline__ bool ent_in(int e, int grp) {
+  return e >= 0 && ((e >> (30 - grp)) & 1);
+}
+
 __global__ void __launch_bounds__(512, 1)
 fwd_bf16_t128_d128(FwdLaunch a) {
-  // per group one K tile and one V tile; four distinct LDS objects, so the
-  // compiler never mistakes a pending fetch into one for a read of another
-  __shared__ __attribute__((aligned(1024))) char kbuf0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vbuf0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char kbuf1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vbuf1[TILE_BYTES];
+  // K slots [0, 32K) and [32K, 64K) of a 64 KB-aligned array, so one XOR of
+  // bit 15 moves a read address to the other slot; V likewise
+  __shared__ __attribute__((aligned(65536))) char kslots[2 * TILE_BYTES];
+  __shared__ __attribute__((aligned(65536))) char vslots[2 * TILE_BYTES];
+  // landing area of the L2 warm-up loads (4 B per lane, never read)
+  __shared__ __attribute__((aligned(256))) char touch_area[8 * 256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -114,13 +171,13 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   const int wg = wave & 3;    // wave within the group
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  // Wave-uniform LDS bases, kept in the LDS address space throughout (the
-  // LDS-DMA destination M0 is scalar; offset 0 is a valid LDS address, so
-  // these must never pass through a generic pointer, where 0 means null).
-  lds_char_t* const kbuf = (lds_char_t*)(uintptr_t)__builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(grp ? (lds_char_t*)kbuf1 : (lds_char_t*)kbuf0));
-  lds_char_t* const vbuf = (lds_char_t*)(uintptr_t)__builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(grp ? (lds_char_t*)vbuf1 : (lds_char_t*)vbuf0));
+  // Wave-uniform LDS bases, kept in the LDS address space throughout (offset
+  // 0 is a valid LDS address; through a generic pointer it would read as
+  // null).
+  lds_char_t* const kl = uniform_lds((lds_char_t*)kslots);
+  lds_char_t* const vl = uniform_lds((lds_char_t*)vslots);
+  lds_void_t* const touch_dst =
+      (lds_void_t*)uniform_lds((lds_char_t*)touch_area + wave * 256);
 
   // ---- XCD-aware remap of the 1-D grid onto (batch*head, query-tile pair)
   const uint32_t G = gridDim.x, hw = blockIdx.x;
@@ -135,19 +192,29 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   const int N = a.N;
   const int64_t head_row = (int64_t)bh * N;
 
-  // ---- active lists of both groups (both are needed to agree on the
-  // number of phases)
+  // ---- active lists of both groups, merged on the fly (scalar, identical
+  // in every wave)
   const sconst_i32 row_ptr = (sconst_i32)(uintptr_t)a.row_ptr;
   const sconst_i32 col_idx = (sconst_i32)(uintptr_t)a.col_idx;
   const int hrow = (a.mask_heads == 1 ? 0 : h) * a.tiles;
   int jb0 = 0, jb1 = 0;
-  const int nA = list_len(row_ptr, a.col_cap, hrow + qt0, jb0);
-  const int nB = qt0 + 1 < a.tiles ? list_len(row_ptr, a.col_cap, hrow + qt0 + 1, jb1) : 0;
-  const int n = grp ? nB : nA;
-  const int jb = grp ? jb1 : jb0;
-  // group 0 has matrix phases at even indices 0..2nA, group 1 at odd
-  // indices 1..2nB+1
-  const int phases = max(2 * nA, 2 * nB + 1) + 1;
+  const int n0 = list_len(row_ptr, a.col_cap, hrow + qt0, jb0);
+  const int n1 = qt0 + 1 < a.tiles ? list_len(row_ptr, a.col_cap, hrow + qt0 + 1, jb1) : 0;
+  auto head_of = [&](int jbx, int nx, int i) INLINE {
+    if (i >= nx) return LIST_END;
+    const int j = col_idx[jbx + i];
+    return (j >= 0 && j < a.tiles) ? j : BAD_TILE;
+  };
+  int i0 = 0, i1 = 0;
+  int c0 = head_of(jb0, n0, 0), c1 = head_of(jb1, n1, 0);
+  auto next_entry = [&]() INLINE {
+    if (c0 == LIST_END && c1 == LIST_END) return NONE;
+    const int j = min(c0, c1);
+    const int f0 = c0 == j, f1 = c1 == j;
+    if (f0) c0 = head_of(jb0, n0, ++i0);
+    if (f1) c1 = head_of(jb1, n1, ++i1);
+    return j | (f0 << 30) | (f1 << 29);
+  };
 
   // ---- Q^T operand: lane holds q[row l%32][8 d values], 8 chunks of 16 d
   const bool q_tile_real = qt < a.tiles;
@@ -177,9 +244,9 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nbytes, 0x00020000);
 
   // Direct-load offsets.  Load i (0..7) of wave wg fills LDS bytes
-  // [(8 wg + i) * 1024, +1024): rows 32 wg + 4i + (0..3).  Lane l writes
-  // chunk position l % 16 of row 32 wg + 4i + l / 16, so it fetches global
-  // chunk (l % 16) ^ S(row), S(row) = 4 (l / 16) + i % 4.
+  // [(8 wg + i) * 1024, +1024) of a slot: rows 32 wg + 4i + (0..3).  Lane l
+  // writes chunk position l % 16 of row 32 wg + 4i + l / 16, so it fetches
+  // global chunk (l % 16) ^ S(row), S(row) = 4 (l / 16) + i % 4.
   uint32_t ld_off[4];
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) {
@@ -187,42 +254,27 @@ fwd_bf16_t128_d128(FwdLaunch a) {
     const int c = (lane & 15) ^ (((lane >> 4) << 2) | i4);
     ld_off[i4] = (uint32_t)(r * ROW_BYTES + c * 16);
   }
-  // key tile of list entry t; an index outside [0, Tk) is fetched from past
-  // the buffer end (zeros) and all its scores are discarded, i.e. skipped
-  auto tile_of = [&](int t) { return col_idx[jb + t]; };
-  auto fetch_tile = [&](const __amdgpu_buffer_rsrc_t& rs, lds_char_t* buf, int j) {
-    const uint32_t toff =
-        (j >= 0 && j < a.tiles) ? (uint32_t)j * TILE_BYTES : 0x80000000u;
-    // load i = 4 ih + il: the immediate offset 1024 il applies to both the
-    // global and the LDS address, so only two M0 / soffset values are needed
-#define BSATTN_FETCH4(ih)                                                        \
-  do {                                                                           \
-    lds_void_t* dst = (lds_void_t*)(buf + (8 * wg + 4 * (ih)) * 1024);           \
-    const uint32_t so = toff + 4096 * (ih);                                      \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, ld_off[0], so, 0, 0);    \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, ld_off[1], so, 1024, 0); \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, ld_off[2], so, 2048, 0); \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, ld_off[3], so, 3072, 0); \
-  } while (0)
-    BSATTN_FETCH4(0);
-    BSATTN_FETCH4(1);
-#undef BSATTN_FETCH4
+  auto tile_off = [&](int j) INLINE {
+    return (j >= 0 && j < a.tiles) ? (uint32_t)j * TILE_BYTES : 0x80000000u;
+  };
+  // L2 warm-up of a whole tile by one group: lane l of wave wg touches line
+  // 64 wg + l
+  const uint32_t touch_off = (uint32_t)((64 * wg + lane) * 128);
+  auto touch = [&](const __amdgpu_buffer_rsrc_t& rs, int j) INLINE {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, touch_dst, 4, touch_off, tile_off(j), 0, 0);
   };
 
-  // K reader: lane reads key row kb*32 + l%32, chunk 2c + half.
-  // Per-lane LDS addresses (base folded in once), so every read is one VGPR
-  // plus an immediate offset.
+  // Per-lane LDS read addresses of slot 0 (K) and slot 1 (V) (base folded in
+  // once), so every read is one VGPR plus an immediate offset; bit 15 flips
+  // the slot.  K reader: key row kb*32 + l%32, chunk 2c + half.  V^T reader
+  // (ds_read_b64_tr_b16): source lane s (= l % 16) of 16-lane group g16
+  // (= l / 16) points at key row R0 + s/4, d = 32 db + 16 (g16%2) + 4 (s%4);
+  // R0 = kb*32 + 8 i0 + 8 sec + 4 half.
   const int ks = swz(l32);
-  lds_char_t* const kl = kbuf;
-  lds_char_t* const vl = vbuf;
   lds_char_t* kr_addr[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c)
     kr_addr[c] = kl + (l32 * ROW_BYTES + (((2 * c + half) ^ ks) << 4));
-
-  // V^T reader (ds_read_b64_tr_b16): source lane s (= l % 16) of 16-lane
-  // group g16 (= l / 16) points at key row R0 + s/4, d = 32 db + 16 (g16%2) +
-  // 4 (s%4); R0 = kb*32 + 8 i0 + 8 sec + 4 half.
   const int s16 = lane & 15;
   const int g16 = lane >> 4;
   lds_char_t* vr_addr[2][4];
@@ -233,16 +285,27 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       const int rrel = 8 * sec + 4 * half + (s16 >> 2);
       const int chunk = 4 * db + 2 * (g16 & 1) + ((s16 & 3) >> 1);
       const int sw = ((s16 >> 2) << 2) | ((2 * sec + half) & 3);
-      vr_addr[sec][db] = vl + (rrel * ROW_BYTES + ((chunk ^ sw) << 4) + 8 * (s16 & 1));
+      vr_addr[sec][db] =
+          vl + (TILE_BYTES + rrel * ROW_BYTES + ((chunk ^ sw) << 4) + 8 * (s16 & 1));
     }
+  auto flip_slots = [&]() INLINE {
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      kr_addr[c] = (lds_char_t*)((uintptr_t)kr_addr[c] ^ (uintptr_t)TILE_BYTES);
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        vr_addr[sec][db] = (lds_char_t*)((uintptr_t)vr_addr[sec][db] ^ (uintptr_t)TILE_BYTES);
+  };
 
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
-  // S_t^T scores; after the softmax the same registers hold P_t as packed
-  // bf16 pairs: P for keys of chunk kc = 2 kb + hh sits in s[kb][4 hh .. 4 hh + 3]
+  // S^T scores; after the softmax the same registers hold P as packed bf16
+  // pairs: P for keys of chunk kc = 2 kb + hh sits in s[kb][4 hh .. 4 hh + 3]
   f32x16 s[4];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
@@ -253,7 +316,7 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   const float c2 = a.scale_log2;
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  auto v_operand = [&](int kc, int db) {
+  auto v_operand = [&](int kc, int db) INLINE {
     const int rows = (kc >> 1) * 32 * ROW_BYTES + (kc & 1) * 16 * ROW_BYTES;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vr_addr[0][db] + rows));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vr_addr[1][db] + rows));
@@ -264,33 +327,26 @@ fwd_bf16_t128_d128(FwdLaunch a) {
     va[4] = hib[0]; va[5] = hib[1]; va[6] = hib[2]; va[7] = hib[3];
     return va;
   };
-  auto k_operand = [&](int kb, int c) {
+  auto k_operand = [&](int kb, int c) INLINE {
     return *(const lds_bf16x8_t*)(kr_addr[c] + kb * 32 * ROW_BYTES);
   };
-  auto p_operand = [&](int kc) {
+  auto p_operand = [&](int kc) INLINE {
     const f32x16& v = s[kc >> 1];
     const int o = (kc & 1) * 4;
-    typedef float f32x4_t __attribute__((ext_vector_type(4)));
-    const f32x4_t w = {v[o], v[o + 1], v[o + 2], v[o + 3]};
+    const f32x4 w = {v[o], v[o + 1], v[o + 2], v[o + 3]};
     return __builtin_bit_cast(bf16x8, w);
   };
 
-  // matrix phase t: O += P_{t-1} V_{t-1} (if any), then S_t = K_t Q^T (if
-  // any): two streams of 32 MFMAs.  Each MFMA's LDS operand is read PF steps
-  // ahead from a rotating buffer, and the interleave (one MFMA, then the
-  // reads for step + PF) is pinned with scheduling-group barriers, so the
-  // matrix core does not wait for an LDS round trip.  The streams are kept
-  // apart (P and the new scores share registers).
-  constexpr int PF = 4;
-  auto matrix_phase = [&](int t) {
-    const bool do_pv = t >= 1 && t - 1 < n;
-    const bool do_qk = t < n;
-    // step k: 0..31 PV (kc = k / 4, db = k % 4), 32..63 QK (c = (k-32) / 4,
-    // kb = (k-32) % 4)
-    auto load = [&](int k) -> bf16x8 {
+  // matrix phase: O += P V (if do_pv), then S = K Q^T (if do_qk): two
+  // streams of 32 MFMAs.  Each MFMA's LDS operand is read PF steps ahead
+  // from a rotating buffer; the interleave is pinned with scheduling-group
+  // barriers.  No global-memory instruction is issued here, so the MFMA
+  // stream never waits on the memory-address queue.
+  auto matrix_phase = [&](bool do_pv, bool do_qk) INLINE {
+    auto load = [&](int k) INLINE -> bf16x8 {
       return k < 32 ? v_operand(k >> 2, k & 3) : k_operand((k - 32) & 3, (k - 32) >> 2);
     };
-    auto step = [&](int k, const bf16x8& opnd) {
+    auto step = [&](int k, const bf16x8& opnd) INLINE {
       if (k < 32) {
         const int kc = k >> 2, db = k & 3;
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd, p_operand(kc), oacc[db], 0, 0, 0);
@@ -304,108 +360,191 @@ fwd_bf16_t128_d128(FwdLaunch a) {
         }
       }
     };
-#define BSATTN_MATRIX_STREAM(K0, K1)                                                  \
-  do {                                                                                \
-    bf16x8 ring[PF];                                                                  \
-    _Pragma("unroll") for (int i = 0; i < PF; ++i) ring[i] = load((K0) + i);          \
-    __builtin_amdgcn_sched_group_barrier(0x100, (K0) < 32 ? 2 * PF : PF, 0);          \
-    _Pragma("unroll") for (int k = (K0); k < (K1); ++k) {                              \
-      const bf16x8 cur = ring[(k - (K0)) % PF];                                       \
-      if (k + PF < (K1)) ring[(k - (K0)) % PF] = load(k + PF);                        \
-      step(k, cur);                                                                   \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
-      if (k + PF < (K1)) {                                                            \
-        if (k + PF < 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          \
-        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      \
-      }                                                                               \
-    }                                                                                 \
-  } while (0)
     if (do_pv) {
-      BSATTN_MATRIX_STREAM(0, 32);
+      bf16x8 ring[PF];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) ring[i] = load(i);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const bf16x8 cur = ring[k % PF];
+        if (k + PF < 32) ring[k % PF] = load(k + PF);
+        step(k, cur);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (k + PF < 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     if (do_qk) {
-      BSATTN_MATRIX_STREAM(32, 64);
+      bf16x8 ring[PF];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) ring[i] = load(32 + i);
+      __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+      for (int k = 32; k < 64; ++k) {
+        const bf16x8 cur = ring[(k - 32) % PF];
+        if (k + PF < 64) ring[(k - 32) % PF] = load(k + PF);
+        step(k, cur);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (k + PF < 64) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
-#undef BSATTN_MATRIX_STREAM
   };
 
-  // vector phase t: fetch K_{t+1} and V_t, then the online softmax of S_t
-  auto vector_phase = [&](int t) {
-    if (t + 1 < n) fetch_tile(krs, kbuf, tile_of(t + 1));
-    if (t >= 0 && t < n) {
-      const int j = tile_of(t);
-      fetch_tile(vrs, vbuf, j);
-      // keys past the end of the sequence never enter the softmax
-      const int valid = (j >= 0 && j < a.tiles) ? N - j * BT : 0;
-      if (valid < BT) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (kb * 32 + 8 * i + 4 * half + e >= valid) s[kb][4 * i + e] = -INFINITY;
-      }
-      float mx = -INFINITY;
+  // online softmax of S for key tile j (tail mask for the last tile); P
+  // replaces S in the same registers, packed as bf16 pairs
+  auto softmax = [&](int j) INLINE {
+    // keys past the end of the sequence never enter the softmax; integer
+    // select (no per-element compare masks) for this rare tile
+    const int valid = (j >= 0 && j < a.tiles) ? N - j * BT : 0;
+    if (valid < BT) {
+      const int lim = valid - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-      mx = max_across_halves(mx) * c2;
-      if (__any(mx > m + TAU)) {
-        const float m_new = fmaxf(m, mx);
-        // m_new = -inf only while every tile so far was skipped
-        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
-        m = m_new;
-        l *= alpha;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-      }
-      const float msub = m == -INFINITY ? 0.f : m;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          // raw v_exp_f32: results below 2^-126 flush to zero, negligible
-          // next to the row's largest weight (about 1)
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], c2, -msub));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + 1], c2, -msub));
-          bf16x2 pk;
-          pk[0] = (__bf16)p0;
-          pk[1] = (__bf16)p1;
-          l = __builtin_amdgcn_fdot2_f32_bf16(pk, ones2, l, false);
-          // packed pair e/2 of this block; position e/2 <= e was already read
-          s[kb][e >> 1] = __builtin_bit_cast(float, pk);
-        }
+          for (int e = 0; e < 4; ++e) {
+            const int keep = ((kb * 32 + 8 * i + e) - lim) >> 31;  // -1: keep
+            const uint32_t bits = __float_as_uint(s[kb][4 * i + e]);
+            s[kb][4 * i + e] =
+                __uint_as_float((bits & (uint32_t)keep) | (0xff800000u & ~(uint32_t)keep));
+          }
     }
-    WAIT_VM0();  // this wave's share of K_{t+1} and V_t has landed
+    float mxp[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      mxp[kb] = s[kb][0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mxp[kb] = fmaxf(mxp[kb], s[kb][e]);
+    }
+    float mx = fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3]));
+    mx = max_across_halves(mx) * c2;
+    if (__any(mx > m + TAU)) {
+      const float m_new = fmaxf(m, mx);
+      // m_new = -inf only while every tile so far was skipped
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    }
+    const float msub = m == -INFINITY ? 0.f : m;
+    float lp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        // raw v_exp_f32: results below 2^-126 flush to zero, negligible
+        // next to the row's largest weight (about 1)
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], c2, -msub));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + 1], c2, -msub));
+        bf16x2 pk;
+        pk[0] = (__bf16)p0;
+        pk[1] = (__bf16)p1;
+        lp[kb] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones2, lp[kb], false);
+        // packed pair e/2 of this block; position e/2 <= e was already read
+        s[kb][e >> 1] = __builtin_bit_cast(float, pk);
+      }
+    }
+    l += (lp[0] + lp[1]) + (lp[2] + lp[3]);
   };
 
-  // ---- prologue: group 0 fetches its first K tile (group 1 does so in its
-  // first vector phase)
-  if (grp == 0 && n > 0) fetch_tile(krs, kbuf, tile_of(0));
-  WAIT_VM0();
+  // vector phase: this wave's share (8 loads) of one tile fetch into slot
+  // buffer fbuf plus one L2 warm-up load, issued first so they land while
+  // the online softmax of S runs (if do_sm; key tile j for the tail mask),
+  // then awaited.  Row max and row sum use four independent chains.
+  auto vector_phase = [&](bool do_sm, int j, const __amdgpu_buffer_rsrc_t& frs,
+                          lds_char_t* fbuf, uint32_t ftoff, int warm) INLINE {
+#pragma unroll
+    for (int f = 0; f < 8; ++f) fetch_load_i(f, frs, fbuf, wg, ld_off, ftoff);
+    touch(frs, warm);
+    if (do_sm) softmax(j);
+    // this wave's share of the tile has landed; only its warm-up load may
+    // still be in flight (loads complete in issue order)
+    asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+  };
+
+
+  // ---- merged-list window: entries w-1, w, w+1, w+2 at phase pair w
+  int e_m1 = NONE;
+  int e_0 = next_entry();
+  int e_1 = next_entry();
+  int e_2 = next_entry();
+
+  // ---- prologue: K_0 into slot 0 (every wave loads 4 of the 32 KB) and L2
+  // warm-up of K_1 (group 1) and V_0 (group 0)
+  if (e_0 != NONE) {
+    const uint32_t t0 = tile_off(ent_tile(e_0));
+    lds_char_t* dst = kl + (grp * 4) * 1024;  // group g loads rows 16g.. of each 64-row half
+    // each wave of the 8 fills 4 KB: loads 4 grp .. 4 grp + 3 of its wg share
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      fetch_load_i(i, krs, dst, wg, ld_off, t0 + grp * 4096);
+    if (grp == 0) touch(vrs, ent_tile(e_0)); else touch(krs, ent_tile(e_1));
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   BARRIER();
 
-  // group 0: matrix phases at even phase indices; group 1 starts with a
-  // vector phase and is one phase behind.  Both pass `phases` barriers.
-  int ph = 0;
-  if (grp == 1) {
-    vector_phase(-1);
+  // Phase 2w: group 0 matrix (P V of entry w-1, S of entry w), group 1
+  // vector (softmax of entry w-1).  Phase 2w+1: group 0 vector (softmax of
+  // entry w), group 1 matrix.  Fetches for entry w+1's K and entry w's V are
+  // issued in phase 2w and awaited at the end of phase 2w+1.
+  // Every wave alternates matrix and vector phases; group 1 starts with a
+  // vector phase (phase 0) and so is one phase behind.  Pair w = phases 2w
+  // (group 0 matrix, group 1 vector) and 2w+1 (group 0 vector, group 1
+  // matrix).  At each of its vector phases a wave sees the window
+  // (e_m1, e_0, e_1, e_2) = entries (w-1, w, w+1, w+2):
+  //   group 1 (phase 2w):   softmax of entry w-1; fetches K_{w+1} into K
+  //                         slot (w+1)%2 (free since phase 2w-1), warms K_{w+2};
+  //   group 0 (phase 2w+1): softmax of entry w; fetches V_w into V slot w%2
+  //                         (free since phase 2w-1), warms V_{w+1}.
+  // Both tiles are needed from phase 2w+2 on.  Group 0 advances its window
+  // after its vector phase, group 1 after its matrix phase.
+  auto advance = [&]() INLINE {
+    e_m1 = e_0;
+    e_0 = e_1;
+    e_1 = e_2;
+    e_2 = next_entry();
+    flip_slots();
+  };
+  int w = 0;
+  // one call site for both groups (arguments selected by group), so the
+  // softmax is instantiated once
+  auto run_vector_phase = [&]() INLINE {
+    const bool g0 = grp == 0;
+    const int es = g0 ? e_0 : e_m1;  // entry whose softmax runs now
+    const int ef = g0 ? e_0 : e_1;   // entry whose tile is fetched now
+    const int ew = g0 ? e_1 : e_2;   // entry whose tile is warmed in L2
+    lds_char_t* const fbuf =
+        g0 ? vl + (w & 1) * TILE_BYTES : kl + ((w + 1) & 1) * TILE_BYTES;
+    vector_phase(ent_in(es, grp), ent_tile(es), g0 ? vrs : krs, fbuf,
+                 tile_off(ent_tile(ef)), ent_tile(ew));
+  };
+  if (grp == 1 && e_0 != NONE) {
+    // phase 0 (with no entry at all there is none: group 0 runs no
+    // iteration either)
+    run_vector_phase();
     BARRIER();
-    ph = 1;
   }
-  for (int t = 0; ph < phases; ++t) {
-    matrix_phase(t);
+  while (e_0 != NONE || e_m1 != NONE) {
+    matrix_phase(ent_in(e_m1, grp), ent_in(e_0, grp));
+    if (grp == 1) {
+      advance();
+      ++w;
+    }
     BARRIER();
-    if (++ph >= phases) break;
-    vector_phase(t);
+    if (grp == 1 && !(e_0 != NONE || e_m1 != NONE)) break;
+    run_vector_phase();
+    if (grp == 0) {
+      advance();
+      ++w;
+    }
     BARRIER();
-    ++ph;
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: O = O^T / l, rows past N (or of a missing tile) not written
   {
