@@ -1,0 +1,167 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept in profiles/.
+
+Two summaries:
+
+  stats    per-kernel call count and durations from a ``--kernel-trace
+           --stats`` run (the ``*_kernel_stats.csv`` file);
+  traffic  HBM bytes per launch of one kernel from two ``--pmc`` runs, one
+           with FETCH_SIZE and one with WRITE_SIZE (KiB per dispatch).  Both
+           counters are scaled by what they read for a plain device copy of
+           known size in the same run (the largest ``__amd_rocclr_copyBuffer``
+           dispatch: it reads and writes ``copy_mib`` MiB).
+
+The traffic summary records the SHA-256 of the kernel's source file; a reader
+(bench.py) uses the figures only while the source still hashes the same.
+
+Usage:
+  python -m block_sparse_attention_bsattn_amd.rocprof_summary stats \\
+      --csv-dir DIR --command "..." --out profiles/NAME.txt
+  python -m block_sparse_attention_bsattn_amd.rocprof_summary traffic \\
+      --fetch-dir DIR --write-dir DIR --kernel SUBSTR --copy-mib 256 \\
+      --source FILE --command-fetch "..." --command-write "..." --out FILE
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import statistics
+import sys
+
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _one(pattern: str) -> str:
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no file matches {pattern}")
+    return hits[-1]
+
+
+def source_sha256(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def stats_summary(csv_dir: str, command: str, top: int = 12) -> str:
+    path = _one(os.path.join(csv_dir, "**", "*kernel_stats.csv"))
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["# rocprofv3 kernel-trace statistics", "",
+             f"command: {command}", "",
+             f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} "
+             f"{'total_ms':>10} {'pct':>6}  kernel"]
+    for r in rows[:top]:
+        name = r["Name"]
+        if len(name) > 90:
+            name = name[:87] + "..."
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                     f"{float(r['TotalDurationNs']) / 1e6:10.3f} "
+                     f"{float(r['Percentage']):6.2f}  {name}")
+    return "\n".join(lines) + "\n"
+
+
+def _counter_by_dispatch(csv_dir: str, counter: str):
+    """{kernel name: [(dispatch id, value), ...]} for one counter."""
+    path = _one(os.path.join(csv_dir, "**", "*counter_collection.csv"))
+    out: dict = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        out.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return out
+
+
+def _kernel_values(per: dict, substr: str):
+    vals = [v for name, dv in per.items() if substr in name for _, v in dv]
+    if not vals:
+        raise KeyError(f"no dispatch of a kernel matching {substr!r}")
+    return vals
+
+
+def traffic_summary(fetch_dir, write_dir, kernel, copy_mib, source,
+                    command_fetch, command_write):
+    fetch = _counter_by_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_by_dispatch(write_dir, "WRITE_SIZE")
+    copy_kib = copy_mib * 1024.0
+    f_copy = max(_kernel_values(fetch, COPY_KERNEL))
+    w_copy = max(_kernel_values(write, COPY_KERNEL))
+    f_scale = copy_kib / f_copy
+    w_scale = copy_kib / w_copy
+    kf = _kernel_values(fetch, kernel)
+    kw = _kernel_values(write, kernel)
+    f_bytes = statistics.mean(kf) * f_scale * 1024.0
+    w_bytes = statistics.mean(kw) * w_scale * 1024.0
+    lines = [
+        "# HBM traffic per launch from rocprofv3 PMC counters", "",
+        f"kernel: {kernel}",
+        f"source: {os.path.relpath(source)}",
+        f"source_sha256: {source_sha256(source)}",
+        f"command_fetch: {command_fetch}",
+        f"command_write: {command_write}",
+        f"copy_calibration_mib: {copy_mib}",
+        f"copy_fetch_kib_measured: {f_copy:.1f}",
+        f"copy_write_kib_measured: {w_copy:.1f}",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"launches_fetch: {len(kf)}",
+        f"launches_write: {len(kw)}",
+        f"fetch_kib_raw_mean: {statistics.mean(kf):.1f}",
+        f"write_kib_raw_mean: {statistics.mean(kw):.1f}",
+        f"fetch_bytes_per_launch: {f_bytes:.0f}",
+        f"write_bytes_per_launch: {w_bytes:.0f}",
+        f"traffic_bytes_per_launch: {f_bytes + w_bytes:.0f}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def read_traffic(path: str, source: str):
+    """The traffic summary as a dict, or None when it is missing or was taken
+    on a different version of the kernel source."""
+    if not os.path.exists(path) or not os.path.exists(source):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_sha256(source):
+        return None
+    return {"fetch": float(kv["fetch_bytes_per_launch"]),
+            "write": float(kv["write_bytes_per_launch"]),
+            "total": float(kv["traffic_bytes_per_launch"])}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--csv-dir", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch-dir", required=True)
+    t.add_argument("--write-dir", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-mib", type=float, required=True)
+    t.add_argument("--source", required=True)
+    t.add_argument("--command-fetch", required=True)
+    t.add_argument("--command-write", required=True)
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        text = stats_summary(a.csv_dir, a.command)
+    else:
+        text = traffic_summary(a.fetch_dir, a.write_dir, a.kernel, a.copy_mib,
+                               a.source, a.command_fetch, a.command_write)
+    with open(a.out, "w") as f:
+        f.write(text)
+    sys.stdout.write(text)
+
+
+if __name__ == "__main__":
+    main()
