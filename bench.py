@@ -44,6 +44,56 @@ def active_flops(mask_np: np.ndarray, w) -> float:
     return float(4.0 * w.d * w.B * heads_per_slice * per_slice.sum())
 
 
+SWEEP_P = (0.05, 0.1, 0.2, 0.3, 0.5, 0.7, 1.0)
+
+
+def density_sweep(bs, W, torch, dev, q, k, v, o, calls: int = 5):
+    """The forward on the 32 760-token shape with per-head static random
+    masks (seed 3, diagonal forced) at several densities: median ms per call
+    against active TFLOP, and a least-squares line through them."""
+    base = W.WORKLOADS[3]
+    Tn = base.num_tiles
+    Hm = base.H
+    layout = (base.frames, base.grid_h, base.grid_w, base.tile)
+    mask = torch.empty((Hm, Tn, Tn), dtype=torch.uint8, device=dev)
+    row_ptr = torch.empty(Hm * Tn + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(Hm * Tn * Tn, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    pts = []
+    for p in SWEEP_P:
+        spec = base.mask
+        bs.build_mask(layout, mask, kind=W.MASK_STATIC_RANDOM, window=0,
+                      num_anchors=0, rotation=0, seed=spec.seed,
+                      thresh24=W.thresh24_for_density(p),
+                      force_diagonal=1, mask_heads=Hm)
+        bs.compact(mask, row_ptr, col_idx)
+        m_np = mask.cpu().numpy()
+        flops = active_flops(m_np, base)
+        bs.fwd(q, k, v, o, row_ptr, col_idx, base.tile, mask_heads=Hm)
+        evs = [(torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for a, b in evs:
+            a.record(stream)
+            bs.fwd(q, k, v, o, row_ptr, col_idx, base.tile, mask_heads=Hm,
+                   stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        pts.append({"p": p, "density": round(float(m_np.mean()), 4),
+                    "ms": round(ms, 4), "active_tflop": round(flops / 1e12, 4),
+                    "tflops": round(flops / (ms * 1e-3) / 1e12, 1)})
+    x = np.array([pt["active_tflop"] for pt in pts])
+    y = np.array([pt["ms"] for pt in pts])
+    slope, icpt = np.polyfit(x, y, 1)
+    r2 = 1.0 - ((y - (slope * x + icpt)) ** 2).sum() / ((y - y.mean()) ** 2).sum()
+    return {"mask": "static random per head (seed 3, diagonal forced), "
+                    "B=1 H=12 N=32760 d=128 tile 128",
+            "points": pts,
+            "fit_ms_per_active_tflop": round(float(slope), 4),
+            "fit_intercept_ms": round(float(icpt), 4),
+            "fit_r2": round(float(r2), 5)}
+
+
 def cpu_baseline(w, q, k, v, mask_np, tiles: int, workers: int):
     """The oracle as it stands, on `tiles` evenly spaced query tiles (every
     row of them, every head) at rotation 0; TFLOP/s credited like the GPU
@@ -89,6 +139,10 @@ def main():
     ap.add_argument("--dense-calls", type=int, default=5,
                     help="timed calls of the same kernel at density 1.0 "
                          "(0 = skip)")
+    ap.add_argument("--mfma-ceiling", type=int, default=1,
+                    help="measure the register-only MFMA ceiling (0 = skip)")
+    ap.add_argument("--sweep", type=int, default=1,
+                    help="density sweep with static masks (0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB "
                          "(byte-counter calibration under a profiler)")
@@ -126,24 +180,30 @@ def main():
         flops_by_r[r] = active_flops(mask.cpu().numpy(), w)
 
     def step(s, ev=None):
+        """One pass of the path; ev = 4 events bracketing mask build,
+        compaction and the forward on the launch stream."""
         r = s % T  # (layer + step) mod T with layer 0
-        bs.build_mask(layout, mask, stream=stream,
-                      **bs.mask_params_of(w.with_rotation(r).mask))
-        bs.compact(mask, row_ptr, col_idx, stream=stream)
         if ev is not None:
             ev[0].record(stream)
+        bs.build_mask(layout, mask, stream=stream,
+                      **bs.mask_params_of(w.with_rotation(r).mask))
+        if ev is not None:
+            ev[1].record(stream)
+        bs.compact(mask, row_ptr, col_idx, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
         bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, mask_heads=Hm,
                stream=stream)
         if ev is not None:
-            ev[1].record(stream)
+            ev[3].record(stream)
         return flops_by_r[r]
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
 
-    events = [(torch.cuda.Event(enable_timing=True),
-               torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+              for _ in range(args.steps)]
     total_flops = 0.0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -151,11 +211,30 @@ def main():
         total_flops += step(args.warmup + s, events[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    fwd_ms = np.array([a.elapsed_time(b) for a, b in events])
+    fwd_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+    mask_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    compact_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     ms_per_step = elapsed * 1e3 / args.steps
     value = total_flops / elapsed / 1e12
     fwd_flops_mean = total_flops / args.steps
     fwd_tflops = fwd_flops_mean / (fwd_ms.mean() * 1e-3) / 1e12
+
+    # achievable matrix-core rate: register-only MFMA stream, best of 3
+    ceiling = None
+    if args.mfma_ceiling:
+        blocks, iters = 1024, 2000
+        sink = torch.empty(blocks, dtype=torch.float32, device=dev)
+        bs.mfma_ceiling(blocks, iters, sink, stream=stream)
+        rates = []
+        for _ in range(3):
+            a_ev = torch.cuda.Event(enable_timing=True)
+            b_ev = torch.cuda.Event(enable_timing=True)
+            a_ev.record(stream)
+            n = bs.mfma_ceiling(blocks, iters, sink, stream=stream)
+            b_ev.record(stream)
+            torch.cuda.synchronize()
+            rates.append(n / (a_ev.elapsed_time(b_ev) * 1e-3) / 1e12)
+        ceiling = max(rates)
 
     # the same kernel at density 1.0 on the same shape
     dense_ms = dense_flops = None
@@ -173,6 +252,8 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
         dense_ms = float(np.median([a.elapsed_time(b) for a, b in dev_ev]))
+
+    sweep = density_sweep(bs, W, torch, dev, q, k, v, o) if args.sweep else None
 
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -228,14 +309,21 @@ def main():
             "kernel": "fwd_bf16_t128_d128",
             "fwd_ms_mean": round(float(fwd_ms.mean()), 4),
             "active_tflop_per_launch": round(fwd_flops_mean / 1e12, 4),
+            "mfma_ceiling_measured": None if ceiling is None else round(ceiling, 1),
+            "frac_of_measured_ceiling": None if ceiling is None else
+            round(fwd_tflops / ceiling, 4),
         },
         "fwd_ms_per_call": round(float(fwd_ms.mean()), 4),
+        "fwd_ms_median": round(float(np.median(fwd_ms)), 4),
+        "build_mask_us": round(float(np.median(mask_ms)) * 1e3, 2),
+        "compact_us": round(float(np.median(compact_ms)) * 1e3, 2),
         "density": None if dense_flops is None else round(fwd_flops_mean / dense_flops, 4),
         "dense_fwd_ms": None if dense_ms is None else round(dense_ms, 4),
         "dense_tflops": None if dense_ms is None else
         round(dense_flops / (dense_ms * 1e-3) / 1e12, 3),
         "speedup_vs_density_1": None if dense_ms is None else
         round(dense_ms / float(fwd_ms.mean()), 3),
+        "density_sweep": sweep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

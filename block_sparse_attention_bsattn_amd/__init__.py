@@ -36,7 +36,7 @@ MASK_DENSE = 2
 # Every symbol include/bsattn.h exports.
 EXPORTS = ("bsattn_version", "bsattn_status_string", "bsattn_last_error",
            "bsattn_num_tiles", "bsattn_build_mask", "bsattn_compact",
-           "bsattn_fwd")
+           "bsattn_fwd", "bsattn_mfma_ceiling")
 
 
 class BsattnError(RuntimeError):
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
     L.bsattn_fwd.restype = ctypes.c_int
     L.bsattn_fwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                              i32, i32p, i32p, ctypes.c_float, vp]
+    L.bsattn_mfma_ceiling.restype = ctypes.c_int64
+    L.bsattn_mfma_ceiling.argtypes = [i32, i32, vp, vp]
     _lib = L
     return L
 
@@ -200,6 +202,21 @@ def fwd(q, k, v, o, row_ptr, col_idx, tile: int, mask_heads: int = 1,
                           _stream(stream))
     _check(st, "bsattn_fwd")
     return o
+
+
+def mfma_ceiling(blocks: int, iters: int, sink, stream=None) -> int:
+    """bsattn_mfma_ceiling: enqueue the register-only bf16 MFMA
+    microbenchmark; sink is a float32 device tensor of >= blocks entries.
+    Returns the floating-point operations enqueued."""
+    import torch
+    if sink.numel() < blocks:
+        raise ValueError("sink must hold at least `blocks` floats")
+    n = lib().bsattn_mfma_ceiling(blocks, iters,
+                                  _ptr(sink, "sink", torch.float32),
+                                  _stream(stream))
+    if n < 0:
+        _check(int(n), "bsattn_mfma_ceiling")
+    return int(n)
 
 
 # ------------------------------------------------------- allocating helpers

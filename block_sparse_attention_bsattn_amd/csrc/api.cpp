@@ -178,4 +178,14 @@ BSATTN_API int bsattn_fwd(int32_t B, int32_t H, int32_t N, int32_t d,
   return hip_status(bsattn::launch_fwd(a, stream), "fwd");
 }
 
+BSATTN_API int64_t bsattn_mfma_ceiling(int32_t blocks, int32_t iters, float* sink,
+                                       void* stream) {
+  if (blocks < 1 || iters < 1 || !sink)
+    return fail(BSATTN_ERR_INVALID_ARG, "mfma_ceiling: blocks, iters >= 1 and sink required");
+  const int err = bsattn::launch_mfma_ceiling(blocks, iters, sink, stream);
+  if (err != 0) return hip_status(err, "mfma_ceiling");
+  ok();
+  return bsattn::mfma_ceiling_flops(blocks, iters);
+}
+
 }  // extern "C"

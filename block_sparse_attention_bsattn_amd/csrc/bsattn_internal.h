@@ -39,4 +39,8 @@ int launch_fwd(const FwdLaunch& a, void* stream);
 // tuned instance: bf16, head dim 128, 128x128 tiles, N * 256 < 2^31
 int launch_fwd_bf16_t128_d128(const FwdLaunch& a, void* stream);
 
+// matrix-core ceiling microbenchmark
+int64_t mfma_ceiling_flops(int blocks, int iters);
+int launch_mfma_ceiling(int blocks, int iters, float* sink, void* stream);
+
 }  // namespace bsattn

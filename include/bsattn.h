@@ -148,6 +148,19 @@ BSATTN_API int bsattn_fwd(int32_t B, int32_t H, int32_t N, int32_t d,
                           int32_t mask_heads, const int32_t* row_ptr,
                           const int32_t* col_idx, float scale, void* stream);
 
+/* Diagnostic: the achievable bf16 matrix-core rate of the device, against
+ * which the forward's throughput is read (next to the vendor's dense peak).
+ * Enqueues `blocks` workgroups of 512 threads that each run `iters` loop
+ * trips of 16 register-only v_mfma_f32_32x32x16_bf16 per wave (four
+ * independent accumulator chains); no memory is read.
+ *   sink: device float [blocks], written (one value per workgroup, keeps the
+ *         work from being optimised away; the values mean nothing).
+ * Returns the number of floating-point operations enqueued (> 0), or a
+ * negative bsattn_status: INVALID_ARG for blocks < 1, iters < 1 or a null
+ * sink, HIP on a launch failure.  Time it with events on `stream`. */
+BSATTN_API int64_t bsattn_mfma_ceiling(int32_t blocks, int32_t iters, float* sink,
+                                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

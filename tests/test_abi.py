@@ -121,3 +121,11 @@ def test_compact_rejects_bad_arguments():
     assert L.bsattn_compact(4, 4, p, None, p, None) == bs.ERR_INVALID_ARG
     assert L.bsattn_compact(4, 4, None, p, p, None) == bs.ERR_INVALID_ARG
     assert L.bsattn_compact(1 << 16, 1 << 16, p, p, p, None) == bs.ERR_INVALID_ARG
+
+
+def test_mfma_ceiling_rejects_bad_arguments():
+    L = bs.lib()
+    p = ctypes.c_void_p(64)
+    assert L.bsattn_mfma_ceiling(0, 10, p, None) == bs.ERR_INVALID_ARG
+    assert L.bsattn_mfma_ceiling(4, 0, p, None) == bs.ERR_INVALID_ARG
+    assert L.bsattn_mfma_ceiling(4, 10, None, None) == bs.ERR_INVALID_ARG
