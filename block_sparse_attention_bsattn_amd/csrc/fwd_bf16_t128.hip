@@ -54,7 +54,9 @@
 //     operand comes from row-major V via ds_read_b64_tr_b16 (lane i of each
 //     16-lane group receives element i % 4 of source lane 4e + i / 4).  MFMA
 //     operands are read from LDS four MFMAs ahead of use.
-//   * Row sums use v_dot2 on the bf16-rounded P, the values PV consumes.
+//   * Row sums add the fp32 P values with plain VALU adds.  Dot instructions
+//     (v_dot2_*) issue only when the matrix core is idle, so next to the
+//     other group's MFMA stream they would stall the softmax.
 //   * Workgroups are remapped so each XCD (own L2) walks a contiguous range
 //     of (head, query-tile pair); neighbouring query tiles share most of
 //     their key tiles.
@@ -97,7 +99,17 @@ constexpr int PF = 4;                       // MFMA operand read-ahead (steps)
 // Workgroup barrier that first drains this wave's LDS reads (a buffer a
 // barrier releases for refilling must have no read of it still queued) and
 // scalar loads.
-#define BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt fields at their maximum)
+constexpr int WAIT_VM0 = 0x0F70;
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt fields at their maximum)
+constexpr int WAIT_LGKM0 = 0xC07F;
+// The wait is the builtin, so the compiler knows no scalar load is pending
+// after a barrier.
+#define BARRIER()                              \
+  do {                                         \
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);    \
+    asm volatile("s_barrier" ::: "memory");    \
+  } while (0)
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
@@ -136,6 +148,83 @@ __device__ __forceinline__ void fetch_load_i(int i, __amdgpu_buffer_rsrc_t rs, l
     case 6: fetch_load<6>(rs, buf, wg, ld_off[2], toff); break;
     default: fetch_load<7>(rs, buf, wg, ld_off[3], toff); break;
   }
+}
+
+// The same loads written as inline asm, for the fetches of the main loop.
+// The compiler's wait-count pass cannot tell LDS slots apart, and would wait
+// for an in-flight fetch into one slot before any LDS read of another; it
+// does not see these, and the kernel's own s_waitcnt + barrier pairs order
+// them.  They have no register results (the data goes straight to LDS), and
+// their operands are read at issue.  One wait state separates the M0 write
+// from the load.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+template <int IMM>
+__device__ __forceinline__ void dma_b128(const i32x4& rs, uint32_t m0, uint32_t voff,
+                                         uint32_t soff) {
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds"
+      :
+      : "v"(voff), "s"(rs), "s"(soff), "i"(IMM), "{m0}"(m0)
+      : "memory");
+}
+__device__ __forceinline__ void dma_b32(const i32x4& rs, uint32_t m0, uint32_t voff,
+                                        uint32_t soff) {
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dword %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(rs), "s"(soff), "{m0}"(m0)
+      : "memory");
+}
+// Four loads of a tile fetch (loads 4h .. 4h+3 of fetch_load, one M0) as
+// one statement that the wave skips as a whole when `skip` is nonzero: no
+// branch is visible to the compiler, so the statement can be pinned between
+// blocks of other work.
+__device__ __forceinline__ void dma_burst4(const i32x4& rs, uint32_t m0, const uint32_t* voff,
+                                           uint32_t soff, uint32_t skip) {
+  asm volatile(
+      "s_cmp_eq_u32 %0, 0\n\t"
+      "s_cbranch_scc0 .Lbsattn_skip_%=\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %5, %6 offen offset:0 lds\n\t"
+      "buffer_load_dwordx4 %2, %5, %6 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %3, %5, %6 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 lds\n"
+      ".Lbsattn_skip_%=:"
+      :
+      : "s"(skip), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rs), "s"(soff),
+        "{m0}"(m0)
+      : "memory", "scc");
+}
+// One 4-byte-per-lane direct-to-LDS load, skipped when `skip` is nonzero.
+__device__ __forceinline__ void dma_b32_unless(const i32x4& rs, uint32_t m0, uint32_t voff,
+                                               uint32_t soff, uint32_t skip) {
+  asm volatile(
+      "s_cmp_eq_u32 %0, 0\n\t"
+      "s_cbranch_scc0 .Lbsattn_skip_%=\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, %3 offen lds\n"
+      ".Lbsattn_skip_%=:"
+      :
+      : "s"(skip), "v"(voff), "s"(rs), "s"(soff), "{m0}"(m0)
+      : "memory", "scc");
+}
+// Load I (0..7) of a tile fetch, as fetch_load<I>.
+template <int I>
+__device__ __forceinline__ void fetch_asm(const i32x4& rs, uint32_t buf, int wg, uint32_t voff,
+                                          uint32_t toff) {
+  dma_b128<1024 * (I & 3)>(rs, buf + (uint32_t)((8 * wg + 4 * (I >> 2)) * 1024), voff,
+                           toff + 4096 * (I >> 2));
+}
+__device__ __forceinline__ i32x4 raw_rsrc(const void* base, int nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);  // stride 0
+  r[2] = nbytes;                                  // range, in bytes
+  r[3] = 0x00020000;                              // as the builtin's flags
+  return r;
 }
 
 __device__ __forceinline__ lds_char_t* uniform_lds(lds_char_t* p) {
@@ -200,19 +289,24 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   int jb0 = 0, jb1 = 0;
   const int n0 = list_len(row_ptr, a.col_cap, hrow + qt0, jb0);
   const int n1 = qt0 + 1 < a.tiles ? list_len(row_ptr, a.col_cap, hrow + qt0 + 1, jb1) : 0;
-  auto head_of = [&](int jbx, int nx, int i) INLINE {
-    if (i >= nx) return LIST_END;
-    const int j = col_idx[jbx + i];
-    return (j >= 0 && j < a.tiles) ? j : BAD_TILE;
-  };
+  // Each list keeps its validated head c (index i) and the raw entry at
+  // index i + 1, loaded one step ahead: a value is validated only when it
+  // becomes the head, by which time its scalar load has long completed.
+  auto valid = [&](int r) INLINE { return (r >= 0 && r < a.tiles) ? r : BAD_TILE; };
+  auto raw_at = [&](int jbx, int nx, int i) INLINE { return i < nx ? col_idx[jbx + i] : 0; };
   int i0 = 0, i1 = 0;
-  int c0 = head_of(jb0, n0, 0), c1 = head_of(jb1, n1, 0);
+  int c0 = n0 > 0 ? valid(col_idx[jb0]) : LIST_END;
+  int c1 = n1 > 0 ? valid(col_idx[jb1]) : LIST_END;
+  int r0 = raw_at(jb0, n0, 1), r1 = raw_at(jb1, n1, 1);
   auto next_entry = [&]() INLINE {
     if (c0 == LIST_END && c1 == LIST_END) return NONE;
     const int j = min(c0, c1);
     const int f0 = c0 == j, f1 = c1 == j;
-    if (f0) c0 = head_of(jb0, n0, ++i0);
-    if (f1) c1 = head_of(jb1, n1, ++i1);
+    // new heads first, from values loaded earlier; then the new look-aheads
+    if (f0) c0 = ++i0 < n0 ? valid(r0) : LIST_END;
+    if (f1) c1 = ++i1 < n1 ? valid(r1) : LIST_END;
+    if (f0) r0 = raw_at(jb0, n0, i0 + 1);
+    if (f1) r1 = raw_at(jb1, n1, i1 + 1);
     return j | (f0 << 30) | (f1 << 29);
   };
 
@@ -242,6 +336,8 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nbytes, 0x00020000);
+  const i32x4 krs4 = raw_rsrc(kbase, nbytes);
+  const i32x4 vrs4 = raw_rsrc(vbase, nbytes);
 
   // Direct-load offsets.  Load i (0..7) of wave wg fills LDS bytes
   // [(8 wg + i) * 1024, +1024) of a slot: rows 32 wg + 4i + (0..3).  Lane l
@@ -314,7 +410,6 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   float m = -INFINITY;
   float l = 0.f;
   const float c2 = a.scale_log2;
-  const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   auto v_operand = [&](int kc, int db) INLINE {
     const int rows = (kc >> 1) * 32 * ROW_BYTES + (kc & 1) * 16 * ROW_BYTES;
@@ -343,6 +438,8 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // barriers.  No global-memory instruction is issued here, so the MFMA
   // stream never waits on the memory-address queue.
   auto matrix_phase = [&](bool do_pv, bool do_qk) INLINE {
+    // the MFMA stream wins issue ties against the other group's VALU work
+    __builtin_amdgcn_s_setprio(1);
     auto load = [&](int k) INLINE -> bf16x8 {
       return k < 32 ? v_operand(k >> 2, k & 3) : k_operand((k - 32) & 3, (k - 32) >> 2);
     };
@@ -389,11 +486,12 @@ fwd_bf16_t128_d128(FwdLaunch a) {
         if (k + PF < 64) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // online softmax of S for key tile j (tail mask for the last tile); P
   // replaces S in the same registers, packed as bf16 pairs
-  auto softmax = [&](int j) INLINE {
+  auto softmax = [&](int j, auto&& fetch_part) INLINE {
     // keys past the end of the sequence never enter the softmax; integer
     // select (no per-element compare masks) for this rare tile
     const int valid = (j >= 0 && j < a.tiles) ? N - j * BT : 0;
@@ -435,6 +533,7 @@ fwd_bf16_t128_d128(FwdLaunch a) {
     float lp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
+      fetch_part(kb);
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
         // raw v_exp_f32: results below 2^-126 flush to zero, negligible
@@ -444,7 +543,9 @@ fwd_bf16_t128_d128(FwdLaunch a) {
         bf16x2 pk;
         pk[0] = (__bf16)p0;
         pk[1] = (__bf16)p1;
-        lp[kb] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones2, lp[kb], false);
+        // plain fp32 adds: a v_dot2 here would wait for the matrix core,
+        // which the other wave on this SIMD keeps busy
+        lp[kb] += p0 + p1;
         // packed pair e/2 of this block; position e/2 <= e was already read
         s[kb][e >> 1] = __builtin_bit_cast(float, pk);
       }
@@ -452,21 +553,43 @@ fwd_bf16_t128_d128(FwdLaunch a) {
     l += (lp[0] + lp[1]) + (lp[2] + lp[3]);
   };
 
-  // vector phase: this wave's share (8 loads) of one tile fetch into slot
-  // buffer fbuf plus one L2 warm-up load, issued first so they land while
-  // the online softmax of S runs (if do_sm; key tile j for the tail mask),
-  // then awaited.  Row max and row sum use four independent chains.
-  auto vector_phase = [&](bool do_sm, int j, const __amdgpu_buffer_rsrc_t& frs,
-                          lds_char_t* fbuf, uint32_t ftoff, int warm) INLINE {
-#pragma unroll
-    for (int f = 0; f < 8; ++f) fetch_load_i(f, frs, fbuf, wg, ld_off, ftoff);
-    touch(frs, warm);
-    if (do_sm) softmax(j);
-    // this wave's share of the tile has landed; only its warm-up load may
-    // still be in flight (loads complete in issue order)
-    asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-  };
+  int w = 0;  // phase pair index (counted per group)
 
+  // vector phase: the online softmax of S (if do_sm; key tile j for the
+  // tail mask).  Group 1 also issues this wave's share of two tile fetches
+  // (8 loads each) and two L2 warm-up loads, in four bursts spread over the
+  // exponentials: the direct-to-LDS path drains about 64 B per clock per CU,
+  // and issuing all 18 loads at once would stall the wave until the queue
+  // had room.  The fetches are awaited at the end of group 1's next matrix
+  // phase.
+  auto vector_phase = [&](bool do_sm, int j, int tk, int tv, int wk, int wv) INLINE {
+    const uint32_t tko = tile_off(tk), tvo = tile_off(tv);
+    const uint32_t kbuf = (uint32_t)(uintptr_t)(kl + ((w + 1) & 1) * TILE_BYTES);
+    const uint32_t vbuf = (uint32_t)(uintptr_t)(vl + (w & 1) * TILE_BYTES);
+    const uint32_t tdst = (uint32_t)(uintptr_t)touch_dst;
+    // part 0: K loads 0-3; 1: K loads 4-7; 2: V loads 0-3; 3: V loads 4-7,
+    // then the two warm-ups, last, so that vmcnt(2) covers every fetch
+    // (part is a constant after unrolling)
+    const uint32_t skip = __builtin_amdgcn_readfirstlane(grp != 1 ? 1u : 0u);
+    auto fetch_part = [&](int part) INLINE {
+      const i32x4& rs = part < 2 ? krs4 : vrs4;
+      const uint32_t buf = (part < 2 ? kbuf : vbuf) + (uint32_t)(8 * wg * 1024);
+      const uint32_t to = part < 2 ? tko : tvo;
+      // loads 4(part%2) .. +3: rows 16(part%2) .. of this wave's 32-row share
+      dma_burst4(rs, buf + (part & 1) * 4096, ld_off, to + (part & 1) * 4096, skip);
+      if (part == 3) {
+        dma_b32_unless(krs4, tdst, touch_off, tile_off(wk), skip);
+        dma_b32_unless(vrs4, tdst, touch_off, tile_off(wv), skip);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (do_sm) {
+      softmax(j, fetch_part);
+    } else {
+#pragma unroll
+      for (int part = 0; part < 4; ++part) fetch_part(part);
+    }
+  };
 
   // ---- merged-list window: entries w-1, w, w+1, w+2 at phase pair w
   int e_m1 = NONE;
@@ -485,24 +608,21 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       fetch_load_i(i, krs, dst, wg, ld_off, t0 + grp * 4096);
     if (grp == 0) touch(vrs, ent_tile(e_0)); else touch(krs, ent_tile(e_1));
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // as a builtin, so the compiler knows every load before the loop is done
+  // and inserts no wait of its own inside it
+  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
   BARRIER();
 
-  // Phase 2w: group 0 matrix (P V of entry w-1, S of entry w), group 1
-  // vector (softmax of entry w-1).  Phase 2w+1: group 0 vector (softmax of
-  // entry w), group 1 matrix.  Fetches for entry w+1's K and entry w's V are
-  // issued in phase 2w and awaited at the end of phase 2w+1.
   // Every wave alternates matrix and vector phases; group 1 starts with a
   // vector phase (phase 0) and so is one phase behind.  Pair w = phases 2w
-  // (group 0 matrix, group 1 vector) and 2w+1 (group 0 vector, group 1
-  // matrix).  At each of its vector phases a wave sees the window
-  // (e_m1, e_0, e_1, e_2) = entries (w-1, w, w+1, w+2):
-  //   group 1 (phase 2w):   softmax of entry w-1; fetches K_{w+1} into K
-  //                         slot (w+1)%2 (free since phase 2w-1), warms K_{w+2};
-  //   group 0 (phase 2w+1): softmax of entry w; fetches V_w into V slot w%2
-  //                         (free since phase 2w-1), warms V_{w+1}.
-  // Both tiles are needed from phase 2w+2 on.  Group 0 advances its window
-  // after its vector phase, group 1 after its matrix phase.
+  // (group 0 matrix: P V of entry w-1, S of entry w; group 1 vector:
+  // softmax of entry w-1) and 2w+1 (group 0 vector: softmax of entry w;
+  // group 1 matrix: P V of entry w-1, S of entry w).  In its vector phase
+  // 2w, group 1 sees the window (e_m1, e_0, e_1, e_2) = entries
+  // (w-1, w, w+1, w+2) and fetches K_{w+1} into K slot (w+1)%2 (last read in
+  // phase 2w-1) and V_w into V slot w%2 (last read in phase 2w-1), and warms
+  // K_{w+2} and V_{w+1}.  It waits for both fetches at the end of its matrix
+  // phase 2w+1; both tiles are first read in phase 2w+2.
   auto advance = [&]() INLINE {
     e_m1 = e_0;
     e_0 = e_1;
@@ -510,38 +630,45 @@ fwd_bf16_t128_d128(FwdLaunch a) {
     e_2 = next_entry();
     flip_slots();
   };
-  int w = 0;
-  // one call site for both groups (arguments selected by group), so the
-  // softmax is instantiated once
-  auto run_vector_phase = [&]() INLINE {
-    const bool g0 = grp == 0;
-    const int es = g0 ? e_0 : e_m1;  // entry whose softmax runs now
-    const int ef = g0 ? e_0 : e_1;   // entry whose tile is fetched now
-    const int ew = g0 ? e_1 : e_2;   // entry whose tile is warmed in L2
-    lds_char_t* const fbuf =
-        g0 ? vl + (w & 1) * TILE_BYTES : kl + ((w + 1) & 1) * TILE_BYTES;
-    vector_phase(ent_in(es, grp), ent_tile(es), g0 ? vrs : krs, fbuf,
-                 tile_off(ent_tile(ef)), ent_tile(ew));
+  // One call site for both groups (arguments selected by group), so the
+  // softmax is instantiated once.  The window advances at the start of a
+  // vector phase: its scalar loads of the next list entries then complete
+  // under the softmax (a vector phase reads no LDS), not at a barrier.
+  // Group 0's softmax is of entry w (its window before the advance); group
+  // 1 advances first (except in phase 0) and runs the softmax of entry w-1.
+  auto run_vector_phase = [&](bool adv) INLINE {
+    int es;
+    if (grp == 0) {
+      es = e_0;
+      advance();
+      ++w;
+    } else {
+      if (adv) {
+        advance();
+        ++w;
+      }
+      es = e_m1;
+    }
+    vector_phase(ent_in(es, grp), ent_tile(es), ent_tile(e_1), ent_tile(e_0),
+                 ent_tile(e_2), ent_tile(e_1));
   };
   if (grp == 1 && e_0 != NONE) {
     // phase 0 (with no entry at all there is none: group 0 runs no
     // iteration either)
-    run_vector_phase();
+    run_vector_phase(false);
     BARRIER();
   }
   while (e_0 != NONE || e_m1 != NONE) {
     matrix_phase(ent_in(e_m1, grp), ent_in(e_0, grp));
     if (grp == 1) {
-      advance();
-      ++w;
+      // the tiles fetched in the previous vector phase have landed (only the
+      // two warm-up loads may still be in flight: loads complete in order)
+      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
     }
     BARRIER();
-    if (grp == 1 && !(e_0 != NONE || e_m1 != NONE)) break;
-    run_vector_phase();
-    if (grp == 0) {
-      advance();
-      ++w;
-    }
+    // group 1's window after its next advance would be (e_0, e_1, ...)
+    if (grp == 1 && !(e_1 != NONE || e_0 != NONE)) break;
+    run_vector_phase(true);
     BARRIER();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
