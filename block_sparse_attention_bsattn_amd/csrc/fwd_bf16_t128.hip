@@ -30,17 +30,14 @@
 //     tiles, and L2 -> LDS staging traffic per flop halves.
 //   * K and V tiles are double-buffered in LDS (2 x 2 x 32 KB).  Entry w's
 //     K is read in phases 2w (group 0) and 2w+1 (group 1), its V in phases
-//     2w+2 and 2w+3, so K_{w+1} and V_w are fetched during phases 2w and
-//     2w+1, two phases ahead of use.  Each wave issues its share of one
-//     fetch (8 loads of 1 KB) at the start of its vector phase and waits for
-//     it at the end: group 1 fetches K_{w+1} in phase 2w, group 0 fetches
-//     V_w in phase 2w+1.  Matrix phases issue no global-memory instruction,
-//     so the MFMA stream never stalls on the memory-address queue.  Loads
-//     are buffer_load ... lds (16 B per lane, no VGPR staging; rows past the
-//     sequence end are outside the buffer range and arrive as zeros).  The
-//     lines of the tile one entry further ahead are touched in the same
-//     phase (4 B per 128-byte line into a scratch LDS area), so the real
-//     fetches hit L2.
+//     2w+2 and 2w+3.  Both slots that K_{w+1} and V_w go to are free from
+//     phase 2w, so group 1 fetches both in its vector phase 2w (each wave 8
+//     KB of each tile, in bursts spread over its exponentials) and waits for
+//     them at the end of its matrix phase 2w+1, a phase before first use.
+//     Matrix phases issue no global-memory instruction, so the MFMA stream
+//     never stalls on the memory-address queue.  Loads are buffer_load ...
+//     lds (16 B per lane, no VGPR staging; rows past the sequence end are
+//     outside the buffer range and arrive as zeros).
 //   * LDS layout: row-major, 256 B per row, 16-byte chunk c of row R at chunk
 //     position c ^ S(R), S(R) = 4*(R % 4) + (R / 4) % 4: conflict-free for the
 //     K reader (16 consecutive rows, one chunk column) and for the
@@ -157,30 +154,12 @@ __device__ __forceinline__ void fetch_load_i(int i, __amdgpu_buffer_rsrc_t rs, l
 // them.  They have no register results (the data goes straight to LDS), and
 // their operands are read at issue.  One wait state separates the M0 write
 // from the load.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-template <int IMM>
-__device__ __forceinline__ void dma_b128(const i32x4& rs, uint32_t m0, uint32_t voff,
-                                         uint32_t soff) {
-  asm volatile(
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds"
-      :
-      : "v"(voff), "s"(rs), "s"(soff), "i"(IMM), "{m0}"(m0)
-      : "memory");
-}
-__device__ __forceinline__ void dma_b32(const i32x4& rs, uint32_t m0, uint32_t voff,
-                                        uint32_t soff) {
-  asm volatile(
-      "s_nop 0\n\t"
-      "buffer_load_dword %0, %1, %2 offen lds"
-      :
-      : "v"(voff), "s"(rs), "s"(soff), "{m0}"(m0)
-      : "memory");
-}
+//
 // Four loads of a tile fetch (loads 4h .. 4h+3 of fetch_load, one M0) as
 // one statement that the wave skips as a whole when `skip` is nonzero: no
 // branch is visible to the compiler, so the statement can be pinned between
 // blocks of other work.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void dma_burst4(const i32x4& rs, uint32_t m0, const uint32_t* voff,
                                            uint32_t soff, uint32_t skip) {
   asm volatile(
@@ -196,26 +175,6 @@ __device__ __forceinline__ void dma_burst4(const i32x4& rs, uint32_t m0, const u
       : "s"(skip), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rs), "s"(soff),
         "{m0}"(m0)
       : "memory", "scc");
-}
-// One 4-byte-per-lane direct-to-LDS load, skipped when `skip` is nonzero.
-__device__ __forceinline__ void dma_b32_unless(const i32x4& rs, uint32_t m0, uint32_t voff,
-                                               uint32_t soff, uint32_t skip) {
-  asm volatile(
-      "s_cmp_eq_u32 %0, 0\n\t"
-      "s_cbranch_scc0 .Lbsattn_skip_%=\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dword %1, %2, %3 offen lds\n"
-      ".Lbsattn_skip_%=:"
-      :
-      : "s"(skip), "v"(voff), "s"(rs), "s"(soff), "{m0}"(m0)
-      : "memory", "scc");
-}
-// Load I (0..7) of a tile fetch, as fetch_load<I>.
-template <int I>
-__device__ __forceinline__ void fetch_asm(const i32x4& rs, uint32_t buf, int wg, uint32_t voff,
-                                          uint32_t toff) {
-  dma_b128<1024 * (I & 3)>(rs, buf + (uint32_t)((8 * wg + 4 * (I >> 2)) * 1024), voff,
-                           toff + 4096 * (I >> 2));
 }
 __device__ __forceinline__ i32x4 raw_rsrc(const void* base, int nbytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -248,8 +207,6 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // bit 15 moves a read address to the other slot; V likewise
   __shared__ __attribute__((aligned(65536))) char kslots[2 * TILE_BYTES];
   __shared__ __attribute__((aligned(65536))) char vslots[2 * TILE_BYTES];
-  // landing area of the L2 warm-up loads (4 B per lane, never read)
-  __shared__ __attribute__((aligned(256))) char touch_area[8 * 256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -265,8 +222,6 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // null).
   lds_char_t* const kl = uniform_lds((lds_char_t*)kslots);
   lds_char_t* const vl = uniform_lds((lds_char_t*)vslots);
-  lds_void_t* const touch_dst =
-      (lds_void_t*)uniform_lds((lds_char_t*)touch_area + wave * 256);
 
   // ---- XCD-aware remap of the 1-D grid onto (batch*head, query-tile pair)
   const uint32_t G = gridDim.x, hw = blockIdx.x;
@@ -353,12 +308,6 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   auto tile_off = [&](int j) INLINE {
     return (j >= 0 && j < a.tiles) ? (uint32_t)j * TILE_BYTES : 0x80000000u;
   };
-  // L2 warm-up of a whole tile by one group: lane l of wave wg touches line
-  // 64 wg + l
-  const uint32_t touch_off = (uint32_t)((64 * wg + lane) * 128);
-  auto touch = [&](const __amdgpu_buffer_rsrc_t& rs, int j) INLINE {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, touch_dst, 4, touch_off, tile_off(j), 0, 0);
-  };
 
   // Per-lane LDS read addresses of slot 0 (K) and slot 1 (V) (base folded in
   // once), so every read is one VGPR plus an immediate offset; bit 15 flips
@@ -367,32 +316,23 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // (= l / 16) points at key row R0 + s/4, d = 32 db + 16 (g16%2) + 4 (s%4);
   // R0 = kb*32 + 8 i0 + 8 sec + 4 half.
   const int ks = swz(l32);
-  lds_char_t* kr_addr[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c)
-    kr_addr[c] = kl + (l32 * ROW_BYTES + (((2 * c + half) ^ ks) << 4));
+  uint32_t kr = (uint32_t)(uintptr_t)kl +
+                (uint32_t)(l32 * ROW_BYTES + ((ks >> 1) << 5) + ((half ^ (ks & 1)) << 4));
   const int s16 = lane & 15;
   const int g16 = lane >> 4;
-  lds_char_t* vr_addr[2][4];
+  uint32_t vr[2];
 #pragma unroll
-  for (int sec = 0; sec < 2; ++sec)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int rrel = 8 * sec + 4 * half + (s16 >> 2);
-      const int chunk = 4 * db + 2 * (g16 & 1) + ((s16 & 3) >> 1);
-      const int sw = ((s16 >> 2) << 2) | ((2 * sec + half) & 3);
-      vr_addr[sec][db] =
-          vl + (TILE_BYTES + rrel * ROW_BYTES + ((chunk ^ sw) << 4) + 8 * (s16 & 1));
-    }
+  for (int sec = 0; sec < 2; ++sec) {
+    const int q4 = s16 >> 2;
+    const int rrel = 8 * sec + 4 * half + q4;
+    const int low = (2 * (g16 & 1) + ((s16 & 3) >> 1)) ^ ((2 * sec + half) & 3);
+    vr[sec] = (uint32_t)(uintptr_t)vl +
+              (uint32_t)(TILE_BYTES + rrel * ROW_BYTES + (q4 << 6) + (low << 4) + 8 * (s16 & 1));
+  }
   auto flip_slots = [&]() INLINE {
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      kr_addr[c] = (lds_char_t*)((uintptr_t)kr_addr[c] ^ (uintptr_t)TILE_BYTES);
-#pragma unroll
-    for (int sec = 0; sec < 2; ++sec)
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        vr_addr[sec][db] = (lds_char_t*)((uintptr_t)vr_addr[sec][db] ^ (uintptr_t)TILE_BYTES);
+    kr ^= (uint32_t)TILE_BYTES;
+    vr[0] ^= (uint32_t)TILE_BYTES;
+    vr[1] ^= (uint32_t)TILE_BYTES;
   };
 
   f32x16 oacc[4];
@@ -413,8 +353,10 @@ fwd_bf16_t128_d128(FwdLaunch a) {
 
   auto v_operand = [&](int kc, int db) INLINE {
     const int rows = (kc >> 1) * 32 * ROW_BYTES + (kc & 1) * 16 * ROW_BYTES;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vr_addr[0][db] + rows));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vr_addr[1][db] + rows));
+    const uint32_t a0 = (vr[0] ^ (uint32_t)(db << 6)) + (uint32_t)rows;
+    const uint32_t a1 = (vr[1] ^ (uint32_t)(db << 6)) + (uint32_t)rows;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)a0);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)a1);
     const bf16x4 lob = __builtin_bit_cast(bf16x4, lo);
     const bf16x4 hib = __builtin_bit_cast(bf16x4, hi);
     bf16x8 va;
@@ -423,7 +365,8 @@ fwd_bf16_t128_d128(FwdLaunch a) {
     return va;
   };
   auto k_operand = [&](int kb, int c) INLINE {
-    return *(const lds_bf16x8_t*)(kr_addr[c] + kb * 32 * ROW_BYTES);
+    const uint32_t ad = (kr ^ (uint32_t)(c << 5)) + (uint32_t)(kb * 32 * ROW_BYTES);
+    return *(const lds_bf16x8_t*)(uintptr_t)ad;
   };
   auto p_operand = [&](int kc) INLINE {
     const f32x16& v = s[kc >> 1];
@@ -440,15 +383,19 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   auto matrix_phase = [&](bool do_pv, bool do_qk) INLINE {
     // the MFMA stream wins issue ties against the other group's VALU work
     __builtin_amdgcn_s_setprio(1);
+    // S stream order: chunk-outer, four interleaved accumulation chains
+    // (one per key block), which hides the MFMA result latency
+    auto qk_kb = [](int k) { return (k - 32) & 3; };
+    auto qk_c = [](int k) { return (k - 32) >> 2; };
     auto load = [&](int k) INLINE -> bf16x8 {
-      return k < 32 ? v_operand(k >> 2, k & 3) : k_operand((k - 32) & 3, (k - 32) >> 2);
+      return k < 32 ? v_operand(k >> 2, k & 3) : k_operand(qk_kb(k), qk_c(k));
     };
     auto step = [&](int k, const bf16x8& opnd) INLINE {
       if (k < 32) {
         const int kc = k >> 2, db = k & 3;
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd, p_operand(kc), oacc[db], 0, 0, 0);
       } else {
-        const int c = (k - 32) >> 2, kb = (k - 32) & 3;
+        const int c = qk_c(k), kb = qk_kb(k);
         if (c == 0) {
           const f32x16 zero = {};
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd, qf[0], zero, 0, 0, 0);
@@ -557,18 +504,16 @@ fwd_bf16_t128_d128(FwdLaunch a) {
 
   // vector phase: the online softmax of S (if do_sm; key tile j for the
   // tail mask).  Group 1 also issues this wave's share of two tile fetches
-  // (8 loads each) and two L2 warm-up loads, in four bursts spread over the
+  // (8 loads each, K tile tk and V tile tv) in four bursts spread over the
   // exponentials: the direct-to-LDS path drains about 64 B per clock per CU,
-  // and issuing all 18 loads at once would stall the wave until the queue
+  // and issuing all 16 loads at once would stall the wave until the queue
   // had room.  The fetches are awaited at the end of group 1's next matrix
   // phase.
-  auto vector_phase = [&](bool do_sm, int j, int tk, int tv, int wk, int wv) INLINE {
+  auto vector_phase = [&](bool do_sm, int j, int tk, int tv) INLINE {
     const uint32_t tko = tile_off(tk), tvo = tile_off(tv);
     const uint32_t kbuf = (uint32_t)(uintptr_t)(kl + ((w + 1) & 1) * TILE_BYTES);
     const uint32_t vbuf = (uint32_t)(uintptr_t)(vl + (w & 1) * TILE_BYTES);
-    const uint32_t tdst = (uint32_t)(uintptr_t)touch_dst;
-    // part 0: K loads 0-3; 1: K loads 4-7; 2: V loads 0-3; 3: V loads 4-7,
-    // then the two warm-ups, last, so that vmcnt(2) covers every fetch
+    // part 0: K loads 0-3; 1: K loads 4-7; 2: V loads 0-3; 3: V loads 4-7
     // (part is a constant after unrolling)
     const uint32_t skip = __builtin_amdgcn_readfirstlane(grp != 1 ? 1u : 0u);
     auto fetch_part = [&](int part) INLINE {
@@ -577,10 +522,6 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       const uint32_t to = part < 2 ? tko : tvo;
       // loads 4(part%2) .. +3: rows 16(part%2) .. of this wave's 32-row share
       dma_burst4(rs, buf + (part & 1) * 4096, ld_off, to + (part & 1) * 4096, skip);
-      if (part == 3) {
-        dma_b32_unless(krs4, tdst, touch_off, tile_off(wk), skip);
-        dma_b32_unless(vrs4, tdst, touch_off, tile_off(wv), skip);
-      }
       __builtin_amdgcn_sched_barrier(0);
     };
     if (do_sm) {
@@ -597,8 +538,7 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   int e_1 = next_entry();
   int e_2 = next_entry();
 
-  // ---- prologue: K_0 into slot 0 (every wave loads 4 of the 32 KB) and L2
-  // warm-up of K_1 (group 1) and V_0 (group 0)
+  // ---- prologue: K_0 into slot 0 (every wave loads 4 of the 32 KB)
   if (e_0 != NONE) {
     const uint32_t t0 = tile_off(ent_tile(e_0));
     lds_char_t* dst = kl + (grp * 4) * 1024;  // group g loads rows 16g.. of each 64-row half
@@ -606,7 +546,6 @@ fwd_bf16_t128_d128(FwdLaunch a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       fetch_load_i(i, krs, dst, wg, ld_off, t0 + grp * 4096);
-    if (grp == 0) touch(vrs, ent_tile(e_0)); else touch(krs, ent_tile(e_1));
   }
   // as a builtin, so the compiler knows every load before the loop is done
   // and inserts no wait of its own inside it
@@ -620,8 +559,8 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // group 1 matrix: P V of entry w-1, S of entry w).  In its vector phase
   // 2w, group 1 sees the window (e_m1, e_0, e_1, e_2) = entries
   // (w-1, w, w+1, w+2) and fetches K_{w+1} into K slot (w+1)%2 (last read in
-  // phase 2w-1) and V_w into V slot w%2 (last read in phase 2w-1), and warms
-  // K_{w+2} and V_{w+1}.  It waits for both fetches at the end of its matrix
+  // phase 2w-1) and V_w into V slot w%2 (last read in phase 2w-1).  It
+  // waits for both fetches at the end of its matrix
   // phase 2w+1; both tiles are first read in phase 2w+2.
   auto advance = [&]() INLINE {
     e_m1 = e_0;
@@ -649,8 +588,7 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       }
       es = e_m1;
     }
-    vector_phase(ent_in(es, grp), ent_tile(es), ent_tile(e_1), ent_tile(e_0),
-                 ent_tile(e_2), ent_tile(e_1));
+    vector_phase(ent_in(es, grp), ent_tile(es), ent_tile(e_1), ent_tile(e_0));
   };
   if (grp == 1 && e_0 != NONE) {
     // phase 0 (with no entry at all there is none: group 0 runs no
@@ -661,9 +599,8 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   while (e_0 != NONE || e_m1 != NONE) {
     matrix_phase(ent_in(e_m1, grp), ent_in(e_0, grp));
     if (grp == 1) {
-      // the tiles fetched in the previous vector phase have landed (only the
-      // two warm-up loads may still be in flight: loads complete in order)
-      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      // the tiles fetched in the previous vector phase have landed
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     BARRIER();
     // group 1's window after its next advance would be (e_0, e_1, ...)
