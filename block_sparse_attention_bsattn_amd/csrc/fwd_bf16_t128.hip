@@ -247,22 +247,32 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // Each list keeps its validated head c (index i) and the raw entry at
   // index i + 1, loaded one step ahead: a value is validated only when it
   // becomes the head, by which time its scalar load has long completed.
+  // Branch-free (selects only), so the scalar work interleaves with the
+  // vector work around it: the look-ahead is reloaded on every step from a
+  // clamped index (the same entry again when its list did not move; a
+  // row_ptr entry when the list is empty).
   auto valid = [&](int r) INLINE { return (r >= 0 && r < a.tiles) ? r : BAD_TILE; };
-  auto raw_at = [&](int jbx, int nx, int i) INLINE { return i < nx ? col_idx[jbx + i] : 0; };
+  const sconst_i32 la0 = n0 > 0 ? col_idx + jb0 : row_ptr;
+  const sconst_i32 la1 = n1 > 0 ? col_idx + jb1 : row_ptr;
+  const int last0 = n0 > 0 ? n0 - 1 : 0, last1 = n1 > 0 ? n1 - 1 : 0;
   int i0 = 0, i1 = 0;
-  int c0 = n0 > 0 ? valid(col_idx[jb0]) : LIST_END;
-  int c1 = n1 > 0 ? valid(col_idx[jb1]) : LIST_END;
-  int r0 = raw_at(jb0, n0, 1), r1 = raw_at(jb1, n1, 1);
+  int c0 = n0 > 0 ? valid(la0[0]) : LIST_END;
+  int c1 = n1 > 0 ? valid(la1[0]) : LIST_END;
+  int r0 = la0[min(1, last0)], r1 = la1[min(1, last1)];
   auto next_entry = [&]() INLINE {
-    if (c0 == LIST_END && c1 == LIST_END) return NONE;
+    const bool done = c0 == LIST_END && c1 == LIST_END;
     const int j = min(c0, c1);
-    const int f0 = c0 == j, f1 = c1 == j;
+    const int f0 = !done && c0 == j, f1 = !done && c1 == j;
     // new heads first, from values loaded earlier; then the new look-aheads
-    if (f0) c0 = ++i0 < n0 ? valid(r0) : LIST_END;
-    if (f1) c1 = ++i1 < n1 ? valid(r1) : LIST_END;
-    if (f0) r0 = raw_at(jb0, n0, i0 + 1);
-    if (f1) r1 = raw_at(jb1, n1, i1 + 1);
-    return j | (f0 << 30) | (f1 << 29);
+    i0 += f0;
+    i1 += f1;
+    const int h0 = i0 < n0 ? valid(r0) : LIST_END;
+    const int h1 = i1 < n1 ? valid(r1) : LIST_END;
+    c0 = f0 ? h0 : c0;
+    c1 = f1 ? h1 : c1;
+    r0 = la0[min(i0 + 1, last0)];
+    r1 = la1[min(i1 + 1, last1)];
+    return done ? NONE : (j | (f0 << 30) | (f1 << 29));
   };
 
   // ---- Q^T operand: lane holds q[row l%32][8 d values], 8 chunks of 16 d
@@ -572,23 +582,20 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // One call site for both groups (arguments selected by group), so the
   // softmax is instantiated once.  The window advances at the start of a
   // vector phase: its scalar loads of the next list entries then complete
-  // under the softmax (a vector phase reads no LDS), not at a barrier.
-  // Group 0's softmax is of entry w (its window before the advance); group
-  // 1 advances first (except in phase 0) and runs the softmax of entry w-1.
-  auto run_vector_phase = [&](bool adv) INLINE {
-    int es;
-    if (grp == 0) {
-      es = e_0;
+  // under the softmax (a vector phase reads no LDS), not at a barrier.  In
+  // the loop both groups run the softmax of entry e_0 (before the advance)
+  // and group 1 fetches K of e_2 and V of e_1 (also before the advance);
+  // in phase 0 group 1 does not advance (softmax of nothing, fetches K of
+  // e_1 and V of e_0).
+  auto run_vector_phase = [&](bool in_loop) INLINE {
+    const int es = in_loop ? e_0 : NONE;
+    const int tk = ent_tile(in_loop ? e_2 : e_1);
+    const int tv = ent_tile(in_loop ? e_1 : e_0);
+    if (in_loop) {
       advance();
       ++w;
-    } else {
-      if (adv) {
-        advance();
-        ++w;
-      }
-      es = e_m1;
     }
-    vector_phase(ent_in(es, grp), ent_tile(es), ent_tile(e_1), ent_tile(e_0));
+    vector_phase(ent_in(es, grp), ent_tile(es), tk, tv);
   };
   if (grp == 1 && e_0 != NONE) {
     // phase 0 (with no entry at all there is none: group 0 runs no
