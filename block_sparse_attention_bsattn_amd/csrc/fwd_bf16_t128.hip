@@ -228,10 +228,10 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   const uint32_t q8 = G / NXCD, r8 = G % NXCD, xcd = hw % NXCD, slot = hw / NXCD;
   const uint32_t logical =
       (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + slot;
+  // one workgroup per query-tile pair (qt0, qt0 + 1)
   const uint32_t pairs = (uint32_t)(a.tiles + 1) >> 1;
   const int bh = (int)(logical / pairs);
   const int qt0 = 2 * (int)(logical % pairs);
-  const int qt = qt0 + grp;
   const int h = bh % a.H;
   const int N = a.N;
   const int64_t head_row = (int64_t)bh * N;
@@ -252,13 +252,23 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // clamped index (the same entry again when its list did not move; a
   // row_ptr entry when the list is empty).
   auto valid = [&](int r) INLINE { return (r >= 0 && r < a.tiles) ? r : BAD_TILE; };
-  const sconst_i32 la0 = n0 > 0 ? col_idx + jb0 : row_ptr;
-  const sconst_i32 la1 = n1 > 0 ? col_idx + jb1 : row_ptr;
-  const int last0 = n0 > 0 ? n0 - 1 : 0, last1 = n1 > 0 ? n1 - 1 : 0;
-  int i0 = 0, i1 = 0;
-  int c0 = n0 > 0 ? valid(la0[0]) : LIST_END;
-  int c1 = n1 > 0 ? valid(la1[0]) : LIST_END;
-  int r0 = la0[min(1, last0)], r1 = la1[min(1, last1)];
+  sconst_i32 la0, la1;
+  int m0n, m1n, last0, last1, i0, i1, c0, c1, r0, r1;
+  // (re)start the iterator on lists A = (jbA, nA) and B = (jbB, nB)
+  auto init_lists = [&](int jbA, int nA, int jbB, int nB) INLINE {
+    m0n = nA;
+    m1n = nB;
+    la0 = nA > 0 ? col_idx + jbA : row_ptr;
+    la1 = nB > 0 ? col_idx + jbB : row_ptr;
+    last0 = nA > 0 ? nA - 1 : 0;
+    last1 = nB > 0 ? nB - 1 : 0;
+    i0 = 0;
+    i1 = 0;
+    c0 = nA > 0 ? valid(la0[0]) : LIST_END;
+    c1 = nB > 0 ? valid(la1[0]) : LIST_END;
+    r0 = la0[min(1, last0)];
+    r1 = la1[min(1, last1)];
+  };
   auto next_entry = [&]() INLINE {
     const bool done = c0 == LIST_END && c1 == LIST_END;
     const int j = min(c0, c1);
@@ -266,8 +276,8 @@ fwd_bf16_t128_d128(FwdLaunch a) {
     // new heads first, from values loaded earlier; then the new look-aheads
     i0 += f0;
     i1 += f1;
-    const int h0 = i0 < n0 ? valid(r0) : LIST_END;
-    const int h1 = i1 < n1 ? valid(r1) : LIST_END;
+    const int h0 = i0 < m0n ? valid(r0) : LIST_END;
+    const int h1 = i1 < m1n ? valid(r1) : LIST_END;
     c0 = f0 ? h0 : c0;
     c1 = f1 ? h1 : c1;
     r0 = la0[min(i0 + 1, last0)];
@@ -275,23 +285,59 @@ fwd_bf16_t128_d128(FwdLaunch a) {
     return done ? NONE : (j | (f0 << 30) | (f1 << 29));
   };
 
-  // ---- Q^T operand: lane holds q[row l%32][8 d values], 8 chunks of 16 d
-  const bool q_tile_real = qt < a.tiles;
-  const int qrow = qt * BT + wg * 32 + l32;
-  bf16x8 qf[8];
+  // ---- mode of this workgroup.  Pair mode (both groups walk the union of
+  // their two lists, each staged tile serving both query tiles) wins when
+  // the lists largely coincide, as for window masks.  When they do not (a
+  // random static mask), each group would sit idle through the entries
+  // only the other needs; split mode instead runs the two query tiles one
+  // after the other, both groups on the same tile, taking alternate list
+  // entries.  A split phase costs about 1.6 pair phases (each staged tile
+  // serves half the rows, and a fetch has one phase to land instead of
+  // two), so split mode is taken below 40 % estimated overlap, and always
+  // when one list is empty.  The overlap is estimated on the first 8
+  // entries of both lists; the choice affects speed only.
+  bool split;
   {
-    const __bf16* qptr =
-        reinterpret_cast<const __bf16*>(a.q) + (head_row + qrow) * D + half * 8;
+    constexpr int KS = 8;
+    const int ks_ = min(min(n0, n1), KS);
+    int va[KS], vb[KS];
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      va[i] = n0 > 0 ? col_idx[jb0 + min(i, n0 - 1)] : 0;
+      vb[i] = n1 > 0 ? col_idx[jb1 + min(i, n1 - 1)] : 0;
+    }
+    int ia = 0, ib = 0, match = 0;
+#pragma unroll
+    for (int st = 0; st < 2 * KS; ++st) {
+      int x = va[0], y = vb[0];
+#pragma unroll
+      for (int i = 1; i < KS; ++i) {
+        x = ia == i ? va[i] : x;
+        y = ib == i ? vb[i] : y;
+      }
+      const bool live = ia < ks_ && ib < ks_;
+      match += (live && x == y) ? 1 : 0;
+      ia += (live && x <= y) ? 1 : 0;
+      ib += (live && y <= x) ? 1 : 0;
+    }
+    split = ks_ == 0 || 5 * match < 2 * ks_;
+  }
+
+  // ---- Q^T operand: lane holds q[row l%32][8 d values], 8 chunks of 16 d
+  bf16x8 qf[8];
+  auto load_q = [&](int tq) INLINE {
+    const int qr = tq * BT + wg * 32 + l32;
+    const __bf16* qptr = reinterpret_cast<const __bf16*>(a.q) + (head_row + qr) * D + half * 8;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      if (q_tile_real && qrow < N) {
+      if (tq < a.tiles && qr < N) {
         qf[c] = *reinterpret_cast<const bf16x8*>(qptr + c * 16);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) qf[c][e] = (__bf16)0.f;
       }
     }
-  }
+  };
 
   // ---- buffer resources for this head's K and V rows
   const char* kbase = reinterpret_cast<const char*>(a.k) + head_row * ROW_BYTES;
@@ -510,22 +556,17 @@ fwd_bf16_t128_d128(FwdLaunch a) {
     l += (lp[0] + lp[1]) + (lp[2] + lp[3]);
   };
 
-  int w = 0;  // phase pair index (counted per group)
-
   // vector phase: the online softmax of S (if do_sm; key tile j for the
-  // tail mask).  Group 1 also issues this wave's share of two tile fetches
-  // (8 loads each, K tile tk and V tile tv) in four bursts spread over the
-  // exponentials: the direct-to-LDS path drains about 64 B per clock per CU,
-  // and issuing all 16 loads at once would stall the wave until the queue
-  // had room.  The fetches are awaited at the end of group 1's next matrix
-  // phase.
-  auto vector_phase = [&](bool do_sm, int j, int tk, int tv) INLINE {
+  // tail mask) and, unless skip, this wave's share of two tile fetches (8
+  // loads each: K tile tk into LDS slot kbuf, V tile tv into slot vbuf) in
+  // four bursts spread over the exponentials: the direct-to-LDS path drains
+  // about 64 B per clock per CU, and issuing all 16 loads at once would
+  // stall the wave until the queue had room.
+  auto vector_phase = [&](bool do_sm, int j, int tk, int tv, uint32_t kbuf, uint32_t vbuf,
+                          uint32_t skip) INLINE {
     const uint32_t tko = tile_off(tk), tvo = tile_off(tv);
-    const uint32_t kbuf = (uint32_t)(uintptr_t)(kl + ((w + 1) & 1) * TILE_BYTES);
-    const uint32_t vbuf = (uint32_t)(uintptr_t)(vl + (w & 1) * TILE_BYTES);
     // part 0: K loads 0-3; 1: K loads 4-7; 2: V loads 0-3; 3: V loads 4-7
     // (part is a constant after unrolling)
-    const uint32_t skip = __builtin_amdgcn_readfirstlane(grp != 1 ? 1u : 0u);
     auto fetch_part = [&](int part) INLINE {
       const i32x4& rs = part < 2 ? krs4 : vrs4;
       const uint32_t buf = (part < 2 ? kbuf : vbuf) + (uint32_t)(8 * wg * 1024);
@@ -542,110 +583,265 @@ fwd_bf16_t128_d128(FwdLaunch a) {
     }
   };
 
-  // ---- merged-list window: entries w-1, w, w+1, w+2 at phase pair w
-  int e_m1 = NONE;
-  int e_0 = next_entry();
-  int e_1 = next_entry();
-  int e_2 = next_entry();
+  const uint32_t kl32 = (uint32_t)(uintptr_t)kl, vl32 = (uint32_t)(uintptr_t)vl;
+  const uint32_t kr_slot0 = kr, vr0_slot0 = vr[0] ^ (uint32_t)TILE_BYTES,
+                 vr1_slot0 = vr[1] ^ (uint32_t)TILE_BYTES;
 
-  // ---- prologue: K_0 into slot 0 (every wave loads 4 of the 32 KB)
-  if (e_0 != NONE) {
-    const uint32_t t0 = tile_off(ent_tile(e_0));
-    lds_char_t* dst = kl + (grp * 4) * 1024;  // group g loads rows 16g.. of each 64-row half
-    // each wave of the 8 fills 4 KB: loads 4 grp .. 4 grp + 3 of its wg share
+  // K of entry e (a key tile) into K slot 0, loaded by all 8 waves (4 KB
+  // each), then a full wait and a barrier
+  auto load_first_k = [&](int e) INLINE {
+    if (e != NONE) {
+      const uint32_t t0 = tile_off(ent_tile(e));
+      lds_char_t* dst = kl + (grp * 4) * 1024;  // group g loads rows 16g.. of each 64-row half
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      fetch_load_i(i, krs, dst, wg, ld_off, t0 + grp * 4096);
-  }
-  // as a builtin, so the compiler knows every load before the loop is done
-  // and inserts no wait of its own inside it
-  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-  BARRIER();
-
-  // Every wave alternates matrix and vector phases; group 1 starts with a
-  // vector phase (phase 0) and so is one phase behind.  Pair w = phases 2w
-  // (group 0 matrix: P V of entry w-1, S of entry w; group 1 vector:
-  // softmax of entry w-1) and 2w+1 (group 0 vector: softmax of entry w;
-  // group 1 matrix: P V of entry w-1, S of entry w).  In its vector phase
-  // 2w, group 1 sees the window (e_m1, e_0, e_1, e_2) = entries
-  // (w-1, w, w+1, w+2) and fetches K_{w+1} into K slot (w+1)%2 (last read in
-  // phase 2w-1) and V_w into V slot w%2 (last read in phase 2w-1).  It
-  // waits for both fetches at the end of its matrix
-  // phase 2w+1; both tiles are first read in phase 2w+2.
-  auto advance = [&]() INLINE {
-    e_m1 = e_0;
-    e_0 = e_1;
-    e_1 = e_2;
-    e_2 = next_entry();
-    flip_slots();
-  };
-  // One call site for both groups (arguments selected by group), so the
-  // softmax is instantiated once.  The window advances at the start of a
-  // vector phase: its scalar loads of the next list entries then complete
-  // under the softmax (a vector phase reads no LDS), not at a barrier.  In
-  // the loop both groups run the softmax of entry e_0 (before the advance)
-  // and group 1 fetches K of e_2 and V of e_1 (also before the advance);
-  // in phase 0 group 1 does not advance (softmax of nothing, fetches K of
-  // e_1 and V of e_0).
-  auto run_vector_phase = [&](bool in_loop) INLINE {
-    const int es = in_loop ? e_0 : NONE;
-    const int tk = ent_tile(in_loop ? e_2 : e_1);
-    const int tv = ent_tile(in_loop ? e_1 : e_0);
-    if (in_loop) {
-      advance();
-      ++w;
+      for (int i = 0; i < 4; ++i) fetch_load_i(i, krs, dst, wg, ld_off, t0 + grp * 4096);
     }
-    vector_phase(ent_in(es, grp), ent_tile(es), tk, tv);
+    // as a builtin, so the compiler knows every load before the loop is done
+    // and inserts no wait of its own inside it
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+    BARRIER();
   };
-  if (grp == 1 && e_0 != NONE) {
-    // phase 0 (with no entry at all there is none: group 0 runs no
-    // iteration either)
-    run_vector_phase(false);
-    BARRIER();
-  }
-  while (e_0 != NONE || e_m1 != NONE) {
-    matrix_phase(ent_in(e_m1, grp), ent_in(e_0, grp));
-    if (grp == 1) {
-      // the tiles fetched in the previous vector phase have landed
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    BARRIER();
-    // group 1's window after its next advance would be (e_0, e_1, ...)
-    if (grp == 1 && !(e_1 != NONE || e_0 != NONE)) break;
-    run_vector_phase(true);
-    BARRIER();
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- epilogue: O = O^T / l, rows past N (or of a missing tile) not written
-  {
+  // O = O^T / l for this wave's rows of query tile tq (rows past N not
+  // written); db0 .. db0 + ndb - 1 are the 32-wide d blocks written
+  auto store_o = [&](int tq, float inv, int db0, int ndb) INLINE {
+    const int qr = tq * BT + wg * 32 + l32;
+    if (tq < a.tiles && qr < N) {
+      __bf16* op = reinterpret_cast<__bf16*>(a.o) + (head_row + qr) * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        if (db < db0 || db >= db0 + ndb) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bf16x4 v;
+          v[0] = (__bf16)(oacc[db][4 * i] * inv);
+          v[1] = (__bf16)(oacc[db][4 * i + 1] * inv);
+          v[2] = (__bf16)(oacc[db][4 * i + 2] * inv);
+          v[3] = (__bf16)(oacc[db][4 * i + 3] * inv);
+          *reinterpret_cast<bf16x4*>(op + db * 32 + 8 * i + 4 * half) = v;
+        }
+      }
+    }
+  };
+  auto store_lse = [&](int tq, float mm, float ll) INLINE {
+    const int qr = tq * BT + wg * 32 + l32;
+    if (tq < a.tiles && qr < N && a.lse != nullptr && half == 0)
+      a.lse[head_row + qr] = ll > 0.f ? (mm + log2f(ll)) * 0.69314718055994531f : -INFINITY;
+  };
+  auto l_over_halves = [&]() INLINE {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l),
                                                     false, false);
     l = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  if (q_tile_real && qrow < N) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    __bf16* op = reinterpret_cast<__bf16*>(a.o) + (head_row + qrow) * D;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bf16x4 v;
-        v[0] = (__bf16)(oacc[db][4 * i] * inv);
-        v[1] = (__bf16)(oacc[db][4 * i + 1] * inv);
-        v[2] = (__bf16)(oacc[db][4 * i + 2] * inv);
-        v[3] = (__bf16)(oacc[db][4 * i + 3] * inv);
-        *reinterpret_cast<bf16x4*>(op + db * 32 + 8 * i + 4 * half) = v;
+  };
+
+  int e_m1, e_0, e_1, e_2;
+  if (!split) {
+    // ================= pair mode =================
+    const int qt = qt0 + grp;
+    load_q(qt);
+    init_lists(jb0, n0, jb1, n1);
+    kr = kr_slot0;
+    vr[0] = vr0_slot0 ^ (uint32_t)TILE_BYTES;
+    vr[1] = vr1_slot0 ^ (uint32_t)TILE_BYTES;
+    int w = 0;  // phase pair index (counted per group)
+
+    // ---- merged-list window: entries w-1, w, w+1, w+2 at phase pair w
+    e_m1 = NONE;
+    e_0 = next_entry();
+    e_1 = next_entry();
+    e_2 = next_entry();
+
+    // ---- prologue: K_0 into slot 0
+    load_first_k(e_0);
+
+    // Every wave alternates matrix and vector phases; group 1 starts with a
+    // vector phase (phase 0) and so is one phase behind.  Pair w = phases
+    // 2w (group 0 matrix: P V of entry w-1, S of entry w; group 1 vector:
+    // softmax of entry w-1) and 2w+1 (group 0 vector: softmax of entry w;
+    // group 1 matrix: P V of entry w-1, S of entry w).  In its vector phase
+    // 2w, group 1 sees the window (e_m1, e_0, e_1, e_2) = entries
+    // (w-1, w, w+1, w+2) and fetches K_{w+1} into K slot (w+1)%2 (last read
+    // in phase 2w-1) and V_w into V slot w%2 (last read in phase 2w-1).  It
+    // waits for both fetches at the end of its matrix phase 2w+1; both tiles
+    // are first read in phase 2w+2.
+    auto advance = [&]() INLINE {
+      e_m1 = e_0;
+      e_0 = e_1;
+      e_1 = e_2;
+      e_2 = next_entry();
+      flip_slots();
+    };
+    // One call site for both groups (arguments selected by group), so the
+    // softmax is instantiated once per mode.  The window advances at the
+    // start of a vector phase: its scalar loads of the next list entries
+    // then complete under the softmax (a vector phase reads no LDS), not at
+    // a barrier.  In the loop both groups run the softmax of entry e_0
+    // (before the advance) and group 1 fetches K of e_2 and V of e_1 (also
+    // before the advance); in phase 0 group 1 does not advance (softmax of
+    // nothing, fetches K of e_1 and V of e_0).
+    const uint32_t skip = __builtin_amdgcn_readfirstlane(grp != 1 ? 1u : 0u);
+    auto run_vector_phase = [&](bool in_loop) INLINE {
+      const int es = in_loop ? e_0 : NONE;
+      const int tk = ent_tile(in_loop ? e_2 : e_1);
+      const int tv = ent_tile(in_loop ? e_1 : e_0);
+      if (in_loop) {
+        advance();
+        ++w;
       }
-    if (a.lse != nullptr && half == 0)
-      a.lse[head_row + qrow] =
-          l > 0.f ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+      vector_phase(ent_in(es, grp), ent_tile(es), tk, tv,
+                   kl32 + (uint32_t)(((w + 1) & 1) * TILE_BYTES),
+                   vl32 + (uint32_t)((w & 1) * TILE_BYTES), skip);
+    };
+    if (grp == 1 && e_0 != NONE) {
+      // phase 0 (with no entry at all there is none: group 0 runs no
+      // iteration either)
+      run_vector_phase(false);
+      BARRIER();
+    }
+    while (e_0 != NONE || e_m1 != NONE) {
+      matrix_phase(ent_in(e_m1, grp), ent_in(e_0, grp));
+      if (grp == 1) {
+        // the tiles fetched in the previous vector phase have landed
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      BARRIER();
+      // group 1's window after its next advance would be (e_0, e_1, ...)
+      if (grp == 1 && !(e_1 != NONE || e_0 != NONE)) break;
+      run_vector_phase(true);
+      BARRIER();
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // ---- epilogue: O = O^T / l
+    l_over_halves();
+    store_o(qt, l > 0.f ? 1.f / l : 0.f, 0, 4);
+    store_lse(qt, m, l);
+  } else {
+    // ================= split mode =================
+    // Both groups work on one query tile (the same 128 rows, the same Q),
+    // entry e of its list going to group e % 2.  Phase p: group p % 2 runs
+    // its matrix phase (P V of entry p-2, S of entry p) from its own K and
+    // V slots (slot g of group g); the other group runs the softmax of
+    // entry p-1 and fetches K of entry p+1 and V of entry p-1 into its own
+    // slots (last read in phase p-1), awaited before the barrier that ends
+    // phase p.  Each group thus holds partial (m, l, O) over its entries;
+    // they are combined at the end.
+    float* const xo = reinterpret_cast<float*>(kslots);  // exchange area
+    float* const xml = reinterpret_cast<float*>(vslots);
+#pragma unroll 1
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tq = qt0 + tt;
+      if (tq >= a.tiles) break;
+      if (tt > 0) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+        m = -INFINITY;
+        l = 0.f;
+      }
+      load_q(tq);
+      init_lists(tt == 0 ? jb0 : jb1, tt == 0 ? n0 : n1, 0, 0);
+      kr = kr_slot0 ^ (uint32_t)(grp * TILE_BYTES);
+      vr[0] = vr0_slot0 ^ (uint32_t)(grp * TILE_BYTES);
+      vr[1] = vr1_slot0 ^ (uint32_t)(grp * TILE_BYTES);
+      // window: entries p-2, p-1, p, p+1 in phase p
+      e_2 = NONE;  // entry p-2
+      e_m1 = NONE;
+      e_0 = next_entry();
+      e_1 = next_entry();
+      load_first_k(e_0);
+      const uint32_t kown = kl32 + (uint32_t)(grp * TILE_BYTES);
+      const uint32_t vown = vl32 + (uint32_t)(grp * TILE_BYTES);
+      // n + 2 phases (p = 0 .. n+1); group g runs its matrix phases at
+      // p = g, g+2, ... and its vector phases in between, so both groups
+      // pass the same n + 2 barriers
+      const int nphase = (tt == 0 ? n0 : n1) + 2;
+      auto split_advance = [&]() INLINE {
+        e_2 = e_m1;
+        e_m1 = e_0;
+        e_0 = e_1;
+        e_1 = next_entry();
+      };
+      auto split_vector = [&]() INLINE {
+        // the softmax always runs: with no entry (j = -1) every score is
+        // masked to -inf, so P = 0 and m, l and O stay as they are (a
+        // runtime choice here costs the register allocator dearly)
+        vector_phase(true, ent_tile(e_m1), ent_tile(e_1), ent_tile(e_m1), kown, vown, 0u);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        BARRIER();
+        split_advance();
+      };
+      if (grp == 1) split_vector();  // phase 0
+      // (an exit rather than a conditional vector phase: the matrix and
+      // vector phases then never sit on alternative paths, which costs the
+      // register allocator dearly)
+#pragma unroll 1
+      for (int p = grp; p < nphase; p += 2) {
+        matrix_phase(e_2 != NONE, e_0 != NONE);
+        BARRIER();
+        split_advance();
+        if (p + 1 >= nphase) break;
+        split_vector();
+      }
+      // ---- combine the two groups' (m, l, O): group 0 finishes d blocks 0
+      // and 1, group 1 blocks 2 and 3; each hands the other half over
+      // through LDS (the K slots, free now)
+      l_over_halves();
+      // (d-block indices are compile-time constants in every access: a
+      // runtime index would move the accumulators to scratch memory)
+      auto give_half = [&](int base) INLINE {
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+          for (int f4 = 0; f4 < 4; ++f4) {
+            f32x4 v;
+            v[0] = oacc[base + d2][4 * f4];
+            v[1] = oacc[base + d2][4 * f4 + 1];
+            v[2] = oacc[base + d2][4 * f4 + 2];
+            v[3] = oacc[base + d2][4 * f4 + 3];
+            *reinterpret_cast<f32x4*>(xo + ((wave * 8 + d2 * 4 + f4) * 64 + lane) * 4) = v;
+          }
+      };
+      if (grp == 0) give_half(2); else give_half(0);
+      xml[(wave * 64 + lane) * 2] = m;
+      xml[(wave * 64 + lane) * 2 + 1] = l;
+      BARRIER();
+      const int pw = wave ^ 4;  // the other group's wave with the same rows
+      const float mp = xml[(pw * 64 + lane) * 2];
+      const float lpn = xml[(pw * 64 + lane) * 2 + 1];
+      const float mt = fmaxf(m, mp);
+      const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mt);
+      const float a1 = mp == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mp - mt);
+      auto keep_half = [&](int base) INLINE {
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+          for (int f4 = 0; f4 < 4; ++f4) {
+            const f32x4 v =
+                *reinterpret_cast<const f32x4*>(xo + ((pw * 8 + d2 * 4 + f4) * 64 + lane) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              oacc[base + d2][4 * f4 + e] = oacc[base + d2][4 * f4 + e] * a0 + v[e] * a1;
+          }
+      };
+      if (grp == 0) keep_half(0); else keep_half(2);
+      const float lt = l * a0 + lpn * a1;
+      if (grp == 0)
+        store_o(tq, lt > 0.f ? 1.f / lt : 0.f, 0, 2);
+      else
+        store_o(tq, lt > 0.f ? 1.f / lt : 0.f, 2, 2);
+      if (grp == 0) store_lse(tq, mt, lt);
+      // the exchange area is the next tile's K slot 0
+      BARRIER();
+    }
   }
 }
 
 }  // namespace
 
 int launch_fwd_bf16_t128_d128(const FwdLaunch& a, void* stream) {
+  // one workgroup per (batch*head, query-tile pair), in either mode
   const int64_t blocks = (int64_t)a.B * a.H * ((a.tiles + 1) / 2);
   hipLaunchKernelGGL(fwd_bf16_t128_d128, dim3((unsigned)blocks), dim3(512), 0,
                      (hipStream_t)stream, a);
