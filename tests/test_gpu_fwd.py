@@ -194,3 +194,97 @@ def test_full_size_sampled_rows(cfg, stride):
     idx = torch.from_numpy(rows).cuda()
     assert_close(f"{w.name} ({len(rows)} rows x {w.B * w.H} heads)",
                  to64(o[:, :, idx]), o_ref, to64(lse[:, :, idx]), lse_ref)
+
+
+def test_tuned_kernel_pair_and_split_lists_and_bad_indices():
+    """bf16 / d 128 / tile 128 (the tuned kernel) on hand-built lists whose
+    query-tile pairs have identical, disjoint, empty, nearly identical and
+    random lists, so both of its per-workgroup modes run in one launch; then
+    the same lists with out-of-range key-tile indices mixed in, which must be
+    skipped."""
+    w = W.small_workload(frames=16, grid_h=8, grid_w=16, tile=128, d=128, H=2)
+    Tn = w.num_tiles
+    assert Tn == 16
+    g = np.random.default_rng(77)
+    m = np.zeros((2, Tn, Tn), dtype=np.uint8)
+    for h in range(2):
+        lists = {
+            0: [0, 3, 5, 9, 15], 1: [0, 3, 5, 9, 15],          # identical
+            2: [1, 2, 3, 4, 5, 6, 7, 8], 3: [1, 2, 3, 4, 5, 6, 7, 8],
+            4: [0, 2, 4, 6], 5: [1, 3, 7, 11, 13],            # disjoint
+            6: [], 7: [6, 7, 8],                              # one empty
+            8: [1, 2, 3, 4, 5, 9], 9: [2, 3, 4, 5, 9, 10],     # near-identical
+            10: [], 11: [],                                   # both empty
+        }
+        for i in range(12, 16):
+            lists[i] = sorted(g.choice(Tn, size=int(g.integers(1, 9)),
+                                       replace=False).tolist())
+        if h == 1:  # another arrangement for the second head
+            lists = {i: lists[(i + 4) % 16] for i in range(16)}
+        for i, js in lists.items():
+            m[h, i, js] = 1
+    q, k, v = W.make_qkv(w, device="cuda")
+    rp, ci = bs.make_csr(torch.from_numpy(m).cuda())
+    o, lse = bs.attention(q, k, v, rp, ci, w.tile, mask_heads=2, want_lse=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.block_sparse_attention(q.cpu(), k.cpu(), v.cpu(), m,
+                                                   w.tile)
+    assert_close("pair/split lists", to64(o), o_ref, to64(lse), lse_ref)
+
+    # the same lists with out-of-range entries (-1, Tk, a large index) added
+    rows, cols = [0], []
+    for r in range(2 * Tn):
+        js = np.nonzero(m.reshape(2 * Tn, Tn)[r])[0].tolist()
+        if r % 3 == 0:
+            js = js + [Tn]
+        if r % 4 == 1:
+            js = [-1] + js
+        if r % 5 == 2:
+            js = js + [1 << 20]
+        cols += js
+        rows.append(len(cols))
+    rp2 = torch.tensor(rows, dtype=torch.int32, device="cuda")
+    ci2 = torch.tensor(cols + [0], dtype=torch.int32, device="cuda")
+    o2, lse2 = bs.attention(q, k, v, rp2, ci2, w.tile, mask_heads=2,
+                            want_lse=True)
+    torch.cuda.synchronize()
+    assert_close("out-of-range entries skipped", to64(o2), o_ref, to64(lse2),
+                 lse_ref)
+
+
+@pytest.mark.parametrize("mode", ["pair", "split"])
+def test_tuned_kernel_never_reads_the_partner_tiles(mode):
+    """In a query-tile pair, key tiles that only one tile of the pair reads
+    are filled with NaN: the other tile's rows must be bitwise unchanged
+    (pair mode skips them, split mode never fetches them for that tile)."""
+    w = W.small_workload(frames=4, grid_h=8, grid_w=16, tile=128, d=128, H=1)
+    Tn = w.num_tiles
+    m = np.zeros((1, Tn, Tn), dtype=np.uint8)
+    if mode == "pair":   # nearly identical lists
+        m[0, 0, [0, 1, 2, 3]] = 1
+        m[0, 1, [0, 1, 3]] = 1
+        m[0, 2, [0, 1, 2, 3]] = 1
+        m[0, 3, [0, 1, 2, 3]] = 1
+        only_a = [2]
+    else:                # unrelated lists
+        m[0, 0, [0, 2]] = 1
+        m[0, 1, [1, 3]] = 1
+        m[0, 2, [0, 1, 2, 3]] = 1
+        m[0, 3, [0, 1, 2, 3]] = 1
+        only_a = [0, 2]
+    q, k, v = W.make_qkv(w, device="cuda")
+    rp, ci = bs.make_csr(torch.from_numpy(m).cuda())
+    o1, l1 = bs.attention(q, k, v, rp, ci, w.tile, want_lse=True)
+    kp, vp = k.clone(), v.clone()
+    for j in only_a:
+        kp[:, :, j * w.tile:(j + 1) * w.tile] = float("nan")
+        vp[:, :, j * w.tile:(j + 1) * w.tile] = float("nan")
+    o2, l2 = bs.attention(q, kp, vp, rp, ci, w.tile, want_lse=True)
+    torch.cuda.synchronize()
+    rows_b = slice(w.tile, 2 * w.tile)   # query tile 1
+    assert torch.isfinite(o2[:, :, rows_b].float()).all()
+    assert torch.equal(o1[:, :, rows_b], o2[:, :, rows_b])
+    assert torch.equal(l1[:, :, rows_b], l2[:, :, rows_b])
+    o_ref, l_ref = oracle.block_sparse_attention(q.cpu(), k.cpu(), v.cpu(), m,
+                                                 w.tile)
+    assert_close(f"{mode} mode", to64(o1), o_ref, to64(l1), l_ref)
