@@ -8,7 +8,8 @@ library never does, and nothing here imports the library.
 Sources (page title, then section):
   * "LVSA: Training-Free Sparse Attention for Long Video Diffusion",
     Meccanismo Core: the frame set A(t) = G u W(t) of a query frame t, the
-    rotating periodic global anchors G and the local window W(t).
+    rotating periodic global anchors G and the local window W(t), plain or
+    expanded to a frame budget C.
   * "Accelerating Text-to-Video Generation with Calibrated Sparse Attention",
     A. Fase di Calibrazione / B. Fase di Inferenza: 128x128 attention blocks,
     a static per-(timestep, layer, head) block mask, attention computed only
@@ -29,6 +30,8 @@ attention output itself has no printed worked example on the pages; it is
 pinned only through those definitions and invariants.
 """
 from .masks import (anchor_frames, window_frames, frame_set, frame_mask,
+                    expanded_window_frames, frame_set_expanded,
+                    frame_mask_expanded, tile_mask_expanded,
                     tile_frame_range, tile_mask_window_anchor,
                     splitmix64_stream, static_hash24, tile_mask_static,
                     tile_mask_dense, tile_mask)
@@ -37,6 +40,8 @@ from .attention import block_sparse_attention, block_sparse_attention_rows
 
 __all__ = [
     "anchor_frames", "window_frames", "frame_set", "frame_mask",
+    "expanded_window_frames", "frame_set_expanded", "frame_mask_expanded",
+    "tile_mask_expanded",
     "tile_frame_range", "tile_mask_window_anchor", "splitmix64_stream",
     "static_hash24", "tile_mask_static", "tile_mask_dense", "tile_mask",
     "tile_csr", "block_sparse_attention", "block_sparse_attention_rows",

@@ -13,7 +13,7 @@ exactly once.
 
 Readings taken where the page leaves a step open:
   * W(t) = {f in [0, T) : |f - t| <= w}, a symmetric window of half-width w,
-    clipped to the video; the adaptive expansion is not applied.
+    clipped to the video (the plain window mode).
   * n_a anchors evenly spaced from the rotation r:
     G_r = {(r + floor(k*T/n_a)) mod T : 0 <= k < n_a}; the caller chooses r
     (e.g. step mod T_per, or (layer + step) mod T).
@@ -21,6 +21,23 @@ Readings taken where the page leaves a step open:
   * A frame pair lifts to tiles by "any overlap": tile pair (i, j) is active
     when some frame covered by tile i may attend to some frame covered by
     tile j.  Inside an active tile pair every token pair is computed.
+
+Expanded adaptive windows (LVSA page, Meccanismo Core, the expanded window
+bounds that keep |A(t)| close to a frame budget C, e.g. the model's training
+horizon).  The page says the window grows to make up for frames it shares with
+G, but not on which side or in which order.  Reading taken:
+  * the target is min(C, T) distinct frames in A(t);
+  * the window starts as the plain W(t) above and only ever grows;
+  * it grows one frame at a time, taking the frame nearest to t that is not
+    yet in it, the earlier frame first when two are equally near; frames
+    outside [0, T) do not exist, so at either end of the video it grows on
+    the other side only;
+  * an anchor frame reached this way joins the window but adds nothing to
+    |A(t)|, so growth continues past it;
+  * growth stops as soon as |G u W(t)| >= min(C, T).
+So W(t) stays a contiguous run of frames around t, |A(t)| equals
+max(min(C, T), |G u W_plain(t)|), and C = n_a + 2w + 1 makes up exactly for
+anchor overlap and for the clipped window at the ends of the video.
 
 Static mode (CalibAtt page, B. Fase di Inferenza: a precomputed, deterministic
 per-(timestep, layer, head) block list).  Real calibrated masks need the model
@@ -69,6 +86,38 @@ def frame_mask(T: int, w: int, n_a: int, r: int) -> np.ndarray:
     return F
 
 
+def expanded_window_frames(t: int, T: int, w: int, n_a: int, r: int,
+                           budget: int) -> set:
+    """W(t) grown from the plain window until |G u W(t)| reaches min(C, T)
+    (LVSA page, Meccanismo Core, expanded adaptive windows)."""
+    G = anchor_frames(T, n_a, r)
+    W = window_frames(t, T, w)
+    target = min(budget, T)
+    nearest_first = sorted(range(T), key=lambda f: (abs(f - t), f))
+    for f in nearest_first:
+        if len(G | W) >= target:
+            break
+        W.add(f)
+    return W
+
+
+def frame_set_expanded(t: int, T: int, w: int, n_a: int, r: int,
+                       budget: int) -> set:
+    """A(t) = G_r u W(t) with the expanded window."""
+    return anchor_frames(T, n_a, r) | expanded_window_frames(t, T, w, n_a, r,
+                                                             budget)
+
+
+def frame_mask_expanded(T: int, w: int, n_a: int, r: int,
+                        budget: int) -> np.ndarray:
+    """F[t, f] = 1 when query frame t attends to key frame f (expanded)."""
+    F = np.zeros((T, T), dtype=np.uint8)
+    for t in range(T):
+        for f in frame_set_expanded(t, T, w, n_a, r, budget):
+            F[t, f] = 1
+    return F
+
+
 # --------------------------------------------------------------- tile lift
 def tile_frame_range(i: int, N: int, P: int, BT: int):
     """First and last frame covered by tile i."""
@@ -88,21 +137,39 @@ def _tile_frame_incidence(T: int, P: int, BT: int) -> np.ndarray:
     return inc
 
 
-def tile_mask_window_anchor(T: int, grid_h: int, grid_w: int, BT: int,
-                            w: int, n_a: int, r: int) -> np.ndarray:
+def _lift(F: np.ndarray, T: int, grid_h: int, grid_w: int,
+          BT: int) -> np.ndarray:
     """M[i, j] = OR over frames t of tile i and f of tile j of F[t, f].
 
     With tile-frame incidence matrix I this is [I F I^T > 0]."""
+    inc = _tile_frame_incidence(T, grid_h * grid_w, BT)
+    return ((inc @ F.astype(np.int64) @ inc.T) > 0).astype(np.uint8)
+
+
+def _check_frame_args(T: int, w: int, n_a: int):
     if T <= 0:
         raise ValueError("need at least one frame")
     if not (0 <= n_a <= T):
         raise ValueError("anchor count must lie in [0, T]")
     if w < 0:
         raise ValueError("window half-width must be >= 0")
-    P = grid_h * grid_w
-    F = frame_mask(T, w, n_a, r).astype(np.int64)
-    inc = _tile_frame_incidence(T, P, BT)
-    return ((inc @ F @ inc.T) > 0).astype(np.uint8)
+
+
+def tile_mask_window_anchor(T: int, grid_h: int, grid_w: int, BT: int,
+                            w: int, n_a: int, r: int) -> np.ndarray:
+    """Tile mask of the plain window + anchor rule."""
+    _check_frame_args(T, w, n_a)
+    return _lift(frame_mask(T, w, n_a, r), T, grid_h, grid_w, BT)
+
+
+def tile_mask_expanded(T: int, grid_h: int, grid_w: int, BT: int, w: int,
+                       n_a: int, r: int, budget: int) -> np.ndarray:
+    """Tile mask of the expanded-window + anchor rule."""
+    _check_frame_args(T, w, n_a)
+    if budget < 0:
+        raise ValueError("frame budget must be >= 0")
+    return _lift(frame_mask_expanded(T, w, n_a, r, budget), T, grid_h, grid_w,
+                 BT)
 
 
 # ------------------------------------------------------------- static mode
@@ -142,9 +209,9 @@ def tile_mask_dense(Hm: int, Tq: int, Tk: int) -> np.ndarray:
 def tile_mask(kind: int, frames: int, grid_h: int, grid_w: int, tile: int,
               window: int = 0, num_anchors: int = 0, rotation: int = 0,
               seed: int = 0, thresh24: int = 0, force_diagonal: int = 0,
-              mask_heads: int = 1) -> np.ndarray:
+              mask_heads: int = 1, budget: int = 0) -> np.ndarray:
     """uint8 [Hm, Tq, Tk] tile mask for kind 0 (window + anchors),
-    1 (static random) or 2 (dense)."""
+    1 (static random), 2 (dense) or 3 (expanded window + anchors)."""
     N = frames * grid_h * grid_w
     nt = -(-N // tile)
     if kind == 0:
@@ -156,4 +223,8 @@ def tile_mask(kind: int, frames: int, grid_h: int, grid_w: int, tile: int,
                                 bool(force_diagonal))
     if kind == 2:
         return tile_mask_dense(mask_heads, nt, nt)
+    if kind == 3:
+        M = tile_mask_expanded(frames, grid_h, grid_w, tile, window,
+                               num_anchors, rotation, budget)
+        return np.repeat(M[None], mask_heads, axis=0)
     raise ValueError(f"unknown mask kind {kind}")

@@ -207,3 +207,111 @@ def test_thresh24_encoding():
     assert W.thresh24_for_density(0.3) == 5033164
     assert W.thresh24_for_density(1.0) == 1 << 24
     assert W.thresh24_for_density(0.0) == 0
+
+
+# -------------------------------------------------- expanded adaptive windows
+def _golden_cases(name):
+    cases, cur = [], None
+    for ln in read_golden(name):
+        if ln.startswith("case"):
+            kv = ln.split()[1:]
+            cur = (dict(zip(kv[0::2], map(int, kv[1::2]))), {})
+            cases.append(cur)
+        else:
+            t, frames = ln.split(":")
+            cur[1][int(t)] = {int(f) for f in frames.split()}
+    return cases
+
+
+def test_expanded_frame_sets_match_hand_enumeration():
+    cases = _golden_cases("expanded_window_frame_sets.txt")
+    assert len(cases) == 2
+    for kv, want in cases:
+        T = kv["T"]
+        assert sorted(want) == list(range(T))
+        for t in range(T):
+            got = oracle.frame_set_expanded(t, T, kv["window"], kv["anchors"],
+                                            kv["rotation"], kv["budget"])
+            assert got == want[t], (kv, t)
+            assert len(got) == kv["budget"]
+
+
+def test_expanded_tile_mask_matches_hand_enumeration():
+    lines = read_golden("expanded_window_tile_mask.txt")
+    hdr = lines[0].split()
+    kv = dict(zip(hdr[0::2], map(int, hdr[1::2])))
+    want = _parse_rows(lines[1:])
+    got = oracle.tile_mask(3, kv["frames"], kv["grid_h"], kv["grid_w"],
+                           kv["tile"], window=kv["window"],
+                           num_anchors=kv["anchors"], rotation=kv["rotation"],
+                           budget=kv["budget"], mask_heads=2)
+    assert got.shape == (2,) + want.shape
+    np.testing.assert_array_equal(got[0], want)
+    np.testing.assert_array_equal(got[1], want)
+
+
+@pytest.mark.parametrize("T,w,n_a,r", [(10, 1, 2, 3), (21, 1, 2, 5),
+                                       (7, 0, 0, 0), (13, 3, 13, 4)])
+def test_expanded_small_budget_is_the_plain_window(T, w, n_a, r):
+    """A budget no larger than |G u W_plain(t)| leaves the window alone, so
+    the mask equals the plain window + anchor mask."""
+    for C in (0, 1, n_a + 1):
+        np.testing.assert_array_equal(
+            oracle.frame_mask_expanded(T, w, n_a, r, C),
+            oracle.frame_mask(T, w, n_a, r))
+
+
+@pytest.mark.parametrize("T,w,n_a,r", [(9, 1, 3, 1), (21, 0, 2, 20),
+                                       (5, 4, 1, 0)])
+def test_expanded_budget_of_whole_video_is_dense(T, w, n_a, r):
+    for C in (T, T + 1, 10 * T):
+        assert (oracle.frame_mask_expanded(T, w, n_a, r, C) == 1).all()
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 12, 21])
+def test_expanded_without_anchors_is_the_nearest_run(T):
+    """No anchors, w = 0: A(t) is the run of L = min(C, T) frames around t,
+    one more frame before t than after when L is even, pushed inward at the
+    ends of the video: lo = max(0, min(t - ceil((L-1)/2), T - L))."""
+    for C in range(1, T + 3):
+        L = min(C, T)
+        for t in range(T):
+            lo = max(0, min(t - (L // 2), T - L))
+            want = set(range(lo, lo + L))
+            assert oracle.frame_set_expanded(t, T, 0, 0, 0, C) == want, (C, t)
+
+
+def test_expanded_window_is_balanced_and_minimal():
+    """Properties of the growth order on a sweep of small cases: W(t) is one
+    run [lo, hi] around t containing the plain window; away from the ends it
+    reaches at most one frame further back than forward (earlier frame
+    first); |A(t)| = max(min(C, T), |G u W_plain(t)|); and if the window grew
+    at all, dropping the frame added last falls short of the target."""
+    n = 0
+    for T in (1, 2, 3, 6, 11, 16):
+        for n_a in sorted({0, 1, 2, T // 3, T}):
+            for w in (0, 1, 3):
+                for r in (0, T // 2 + 1):
+                    G = oracle.anchor_frames(T, n_a, r)
+                    for C in range(0, T + 2):
+                        target = min(C, T)
+                        for t in range(T):
+                            Wp = oracle.window_frames(t, T, w)
+                            W = oracle.expanded_window_frames(t, T, w, n_a, r,
+                                                              C)
+                            lo, hi = min(W), max(W)
+                            assert W == set(range(lo, hi + 1))
+                            assert Wp <= W and lo <= t <= hi
+                            A = G | W
+                            assert len(A) == max(target, len(G | Wp))
+                            if W == Wp:
+                                continue
+                            back, fwd = t - lo, hi - t
+                            if lo > 0 and hi < T - 1:
+                                assert back - fwd in (0, 1)
+                            # the frame added last is the farthest from t,
+                            # the later one of two equally far
+                            last = max(W, key=lambda f: (abs(f - t), f))
+                            assert len(G | (W - {last})) < target
+                            n += 1
+    assert n > 500
