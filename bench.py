@@ -12,7 +12,9 @@ Printed: ONE JSON line with
   roofline     the forward kernel's active TFLOP/s per launch (HIP events on
                the launch stream) against the bf16 dense MFMA peak,
   cpu_baseline the float64 CPU oracle on a bounded row sample,
-plus the forward-only time, the same kernel at density 1.0 and the speedup.
+plus the forward-only time, the same kernel at density 1.0 and the speedup,
+a density sweep, and the path with LVSA expanded windows on the 84-frame
+long-video shape.
 """
 from __future__ import annotations
 
@@ -94,6 +96,59 @@ def density_sweep(bs, W, torch, dev, q, k, v, o, calls: int = 5):
             "fit_r2": round(float(r2), 5)}
 
 
+def expanded_windows(bs, W, torch, dev, calls: int):
+    """The whole path with LVSA expanded windows on the 84-frame long-video
+    shape (131 040 tokens, window +-2 grown to a 21-frame budget, 4 rotating
+    anchors): `calls` steps at rotations 0, 1, ..., each timed in its three
+    parts with events on the launch stream."""
+    w = W.EXPANDED
+    q, k, v = W.make_qkv(w, device=dev)
+    o = torch.empty_like(q)
+    Tn = w.num_tiles
+    mask = torch.empty((1, Tn, Tn), dtype=torch.uint8, device=dev)
+    row_ptr = torch.empty(Tn + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(Tn * Tn, dtype=torch.int32, device=dev)
+    layout = (w.frames, w.grid_h, w.grid_w, w.tile)
+    stream = torch.cuda.current_stream()
+
+    def run(r, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        bs.build_mask(layout, mask, stream=stream,
+                      **bs.mask_params_of(w.with_rotation(r).mask))
+        if ev is not None:
+            ev[1].record(stream)
+        bs.compact(mask, row_ptr, col_idx, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    flops, dens = [], []
+    for r in range(calls):
+        run(r)
+        m_np = mask.cpu().numpy()
+        flops.append(active_flops(m_np, w))
+        dens.append(float(m_np.mean()))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+           for _ in range(calls)]
+    for r in range(calls):
+        run(r, evs[r])
+    torch.cuda.synchronize()
+    part = lambda a, b: np.array([e[a].elapsed_time(e[b]) for e in evs])
+    fwd_ms, step_ms = part(2, 3), part(0, 3)
+    return {"workload": w.name,
+            "mask": "window +-2 frames grown to a 21-frame budget + 4 anchors, "
+                    "rotation 0.." + str(calls - 1),
+            "density_mean": round(float(np.mean(dens)), 4),
+            "build_mask_us": round(float(np.median(part(0, 1))) * 1e3, 2),
+            "compact_us": round(float(np.median(part(1, 2))) * 1e3, 2),
+            "fwd_ms_median": round(float(np.median(fwd_ms)), 4),
+            "fwd_tflops": round(float(np.sum(flops) / (fwd_ms.sum() * 1e-3)) / 1e12, 1),
+            "step_tflops": round(float(np.sum(flops) / (step_ms.sum() * 1e-3)) / 1e12, 1)}
+
+
 def cpu_baseline(w, q, k, v, mask_np, tiles: int, workers: int):
     """The oracle as it stands, on `tiles` evenly spaced query tiles (every
     row of them, every head) at rotation 0; TFLOP/s credited like the GPU
@@ -143,6 +198,9 @@ def main():
                     help="measure the register-only MFMA ceiling (0 = skip)")
     ap.add_argument("--sweep", type=int, default=1,
                     help="density sweep with static masks (0 = skip)")
+    ap.add_argument("--expanded", type=int, default=6,
+                    help="steps of the expanded-window long-video path "
+                         "(0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB "
                          "(byte-counter calibration under a profiler)")
@@ -255,6 +313,9 @@ def main():
 
     sweep = density_sweep(bs, W, torch, dev, q, k, v, o) if args.sweep else None
 
+    expanded = expanded_windows(bs, W, torch, dev, args.expanded) \
+        if args.expanded > 0 else None
+
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -324,6 +385,7 @@ def main():
         "speedup_vs_density_1": None if dense_ms is None else
         round(dense_ms / float(fwd_ms.mean()), 3),
         "density_sweep": sweep,
+        "expanded_windows": expanded,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

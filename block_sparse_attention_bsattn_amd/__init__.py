@@ -55,7 +55,7 @@ class MaskParams(ctypes.Structure):
                 ("num_anchors", ctypes.c_int32), ("rotation", ctypes.c_int32),
                 ("seed", ctypes.c_uint64), ("thresh24", ctypes.c_uint32),
                 ("force_diagonal", ctypes.c_int32),
-                ("mask_heads", ctypes.c_int32)]
+                ("mask_heads", ctypes.c_int32), ("budget", ctypes.c_int32)]
 
 
 _lib = None
@@ -134,10 +134,10 @@ def num_tiles(tokens: int, tile: int) -> int:
 
 
 def _params(kind, window=0, num_anchors=0, rotation=0, seed=0, thresh24=0,
-            force_diagonal=0, mask_heads=1) -> MaskParams:
+            force_diagonal=0, mask_heads=1, budget=0) -> MaskParams:
     return MaskParams(kind, window, num_anchors, rotation,
                       seed & 0xFFFFFFFFFFFFFFFF, thresh24, int(force_diagonal),
-                      mask_heads)
+                      mask_heads, budget)
 
 
 def build_mask(layout: Sequence[int], mask, stream=None, **params):
@@ -145,7 +145,7 @@ def build_mask(layout: Sequence[int], mask, stream=None, **params):
 
     layout = (frames, grid_h, grid_w, tile); params are the fields of
     bsattn_mask_params (kind, window, num_anchors, rotation, seed, thresh24,
-    force_diagonal, mask_heads)."""
+    force_diagonal, mask_heads, budget)."""
     import torch
     L = Layout(*[int(x) for x in layout])
     P = _params(**params)
@@ -258,4 +258,4 @@ def mask_params_of(spec) -> dict:
                 num_anchors=spec.num_anchors, rotation=spec.rotation,
                 seed=spec.seed, thresh24=spec.thresh24,
                 force_diagonal=spec.force_diagonal,
-                mask_heads=spec.mask_heads)
+                mask_heads=spec.mask_heads, budget=spec.budget)

@@ -77,17 +77,21 @@ BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
   const int64_t tokens = per_frame * L.frames;
   if (tokens > INT32_MAX)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: more than 2^31-1 tokens");
-  if (M.kind < BSATTN_MASK_WINDOW_ANCHOR || M.kind > BSATTN_MASK_DENSE)
+  if (M.kind < BSATTN_MASK_WINDOW_ANCHOR || M.kind > BSATTN_MASK_WINDOW_ANCHOR_EXPANDED)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: unknown mask kind %d", M.kind);
   if (M.mask_heads < 1)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: mask_heads must be >= 1");
-  if (M.kind == BSATTN_MASK_WINDOW_ANCHOR) {
+  const bool frame_rule = M.kind == BSATTN_MASK_WINDOW_ANCHOR ||
+                          M.kind == BSATTN_MASK_WINDOW_ANCHOR_EXPANDED;
+  if (frame_rule) {
     if (M.window < 0)
       return fail(BSATTN_ERR_INVALID_ARG, "build_mask: window must be >= 0");
     if (M.num_anchors < 0 || M.num_anchors > L.frames)
       return fail(BSATTN_ERR_INVALID_ARG,
                   "build_mask: num_anchors must lie in [0, frames]");
   }
+  if (M.kind == BSATTN_MASK_WINDOW_ANCHOR_EXPANDED && M.budget < 0)
+    return fail(BSATTN_ERR_INVALID_ARG, "build_mask: budget must be >= 0");
   if (M.kind == BSATTN_MASK_STATIC_RANDOM && M.thresh24 > (1u << 24))
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: thresh24 exceeds 2^24");
   const int32_t tiles = bsattn_num_tiles(tokens, L.tile);
@@ -104,7 +108,10 @@ BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
   a.tq = tiles;
   a.tk = tiles;
   a.mask_heads = M.mask_heads;
-  a.window = M.window;
+  a.window = frame_rule ? (M.window < L.frames ? M.window : L.frames) : 0;
+  a.budget = M.kind == BSATTN_MASK_WINDOW_ANCHOR_EXPANDED
+                 ? (M.budget < L.frames ? M.budget : L.frames)
+                 : 0;
   a.num_anchors = M.num_anchors;
   a.rotation = ((M.rotation % L.frames) + L.frames) % L.frames;
   a.seed = M.seed;

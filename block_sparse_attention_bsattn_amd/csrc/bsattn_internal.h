@@ -10,7 +10,8 @@ struct MaskLaunch {
   int32_t kind;
   int32_t frames, tokens_per_frame, tokens, tile;
   int32_t tq, tk, mask_heads;
-  int32_t window, num_anchors, rotation;  // rotation already in [0, frames)
+  int32_t window, num_anchors, rotation;  // window <= frames, rotation in [0, frames)
+  int32_t budget;                         // expanded mode: min(C, frames)
   uint64_t seed;
   uint32_t thresh24;
   int32_t force_diagonal;

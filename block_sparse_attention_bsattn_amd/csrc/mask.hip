@@ -12,6 +12,16 @@
 // The anchor part is independent of the query tile: some anchor frame
 // g_k = (r + floor(k*T/n_a)) mod T lies in the key tile's range.
 //
+// Expanded mode (same section, the expanded adaptive windows that hold |A(t)|
+// near a frame budget C): the window of query frame t grows from [t-w, t+w]
+// by the nearest missing frame, the earlier one on a tie and never past the
+// video's ends, until |G u W(t)| >= min(C, T); an anchor frame it passes adds
+// nothing.  W(t) stays one interval [lo(t), hi(t)], found by walking outward
+// from the plain window while counting the non-anchor frames taken.  Whether
+// a frame is an anchor is O(1): the offsets floor(k*T/n_a) strictly increase
+// with k (n_a <= T), so frame f is an anchor exactly when k = ceil(g*n_a/T),
+// g = (f - r) mod T, satisfies k < n_a and floor(k*T/n_a) == g.
+//
 // Static mode (CalibAtt page, "B. Fase di Inferenza": the block lists are
 // precomputed and deterministic) draws one SplitMix64 value per cell
 // c = (h*Tq + i)*Tk + j: the (c+1)-th output of the generator seeded with
@@ -39,6 +49,44 @@ __device__ __forceinline__ void frame_range(int tile_idx, int tile, int tokens,
   hi = last / per_frame;
 }
 
+__device__ __forceinline__ int is_anchor(int f, const MaskLaunch& a) {
+  if (a.num_anchors == 0) return 0;
+  const int g = f >= a.rotation ? f - a.rotation : f - a.rotation + a.frames;
+  const int64_t k = ((int64_t)g * a.num_anchors + a.frames - 1) / a.frames;
+  return k < a.num_anchors && ((int64_t)k * a.frames) / a.num_anchors == g;
+}
+
+// [lo, hi]: the expanded window of query frame t.
+__device__ void expanded_window(int t, const MaskLaunch& a, int& lo, int& hi) {
+  const int T = a.frames;
+  lo = max(0, t - a.window);
+  hi = min(T - 1, t + a.window);
+  int count = a.num_anchors;
+  for (int f = lo; f <= hi; ++f) count += !is_anchor(f, a);
+  // count reaches T once [lo, hi] = [0, T-1], and budget <= T, so the walk
+  // stops by then; d < T bounds it regardless.
+  for (int d = a.window + 1; count < a.budget && d < T; ++d) {
+    if (t - d >= 0) {
+      lo = t - d;
+      count += !is_anchor(lo, a);
+      if (count >= a.budget) break;
+    }
+    if (t + d < T) {
+      hi = t + d;
+      count += !is_anchor(hi, a);
+    }
+  }
+}
+
+__device__ __forceinline__ int anchor_in(int ka, int kb, const MaskLaunch& a) {
+  for (int k = 0; k < a.num_anchors; ++k) {
+    const int g = (int)((a.rotation + ((int64_t)k * a.frames) / a.num_anchors) %
+                        a.frames);
+    if (g >= ka && g <= kb) return 1;
+  }
+  return 0;
+}
+
 __global__ void build_mask_kernel(MaskLaunch a, uint8_t* __restrict__ mask) {
   const int64_t total = (int64_t)a.mask_heads * a.tq * a.tk;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -48,17 +96,21 @@ __global__ void build_mask_kernel(MaskLaunch a, uint8_t* __restrict__ mask) {
     const int64_t hi_row = c / a.tk;
     const int i = (int)(hi_row % a.tq);
     uint8_t on = 0;
-    if (a.kind == 0) {
+    if (a.kind == 0 || a.kind == 3) {
       int qa, qb, ka, kb;
       frame_range(i, a.tile, a.tokens, a.tokens_per_frame, qa, qb);
       frame_range(j, a.tile, a.tokens, a.tokens_per_frame, ka, kb);
-      const int gap = max(0, max(ka - qb, qa - kb));
-      on = gap <= a.window;
-      for (int k = 0; k < a.num_anchors && !on; ++k) {
-        const int g = (int)((a.rotation + ((int64_t)k * a.frames) / a.num_anchors) %
-                            a.frames);
-        on = (g >= ka) && (g <= kb);
+      if (a.kind == 0) {
+        const int gap = max(0, max(ka - qb, qa - kb));
+        on = gap <= a.window;
+      } else {
+        for (int t = qa; t <= qb && !on; ++t) {
+          int lo, hi;
+          expanded_window(t, a, lo, hi);
+          on = lo <= kb && ka <= hi;
+        }
       }
+      if (!on) on = anchor_in(ka, kb, a);
     } else if (a.kind == 1) {
       const uint64_t z = splitmix64_at(a.seed, (uint64_t)c + 1);
       on = ((uint32_t)(z >> 40) < a.thresh24) || (a.force_diagonal && i == j);

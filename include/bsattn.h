@@ -48,7 +48,8 @@ typedef enum { BSATTN_DTYPE_BF16 = 0, BSATTN_DTYPE_F32 = 1 } bsattn_dtype;
 typedef enum {
   BSATTN_MASK_WINDOW_ANCHOR = 0, /* LVSA local window + rotating global anchors */
   BSATTN_MASK_STATIC_RANDOM = 1, /* seeded stand-in for a calibrated static mask */
-  BSATTN_MASK_DENSE = 2          /* all tiles active (full attention) */
+  BSATTN_MASK_DENSE = 2,         /* all tiles active (full attention) */
+  BSATTN_MASK_WINDOW_ANCHOR_EXPANDED = 3 /* LVSA window grown to a frame budget + anchors */
 } bsattn_mask_kind;
 
 /* Token geometry of the video latent.  N = frames*grid_h*grid_w; the number
@@ -69,6 +70,15 @@ typedef struct {
  *   layer; the page shifts the anchors with the step).  Tile pair (i, j) is
  *   active when some frame covered by query tile i attends to some frame
  *   covered by key tile j.  All mask_heads slices are identical.
+ * WINDOW_ANCHOR_EXPANDED (LVSA page, "Meccanismo Core", expanded adaptive
+ *   windows): as WINDOW_ANCHOR, but each query frame's window grows until
+ *   |G u W(t)| >= min(budget, T).  Growth starts from the plain window and
+ *   adds the nearest frame not yet in it, the earlier of two equally near
+ *   frames first and never a frame outside [0, T); an anchor frame it reaches
+ *   adds nothing to the count.  W(t) stays one run of frames around t, and
+ *   budget = num_anchors + 2*window + 1 makes up exactly for the frames the
+ *   window shares with G and for the clipped window at the video's ends.
+ *   A budget no larger than |G u W(t)| leaves the window as it is.
  * STATIC_RANDOM (CalibAtt page, "B. Fase di Inferenza": a precomputed,
  *   deterministic per-head block list): cell c = (h*Tq + i)*Tk + j is active
  *   when the top 24 bits of the (c+1)-th SplitMix64 output for `seed` are
@@ -84,6 +94,7 @@ typedef struct {
   uint32_t thresh24;      /* STATIC_RANDOM, <= 2^24 */
   int32_t force_diagonal; /* STATIC_RANDOM */
   int32_t mask_heads;     /* Hm >= 1: number of mask slices (1 = shared by all heads) */
+  int32_t budget;         /* WINDOW_ANCHOR_EXPANDED: C >= 0 frames per query frame */
 } bsattn_mask_params;
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
@@ -103,8 +114,8 @@ BSATTN_API int32_t bsattn_num_tiles(int64_t tokens, int32_t tile);
  *   mask: device uint8 [Hm, Tq, Tk], row-major, Hm = params->mask_heads;
  *         every byte is written (0 or 1).
  * Errors: INVALID_ARG on null pointers, non-positive sizes, window < 0,
- * num_anchors outside [0, T], thresh24 > 2^24, mask_heads < 1, an unknown
- * kind, or Hm*Tq*Tk >= 2^31. */
+ * num_anchors outside [0, T], budget < 0 (expanded mode), thresh24 > 2^24,
+ * mask_heads < 1, an unknown kind, or Hm*Tq*Tk >= 2^31. */
 BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
                                  const bsattn_mask_params* params,
                                  uint8_t* mask, void* stream);

@@ -104,7 +104,12 @@ def test_build_mask_rejects_bad_arguments():
     assert call(mask=None) == bs.ERR_INVALID_ARG
     assert call(layout=bs.Layout(0, 8, 8, 64)) == bs.ERR_INVALID_ARG
     assert call(layout=bs.Layout(4, 8, 8, 0)) == bs.ERR_INVALID_ARG
-    assert call(params=bs.MaskParams(3, 1, 1, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
+    assert call(params=bs.MaskParams(4, 1, 1, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
+    assert call(params=bs.MaskParams(-1, 1, 1, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
+    # expanded windows: negative budget, and the window/anchor checks apply
+    assert call(params=bs.MaskParams(3, 1, 1, 0, 0, 0, 0, 1, -1)) == bs.ERR_INVALID_ARG
+    assert call(params=bs.MaskParams(3, -1, 1, 0, 0, 0, 0, 1, 5)) == bs.ERR_INVALID_ARG
+    assert call(params=bs.MaskParams(3, 1, 5, 0, 0, 0, 0, 1, 5)) == bs.ERR_INVALID_ARG
     assert call(params=bs.MaskParams(0, -1, 1, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
     assert call(params=bs.MaskParams(0, 1, 5, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
     assert call(params=bs.MaskParams(1, 0, 0, 0, 0, (1 << 24) + 1, 0, 1)) == \
@@ -129,3 +134,33 @@ def test_mfma_ceiling_rejects_bad_arguments():
     assert L.bsattn_mfma_ceiling(0, 10, p, None) == bs.ERR_INVALID_ARG
     assert L.bsattn_mfma_ceiling(4, 0, p, None) == bs.ERR_INVALID_ARG
     assert L.bsattn_mfma_ceiling(4, 10, None, None) == bs.ERR_INVALID_ARG
+
+
+def test_ctypes_structs_match_the_c_header(tmp_path):
+    """The binding's Layout and MaskParams have the C structs' size and field
+    offsets (checked by compiling a probe against include/bsattn.h)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = {"bsattn_layout": bs.Layout, "bsattn_mask_params": bs.MaskParams}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "bsattn.h"',
+             "int main(void) {"]
+    for cname, py in fields.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "probe.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "probe"
+    inc = os.path.join(ROOT, "include")
+    subprocess.run([cc, "-I", inc, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True,
+                         text=True).stdout.split("\n")
+    got = {tuple(ln.split()[:2]): int(ln.split()[2]) for ln in out if ln}
+    for cname, py in fields.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)

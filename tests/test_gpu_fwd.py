@@ -67,6 +67,12 @@ SMALL = [
      W.MaskSpec(W.MASK_DENSE)),
     ("exact_tiles_t128", 4, 8, 16, 128, 128, 2, 1, W.DTYPE_BF16,
      W.MaskSpec(W.MASK_WINDOW_ANCHOR, window=1, num_anchors=1)),
+    ("expanded_t64_d64", 9, 4, 5, 64, 64, 2, 1, W.DTYPE_BF16,
+     W.MaskSpec(W.MASK_WINDOW_ANCHOR_EXPANDED, window=1, num_anchors=2,
+                rotation=5, budget=6)),
+    ("expanded_t128_d128", 12, 6, 11, 128, 128, 2, 1, W.DTYPE_BF16,
+     W.MaskSpec(W.MASK_WINDOW_ANCHOR_EXPANDED, window=0, num_anchors=3,
+                rotation=7, budget=5)),
     ("single_token", 1, 1, 1, 128, 128, 1, 1, W.DTYPE_BF16,
      W.MaskSpec(W.MASK_DENSE)),
     ("one_partial_tile", 1, 5, 7, 64, 64, 2, 1, W.DTYPE_BF16,
@@ -178,11 +184,12 @@ def sample_rows(w, per_tile_random=1, seed=0):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("cfg,stride", [(2, 1), (3, 1), (4, 4), (5, 2)])
+@pytest.mark.parametrize("cfg,stride", [(2, 1), (3, 1), (4, 4), (5, 2),
+                                        ("expanded", 8)])
 def test_full_size_sampled_rows(cfg, stride):
     """Full-size workload on the GPU; the oracle computes sampled rows (every
     `stride`-th query tile's first and last row plus one random row)."""
-    w = W.WORKLOADS[cfg]
+    w = W.EXPANDED if cfg == "expanded" else W.WORKLOADS[cfg]
     q, k, v, mask, rp, ci, o, lse = run_gpu(w)
     m_ref = check_mask_csr(w, mask, rp, ci)
     rows = sample_rows(w)

@@ -89,3 +89,50 @@ def test_mask_and_csr_repeatable():
     assert torch.equal(m1, m2) and torch.equal(rp1, rp2)
     n = int(rp1[-1])
     assert torch.equal(ci1[:n], ci2[:n])
+
+
+# ------------------------------------------------ expanded adaptive windows
+def test_expanded_hand_enumerated_tile_mask():
+    lines = read_golden("expanded_window_tile_mask.txt")
+    hdr = lines[0].split()
+    kv = dict(zip(hdr[0::2], map(int, hdr[1::2])))
+    want = np.array([[int(c) for c in ln] for ln in lines[1:]], dtype=np.uint8)
+    mask = bs.make_mask(kv["frames"], kv["grid_h"], kv["grid_w"], kv["tile"],
+                        kind=W.MASK_WINDOW_ANCHOR_EXPANDED, window=kv["window"],
+                        num_anchors=kv["anchors"], rotation=kv["rotation"],
+                        budget=kv["budget"], mask_heads=2)
+    m = mask.cpu().numpy()
+    assert np.array_equal(m[0], want) and np.array_equal(m[1], want)
+
+
+def test_expanded_long_video_every_rotation():
+    w = W.EXPANDED
+    dens = []
+    for r in w.rotations:
+        wr = w.with_rotation(r)
+        mask, rp, ci = gpu_mask_csr(wr)
+        m_ref = check_mask_csr(wr, mask, rp, ci)
+        dens.append(m_ref.mean())
+    # C = 21 of 84 frames, plus the spill of tiles that straddle two frames
+    assert 0.25 <= min(dens) and max(dens) <= 0.32, (min(dens), max(dens))
+
+
+@pytest.mark.parametrize("T,gh,gw,BT,w,na,r,C,hm", [
+    (10, 1, 2, 3, 1, 2, 3, 5, 1),      # the hand-enumerated case
+    (9, 1, 3, 2, 1, 3, 1, 6, 2),       # anchors in the growth path
+    (21, 30, 52, 128, 1, 2, 7, 5, 1),  # headline shape, C = n_a + 2w + 1
+    (21, 30, 52, 128, 1, 2, 7, 21, 1),  # C = T: every tile
+    (33, 4, 5, 64, 3, 5, 11, 0, 1),    # C = 0: the plain window
+    (40, 2, 2, 1, 0, 0, 0, 7, 1),      # no anchors, one token per tile
+    (64, 1, 1, 16, 0, 3, 60, 9, 1),    # 16 frames per tile
+    (1, 3, 3, 4, 0, 1, 0, 3, 1),       # one frame
+    (17, 3, 7, 32, 20, 2, 5, 4, 1),    # window wider than the video
+    (50, 2, 3, 8, 2, 50, 3, 10, 1),    # every frame an anchor
+])
+def test_expanded_odd_layouts(T, gh, gw, BT, w, na, r, C, hm):
+    wl = W.small_workload(frames=T, grid_h=gh, grid_w=gw, tile=BT,
+                          mask=W.MaskSpec(W.MASK_WINDOW_ANCHOR_EXPANDED,
+                                          window=w, num_anchors=na, rotation=r,
+                                          budget=C, mask_heads=hm))
+    mask, rp, ci = gpu_mask_csr(wl)
+    check_mask_csr(wl, mask, rp, ci)

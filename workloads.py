@@ -24,6 +24,7 @@ import torch
 MASK_WINDOW_ANCHOR = 0
 MASK_STATIC_RANDOM = 1
 MASK_DENSE = 2
+MASK_WINDOW_ANCHOR_EXPANDED = 3
 
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
@@ -47,6 +48,7 @@ class MaskSpec:
     thresh24: int = 0        # static mode
     force_diagonal: int = 0  # static mode
     mask_heads: int = 1      # Hm: 1 (shared by all heads) or H
+    budget: int = 0          # C, frames per query frame (expanded windows)
 
 
 @dataclass(frozen=True)
@@ -113,6 +115,17 @@ WORKLOADS = {
                 grid_w=52, tile=128, dtype=DTYPE_BF16,
                 mask=MaskSpec(MASK_DENSE), seed=1005),
 }
+
+
+# The long-video shape with the LVSA expanded adaptive windows: every query
+# frame attends to a budget of C = 21 frames (the 21-frame training horizon),
+# made of 4 rotating anchors and a window grown from +/-2 frames.  A parity and
+# measurement case of the expanded mask mode, beside the five above.
+EXPANDED = Workload("long_84x30x52_expanded_c21", B=1, H=12, d=128, frames=84,
+                    grid_h=30, grid_w=52, tile=128, dtype=DTYPE_BF16,
+                    mask=MaskSpec(MASK_WINDOW_ANCHOR_EXPANDED, window=2,
+                                  num_anchors=4, budget=21),
+                    seed=1006, rotations=tuple(range(84)))
 
 
 def make_qkv(w: Workload, seed: Optional[int] = None, device: str = "cpu"):
