@@ -10,6 +10,10 @@
 // The running max is only moved when a tile's max exceeds it by more than
 // TAU (then every value is rescaled); otherwise P may exceed 1 by at most
 // 2^TAU, which is harmless in fp32 and bf16, and the result is unchanged.
+// Q is multiplied by scale * log2(e) once, as it is loaded (rounded back to
+// bf16), and the score MFMAs start from an accumulator holding -m, so they
+// deliver x - m directly: the softmax spends no instruction per score on the
+// scale or the shift, only the exponential, the pack and the row sum.
 //
 // Mapping onto CDNA4 (gfx950)
 // ---------------------------
@@ -331,7 +335,9 @@ fwd_bf16_t128_d128(FwdLaunch a) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       if (tq < a.tiles && qr < N) {
-        qf[c] = *reinterpret_cast<const bf16x8*>(qptr + c * 16);
+        const bf16x8 raw = *reinterpret_cast<const bf16x8*>(qptr + c * 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[c][e] = (__bf16)((float)raw[e] * a.scale_log2);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) qf[c][e] = (__bf16)0.f;
@@ -345,8 +351,6 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   const int nbytes = N * ROW_BYTES;
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, nbytes, 0x00020000);
   const i32x4 krs4 = raw_rsrc(kbase, nbytes);
   const i32x4 vrs4 = raw_rsrc(vbase, nbytes);
 
@@ -405,7 +409,11 @@ fwd_bf16_t128_d128(FwdLaunch a) {
     for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
   float m = -INFINITY;
   float l = 0.f;
-  const float c2 = a.scale_log2;
+  // -m in every element (0 while m = -inf): the accumulator the first MFMA
+  // of each score chain starts from, so S arrives as x - m
+  f32x16 nm;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) nm[e] = 0.f;
 
   auto v_operand = [&](int kc, int db) INLINE {
     const int rows = (kc >> 1) * 32 * ROW_BYTES + (kc & 1) * 16 * ROW_BYTES;
@@ -453,8 +461,7 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       } else {
         const int c = qk_c(k), kb = qk_kb(k);
         if (c == 0) {
-          const f32x16 zero = {};
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd, qf[0], zero, 0, 0, 0);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd, qf[0], nm, 0, 0, 0);
         } else {
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd, qf[c], s[kb], 0, 0, 0);
         }
@@ -520,19 +527,29 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       for (int e = 1; e < 16; ++e) mxp[kb] = fmaxf(mxp[kb], s[kb][e]);
     }
     float mx = fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3]));
-    mx = max_across_halves(mx) * c2;
-    if (__any(mx > m + TAU)) {
-      const float m_new = fmaxf(m, mx);
+    // the tile's max relative to the bias the scores carry (-m, or 0 while
+    // m = -inf)
+    mx = max_across_halves(mx);
+    if (__any(m == -INFINITY ? mx != -INFINITY : mx > TAU)) {
+      const float msub = m == -INFINITY ? 0.f : m;
+      const float m_new = fmaxf(m, msub + mx);
       // m_new = -inf only while every tile so far was skipped
       const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+      const float shift = m_new == -INFINITY ? 0.f : m_new - msub;
       m = m_new;
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kb][e] -= shift;
+      const float nb = m == -INFINITY ? 0.f : -m;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) nm[e] = nb;
     }
-    const float msub = m == -INFINITY ? 0.f : m;
     float lp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -541,8 +558,8 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       for (int e = 0; e < 16; e += 2) {
         // raw v_exp_f32: results below 2^-126 flush to zero, negligible
         // next to the row's largest weight (about 1)
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], c2, -msub));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + 1], c2, -msub));
+        const float p0 = __builtin_amdgcn_exp2f(s[kb][e]);
+        const float p1 = __builtin_amdgcn_exp2f(s[kb][e + 1]);
         bf16x2 pk;
         pk[0] = (__bf16)p0;
         pk[1] = (__bf16)p1;
@@ -739,6 +756,8 @@ fwd_bf16_t128_d128(FwdLaunch a) {
           for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
         m = -INFINITY;
         l = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) nm[e] = 0.f;
       }
       load_q(tq);
       init_lists(tt == 0 ? jb0 : jb1, tt == 0 ? n0 : n1, 0, 0);

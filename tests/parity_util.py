@@ -57,17 +57,50 @@ def to64(t):
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
+# fp32 accumulation, the hardware exponential and reassociation: what the
+# log-sum-exp may differ by beyond the input-rounding term below
+LSE_BASE = 3e-4
+
+
+def lse_tolerance(q, k, mask, tile, rows=None, workers=8):
+    """Per-row bound on |LSE_gpu - LSE_oracle| for bf16 inputs, [B, H, R].
+
+    The tuned kernel multiplies Q by scale*log2(e) as it loads it and rounds
+    the product to bf16, so score j of row n carries
+        dx_j = scale * sum_i e_i q_i k_ji,   |e_i| <= 2^-9
+    (one bf16 rounding per element of q).  The log-sum-exp moves by the
+    attention-weighted mean of these, dLSE = scale * sum_i e_i q_i kbar_i with
+    kbar = sum_j p_j k_j, so
+        |dLSE| <= 2^-9 * scale * sum_i |q_i| |kbar_i|.
+    kbar is the oracle's attention output with V := K.  A missing or extra
+    tile moves LSE by about ln(1 +- 1/tiles_in_row), far above this bound
+    wherever attention is spread over many keys."""
+    N = q.shape[2]
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    kbar, _ = oracle.block_sparse_attention_rows(q.cpu(), k.cpu(), k.cpu(), mask,
+                                                 tile, rows, workers=workers)
+    q64 = q.detach().cpu().to(torch.float64).numpy()[:, :, rows]
+    scale = 1.0 / np.sqrt(q.shape[-1])
+    return LSE_BASE + 2.0 ** -9 * scale * (np.abs(q64) * np.abs(kbar)).sum(-1)
+
+
 def assert_close(name, o_gpu, o_ref, lse_gpu=None, lse_ref=None,
-                 lse_tol=1e-3):
+                 lse_tol=None):
     mx, mean, rel = errors(o_gpu, o_ref)
     msg = f"{name}: max|err| {mx:.3e} mean|err| {mean:.3e} rel-fro {rel:.3e}"
     print(msg, flush=True)
     assert np.isfinite(o_gpu).all(), name + ": non-finite output"
     assert mx <= MAX_ABS and mean <= MEAN_ABS, msg
     if lse_gpu is not None:
+        assert lse_tol is not None, name + ": an LSE check needs a tolerance"
         fin = np.isfinite(lse_ref)
         assert np.array_equal(np.isfinite(lse_gpu), fin), name + ": lse -inf rows"
         assert np.array_equal(lse_gpu[~fin], lse_ref[~fin])
         if fin.any():
-            dl = float(np.abs(lse_gpu[fin] - lse_ref[fin]).max())
-            assert dl <= lse_tol, f"{name}: max|dlse| {dl:.3e}"
+            tol = np.broadcast_to(np.asarray(lse_tol, dtype=np.float64),
+                                  lse_ref.shape)
+            dl = np.abs(lse_gpu - np.where(fin, lse_ref, 0.0))
+            worst = float((dl[fin] / tol[fin]).max())
+            print(f"{name}: max|dlse| {float(dl[fin].max()):.3e}, "
+                  f"worst |dlse|/tol {worst:.3f}", flush=True)
+            assert worst <= 1.0, f"{name}: |dlse| over tolerance ({worst:.3f}x)"
