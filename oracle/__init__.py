@@ -13,7 +13,8 @@ Sources (page title, then section):
   * "Accelerating Text-to-Video Generation with Calibrated Sparse Attention",
     A. Fase di Calibrazione / B. Fase di Inferenza: 128x128 attention blocks,
     a static per-(timestep, layer, head) block mask, attention computed only
-    over the selected blocks.
+    over the selected blocks; the calibration that builds those masks from
+    block energies and cross-prompt agreement.
   * Softmax attention itself (all pages assume full softmax attention inside
     the selected blocks), written as its textbook definition.
 
@@ -21,6 +22,8 @@ Modules:
   masks      frame rule, tile lift, static (SplitMix64) and dense tile masks
   csr        per-query-tile lists of active key tiles
   attention  dense float64 softmax attention with masked blocks set to -inf
+  calibration  block energies of dense attention, energy-based block
+             selection, cross-prompt aggregation
 
 Every function here is pinned by tests/test_oracle_*.py against values and
 properties fixed by the pages or by mathematics (hand-enumerated masks,
@@ -36,6 +39,7 @@ from .masks import (anchor_frames, window_frames, frame_set, frame_mask,
                     splitmix64_stream, static_hash24, tile_mask_static,
                     tile_mask_dense, tile_mask)
 from .csr import tile_csr
+from .calibration import block_energy, select_row, select_mask, aggregate
 from .attention import block_sparse_attention, block_sparse_attention_rows
 
 __all__ = [
@@ -45,4 +49,5 @@ __all__ = [
     "tile_frame_range", "tile_mask_window_anchor", "splitmix64_stream",
     "static_hash24", "tile_mask_static", "tile_mask_dense", "tile_mask",
     "tile_csr", "block_sparse_attention", "block_sparse_attention_rows",
+    "block_energy", "select_row", "select_mask", "aggregate",
 ]
