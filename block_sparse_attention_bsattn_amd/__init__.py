@@ -7,9 +7,12 @@ The calls mirror include/bsattn.h:
     build_mask(layout, params, mask)                    -> bsattn_build_mask
     compact(mask, row_ptr, col_idx)                     -> bsattn_compact
     fwd(q, k, v, o, row_ptr, col_idx, tile, ...)        -> bsattn_fwd
+    block_energy(q, k, energy, tile, ...)               -> bsattn_block_energy
+    select_blocks(energy, eps, mask)                    -> bsattn_select_blocks
+    aggregate_masks(masks, rho, out)                    -> bsattn_aggregate_masks
 
 plus small helpers that allocate the outputs with torch (make_mask,
-make_csr, attention).  There is no fallback: if libbsattn.so is missing or a
+make_csr, attention, calibrate).  There is no fallback: if libbsattn.so is missing or a
 call fails, an exception is raised.
 """
 from __future__ import annotations
@@ -32,11 +35,13 @@ DTYPE_F32 = 1
 MASK_WINDOW_ANCHOR = 0
 MASK_STATIC_RANDOM = 1
 MASK_DENSE = 2
+MASK_WINDOW_ANCHOR_EXPANDED = 3
 
 # Every symbol include/bsattn.h exports.
 EXPORTS = ("bsattn_version", "bsattn_status_string", "bsattn_last_error",
            "bsattn_num_tiles", "bsattn_build_mask", "bsattn_compact",
-           "bsattn_fwd", "bsattn_mfma_ceiling")
+           "bsattn_fwd", "bsattn_block_energy", "bsattn_select_blocks",
+           "bsattn_aggregate_masks", "bsattn_mfma_ceiling")
 
 
 class BsattnError(RuntimeError):
@@ -89,6 +94,14 @@ def lib() -> ctypes.CDLL:
     L.bsattn_fwd.restype = ctypes.c_int
     L.bsattn_fwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                              i32, i32p, i32p, ctypes.c_float, vp]
+    L.bsattn_block_energy.restype = ctypes.c_int
+    L.bsattn_block_energy.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp,
+                                      ctypes.c_float, vp]
+    L.bsattn_select_blocks.restype = ctypes.c_int
+    L.bsattn_select_blocks.argtypes = [i32, i32, vp, ctypes.c_double, u8p, vp]
+    L.bsattn_aggregate_masks.restype = ctypes.c_int
+    L.bsattn_aggregate_masks.argtypes = [i32, ctypes.c_int64, u8p,
+                                         ctypes.c_double, u8p, vp]
     L.bsattn_mfma_ceiling.restype = ctypes.c_int64
     L.bsattn_mfma_ceiling.argtypes = [i32, i32, vp, vp]
     _lib = L
@@ -204,6 +217,61 @@ def fwd(q, k, v, o, row_ptr, col_idx, tile: int, mask_heads: int = 1,
     return o
 
 
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def block_energy(q, k, energy, tile: int, scale: float = 0.0, stream=None):
+    """bsattn_block_energy: energy [B, H, T, T] (float32) = block sums of the
+    full softmax attention probabilities of q, k ([B, H, N, d])."""
+    import torch
+    if q.dim() != 4 or tuple(k.shape) != tuple(q.shape):
+        raise ValueError("q and k must share the shape [B, H, N, d]")
+    B, H, N, d = q.shape
+    t = num_tiles(N, tile) if N > 0 else 0
+    if tuple(energy.shape) != (B, H, t, t):
+        raise ValueError(f"energy must have shape {(B, H, t, t)}")
+    st = lib().bsattn_block_energy(B, H, N, d, tile, _dtype_code(q),
+                                   _ptr(q, "q", q.dtype), _ptr(k, "k", q.dtype),
+                                   _ptr(energy, "energy", torch.float32),
+                                   float(scale), _stream(stream))
+    _check(st, "bsattn_block_energy")
+    return energy
+
+
+def select_blocks(energy, eps: float, mask, stream=None):
+    """bsattn_select_blocks over the last axis of energy [..., Tk] into the
+    uint8 tensor mask of the same shape."""
+    import torch
+    if tuple(mask.shape) != tuple(energy.shape):
+        raise ValueError("mask must have the shape of energy")
+    Tk = energy.shape[-1] if energy.dim() else 0
+    rows = energy.numel() // Tk if Tk else 0
+    st = lib().bsattn_select_blocks(rows, Tk, _ptr(energy, "energy", torch.float32),
+                                    float(eps), _ptr(mask, "mask", torch.uint8),
+                                    _stream(stream))
+    _check(st, "bsattn_select_blocks")
+    return mask
+
+
+def aggregate_masks(masks, rho: float, out, stream=None):
+    """bsattn_aggregate_masks: out [...] = 1 where >= rho of the P masks
+    [P, ...] select the cell."""
+    import torch
+    if tuple(out.shape) != tuple(masks.shape[1:]):
+        raise ValueError("out must have the shape of one mask")
+    st = lib().bsattn_aggregate_masks(masks.shape[0], out.numel(),
+                                      _ptr(masks, "masks", torch.uint8), float(rho),
+                                      _ptr(out, "out", torch.uint8), _stream(stream))
+    _check(st, "bsattn_aggregate_masks")
+    return out
+
+
 def mfma_ceiling(blocks: int, iters: int, sink, stream=None) -> int:
     """bsattn_mfma_ceiling: enqueue the register-only bf16 MFMA
     microbenchmark; sink is a float32 device tensor of >= blocks entries.
@@ -249,6 +317,22 @@ def attention(q, k, v, row_ptr, col_idx, tile, mask_heads=1, want_lse=False,
     fwd(q, k, v, o, row_ptr, col_idx, tile, mask_heads=mask_heads, lse=lse,
         scale=scale, stream=stream)
     return (o, lse) if want_lse else o
+
+
+def calibrate(q, k, tile, eps, rho, scale=0.0, stream=None):
+    """The static mask [H, T, T] (uint8) from the prompts along q's and k's
+    batch axis: block energies, per-prompt selection at eps, agreement at
+    rho.  Returns (mask, energy, per_prompt_masks)."""
+    import torch
+    B, H, N, d = q.shape
+    t = num_tiles(N, tile)
+    energy = torch.empty((B, H, t, t), dtype=torch.float32, device=q.device)
+    block_energy(q, k, energy, tile, scale=scale, stream=stream)
+    sel = torch.empty((B, H, t, t), dtype=torch.uint8, device=q.device)
+    select_blocks(energy, eps, sel, stream=stream)
+    mask = torch.empty((H, t, t), dtype=torch.uint8, device=q.device)
+    aggregate_masks(sel, rho, mask, stream=stream)
+    return mask, energy, sel
 
 
 def mask_params_of(spec) -> dict:

@@ -185,6 +185,73 @@ BSATTN_API int bsattn_fwd(int32_t B, int32_t H, int32_t N, int32_t d,
   return hip_status(bsattn::launch_fwd(a, stream), "fwd");
 }
 
+BSATTN_API int bsattn_block_energy(int32_t B, int32_t H, int32_t N, int32_t d, int32_t tile,
+                                   int32_t dtype, const void* q, const void* k, float* energy,
+                                   float scale, void* stream) {
+  if (B < 0 || H < 0 || N < 0 || d < 0)
+    return fail(BSATTN_ERR_INVALID_ARG, "block_energy: B, H, N and d must be >= 0");
+  if (d != 64 && d != 128)
+    return fail(BSATTN_ERR_UNSUPPORTED, "block_energy: head dim %d (supported: 64, 128)", d);
+  if (tile != 64 && tile != 128)
+    return fail(BSATTN_ERR_UNSUPPORTED, "block_energy: tile %d (supported: 64, 128)", tile);
+  if (dtype != BSATTN_DTYPE_BF16 && dtype != BSATTN_DTYPE_F32)
+    return fail(BSATTN_ERR_UNSUPPORTED, "block_energy: dtype %d", dtype);
+  if ((int64_t)B * H * N == 0) return ok();
+  if (B > 65535 || H > 65535)
+    return fail(BSATTN_ERR_INVALID_ARG, "block_energy: B and H must be <= 65535");
+  if (!q || !k || !energy) return fail(BSATTN_ERR_INVALID_ARG, "block_energy: null pointer");
+  if (!aligned16(q) || !aligned16(k))
+    return fail(BSATTN_ERR_INVALID_ARG, "block_energy: q and k must be 16-byte aligned");
+  if (!(scale == scale) || isinf(scale))
+    return fail(BSATTN_ERR_INVALID_ARG, "block_energy: scale must be finite");
+  const int32_t tiles = bsattn_num_tiles(N, tile);
+  if ((int64_t)B * H * tiles * tiles >= kMaxCells)
+    return fail(BSATTN_ERR_INVALID_ARG, "block_energy: energy tensor has >= 2^31 cells");
+  bsattn::EnergyLaunch a;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.tile = tile;
+  a.dtype = dtype;
+  a.q = q;
+  a.k = k;
+  a.energy = energy;
+  a.tiles = tiles;
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  return hip_status(bsattn::launch_block_energy(a, stream), "block_energy");
+}
+
+BSATTN_API int bsattn_select_blocks(int32_t rows, int32_t Tk, const float* energy, double eps,
+                                    uint8_t* mask, void* stream) {
+  if (rows < 0 || Tk < 0)
+    return fail(BSATTN_ERR_INVALID_ARG, "select_blocks: rows and Tk must be >= 0");
+  if (Tk > 4096) return fail(BSATTN_ERR_UNSUPPORTED, "select_blocks: Tk %d > 4096", Tk);
+  if ((int64_t)rows * Tk >= kMaxCells)
+    return fail(BSATTN_ERR_INVALID_ARG, "select_blocks: >= 2^31 cells");
+  if (!(eps == eps) || isinf(eps))
+    return fail(BSATTN_ERR_INVALID_ARG, "select_blocks: eps must be finite");
+  if ((int64_t)rows * Tk == 0) return ok();
+  if (!energy || !mask) return fail(BSATTN_ERR_INVALID_ARG, "select_blocks: null pointer");
+  return hip_status(bsattn::launch_select_blocks(rows, Tk, energy, eps, mask, stream),
+                    "select_blocks");
+}
+
+BSATTN_API int bsattn_aggregate_masks(int32_t P, int64_t cells, const uint8_t* masks, double rho,
+                                      uint8_t* out, void* stream) {
+  if (P < 1 || cells < 0)
+    return fail(BSATTN_ERR_INVALID_ARG, "aggregate_masks: P >= 1 and cells >= 0 required");
+  if ((double)P * (double)cells >= 9.0e18)
+    return fail(BSATTN_ERR_INVALID_ARG, "aggregate_masks: P * cells too large");
+  if (!(rho == rho) || isinf(rho))
+    return fail(BSATTN_ERR_INVALID_ARG, "aggregate_masks: rho must be finite");
+  if (cells == 0) return ok();
+  if (!masks || !out) return fail(BSATTN_ERR_INVALID_ARG, "aggregate_masks: null pointer");
+  return hip_status(bsattn::launch_aggregate(P, cells, masks, rho, out, stream),
+                    "aggregate_masks");
+}
+
 BSATTN_API int64_t bsattn_mfma_ceiling(int32_t blocks, int32_t iters, float* sink,
                                        void* stream) {
   if (blocks < 1 || iters < 1 || !sink)

@@ -33,12 +33,28 @@ struct FwdLaunch {
 };
 
 // Each returns a hipError_t value (0 = success).
+struct EnergyLaunch {
+  int32_t B, H, N, d, tile, dtype;
+  const void* q;
+  const void* k;
+  float* energy;      // [B, H, tiles, tiles]
+  int32_t tiles;
+  float scale_log2;   // softmax scale * log2(e)
+};
+
 int launch_build_mask(const MaskLaunch& a, uint8_t* mask, void* stream);
 int launch_compact(int32_t rows, int32_t tk, const uint8_t* mask,
                    int32_t* row_ptr, int32_t* col_idx, void* stream);
 int launch_fwd(const FwdLaunch& a, void* stream);
 // tuned instance: bf16, head dim 128, 128x128 tiles, N * 256 < 2^31
 int launch_fwd_bf16_t128_d128(const FwdLaunch& a, void* stream);
+
+// static-mask calibration
+int launch_block_energy(const EnergyLaunch& a, void* stream);
+int launch_select_blocks(int32_t rows, int32_t tk, const float* energy, double eps,
+                         uint8_t* mask, void* stream);
+int launch_aggregate(int32_t P, int64_t cells, const uint8_t* masks, double rho, uint8_t* out,
+                     void* stream);
 
 // matrix-core ceiling microbenchmark
 int64_t mfma_ceiling_flops(int blocks, int iters);

@@ -10,7 +10,9 @@
  * a tile mask says which key tiles each query tile reads, and only those
  * tiles are computed.  The output O has the shape of Q.
  *
- * Pipeline: bsattn_build_mask -> bsattn_compact -> bsattn_fwd.
+ * Pipeline: bsattn_build_mask -> bsattn_compact -> bsattn_fwd.  A static mask
+ * can instead be calibrated: bsattn_block_energy -> bsattn_select_blocks ->
+ * bsattn_aggregate_masks, then bsattn_compact -> bsattn_fwd.
  *
  * Conventions shared by every call:
  *   - Every pointer argument named "device" is device memory on the current
@@ -158,6 +160,54 @@ BSATTN_API int bsattn_fwd(int32_t B, int32_t H, int32_t N, int32_t d,
                           const void* k, const void* v, void* o, float* lse,
                           int32_t mask_heads, const int32_t* row_ptr,
                           const int32_t* col_idx, float scale, void* stream);
+
+/* ---- Static-mask calibration (CalibAtt page, "A. Fase di Calibrazione").
+ * The calibration runs full attention on a few prompts, measures how much
+ * attention every block receives, keeps per query block the fewest key
+ * blocks that carry a fraction eps of it, and keeps a block in the final
+ * static mask when enough prompts agree.  The result feeds bsattn_compact and
+ * bsattn_fwd like any other tile mask. */
+
+/* Block energies of full softmax attention (step 1):
+ *   E[b, h, i, j] = sum over query rows n of tile i and key columns m of
+ *   tile j of softmax_m(scale * q_n . k_m), the softmax over all N keys.
+ * Each row of E sums to the number of query rows in tile i.
+ *   q, k:    device [B, H, N, d] contiguous, element type `dtype` (BF16, or
+ *            F32 rounded to bf16 for the products, which accumulate in fp32).
+ *   energy:  device float [B, H, T, T], T = ceil(N / tile), written.
+ *   scale:   softmax scale; <= 0 selects 1/sqrt(d).
+ * The batch index plays the role of the calibration prompt.  Supported:
+ * d in {64, 128}, tile in {64, 128}.  B*H*N == 0 is a no-op.
+ * Errors: INVALID_ARG (null pointers, negative sizes, B or H > 65535,
+ * unaligned q or k, non-finite scale, B*H*T*T >= 2^31), UNSUPPORTED (d,
+ * tile, dtype), HIP. */
+BSATTN_API int bsattn_block_energy(int32_t B, int32_t H, int32_t N, int32_t d, int32_t tile,
+                                   int32_t dtype, const void* q, const void* k, float* energy,
+                                   float scale, void* stream);
+
+/* Energy-based block selection (step 1), one row at a time:
+ *   energy: device float [rows, Tk], finite and >= 0 (as written by
+ *           bsattn_block_energy, viewed as [B*H*T, T]).
+ *   mask:   device uint8 [rows, Tk], written: 1 for the kept key blocks.
+ * Per row the key blocks are ordered by decreasing energy (the lower index
+ * first on equal energy) and the shortest prefix whose cumulative energy is
+ * >= eps * (row total) is kept; the sums are float64, added one at a time in
+ * that order, the total included.  eps <= 0 keeps nothing, eps > 1 keeps
+ * every block.  The threshold eps(t) of the page varies with the timestep:
+ * the caller passes the value for the step being calibrated.
+ * Errors: INVALID_ARG (negative sizes, null pointers, non-finite eps,
+ * rows*Tk >= 2^31), UNSUPPORTED (Tk > 4096), HIP. */
+BSATTN_API int bsattn_select_blocks(int32_t rows, int32_t Tk, const float* energy, double eps,
+                                    uint8_t* mask, void* stream);
+
+/* Cross-prompt agreement (step 2):
+ *   masks: device uint8 [P, cells] (P prompt masks, any nonzero = selected).
+ *   out:   device uint8 [cells], written: 1 where the number of prompts that
+ *          selected the cell is >= rho * P (float64), else 0.
+ * Errors: INVALID_ARG (P < 1, cells < 0, null pointers, non-finite rho),
+ * HIP. */
+BSATTN_API int bsattn_aggregate_masks(int32_t P, int64_t cells, const uint8_t* masks, double rho,
+                                      uint8_t* out, void* stream);
 
 /* Diagnostic: the achievable bf16 matrix-core rate of the device, against
  * which the forward's throughput is read (next to the vendor's dense peak).

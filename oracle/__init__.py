@@ -39,7 +39,8 @@ from .masks import (anchor_frames, window_frames, frame_set, frame_mask,
                     splitmix64_stream, static_hash24, tile_mask_static,
                     tile_mask_dense, tile_mask)
 from .csr import tile_csr
-from .calibration import block_energy, select_row, select_mask, aggregate
+from .calibration import (block_energy, block_energy_rows, select_row,
+                          select_mask, aggregate)
 from .attention import block_sparse_attention, block_sparse_attention_rows
 
 __all__ = [
@@ -49,5 +50,6 @@ __all__ = [
     "tile_frame_range", "tile_mask_window_anchor", "splitmix64_stream",
     "static_hash24", "tile_mask_static", "tile_mask_dense", "tile_mask",
     "tile_csr", "block_sparse_attention", "block_sparse_attention_rows",
-    "block_energy", "select_row", "select_mask", "aggregate",
+    "block_energy", "block_energy_rows", "select_row", "select_mask",
+    "aggregate",
 ]

@@ -64,6 +64,32 @@ def block_energy(q, k, tile: int, scale: float | None = None) -> np.ndarray:
     return E
 
 
+def block_energy_rows(q, k, tile: int, query_tiles,
+                      scale: float | None = None) -> np.ndarray:
+    """The rows E[b, h, i, :] for the query tiles i in `query_tiles` only
+    (same definition as block_energy), [B, H, len(query_tiles), T]."""
+    q = _as_f64(q)
+    k = _as_f64(k)
+    B, H, N, d = q.shape
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(d)
+    nt = -(-N // tile)
+    onehot = np.zeros((N, nt), dtype=np.float64)
+    onehot[np.arange(N), np.arange(N) // tile] = 1.0
+    qts = list(query_tiles)
+    E = np.zeros((B, H, len(qts), nt), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r, i in enumerate(qts):
+                rows = slice(i * tile, min((i + 1) * tile, N))
+                s = (q[b, h, rows] @ k[b, h].T) * scale
+                s -= s.max(axis=1, keepdims=True)
+                p = np.exp(s)
+                p /= p.sum(axis=1, keepdims=True)
+                E[b, h, r] = p.sum(axis=0) @ onehot
+    return E
+
+
 def select_row(energy_row, eps: float) -> np.ndarray:
     """uint8 [Tk]: the fewest key blocks reaching eps of the row's energy
     (float32 energies, float64 sequential sums in the sorted order)."""

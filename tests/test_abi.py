@@ -164,3 +164,31 @@ def test_ctypes_structs_match_the_c_header(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(py), cname
         for f, _ in py._fields_:
             assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
+
+
+def test_calibration_calls_reject_bad_arguments():
+    L = bs.lib()
+    p = ctypes.c_void_p(64)
+    E = L.bsattn_block_energy
+    assert E(1, 1, 256, 128, 128, 0, p, p, None, 0.0, None) == bs.ERR_INVALID_ARG
+    assert E(1, 1, 256, 96, 128, 0, p, p, p, 0.0, None) == bs.ERR_UNSUPPORTED
+    assert E(1, 1, 256, 128, 32, 0, p, p, p, 0.0, None) == bs.ERR_UNSUPPORTED
+    assert E(1, 1, 256, 128, 128, 7, p, p, p, 0.0, None) == bs.ERR_UNSUPPORTED
+    assert E(-1, 1, 256, 128, 128, 0, p, p, p, 0.0, None) == bs.ERR_INVALID_ARG
+    assert E(1, 1, 256, 128, 128, 0, ctypes.c_void_p(65), p, p, 0.0, None) == \
+        bs.ERR_INVALID_ARG
+    assert E(1, 1, 256, 128, 128, 0, p, p, p, float("nan"), None) == bs.ERR_INVALID_ARG
+    assert E(70000, 1, 256, 128, 128, 0, p, p, p, 0.0, None) == bs.ERR_INVALID_ARG
+    assert E(0, 1, 256, 128, 128, 0, None, None, None, 0.0, None) == bs.OK
+    S = L.bsattn_select_blocks
+    assert S(-1, 4, p, 0.5, p, None) == bs.ERR_INVALID_ARG
+    assert S(4, 4097, p, 0.5, p, None) == bs.ERR_UNSUPPORTED
+    assert S(4, 4, None, 0.5, p, None) == bs.ERR_INVALID_ARG
+    assert S(4, 4, p, float("inf"), p, None) == bs.ERR_INVALID_ARG
+    assert S(0, 4, None, 0.5, None, None) == bs.OK
+    A = L.bsattn_aggregate_masks
+    assert A(0, 4, p, 0.5, p, None) == bs.ERR_INVALID_ARG
+    assert A(2, -1, p, 0.5, p, None) == bs.ERR_INVALID_ARG
+    assert A(2, 4, p, float("nan"), p, None) == bs.ERR_INVALID_ARG
+    assert A(2, 4, None, 0.5, p, None) == bs.ERR_INVALID_ARG
+    assert A(2, 0, None, 0.5, None, None) == bs.OK

@@ -76,6 +76,13 @@ def test_energy_one_hot_attention():
     np.testing.assert_allclose(E, want, atol=1e-20)
 
 
+def test_energy_rows_are_rows_of_the_full_tensor():
+    q, k = _qk(1, 2, 50, 8, 21)
+    full = oracle.block_energy(q, k, 16)
+    part = oracle.block_energy_rows(q, k, 16, [3, 0])
+    np.testing.assert_allclose(part, full[:, :, [3, 0]], rtol=1e-13, atol=1e-15)
+
+
 # -------------------------------------------------------------- selection
 def test_selection_matches_hand_enumeration():
     lines = read_golden("calib_select_rows.txt")

@@ -142,6 +142,59 @@ def make_qkv(w: Workload, seed: Optional[int] = None, device: str = "cpu"):
     return tuple(out)
 
 
+def make_qk_frame_local(w: Workload, strength: float = 1.0,
+                        seed: Optional[int] = None, device: str = "cpu"):
+    """Q and K with a shared per-(head, frame) component, so a query scores
+    the keys of its own frame higher (attention concentrates locally, the
+    structure calibration is meant to find): q_n = a_n + strength * c_f(n),
+    k_n = b_n + strength * c_f(n), with a, b, c i.i.d. N(0, 1), the same c for
+    every batch entry (prompt) and a, b drawn per batch entry.  Rounded to
+    the workload's dtype."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    c = torch.randn((1, w.H, w.frames, w.d), generator=g, dtype=torch.float32)
+    cf = c.repeat_interleave(w.P, dim=2)                   # [1, H, N, d]
+    q = torch.randn((w.B, w.H, w.N, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.H, w.N, w.d), generator=g, dtype=torch.float32)
+    q = q + strength * cf
+    k = k + strength * cf
+    return (q.to(w.torch_dtype()).to(device), k.to(w.torch_dtype()).to(device))
+
+
+def make_energies(rows: int, tk: int, seed: int, zero_frac: float = 0.1,
+                  tie_frac: float = 0.1) -> torch.Tensor:
+    """Synthetic float32 block energies [rows, tk] >= 0: heavy-tailed values
+    (u^4 for u uniform), a fraction set to exactly 0, and a fraction copied
+    from another entry of the same row (exact ties)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    e = torch.rand((rows, tk), generator=g, dtype=torch.float32) ** 4
+    z = torch.rand((rows, tk), generator=g) < zero_frac
+    e[z] = 0.0
+    t = torch.rand((rows, tk), generator=g) < tie_frac
+    src = torch.randint(0, tk, (rows, tk), generator=g)
+    e = torch.where(t, torch.gather(e, 1, src), e)
+    return e
+
+
+def make_prompt_masks(p: int, cells: int, seed: int, density: float = 0.5):
+    """Random uint8 masks [p, cells] (each cell 1 with the given probability)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return (torch.rand((p, cells), generator=g) < density).to(torch.uint8)
+
+
+# The static-mask calibration case at the video shape: four prompts (batch
+# entries) with frame-local structure.  rho = 0.5 is the CalibAtt page's
+# example; the page gives no number for eps (a per-step schedule, higher
+# early in denoising), so 0.9 stands for one step of it.
+CALIB = Workload("video_21x30x52_calib_p4", B=4, H=12, d=128, frames=21,
+                 grid_h=30, grid_w=52, tile=128, dtype=DTYPE_BF16,
+                 mask=MaskSpec(MASK_DENSE), seed=1007)
+CALIB_EPS = 0.9
+CALIB_RHO = 0.5
+
+
 def small_workload(frames=3, grid_h=5, grid_w=9, tile=64, d=64, H=2, B=1,
                    dtype=DTYPE_BF16, mask: Optional[MaskSpec] = None,
                    seed=77, name="small") -> Workload:
