@@ -13,8 +13,9 @@ Printed: ONE JSON line with
                the launch stream) against the bf16 dense MFMA peak,
   cpu_baseline the float64 CPU oracle on a bounded row sample,
 plus the forward-only time, the same kernel at density 1.0 and the speedup,
-a density sweep, and the path with LVSA expanded windows on the 84-frame
-long-video shape.
+a density sweep, the path with LVSA expanded windows on the 84-frame
+long-video shape, and the static-mask calibration (block energies, selection,
+agreement) with the forward on the calibrated mask.
 """
 from __future__ import annotations
 
@@ -149,6 +150,71 @@ def expanded_windows(bs, W, torch, dev, calls: int):
             "step_tflops": round(float(np.sum(flops) / (step_ms.sum() * 1e-3)) / 1e12, 1)}
 
 
+def calibration(bs, W, torch, dev, calls: int):
+    """Static-mask calibration at the video shape (4 prompts x 12 heads x
+    32 760 tokens, frame-local Q/K): block energies, per-prompt selection at
+    eps, agreement at rho, each timed with events on the launch stream;
+    then the forward on the calibrated mask."""
+    w = W.CALIB
+    q, k = W.make_qk_frame_local(w, strength=0.7, device=dev)
+    T = w.num_tiles
+    stream = torch.cuda.current_stream()
+    energy = torch.empty((w.B, w.H, T, T), dtype=torch.float32, device=dev)
+    sel = torch.empty((w.B, w.H, T, T), dtype=torch.uint8, device=dev)
+    mask = torch.empty((w.H, T, T), dtype=torch.uint8, device=dev)
+
+    def run(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        bs.block_energy(q, k, energy, w.tile, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        bs.select_blocks(energy, W.CALIB_EPS, sel, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        bs.aggregate_masks(sel, W.CALIB_RHO, mask, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    run()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(calls)]
+    for e in evs:
+        run(e)
+    torch.cuda.synchronize()
+    part = lambda a, b: float(np.median([e[a].elapsed_time(e[b]) for e in evs]))
+    e_ms = part(0, 1)
+    # two sweeps of S = Q K^T over every (query, key) pair
+    flops = 2.0 * 2.0 * w.N * w.N * w.d * w.B * w.H
+    m_np = mask.cpu().numpy()
+    # the forward of one prompt on the calibrated (per-head) mask
+    v = torch.randn(q[:1].shape, generator=torch.Generator().manual_seed(5)).to(
+        torch.bfloat16).to(dev)
+    rp, ci = bs.make_csr(mask)
+    o = torch.empty_like(v)
+    bs.fwd(q[:1], k[:1], v, o, rp, ci, w.tile, mask_heads=w.H)
+    fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for a, b in fe:
+        a.record(stream)
+        bs.fwd(q[:1], k[:1], v, o, rp, ci, w.tile, mask_heads=w.H, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    f_ms = float(np.median([a.elapsed_time(b) for a, b in fe]))
+    from dataclasses import replace
+    w1 = replace(w, B=1)
+    f_flops = active_flops(m_np, w1)
+    return {"workload": w.name,
+            "prompts": w.B, "eps": W.CALIB_EPS, "rho": W.CALIB_RHO,
+            "energy_ms": round(e_ms, 4),
+            "energy_tflops": round(flops / (e_ms * 1e-3) / 1e12, 1),
+            "energy_frac_of_peak": round(flops / (e_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "select_us": round(part(1, 2) * 1e3, 1),
+            "aggregate_us": round(part(2, 3) * 1e3, 1),
+            "calibrated_density": round(float(m_np.mean()), 4),
+            "fwd_ms_on_calibrated_mask": round(f_ms, 4),
+            "fwd_tflops_on_calibrated_mask": round(f_flops / (f_ms * 1e-3) / 1e12, 1)}
+
+
 def cpu_baseline(w, q, k, v, mask_np, tiles: int, workers: int):
     """The oracle as it stands, on `tiles` evenly spaced query tiles (every
     row of them, every head) at rotation 0; TFLOP/s credited like the GPU
@@ -200,6 +266,9 @@ def main():
                     help="density sweep with static masks (0 = skip)")
     ap.add_argument("--expanded", type=int, default=6,
                     help="steps of the expanded-window long-video path "
+                         "(0 = skip)")
+    ap.add_argument("--calib", type=int, default=3,
+                    help="timed calls of the static-mask calibration leg "
                          "(0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB "
@@ -316,6 +385,8 @@ def main():
     expanded = expanded_windows(bs, W, torch, dev, args.expanded) \
         if args.expanded > 0 else None
 
+    calib = calibration(bs, W, torch, dev, args.calib) if args.calib > 0 else None
+
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -386,6 +457,7 @@ def main():
         round(dense_ms / float(fwd_ms.mean()), 3),
         "density_sweep": sweep,
         "expanded_windows": expanded,
+        "calibration": calib,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -17,7 +17,9 @@
 //   K tiles are staged in LDS (row pitch d + 8 bf16, conflict-free for the
 //   operand reads); the next tile's rows are loaded into registers while the
 //   current one is multiplied.  Rows past N contribute nothing; keys past N
-//   never enter a softmax.
+//   never enter a softmax.  The exponentials are the raw v_exp_f32: results
+//   below 2^-126 flush to zero, probabilities far below anything a block sum
+//   can register.
 //
 // Step 1, selection: per query block, the fewest key blocks whose cumulative
 // energy reaches eps of the row's total.  Blocks are ordered by decreasing
@@ -56,8 +58,10 @@ __device__ __forceinline__ bf16x8 load8(const void* base, int64_t off) {
   }
 }
 
+// Two workgroups per CU (two waves per SIMD), so one wave's exponentials
+// overlap the other's matrix products.
 template <int BT, int D, bool F32IN>
-__global__ void __launch_bounds__(BT * 2)
+__global__ void __launch_bounds__(BT * 2, 2)
 block_energy_kernel(EnergyLaunch a) {
   constexpr int NT = BT * 2;           // threads: BT / 32 waves
   constexpr int NW = BT / 32;          // waves
@@ -120,26 +124,36 @@ block_energy_kernel(EnergyLaunch a) {
   // S^T of the staged tile; keys past N set to -inf
   f32x16 s[KB];
   auto scores = [&](int j) {
+    // chunk-outer over the key blocks: KB independent accumulation chains;
+    // the first product of each starts from the constant 0
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int c = 0; c < DC; ++c)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-#pragma unroll
-      for (int c = 0; c < DC; ++c) {
+      for (int kb = 0; kb < KB; ++kb) {
         const bf16x8 ka =
             *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + l32) * KP + c * 16 + half * 8]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[c], s[kb], 0, 0, 0);
+        if (c == 0) {
+          const f32x16 zero = {};
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[0], zero, 0, 0, 0);
+        } else {
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[c], s[kb], 0, 0, 0);
+        }
       }
-    }
+    // an integer select (no per-element compare masks) for the ragged tile
     const int valid = N - j * BT;
     if (valid < BT) {
+      const int lim = valid - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (kb * 32 + 8 * i + 4 * half + e >= valid) s[kb][4 * i + e] = -INFINITY;
+          for (int e = 0; e < 4; ++e) {
+            const int keep = ((kb * 32 + 8 * i + e) - lim) >> 31;  // -1: keep
+            const uint32_t bits = __float_as_uint(s[kb][4 * i + e]);
+            s[kb][4 * i + e] =
+                __uint_as_float((bits & (uint32_t)keep) | (0xff800000u & ~(uint32_t)keep));
+          }
     }
   };
 
@@ -162,7 +176,7 @@ block_energy_kernel(EnergyLaunch a) {
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
     const float m_new = fmaxf(m, mx);
-    const float alpha = (m_new == m) ? 1.f : exp2f(m - m_new);
+    const float alpha = (m_new == m) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
     m = m_new;
     // the tile's share first, then into the running sum: thousands of
     // terms added one by one into a single float would lose ~1e-4 of it
@@ -171,7 +185,7 @@ block_energy_kernel(EnergyLaunch a) {
     for (int kb = 0; kb < KB; ++kb) {
       float lk = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) lk += exp2f(__builtin_fmaf(s[kb][e], c2, -m));
+      for (int e = 0; e < 16; ++e) lk += __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], c2, -m));
       lt += lk;
     }
     l = l * alpha + lt;
@@ -192,7 +206,7 @@ block_energy_kernel(EnergyLaunch a) {
     for (int kb = 0; kb < KB; ++kb) {
       float pk = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) pk += exp2f(__builtin_fmaf(s[kb][e], c2, -L));
+      for (int e = 0; e < 16; ++e) pk += __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], c2, -L));
       ps += pk;
     }
     if (!row_ok) ps = 0.f;
