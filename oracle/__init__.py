@@ -15,6 +15,9 @@ Sources (page title, then section):
     a static per-(timestep, layer, head) block mask, attention computed only
     over the selected blocks; the calibration that builds those masks from
     block energies and cross-prompt agreement.
+  * "SQuad: Sub-Quadratic Attention Distillation for Efficient Video
+    Generation", 1. Operatore di Attenzione SQuad: the two-pass local/global
+    softmax attention.
   * Softmax attention itself (all pages assume full softmax attention inside
     the selected blocks), written as its textbook definition.
 
@@ -24,6 +27,8 @@ Modules:
   attention  dense float64 softmax attention with masked blocks set to -inf
   calibration  block energies of dense attention, energy-based block
              selection, cross-prompt aggregation
+  squad      two-pass local/global attention (local output as the global
+             pass's values)
 
 Every function here is pinned by tests/test_oracle_*.py against values and
 properties fixed by the pages or by mathematics (hand-enumerated masks,
@@ -41,6 +46,9 @@ from .masks import (anchor_frames, window_frames, frame_set, frame_mask,
 from .csr import tile_csr
 from .calibration import (block_energy, block_energy_rows, select_row,
                           select_mask, aggregate)
+from .squad import (squad_local, squad_attention, squad_attention_rows,
+                    window_major_to_position_major,
+                    position_major_to_window_major)
 from .attention import block_sparse_attention, block_sparse_attention_rows
 
 __all__ = [
@@ -51,5 +59,6 @@ __all__ = [
     "static_hash24", "tile_mask_static", "tile_mask_dense", "tile_mask",
     "tile_csr", "block_sparse_attention", "block_sparse_attention_rows",
     "block_energy", "block_energy_rows", "select_row", "select_mask",
-    "aggregate",
+    "aggregate", "squad_local", "squad_attention", "squad_attention_rows",
+    "window_major_to_position_major", "position_major_to_window_major",
 ]
