@@ -10,9 +10,10 @@ The calls mirror include/bsattn.h:
     block_energy(q, k, energy, tile, ...)               -> bsattn_block_energy
     select_blocks(energy, eps, mask)                    -> bsattn_select_blocks
     aggregate_masks(masks, rho, out)                    -> bsattn_aggregate_masks
+    window_reorder(src, dst, w, inverse)                -> bsattn_window_reorder
 
 plus small helpers that allocate the outputs with torch (make_mask,
-make_csr, attention, calibrate).  There is no fallback: if libbsattn.so is missing or a
+make_csr, attention, calibrate, squad).  There is no fallback: if libbsattn.so is missing or a
 call fails, an exception is raised.
 """
 from __future__ import annotations
@@ -36,11 +37,13 @@ MASK_WINDOW_ANCHOR = 0
 MASK_STATIC_RANDOM = 1
 MASK_DENSE = 2
 MASK_WINDOW_ANCHOR_EXPANDED = 3
+MASK_BLOCK_DIAGONAL = 4
 
 # Every symbol include/bsattn.h exports.
 EXPORTS = ("bsattn_version", "bsattn_status_string", "bsattn_last_error",
            "bsattn_num_tiles", "bsattn_build_mask", "bsattn_compact",
-           "bsattn_fwd", "bsattn_block_energy", "bsattn_select_blocks",
+           "bsattn_fwd", "bsattn_window_reorder", "bsattn_block_energy",
+           "bsattn_select_blocks",
            "bsattn_aggregate_masks", "bsattn_mfma_ceiling")
 
 
@@ -60,7 +63,8 @@ class MaskParams(ctypes.Structure):
                 ("num_anchors", ctypes.c_int32), ("rotation", ctypes.c_int32),
                 ("seed", ctypes.c_uint64), ("thresh24", ctypes.c_uint32),
                 ("force_diagonal", ctypes.c_int32),
-                ("mask_heads", ctypes.c_int32), ("budget", ctypes.c_int32)]
+                ("mask_heads", ctypes.c_int32), ("budget", ctypes.c_int32),
+                ("block_tiles", ctypes.c_int32)]
 
 
 _lib = None
@@ -94,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.bsattn_fwd.restype = ctypes.c_int
     L.bsattn_fwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                              i32, i32p, i32p, ctypes.c_float, vp]
+    L.bsattn_window_reorder.restype = ctypes.c_int
+    L.bsattn_window_reorder.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i32, vp]
     L.bsattn_block_energy.restype = ctypes.c_int
     L.bsattn_block_energy.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp,
                                       ctypes.c_float, vp]
@@ -147,10 +153,10 @@ def num_tiles(tokens: int, tile: int) -> int:
 
 
 def _params(kind, window=0, num_anchors=0, rotation=0, seed=0, thresh24=0,
-            force_diagonal=0, mask_heads=1, budget=0) -> MaskParams:
+            force_diagonal=0, mask_heads=1, budget=0, block_tiles=1) -> MaskParams:
     return MaskParams(kind, window, num_anchors, rotation,
                       seed & 0xFFFFFFFFFFFFFFFF, thresh24, int(force_diagonal),
-                      mask_heads, budget)
+                      mask_heads, budget, block_tiles)
 
 
 def build_mask(layout: Sequence[int], mask, stream=None, **params):
@@ -158,7 +164,7 @@ def build_mask(layout: Sequence[int], mask, stream=None, **params):
 
     layout = (frames, grid_h, grid_w, tile); params are the fields of
     bsattn_mask_params (kind, window, num_anchors, rotation, seed, thresh24,
-    force_diagonal, mask_heads, budget)."""
+    force_diagonal, mask_heads, budget, block_tiles)."""
     import torch
     L = Layout(*[int(x) for x in layout])
     P = _params(**params)
@@ -224,6 +230,19 @@ def _dtype_code(t):
     if t.dtype == torch.float32:
         return DTYPE_F32
     raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def window_reorder(src, dst, w: int, inverse: bool = False, stream=None):
+    """bsattn_window_reorder of src [B, H, N, d] into dst (window-major ->
+    position-major, or back with inverse=True)."""
+    if src.dim() != 4 or tuple(dst.shape) != tuple(src.shape) or dst.dtype != src.dtype:
+        raise ValueError("src and dst must share shape [B, H, N, d] and dtype")
+    B, H, N, d = src.shape
+    st = lib().bsattn_window_reorder(B, H, N, d, w, _dtype_code(src),
+                                     _ptr(src, "src", src.dtype), _ptr(dst, "dst", src.dtype),
+                                     int(bool(inverse)), _stream(stream))
+    _check(st, "bsattn_window_reorder")
+    return dst
 
 
 def block_energy(q, k, energy, tile: int, scale: float = 0.0, stream=None):
@@ -335,6 +354,38 @@ def calibrate(q, k, tile, eps, rho, scale=0.0, stream=None):
     return mask, energy, sel
 
 
+def squad(q, k, v, w: int, tile: int, scale: float = 0.0, stream=None):
+    """SQuad's two-pass attention through the library's calls: the local
+    pass (block-diagonal mask, w / tile tiles per block) gives O_L; Q, K and
+    O_L are reordered to position-major; the global pass (block-diagonal,
+    G / tile tiles per block, G = N / w) runs with O_L as values; the result
+    is reordered back.  Needs w and N / w to be multiples of tile."""
+    import torch
+    B, H, N, d = q.shape
+    if w % tile or N % w or (N // w) % tile:
+        raise ValueError("w and N / w must be multiples of the tile size")
+    G = N // w
+    layout = (1, 1, N, tile)
+
+    def pass_(qq, kk, vv, block_tiles):
+        mask = make_mask(*layout, device=q.device, stream=stream,
+                         kind=MASK_BLOCK_DIAGONAL, block_tiles=block_tiles)
+        rp, ci = make_csr(mask, stream=stream)
+        o = torch.empty_like(qq)
+        fwd(qq, kk, vv, o, rp, ci, tile, scale=scale, stream=stream)
+        return o
+
+    o_local = pass_(q, k, v, w // tile)
+    qp, kp, op = torch.empty_like(q), torch.empty_like(k), torch.empty_like(o_local)
+    window_reorder(q, qp, w, stream=stream)
+    window_reorder(k, kp, w, stream=stream)
+    window_reorder(o_local, op, w, stream=stream)
+    og = pass_(qp, kp, op, G // tile)
+    out = torch.empty_like(q)
+    window_reorder(og, out, w, inverse=True, stream=stream)
+    return out
+
+
 def mask_params_of(spec) -> dict:
     """Keyword parameters of build_mask from an object with the fields of
     bsattn_mask_params (e.g. a workload's mask spec)."""
@@ -342,4 +393,5 @@ def mask_params_of(spec) -> dict:
                 num_anchors=spec.num_anchors, rotation=spec.rotation,
                 seed=spec.seed, thresh24=spec.thresh24,
                 force_diagonal=spec.force_diagonal,
-                mask_heads=spec.mask_heads, budget=spec.budget)
+                mask_heads=spec.mask_heads, budget=spec.budget,
+                block_tiles=getattr(spec, "block_tiles", 1))

@@ -77,7 +77,7 @@ BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
   const int64_t tokens = per_frame * L.frames;
   if (tokens > INT32_MAX)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: more than 2^31-1 tokens");
-  if (M.kind < BSATTN_MASK_WINDOW_ANCHOR || M.kind > BSATTN_MASK_WINDOW_ANCHOR_EXPANDED)
+  if (M.kind < BSATTN_MASK_WINDOW_ANCHOR || M.kind > BSATTN_MASK_BLOCK_DIAGONAL)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: unknown mask kind %d", M.kind);
   if (M.mask_heads < 1)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: mask_heads must be >= 1");
@@ -92,6 +92,8 @@ BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
   }
   if (M.kind == BSATTN_MASK_WINDOW_ANCHOR_EXPANDED && M.budget < 0)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: budget must be >= 0");
+  if (M.kind == BSATTN_MASK_BLOCK_DIAGONAL && M.block_tiles < 1)
+    return fail(BSATTN_ERR_INVALID_ARG, "build_mask: block_tiles must be >= 1");
   if (M.kind == BSATTN_MASK_STATIC_RANDOM && M.thresh24 > (1u << 24))
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: thresh24 exceeds 2^24");
   const int32_t tiles = bsattn_num_tiles(tokens, L.tile);
@@ -114,6 +116,7 @@ BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
                  : 0;
   a.num_anchors = M.num_anchors;
   a.rotation = ((M.rotation % L.frames) + L.frames) % L.frames;
+  a.block_tiles = M.kind == BSATTN_MASK_BLOCK_DIAGONAL ? M.block_tiles : 1;
   a.seed = M.seed;
   a.thresh24 = M.thresh24;
   a.force_diagonal = M.force_diagonal != 0;
@@ -183,6 +186,30 @@ BSATTN_API int bsattn_fwd(int32_t B, int32_t H, int32_t N, int32_t d,
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
   a.scale_log2 = sc * 1.4426950408889634f;
   return hip_status(bsattn::launch_fwd(a, stream), "fwd");
+}
+
+BSATTN_API int bsattn_window_reorder(int32_t B, int32_t H, int32_t N, int32_t d, int32_t w,
+                                     int32_t dtype, const void* src, void* dst, int32_t inverse,
+                                     void* stream) {
+  if (B < 0 || H < 0 || N < 0 || d < 1 || w < 1)
+    return fail(BSATTN_ERR_INVALID_ARG, "window_reorder: B, H, N >= 0 and d, w >= 1 required");
+  if (dtype != BSATTN_DTYPE_BF16 && dtype != BSATTN_DTYPE_F32)
+    return fail(BSATTN_ERR_UNSUPPORTED, "window_reorder: dtype %d", dtype);
+  if ((int64_t)B * H * N == 0) return ok();
+  if (N % w != 0)
+    return fail(BSATTN_ERR_INVALID_ARG, "window_reorder: N=%d is not a multiple of w=%d", N, w);
+  if (!src || !dst || src == dst)
+    return fail(BSATTN_ERR_INVALID_ARG, "window_reorder: null or aliased buffers");
+  const int32_t elt = dtype == BSATTN_DTYPE_BF16 ? 2 : 4;
+  const int64_t row_bytes = (int64_t)d * elt;
+  if (row_bytes % 16 != 0 || !aligned16(src) || !aligned16(dst))
+    return fail(BSATTN_ERR_INVALID_ARG,
+                "window_reorder: rows must be 16-byte multiples on 16-byte aligned buffers");
+  if ((double)B * H * N * row_bytes >= 1.0e12)
+    return fail(BSATTN_ERR_INVALID_ARG, "window_reorder: tensor too large");
+  return hip_status(bsattn::launch_window_reorder((int64_t)B * H, N, (int32_t)row_bytes, w, src,
+                                                  dst, inverse != 0, stream),
+                    "window_reorder");
 }
 
 BSATTN_API int bsattn_block_energy(int32_t B, int32_t H, int32_t N, int32_t d, int32_t tile,

@@ -12,6 +12,7 @@ struct MaskLaunch {
   int32_t tq, tk, mask_heads;
   int32_t window, num_anchors, rotation;  // window <= frames, rotation in [0, frames)
   int32_t budget;                         // expanded mode: min(C, frames)
+  int32_t block_tiles;                    // block-diagonal mode
   uint64_t seed;
   uint32_t thresh24;
   int32_t force_diagonal;
@@ -48,6 +49,10 @@ int launch_compact(int32_t rows, int32_t tk, const uint8_t* mask,
 int launch_fwd(const FwdLaunch& a, void* stream);
 // tuned instance: bf16, head dim 128, 128x128 tiles, N * 256 < 2^31
 int launch_fwd_bf16_t128_d128(const FwdLaunch& a, void* stream);
+
+// token reorder between window-major and position-major order
+int launch_window_reorder(int64_t BH, int32_t N, int32_t row_bytes, int32_t w, const void* src,
+                          void* dst, int inverse, void* stream);
 
 // static-mask calibration
 int launch_block_energy(const EnergyLaunch& a, void* stream);

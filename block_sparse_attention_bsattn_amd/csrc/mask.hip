@@ -22,6 +22,10 @@
 // with k (n_a <= T), so frame f is an anchor exactly when k = ceil(g*n_a/T),
 // g = (f - r) mod T, satisfies k < n_a and floor(k*T/n_a) == g.
 //
+// Block-diagonal mode (SQuad page, "1. Operatore di Attenzione SQuad": each
+// pass attends inside disjoint runs of tokens): tile pair (i, j) is active
+// when i and j fall in the same run of block_tiles tiles.
+//
 // Static mode (CalibAtt page, "B. Fase di Inferenza": the block lists are
 // precomputed and deterministic) draws one SplitMix64 value per cell
 // c = (h*Tq + i)*Tk + j: the (c+1)-th output of the generator seeded with
@@ -111,6 +115,8 @@ __global__ void build_mask_kernel(MaskLaunch a, uint8_t* __restrict__ mask) {
         }
       }
       if (!on) on = anchor_in(ka, kb, a);
+    } else if (a.kind == 4) {
+      on = (i / a.block_tiles) == (j / a.block_tiles);
     } else if (a.kind == 1) {
       const uint64_t z = splitmix64_at(a.seed, (uint64_t)c + 1);
       on = ((uint32_t)(z >> 40) < a.thresh24) || (a.force_diagonal && i == j);

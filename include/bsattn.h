@@ -51,7 +51,8 @@ typedef enum {
   BSATTN_MASK_WINDOW_ANCHOR = 0, /* LVSA local window + rotating global anchors */
   BSATTN_MASK_STATIC_RANDOM = 1, /* seeded stand-in for a calibrated static mask */
   BSATTN_MASK_DENSE = 2,         /* all tiles active (full attention) */
-  BSATTN_MASK_WINDOW_ANCHOR_EXPANDED = 3 /* LVSA window grown to a frame budget + anchors */
+  BSATTN_MASK_WINDOW_ANCHOR_EXPANDED = 3, /* LVSA window grown to a frame budget + anchors */
+  BSATTN_MASK_BLOCK_DIAGONAL = 4          /* SQuad passes: square blocks of block_tiles tiles */
 } bsattn_mask_kind;
 
 /* Token geometry of the video latent.  N = frames*grid_h*grid_w; the number
@@ -86,7 +87,12 @@ typedef struct {
  *   when the top 24 bits of the (c+1)-th SplitMix64 output for `seed` are
  *   below thresh24 (thresh24 = floor(p * 2^24) for density p), or when i == j
  *   and force_diagonal != 0.
- * DENSE: every cell active. */
+ * DENSE: every cell active.
+ * BLOCK_DIAGONAL (SQuad page, "1. Operatore di Attenzione SQuad": each pass
+ *   is softmax attention inside disjoint groups of tokens): cell (i, j) is
+ *   active when i / block_tiles == j / block_tiles (integer division), so
+ *   runs of block_tiles * tile consecutive tokens attend only among
+ *   themselves.  The frame layout is irrelevant to this mode. */
 typedef struct {
   int32_t kind;           /* bsattn_mask_kind */
   int32_t window;         /* w >= 0, in frames */
@@ -97,6 +103,7 @@ typedef struct {
   int32_t force_diagonal; /* STATIC_RANDOM */
   int32_t mask_heads;     /* Hm >= 1: number of mask slices (1 = shared by all heads) */
   int32_t budget;         /* WINDOW_ANCHOR_EXPANDED: C >= 0 frames per query frame */
+  int32_t block_tiles;    /* BLOCK_DIAGONAL: b >= 1 tiles per diagonal block */
 } bsattn_mask_params;
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
@@ -116,8 +123,9 @@ BSATTN_API int32_t bsattn_num_tiles(int64_t tokens, int32_t tile);
  *   mask: device uint8 [Hm, Tq, Tk], row-major, Hm = params->mask_heads;
  *         every byte is written (0 or 1).
  * Errors: INVALID_ARG on null pointers, non-positive sizes, window < 0,
- * num_anchors outside [0, T], budget < 0 (expanded mode), thresh24 > 2^24,
- * mask_heads < 1, an unknown kind, or Hm*Tq*Tk >= 2^31. */
+ * num_anchors outside [0, T], budget < 0 (expanded mode), block_tiles < 1
+ * (block-diagonal mode), thresh24 > 2^24, mask_heads < 1, an unknown kind,
+ * or Hm*Tq*Tk >= 2^31. */
 BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
                                  const bsattn_mask_params* params,
                                  uint8_t* mask, void* stream);
@@ -160,6 +168,23 @@ BSATTN_API int bsattn_fwd(int32_t B, int32_t H, int32_t N, int32_t d,
                           const void* k, const void* v, void* o, float* lse,
                           int32_t mask_heads, const int32_t* row_ptr,
                           const int32_t* col_idx, float scale, void* stream);
+
+/* Reorder token rows between window-major and position-major order (SQuad
+ * page, "1. Operatore di Attenzione SQuad": the global pass groups the
+ * tokens at the same position inside every window).  With G = N / w:
+ *   inverse == 0:  dst[b, h, r*G + a, :] = src[b, h, a*w + r, :]
+ *   inverse != 0:  dst[b, h, a*w + r, :] = src[b, h, r*G + a, :]
+ * for a < G, r < w.  After the forward reorder, each position group is a
+ * contiguous run of G tokens, so the global pass is a BLOCK_DIAGONAL mask
+ * with G / tile tiles per block.
+ *   src, dst: device [B, H, N, d] contiguous, element type `dtype`, distinct
+ *             buffers (dst written; src read only).
+ * Errors: INVALID_ARG (null or equal pointers, negative sizes, w < 1, N not
+ * a multiple of w, unaligned buffers, B*H*N*d >= 2^40), UNSUPPORTED (dtype),
+ * HIP.  B*H*N == 0 is a no-op. */
+BSATTN_API int bsattn_window_reorder(int32_t B, int32_t H, int32_t N, int32_t d, int32_t w,
+                                     int32_t dtype, const void* src, void* dst, int32_t inverse,
+                                     void* stream);
 
 /* ---- Static-mask calibration (CalibAtt page, "A. Fase di Calibrazione").
  * The calibration runs full attention on a few prompts, measures how much

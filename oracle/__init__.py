@@ -42,7 +42,7 @@ from .masks import (anchor_frames, window_frames, frame_set, frame_mask,
                     frame_mask_expanded, tile_mask_expanded,
                     tile_frame_range, tile_mask_window_anchor,
                     splitmix64_stream, static_hash24, tile_mask_static,
-                    tile_mask_dense, tile_mask)
+                    tile_mask_dense, tile_mask_block_diagonal, tile_mask)
 from .csr import tile_csr
 from .calibration import (block_energy, block_energy_rows, select_row,
                           select_mask, aggregate)
@@ -56,7 +56,7 @@ __all__ = [
     "expanded_window_frames", "frame_set_expanded", "frame_mask_expanded",
     "tile_mask_expanded",
     "tile_frame_range", "tile_mask_window_anchor", "splitmix64_stream",
-    "static_hash24", "tile_mask_static", "tile_mask_dense", "tile_mask",
+    "static_hash24", "tile_mask_static", "tile_mask_dense", "tile_mask_block_diagonal", "tile_mask",
     "tile_csr", "block_sparse_attention", "block_sparse_attention_rows",
     "block_energy", "block_energy_rows", "select_row", "select_mask",
     "aggregate", "squad_local", "squad_attention", "squad_attention_rows",

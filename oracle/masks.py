@@ -49,6 +49,10 @@ the diagonal is forced.  SplitMix64 is the generator of Steele, Lea and Flood
 and a final xor-shift.
 
 Dense mode: every tile active (the full-attention baseline).
+
+Block-diagonal mode (SQuad page, 1. Operatore di Attenzione SQuad: each of
+its two passes attends inside disjoint groups of consecutive tokens): tile
+pair (i, j) is active when i and j lie in the same run of b tiles.
 """
 from __future__ import annotations
 
@@ -201,6 +205,19 @@ def tile_mask_static(Hm: int, Tq: int, Tk: int, seed: int, thresh24: int,
     return M
 
 
+def tile_mask_block_diagonal(Hm: int, Tq: int, Tk: int, b: int) -> np.ndarray:
+    """M[i, j] = 1 when tiles i and j fall in the same run of b tiles (the
+    groups SQuad's passes attend within)."""
+    if b < 1:
+        raise ValueError("block size must be >= 1 tile")
+    M = np.zeros((Hm, Tq, Tk), dtype=np.uint8)
+    for i in range(Tq):
+        for j in range(Tk):
+            if i // b == j // b:
+                M[:, i, j] = 1
+    return M
+
+
 def tile_mask_dense(Hm: int, Tq: int, Tk: int) -> np.ndarray:
     return np.ones((Hm, Tq, Tk), dtype=np.uint8)
 
@@ -209,9 +226,11 @@ def tile_mask_dense(Hm: int, Tq: int, Tk: int) -> np.ndarray:
 def tile_mask(kind: int, frames: int, grid_h: int, grid_w: int, tile: int,
               window: int = 0, num_anchors: int = 0, rotation: int = 0,
               seed: int = 0, thresh24: int = 0, force_diagonal: int = 0,
-              mask_heads: int = 1, budget: int = 0) -> np.ndarray:
+              mask_heads: int = 1, budget: int = 0,
+              block_tiles: int = 1) -> np.ndarray:
     """uint8 [Hm, Tq, Tk] tile mask for kind 0 (window + anchors),
-    1 (static random), 2 (dense) or 3 (expanded window + anchors)."""
+    1 (static random), 2 (dense), 3 (expanded window + anchors) or
+    4 (block diagonal)."""
     N = frames * grid_h * grid_w
     nt = -(-N // tile)
     if kind == 0:
@@ -223,6 +242,8 @@ def tile_mask(kind: int, frames: int, grid_h: int, grid_w: int, tile: int,
                                 bool(force_diagonal))
     if kind == 2:
         return tile_mask_dense(mask_heads, nt, nt)
+    if kind == 4:
+        return tile_mask_block_diagonal(mask_heads, nt, nt, block_tiles)
     if kind == 3:
         M = tile_mask_expanded(frames, grid_h, grid_w, tile, window,
                                num_anchors, rotation, budget)

@@ -20,7 +20,8 @@ def oracle_mask(w, rotation=None):
                             rotation=s.rotation if rotation is None else rotation,
                             seed=s.seed, thresh24=s.thresh24,
                             force_diagonal=s.force_diagonal,
-                            mask_heads=s.mask_heads, budget=s.budget)
+                            mask_heads=s.mask_heads, budget=s.budget,
+                            block_tiles=s.block_tiles)
 
 
 def gpu_mask_csr(w, device="cuda"):

@@ -104,12 +104,14 @@ def test_build_mask_rejects_bad_arguments():
     assert call(mask=None) == bs.ERR_INVALID_ARG
     assert call(layout=bs.Layout(0, 8, 8, 64)) == bs.ERR_INVALID_ARG
     assert call(layout=bs.Layout(4, 8, 8, 0)) == bs.ERR_INVALID_ARG
-    assert call(params=bs.MaskParams(4, 1, 1, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
     assert call(params=bs.MaskParams(-1, 1, 1, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
     # expanded windows: negative budget, and the window/anchor checks apply
     assert call(params=bs.MaskParams(3, 1, 1, 0, 0, 0, 0, 1, -1)) == bs.ERR_INVALID_ARG
     assert call(params=bs.MaskParams(3, -1, 1, 0, 0, 0, 0, 1, 5)) == bs.ERR_INVALID_ARG
     assert call(params=bs.MaskParams(3, 1, 5, 0, 0, 0, 0, 1, 5)) == bs.ERR_INVALID_ARG
+    # block diagonal: at least one tile per block
+    assert call(params=bs.MaskParams(4, 0, 0, 0, 0, 0, 0, 1, 0, 0)) == bs.ERR_INVALID_ARG
+    assert call(params=bs.MaskParams(5, 0, 0, 0, 0, 0, 0, 1, 0, 1)) == bs.ERR_INVALID_ARG
     assert call(params=bs.MaskParams(0, -1, 1, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
     assert call(params=bs.MaskParams(0, 1, 5, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
     assert call(params=bs.MaskParams(1, 0, 0, 0, 0, (1 << 24) + 1, 0, 1)) == \
@@ -192,3 +194,16 @@ def test_calibration_calls_reject_bad_arguments():
     assert A(2, 4, p, float("nan"), p, None) == bs.ERR_INVALID_ARG
     assert A(2, 4, None, 0.5, p, None) == bs.ERR_INVALID_ARG
     assert A(2, 0, None, 0.5, None, None) == bs.OK
+
+
+def test_window_reorder_rejects_bad_arguments():
+    R = bs.lib().bsattn_window_reorder
+    p, p2 = ctypes.c_void_p(64), ctypes.c_void_p(128)
+    assert R(1, 1, 12, 128, 5, 0, p, p2, 0, None) == bs.ERR_INVALID_ARG    # N % w
+    assert R(1, 1, 12, 128, 0, 0, p, p2, 0, None) == bs.ERR_INVALID_ARG    # w < 1
+    assert R(1, 1, 12, 128, 4, 0, p, p, 0, None) == bs.ERR_INVALID_ARG     # aliased
+    assert R(1, 1, 12, 128, 4, 0, None, p2, 0, None) == bs.ERR_INVALID_ARG
+    assert R(1, 1, 12, 4, 4, 0, p, p2, 0, None) == bs.ERR_INVALID_ARG      # 8-byte rows
+    assert R(1, 1, 12, 128, 4, 3, p, p2, 0, None) == bs.ERR_UNSUPPORTED
+    assert R(1, 1, 12, 128, 4, 0, ctypes.c_void_p(65), p2, 0, None) == bs.ERR_INVALID_ARG
+    assert R(0, 1, 12, 128, 4, 0, None, None, 0, None) == bs.OK

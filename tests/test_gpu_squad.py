@@ -1,0 +1,72 @@
+"""GPU SQuad two-pass attention (SQuad page, "1. Operatore di Attenzione
+SQuad") against the oracle: the block-diagonal masks and the token reorder
+bit-exact, the composed operator within the output bar."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_bsattn_amd as bs
+import oracle
+import workloads as W
+from parity_util import assert_close, check_mask_csr, gpu_mask_csr, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("N,tile,b", [(300, 64, 2), (1024, 128, 1), (4096, 64, 8),
+                                      (65536, 128, 2), (1000, 128, 3)])
+def test_block_diagonal_masks(N, tile, b):
+    w = W.small_workload(frames=1, grid_h=1, grid_w=N, tile=tile,
+                         mask=W.MaskSpec(W.MASK_BLOCK_DIAGONAL, block_tiles=b))
+    mask, rp, ci = gpu_mask_csr(w)
+    check_mask_csr(w, mask, rp, ci)
+
+
+@pytest.mark.parametrize("N,d,w,dt", [(64, 128, 8, torch.bfloat16), (96, 64, 96, torch.float32),
+                                      (4096, 128, 64, torch.bfloat16), (30, 8, 1, torch.bfloat16)])
+def test_window_reorder_bit_exact(N, d, w, dt):
+    g = torch.Generator().manual_seed(N + w)
+    x = torch.randn(2, 3, N, d, generator=g).to(dt)
+    fwd = torch.empty_like(x.cuda())
+    bs.window_reorder(x.cuda(), fwd, w)
+    back = torch.empty_like(fwd)
+    bs.window_reorder(fwd, back, w, inverse=True)
+    torch.cuda.synchronize()
+    want = oracle.window_major_to_position_major(x.float().numpy(), w)
+    assert np.array_equal(fwd.cpu().float().numpy(), want)
+    assert torch.equal(back.cpu(), x)
+
+
+@pytest.mark.parametrize("N,d,w,tile,H", [(4096, 64, 64, 64, 2), (16384, 128, 128, 128, 2),
+                                          (32768, 128, 256, 128, 1), (8192, 128, 128, 64, 1)])
+def test_squad_full_parity(N, d, w, tile, H):
+    g = torch.Generator().manual_seed(zlib.crc32(f"{N}{w}".encode()) & 0xFFFF)
+    q, k, v = (torch.randn(1, H, N, d, generator=g).to(torch.bfloat16) for _ in range(3))
+    o = bs.squad(q.cuda(), k.cuda(), v.cuda(), w, tile)
+    torch.cuda.synchronize()
+    want = oracle.squad_attention(q, k, v, w)
+    assert_close(f"squad N={N} w={w} tile={tile}", to64(o), want)
+
+
+def test_squad_full_size_sampled_rows():
+    """65 536 tokens, w = 256: sampled rows against the oracle, for every
+    head: six positions (first, last and inside a window) in ten windows
+    (first, last and spread), so six global position groups are evaluated."""
+    w = W.SQUAD
+    q, k, v = W.make_qkv(w)
+    o = bs.squad(q.cuda(), k.cuda(), v.cuda(), W.SQUAD_W, w.tile)
+    torch.cuda.synchronize()
+    G = w.N // W.SQUAD_W
+    pos = np.array([0, 1, 77, 128, 200, W.SQUAD_W - 1])
+    win = np.array([0, 1, 31, 64, 100, 127, 128, 190, 230, G - 1])
+    rows = np.sort((win[:, None] * W.SQUAD_W + pos[None, :]).ravel())
+    want = oracle.squad_attention_rows(q, k, v, W.SQUAD_W, rows)
+    assert_close(f"squad 65536 ({len(rows)} rows x {w.H} heads)", to64(o[:, :, rows]), want)
+
+
+def test_squad_rejects_misaligned_windows():
+    q = torch.zeros(1, 1, 1000, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        bs.squad(q, q, q, 100, 64)

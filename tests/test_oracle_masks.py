@@ -315,3 +315,22 @@ def test_expanded_window_is_balanced_and_minimal():
                             assert len(G | (W - {last})) < target
                             n += 1
     assert n > 500
+
+
+# ------------------------------------------------------------ block diagonal
+def test_block_diagonal_by_hand():
+    """5 tiles in runs of 2: {0, 1}, {2, 3}, {4}."""
+    want = np.array([[1, 1, 0, 0, 0],
+                     [1, 1, 0, 0, 0],
+                     [0, 0, 1, 1, 0],
+                     [0, 0, 1, 1, 0],
+                     [0, 0, 0, 0, 1]], dtype=np.uint8)
+    got = oracle.tile_mask(4, 1, 1, 300, 64, block_tiles=2, mask_heads=2)
+    assert got.shape == (2, 5, 5)
+    np.testing.assert_array_equal(got[0], want)
+    np.testing.assert_array_equal(got[1], want)
+    np.testing.assert_array_equal(oracle.tile_mask(4, 1, 1, 300, 64, block_tiles=1)[0],
+                                  np.eye(5, dtype=np.uint8))
+    assert (oracle.tile_mask(4, 1, 1, 300, 64, block_tiles=5)[0] == 1).all()
+    with pytest.raises(ValueError):
+        oracle.tile_mask(4, 1, 1, 300, 64, block_tiles=0)

@@ -25,6 +25,7 @@ MASK_WINDOW_ANCHOR = 0
 MASK_STATIC_RANDOM = 1
 MASK_DENSE = 2
 MASK_WINDOW_ANCHOR_EXPANDED = 3
+MASK_BLOCK_DIAGONAL = 4
 
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
@@ -49,6 +50,7 @@ class MaskSpec:
     force_diagonal: int = 0  # static mode
     mask_heads: int = 1      # Hm: 1 (shared by all heads) or H
     budget: int = 0          # C, frames per query frame (expanded windows)
+    block_tiles: int = 1     # tiles per diagonal block (block-diagonal mode)
 
 
 @dataclass(frozen=True)
@@ -193,6 +195,17 @@ CALIB = Workload("video_21x30x52_calib_p4", B=4, H=12, d=128, frames=21,
                  mask=MaskSpec(MASK_DENSE), seed=1007)
 CALIB_EPS = 0.9
 CALIB_RHO = 0.5
+
+
+# SQuad's two-pass attention at a 65 536-token latent (16 frames of 64x64):
+# windows of w = 256 = sqrt(N) consecutive tokens, so both the local pass
+# (256 windows) and the global pass (256 position groups of 256 tokens) are
+# block-diagonal with 2 x 2-tile blocks.  The mask spec is unused (each pass
+# builds its own block-diagonal mask).
+SQUAD = Workload("squad_16x64x64_w256", B=1, H=12, d=128, frames=16,
+                 grid_h=64, grid_w=64, tile=128, dtype=DTYPE_BF16,
+                 mask=MaskSpec(MASK_BLOCK_DIAGONAL, block_tiles=2), seed=1008)
+SQUAD_W = 256
 
 
 def small_workload(frames=3, grid_h=5, grid_w=9, tile=64, d=64, H=2, B=1,
