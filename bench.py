@@ -14,8 +14,9 @@ Printed: ONE JSON line with
   cpu_baseline the float64 CPU oracle on a bounded row sample,
 plus the forward-only time, the same kernel at density 1.0 and the speedup,
 a density sweep, the path with LVSA expanded windows on the 84-frame
-long-video shape, and the static-mask calibration (block energies, selection,
-agreement) with the forward on the calibrated mask.
+long-video shape, the static-mask calibration (block energies, selection,
+agreement) with the forward on the calibrated mask, and SQuad's two-pass
+attention against dense attention of the same shape.
 """
 from __future__ import annotations
 
@@ -215,6 +216,77 @@ def calibration(bs, W, torch, dev, calls: int):
             "fwd_tflops_on_calibrated_mask": round(f_flops / (f_ms * 1e-3) / 1e12, 1)}
 
 
+def squad_leg(bs, W, torch, dev, calls: int):
+    """SQuad's two-pass attention at 65 536 tokens (w = 256): the local pass,
+    the reorders of Q, K and the local output, the global pass and the
+    inverse reorder, each timed with events on the launch stream; then the
+    same kernel as dense attention for the comparison the page draws."""
+    w = W.SQUAD
+    win = W.SQUAD_W
+    G = w.N // win
+    q, k, v = W.make_qkv(w, device=dev)
+    stream = torch.cuda.current_stream()
+    layout = (1, 1, w.N, w.tile)
+    masks = {}
+    for b in (win // w.tile, G // w.tile):
+        m = bs.make_mask(*layout, device=dev, kind=W.MASK_BLOCK_DIAGONAL, block_tiles=b)
+        masks[b] = bs.make_csr(m)
+    o_l, qp, kp, op, og, out = (torch.empty_like(q) for _ in range(6))
+
+    def run(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        rp, ci = masks[win // w.tile]
+        bs.fwd(q, k, v, o_l, rp, ci, w.tile, stream=stream)
+        mark(1)
+        bs.window_reorder(q, qp, win, stream=stream)
+        bs.window_reorder(k, kp, win, stream=stream)
+        bs.window_reorder(o_l, op, win, stream=stream)
+        mark(2)
+        rp, ci = masks[G // w.tile]
+        bs.fwd(qp, kp, op, og, rp, ci, w.tile, stream=stream)
+        mark(3)
+        bs.window_reorder(og, out, win, inverse=True, stream=stream)
+        mark(4)
+
+    run()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(calls)]
+    for e in evs:
+        run(e)
+    torch.cuda.synchronize()
+    part = lambda a, b: float(np.median([e[a].elapsed_time(e[b]) for e in evs]))
+    flops_local = 4.0 * w.d * w.N * win * w.B * w.H
+    flops_global = 4.0 * w.d * w.N * G * w.B * w.H
+    reorder_bytes = 4 * 2 * w.B * w.H * w.N * w.d * 2   # 4 reorders, read + write
+    l_ms, r_ms, g_ms, i_ms = part(0, 1), part(1, 2), part(2, 3), part(3, 4)
+    total = part(0, 4)
+    # dense attention of the same shape with the same kernel
+    dm = bs.make_mask(*layout, device=dev, kind=W.MASK_DENSE)
+    drp, dci = bs.make_csr(dm)
+    bs.fwd(q, k, v, og, drp, dci, w.tile)
+    de = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(max(1, calls // 2))]
+    for a, b in de:
+        a.record(stream)
+        bs.fwd(q, k, v, og, drp, dci, w.tile, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = float(np.median([a.elapsed_time(b) for a, b in de]))
+    dense_flops = 4.0 * w.d * w.N * w.N * w.B * w.H
+    return {"workload": w.name, "window": win, "groups": G,
+            "ms_total": round(total, 4),
+            "local_ms": round(l_ms, 4), "local_tflops": round(flops_local / (l_ms * 1e-3) / 1e12, 1),
+            "global_ms": round(g_ms, 4), "global_tflops": round(flops_global / (g_ms * 1e-3) / 1e12, 1),
+            "reorder_ms": round(r_ms + i_ms, 4),
+            "reorder_gbs": round(reorder_bytes / ((r_ms + i_ms) * 1e-3) / 1e9, 1),
+            "attention_tflop": round((flops_local + flops_global) / 1e12, 4),
+            "dense_tflop": round(dense_flops / 1e12, 3),
+            "dense_ms": round(dense_ms, 3),
+            "speedup_vs_dense": round(dense_ms / total, 2)}
+
+
 def cpu_baseline(w, q, k, v, mask_np, tiles: int, workers: int):
     """The oracle as it stands, on `tiles` evenly spaced query tiles (every
     row of them, every head) at rotation 0; TFLOP/s credited like the GPU
@@ -270,6 +342,8 @@ def main():
     ap.add_argument("--calib", type=int, default=3,
                     help="timed calls of the static-mask calibration leg "
                          "(0 = skip)")
+    ap.add_argument("--squad", type=int, default=6,
+                    help="timed calls of the SQuad two-pass leg (0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB "
                          "(byte-counter calibration under a profiler)")
@@ -387,6 +461,8 @@ def main():
 
     calib = calibration(bs, W, torch, dev, args.calib) if args.calib > 0 else None
 
+    squad = squad_leg(bs, W, torch, dev, args.squad) if args.squad > 0 else None
+
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -458,6 +534,7 @@ def main():
         "density_sweep": sweep,
         "expanded_windows": expanded,
         "calibration": calib,
+        "squad": squad,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
