@@ -14,7 +14,8 @@ Sources (page title, then section):
     A. Fase di Calibrazione / B. Fase di Inferenza: 128x128 attention blocks,
     a static per-(timestep, layer, head) block mask, attention computed only
     over the selected blocks; the calibration that builds those masks from
-    block energies and cross-prompt agreement.
+    block energies and cross-prompt agreement; spatial repetition (row
+    similarity, anchor rows computed and copied).
   * "SQuad: Sub-Quadratic Attention Distillation for Efficient Video
     Generation", 1. Operatore di Attenzione SQuad: the two-pass local/global
     softmax attention.
@@ -29,6 +30,8 @@ Modules:
              selection, cross-prompt aggregation
   squad      two-pass local/global attention (local output as the global
              pass's values)
+  repetition spatial-row similarity, repetitive heads, attention on anchor
+             rows copied to the other rows
 
 Every function here is pinned by tests/test_oracle_*.py against values and
 properties fixed by the pages or by mathematics (hand-enumerated masks,
@@ -46,6 +49,9 @@ from .masks import (anchor_frames, window_frames, frame_set, frame_mask,
 from .csr import tile_csr
 from .calibration import (block_energy, block_energy_rows, select_row,
                           select_mask, aggregate)
+from .repetition import (anchor_row, row_cosines, repetitive_heads,
+                         anchor_count, gather_anchor_rows,
+                         broadcast_anchor_rows, repeated_attention)
 from .squad import (squad_local, squad_attention, squad_attention_rows,
                     window_major_to_position_major,
                     position_major_to_window_major)
@@ -61,4 +67,6 @@ __all__ = [
     "block_energy", "block_energy_rows", "select_row", "select_mask",
     "aggregate", "squad_local", "squad_attention", "squad_attention_rows",
     "window_major_to_position_major", "position_major_to_window_major",
+    "anchor_row", "row_cosines", "repetitive_heads", "anchor_count",
+    "gather_anchor_rows", "broadcast_anchor_rows", "repeated_attention",
 ]
