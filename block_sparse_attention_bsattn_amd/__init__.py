@@ -11,9 +11,12 @@ The calls mirror include/bsattn.h:
     select_blocks(energy, eps, mask)                    -> bsattn_select_blocks
     aggregate_masks(masks, rho, out)                    -> bsattn_aggregate_masks
     window_reorder(src, dst, w, inverse)                -> bsattn_window_reorder
+    row_cosines(q, k, ..., cos)                         -> bsattn_row_cosines
+    repetitive_heads(cos, stride, gamma, flags)         -> bsattn_repetitive_heads
+    anchor_rows(src, dst, ..., broadcast)               -> bsattn_anchor_rows
 
 plus small helpers that allocate the outputs with torch (make_mask,
-make_csr, attention, calibrate, squad).  There is no fallback: if libbsattn.so is missing or a
+make_csr, attention, calibrate, squad, repeated_attention).  There is no fallback: if libbsattn.so is missing or a
 call fails, an exception is raised.
 """
 from __future__ import annotations
@@ -38,11 +41,13 @@ MASK_STATIC_RANDOM = 1
 MASK_DENSE = 2
 MASK_WINDOW_ANCHOR_EXPANDED = 3
 MASK_BLOCK_DIAGONAL = 4
+MASK_DENSE_ROWS = 5
 
 # Every symbol include/bsattn.h exports.
 EXPORTS = ("bsattn_version", "bsattn_status_string", "bsattn_last_error",
            "bsattn_num_tiles", "bsattn_build_mask", "bsattn_compact",
-           "bsattn_fwd", "bsattn_window_reorder", "bsattn_block_energy",
+           "bsattn_fwd", "bsattn_window_reorder", "bsattn_row_cosines",
+           "bsattn_repetitive_heads", "bsattn_anchor_rows", "bsattn_block_energy",
            "bsattn_select_blocks",
            "bsattn_aggregate_masks", "bsattn_mfma_ceiling")
 
@@ -64,7 +69,7 @@ class MaskParams(ctypes.Structure):
                 ("seed", ctypes.c_uint64), ("thresh24", ctypes.c_uint32),
                 ("force_diagonal", ctypes.c_int32),
                 ("mask_heads", ctypes.c_int32), ("budget", ctypes.c_int32),
-                ("block_tiles", ctypes.c_int32)]
+                ("block_tiles", ctypes.c_int32), ("query_tiles", ctypes.c_int32)]
 
 
 _lib = None
@@ -100,6 +105,13 @@ def lib() -> ctypes.CDLL:
                              i32, i32p, i32p, ctypes.c_float, vp]
     L.bsattn_window_reorder.restype = ctypes.c_int
     L.bsattn_window_reorder.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i32, vp]
+    L.bsattn_row_cosines.restype = ctypes.c_int
+    L.bsattn_row_cosines.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp,
+                                     ctypes.c_float, vp]
+    L.bsattn_repetitive_heads.restype = ctypes.c_int
+    L.bsattn_repetitive_heads.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.c_double, u8p, vp]
+    L.bsattn_anchor_rows.restype = ctypes.c_int
+    L.bsattn_anchor_rows.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, i32, vp]
     L.bsattn_block_energy.restype = ctypes.c_int
     L.bsattn_block_energy.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp,
                                       ctypes.c_float, vp]
@@ -153,10 +165,11 @@ def num_tiles(tokens: int, tile: int) -> int:
 
 
 def _params(kind, window=0, num_anchors=0, rotation=0, seed=0, thresh24=0,
-            force_diagonal=0, mask_heads=1, budget=0, block_tiles=1) -> MaskParams:
+            force_diagonal=0, mask_heads=1, budget=0, block_tiles=1,
+            query_tiles=0) -> MaskParams:
     return MaskParams(kind, window, num_anchors, rotation,
                       seed & 0xFFFFFFFFFFFFFFFF, thresh24, int(force_diagonal),
-                      mask_heads, budget, block_tiles)
+                      mask_heads, budget, block_tiles, query_tiles)
 
 
 def build_mask(layout: Sequence[int], mask, stream=None, **params):
@@ -164,7 +177,7 @@ def build_mask(layout: Sequence[int], mask, stream=None, **params):
 
     layout = (frames, grid_h, grid_w, tile); params are the fields of
     bsattn_mask_params (kind, window, num_anchors, rotation, seed, thresh24,
-    force_diagonal, mask_heads, budget, block_tiles)."""
+    force_diagonal, mask_heads, budget, block_tiles, query_tiles)."""
     import torch
     L = Layout(*[int(x) for x in layout])
     P = _params(**params)
@@ -242,6 +255,50 @@ def window_reorder(src, dst, w: int, inverse: bool = False, stream=None):
                                      _ptr(src, "src", src.dtype), _ptr(dst, "dst", src.dtype),
                                      int(bool(inverse)), _stream(stream))
     _check(st, "bsattn_window_reorder")
+    return dst
+
+
+def row_cosines(q, k, frames, grid_h, grid_w, stride, cos, scale=0.0, stream=None):
+    """bsattn_row_cosines into cos [B, H, frames, grid_h] (float32)."""
+    import torch
+    B, H, N, d = q.shape
+    if N != frames * grid_h * grid_w or tuple(k.shape) != tuple(q.shape):
+        raise ValueError("q, k must be [B, H, frames*grid_h*grid_w, d]")
+    if tuple(cos.shape) != (B, H, frames, grid_h):
+        raise ValueError("cos must have shape [B, H, frames, grid_h]")
+    st = lib().bsattn_row_cosines(B, H, frames, grid_h, grid_w, d, stride, _dtype_code(q),
+                                  _ptr(q, "q", q.dtype), _ptr(k, "k", q.dtype),
+                                  _ptr(cos, "cos", torch.float32), float(scale),
+                                  _stream(stream))
+    _check(st, "bsattn_row_cosines")
+    return cos
+
+
+def repetitive_heads(cos, stride, gamma, flags, stream=None):
+    """bsattn_repetitive_heads: flags [H] (uint8) from cos [B, H, T, grid_h]."""
+    import torch
+    B, H, T, gh = cos.shape
+    if tuple(flags.shape) != (H,):
+        raise ValueError("flags must have shape [H]")
+    st = lib().bsattn_repetitive_heads(B, H, T, gh, stride, _ptr(cos, "cos", torch.float32),
+                                       float(gamma), _ptr(flags, "flags", torch.uint8),
+                                       _stream(stream))
+    _check(st, "bsattn_repetitive_heads")
+    return flags
+
+
+def anchor_rows(src, dst, frames, grid_h, grid_w, stride, broadcast=False, stream=None):
+    """bsattn_anchor_rows between [B, H, N, d] buffers (gather, or broadcast
+    with broadcast=True)."""
+    if src.dim() != 4 or tuple(dst.shape) != tuple(src.shape) or dst.dtype != src.dtype:
+        raise ValueError("src and dst must share shape [B, H, N, d] and dtype")
+    B, H, N, d = src.shape
+    if N != frames * grid_h * grid_w:
+        raise ValueError("N must equal frames * grid_h * grid_w")
+    st = lib().bsattn_anchor_rows(B, H, frames, grid_h, grid_w, d, stride, _dtype_code(src),
+                                  _ptr(src, "src", src.dtype), _ptr(dst, "dst", src.dtype),
+                                  int(bool(broadcast)), _stream(stream))
+    _check(st, "bsattn_anchor_rows")
     return dst
 
 
@@ -386,6 +443,27 @@ def squad(q, k, v, w: int, tile: int, scale: float = 0.0, stream=None):
     return out
 
 
+def repeated_attention(q, k, v, frames, grid_h, grid_w, stride, tile, scale=0.0,
+                       stream=None):
+    """Attention of a repetitive head through the library's calls: the
+    anchor rows' queries are packed to the front, full attention runs for
+    those query tiles only (DENSE_ROWS mask), and every row takes its
+    anchor row's output."""
+    import torch
+    B, H, N, d = q.shape
+    na = frames * (-(-grid_h // stride)) * grid_w
+    qa = torch.zeros_like(q)
+    anchor_rows(q, qa, frames, grid_h, grid_w, stride, stream=stream)
+    mask = make_mask(frames, grid_h, grid_w, tile, device=q.device, stream=stream,
+                     kind=MASK_DENSE_ROWS, query_tiles=-(-na // tile))
+    rp, ci = make_csr(mask, stream=stream)
+    oa = torch.empty_like(q)
+    fwd(qa, k, v, oa, rp, ci, tile, scale=scale, stream=stream)
+    out = torch.empty_like(q)
+    anchor_rows(oa, out, frames, grid_h, grid_w, stride, broadcast=True, stream=stream)
+    return out
+
+
 def mask_params_of(spec) -> dict:
     """Keyword parameters of build_mask from an object with the fields of
     bsattn_mask_params (e.g. a workload's mask spec)."""
@@ -394,4 +472,5 @@ def mask_params_of(spec) -> dict:
                 seed=spec.seed, thresh24=spec.thresh24,
                 force_diagonal=spec.force_diagonal,
                 mask_heads=spec.mask_heads, budget=spec.budget,
-                block_tiles=getattr(spec, "block_tiles", 1))
+                block_tiles=getattr(spec, "block_tiles", 1),
+                query_tiles=getattr(spec, "query_tiles", 0))

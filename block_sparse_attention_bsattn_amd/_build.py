@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsattn.so")
 
 SOURCES = ["mask.hip", "compact.hip", "fwd.hip", "fwd_bf16_t128.hip",
-           "calib.hip", "reorder.hip", "mfma_ceiling.hip", "api.cpp"]
+           "calib.hip", "reorder.hip", "repetition.hip", "mfma_ceiling.hip",
+           "api.cpp"]
 ARCH = "gfx950"
 
 

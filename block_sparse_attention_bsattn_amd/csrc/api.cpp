@@ -77,7 +77,7 @@ BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
   const int64_t tokens = per_frame * L.frames;
   if (tokens > INT32_MAX)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: more than 2^31-1 tokens");
-  if (M.kind < BSATTN_MASK_WINDOW_ANCHOR || M.kind > BSATTN_MASK_BLOCK_DIAGONAL)
+  if (M.kind < BSATTN_MASK_WINDOW_ANCHOR || M.kind > BSATTN_MASK_DENSE_ROWS)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: unknown mask kind %d", M.kind);
   if (M.mask_heads < 1)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: mask_heads must be >= 1");
@@ -94,6 +94,8 @@ BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: budget must be >= 0");
   if (M.kind == BSATTN_MASK_BLOCK_DIAGONAL && M.block_tiles < 1)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: block_tiles must be >= 1");
+  if (M.kind == BSATTN_MASK_DENSE_ROWS && M.query_tiles < 0)
+    return fail(BSATTN_ERR_INVALID_ARG, "build_mask: query_tiles must be >= 0");
   if (M.kind == BSATTN_MASK_STATIC_RANDOM && M.thresh24 > (1u << 24))
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: thresh24 exceeds 2^24");
   const int32_t tiles = bsattn_num_tiles(tokens, L.tile);
@@ -117,6 +119,7 @@ BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
   a.num_anchors = M.num_anchors;
   a.rotation = ((M.rotation % L.frames) + L.frames) % L.frames;
   a.block_tiles = M.kind == BSATTN_MASK_BLOCK_DIAGONAL ? M.block_tiles : 1;
+  a.query_tiles = M.kind == BSATTN_MASK_DENSE_ROWS ? M.query_tiles : 0;
   a.seed = M.seed;
   a.thresh24 = M.thresh24;
   a.force_diagonal = M.force_diagonal != 0;
@@ -210,6 +213,90 @@ BSATTN_API int bsattn_window_reorder(int32_t B, int32_t H, int32_t N, int32_t d,
   return hip_status(bsattn::launch_window_reorder((int64_t)B * H, N, (int32_t)row_bytes, w, src,
                                                   dst, inverse != 0, stream),
                     "window_reorder");
+}
+
+static int check_grid(const char* who, int32_t B, int32_t H, int32_t T, int32_t gh, int32_t gw,
+                      int32_t d, int32_t stride, int32_t dtype, bool mfma_dims) {
+  if (B < 0 || H < 0 || T < 0 || gh < 1 || gw < 1 || stride < 1 || d < 1)
+    return fail(BSATTN_ERR_INVALID_ARG,
+                "%s: B, H, T >= 0 and grid_h, grid_w, stride, d >= 1 required", who);
+  if (mfma_dims && d != 64 && d != 128)
+    return fail(BSATTN_ERR_UNSUPPORTED, "%s: head dim %d (supported: 64, 128)", who, d);
+  if (dtype != BSATTN_DTYPE_BF16 && dtype != BSATTN_DTYPE_F32)
+    return fail(BSATTN_ERR_UNSUPPORTED, "%s: dtype %d", who, dtype);
+  if (B > 65535 || H > 65535)
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: B and H must be <= 65535", who);
+  if ((int64_t)T * gh * gw > INT32_MAX)
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: more than 2^31-1 tokens", who);
+  return BSATTN_OK;
+}
+
+BSATTN_API int bsattn_row_cosines(int32_t B, int32_t H, int32_t T, int32_t grid_h,
+                                  int32_t grid_w, int32_t d, int32_t stride, int32_t dtype,
+                                  const void* q, const void* k, float* cos, float scale,
+                                  void* stream) {
+  const int st = check_grid("row_cosines", B, H, T, grid_h, grid_w, d, stride, dtype, true);
+  if (st != BSATTN_OK) return st;
+  if (grid_w > 256) return fail(BSATTN_ERR_UNSUPPORTED, "row_cosines: grid_w %d > 256", grid_w);
+  if ((int64_t)B * H * T == 0) return ok();
+  if (!q || !k || !cos) return fail(BSATTN_ERR_INVALID_ARG, "row_cosines: null pointer");
+  if (!aligned16(q) || !aligned16(k))
+    return fail(BSATTN_ERR_INVALID_ARG, "row_cosines: q and k must be 16-byte aligned");
+  if (!(scale == scale) || isinf(scale))
+    return fail(BSATTN_ERR_INVALID_ARG, "row_cosines: scale must be finite");
+  if ((int64_t)T * grid_h > INT32_MAX / 2)
+    return fail(BSATTN_ERR_INVALID_ARG, "row_cosines: too many rows");
+  bsattn::RowCosLaunch a;
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.gh = grid_h;
+  a.gw = grid_w;
+  a.N = T * grid_h * grid_w;
+  a.d = d;
+  a.dtype = dtype;
+  a.stride = stride;
+  a.q = q;
+  a.k = k;
+  a.cos = cos;
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  return hip_status(bsattn::launch_row_cosines(a, stream), "row_cosines");
+}
+
+BSATTN_API int bsattn_repetitive_heads(int32_t B, int32_t H, int32_t T, int32_t grid_h,
+                                       int32_t stride, const float* cos, double gamma,
+                                       uint8_t* flags, void* stream) {
+  if (B < 0 || H < 0 || T < 0 || grid_h < 1 || stride < 1)
+    return fail(BSATTN_ERR_INVALID_ARG,
+                "repetitive_heads: B, H, T >= 0 and grid_h, stride >= 1 required");
+  if (!(gamma == gamma) || isinf(gamma))
+    return fail(BSATTN_ERR_INVALID_ARG, "repetitive_heads: gamma must be finite");
+  if (H == 0) return ok();
+  if (!flags || ((int64_t)B * T > 0 && !cos))
+    return fail(BSATTN_ERR_INVALID_ARG, "repetitive_heads: null pointer");
+  return hip_status(bsattn::launch_repetitive_heads(B, H, T, grid_h, stride, cos, gamma, flags,
+                                                    stream),
+                    "repetitive_heads");
+}
+
+BSATTN_API int bsattn_anchor_rows(int32_t B, int32_t H, int32_t T, int32_t grid_h,
+                                  int32_t grid_w, int32_t d, int32_t stride, int32_t dtype,
+                                  const void* src, void* dst, int32_t broadcast, void* stream) {
+  const int st = check_grid("anchor_rows", B, H, T, grid_h, grid_w, d, stride, dtype, false);
+  if (st != BSATTN_OK) return st;
+  if ((d * (dtype == BSATTN_DTYPE_BF16 ? 2 : 4)) % 16 != 0)
+    return fail(BSATTN_ERR_INVALID_ARG, "anchor_rows: rows must be 16-byte multiples");
+  if ((int64_t)B * H * T == 0) return ok();
+  if (!src || !dst || src == dst)
+    return fail(BSATTN_ERR_INVALID_ARG, "anchor_rows: null or aliased buffers");
+  if (!aligned16(src) || !aligned16(dst))
+    return fail(BSATTN_ERR_INVALID_ARG, "anchor_rows: buffers must be 16-byte aligned");
+  const int32_t row_bytes = d * (dtype == BSATTN_DTYPE_BF16 ? 2 : 4);
+  return hip_status(bsattn::launch_anchor_rows((int64_t)B * H, T * grid_h * grid_w, row_bytes,
+                                               grid_h, grid_w, stride, broadcast != 0, src, dst,
+                                               stream),
+                    "anchor_rows");
 }
 
 BSATTN_API int bsattn_block_energy(int32_t B, int32_t H, int32_t N, int32_t d, int32_t tile,

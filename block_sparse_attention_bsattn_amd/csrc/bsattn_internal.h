@@ -13,6 +13,7 @@ struct MaskLaunch {
   int32_t window, num_anchors, rotation;  // window <= frames, rotation in [0, frames)
   int32_t budget;                         // expanded mode: min(C, frames)
   int32_t block_tiles;                    // block-diagonal mode
+  int32_t query_tiles;                    // dense-rows mode
   uint64_t seed;
   uint32_t thresh24;
   int32_t force_diagonal;
@@ -53,6 +54,20 @@ int launch_fwd_bf16_t128_d128(const FwdLaunch& a, void* stream);
 // token reorder between window-major and position-major order
 int launch_window_reorder(int64_t BH, int32_t N, int32_t row_bytes, int32_t w, const void* src,
                           void* dst, int inverse, void* stream);
+
+// spatial repetition
+struct RowCosLaunch {
+  int32_t B, H, T, gh, gw, N, d, dtype, stride;
+  const void* q;
+  const void* k;
+  float* cos;         // [B, H, T, gh]
+  float scale_log2;   // softmax scale * log2(e)
+};
+int launch_row_cosines(const RowCosLaunch& a, void* stream);
+int launch_repetitive_heads(int32_t B, int32_t H, int32_t T, int32_t gh, int32_t stride,
+                            const float* cos, double gamma, uint8_t* flags, void* stream);
+int launch_anchor_rows(int64_t BH, int32_t N, int32_t row_bytes, int32_t gh, int32_t gw,
+                       int32_t stride, int broadcast, const void* src, void* dst, void* stream);
 
 // static-mask calibration
 int launch_block_energy(const EnergyLaunch& a, void* stream);

@@ -26,6 +26,10 @@
 // pass attends inside disjoint runs of tokens): tile pair (i, j) is active
 // when i and j fall in the same run of block_tiles tiles.
 //
+// Dense-rows mode (CalibAtt page, "B. Fase di Inferenza": a repetitive head
+// computes its anchor rows only, packed into the first query tiles): query
+// tiles below query_tiles read every key tile, the others none.
+//
 // Static mode (CalibAtt page, "B. Fase di Inferenza": the block lists are
 // precomputed and deterministic) draws one SplitMix64 value per cell
 // c = (h*Tq + i)*Tk + j: the (c+1)-th output of the generator seeded with
@@ -117,6 +121,8 @@ __global__ void build_mask_kernel(MaskLaunch a, uint8_t* __restrict__ mask) {
       if (!on) on = anchor_in(ka, kb, a);
     } else if (a.kind == 4) {
       on = (i / a.block_tiles) == (j / a.block_tiles);
+    } else if (a.kind == 5) {
+      on = i < a.query_tiles;
     } else if (a.kind == 1) {
       const uint64_t z = splitmix64_at(a.seed, (uint64_t)c + 1);
       on = ((uint32_t)(z >> 40) < a.thresh24) || (a.force_diagonal && i == j);

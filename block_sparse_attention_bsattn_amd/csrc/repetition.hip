@@ -1,0 +1,336 @@
+// Spatial repetition (CalibAtt page, "A. Fase di Calibrazione" step 3 and
+// "B. Fase di Inferenza"): in a repetitive head the spatial rows of a frame
+// attend alike, so attention is computed for the anchor rows only and
+// copied to the rows between them.
+//
+// Tokens are frame-major, n = f*P + y*gw + x (P = gh*gw); the anchor of row
+// y is a(y) = s*floor(y/s) for the stride s.
+//
+// row_cosine_kernel: one workgroup per spatial row (f, y), one wave per 32
+// columns x.  Lane (x, half) holds two queries, q1 = (f, y, x) and its
+// anchor q2 = (f, a(y), x), and 64 keys of each 128-key tile, as in the
+// forward's S^T = K Q^T mapping; each K operand read from LDS feeds the
+// MFMAs of both queries, 64 keys at a time.  Sweep 1 gives each query's
+// normaliser (online max and sum, per-step partial sums); sweep 2 recomputes
+// both score rows and accumulates, per column, sum_k p1 p2, sum_k p1^2 and
+// sum_k p2^2.
+// The workgroup adds its columns (shuffles, then LDS) and writes
+//   cos(y) = sum_x <p1, p2> / sqrt(sum_x |p1|^2 * sum_x |p2|^2);
+// anchor rows get exactly 1.  No N x N matrix is ever stored.
+//
+// repetitive_heads_kernel: one thread per head adds the non-anchor rows'
+// cosines in float64 in (prompt, frame, row) order and compares the mean
+// with gamma, the same arithmetic the oracle uses, so equal cosines give the
+// same decision.
+//
+// anchor_rows_kernel: an HBM-bound row copy.  Gather packs the anchor rows'
+// tokens (frame by frame, row by row) into the first Na rows of a buffer;
+// broadcast gives every token its anchor row's value from such a buffer.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "bsattn_internal.h"
+
+namespace bsattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int KT = 128;  // keys staged per step
+
+template <bool F32IN>
+__device__ __forceinline__ bf16x8 load8(const void* base, int64_t off) {
+  if constexpr (F32IN) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + off);
+    const f32x4 x = p[0], y = p[1];
+    bf16x8 r;
+    r[0] = (__bf16)x[0]; r[1] = (__bf16)x[1]; r[2] = (__bf16)x[2]; r[3] = (__bf16)x[3];
+    r[4] = (__bf16)y[0]; r[5] = (__bf16)y[1]; r[6] = (__bf16)y[2]; r[7] = (__bf16)y[3];
+    return r;
+  } else {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(base) + off);
+  }
+}
+
+template <int D, bool F32IN>
+__global__ void __launch_bounds__(512)
+row_cosine_kernel(RowCosLaunch a) {
+  constexpr int DC = D / 16;
+  constexpr int KP = D + 8;
+  constexpr int KB = KT / 32;
+  __shared__ __bf16 Ks[KT * KP];
+  __shared__ float red[8][3];
+
+  const int tid = threadIdx.x;
+  const int nthreads = blockDim.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int row = blockIdx.x;  // f * gh + y
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int f = row / a.gh, y = row - f * a.gh;
+  const int ya = a.stride * (y / a.stride);
+  float* const cos_out = a.cos + ((int64_t)b * a.H + h) * a.T * a.gh + row;
+  if (ya == y) {
+    if (tid == 0) *cos_out = 1.0f;
+    return;
+  }
+  const int N = a.N;
+  const int P = a.gh * a.gw;
+  const int64_t head_row = ((int64_t)b * a.H + h) * N;
+  const int x = wave * 32 + l32;
+  const bool col_ok = x < a.gw;
+  const int n1 = f * P + y * a.gw + x;
+  const int n2 = f * P + ya * a.gw + x;
+
+  bf16x8 q1[DC], q2[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    if (col_ok) {
+      q1[c] = load8<F32IN>(a.q, (head_row + n1) * D + c * 16 + half * 8);
+      q2[c] = load8<F32IN>(a.q, (head_row + n2) * D + c * 16 + half * 8);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        q1[c][e] = (__bf16)0.f;
+        q2[c][e] = (__bf16)0.f;
+      }
+    }
+  }
+
+  const int tiles = (N + KT - 1) / KT;
+  auto stage = [&](int j) {
+    __syncthreads();  // the previous tile's operand reads are done
+    for (int c = tid; c < KT * D / 8; c += nthreads) {
+      const int r = c / (D / 8);
+      const int cc = (c % (D / 8)) * 8;
+      const int tok = j * KT + r;
+      bf16x8 kv;
+      if (tok < N) {
+        kv = load8<F32IN>(a.k, (head_row + tok) * D + cc);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kv[e] = (__bf16)0.f;
+      }
+      *reinterpret_cast<bf16x8*>(&Ks[r * KP + cc]) = kv;
+    }
+    __syncthreads();
+  };
+  // S^T of key blocks kb0, kb0 + 1 of the staged tile for both queries (one
+  // K operand read feeds two MFMAs); keys past N -> -inf
+  auto scores2 = [&](f32x16* a1, f32x16* a2, int j, int kb0) {
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
+            &Ks[((kb0 + u) * 32 + l32) * KP + c * 16 + half * 8]);
+        if (c == 0) {
+          const f32x16 zero = {};
+          a1[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, q1[0], zero, 0, 0, 0);
+          a2[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, q2[0], zero, 0, 0, 0);
+        } else {
+          a1[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, q1[c], a1[u], 0, 0, 0);
+          a2[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, q2[c], a2[u], 0, 0, 0);
+        }
+      }
+    const int valid = N - j * KT;
+    if (valid < KT) {
+      const int lim = valid - 4 * half;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int keep = (((kb0 + u) * 32 + 8 * i + e) - lim) >> 31;  // -1: keep
+            const uint32_t sel = (uint32_t)keep;
+            a1[u][4 * i + e] = __uint_as_float((__float_as_uint(a1[u][4 * i + e]) & sel) |
+                                               (0xff800000u & ~sel));
+            a2[u][4 * i + e] = __uint_as_float((__float_as_uint(a2[u][4 * i + e]) & sel) |
+                                               (0xff800000u & ~sel));
+          }
+    }
+  };
+  const float c2 = a.scale_log2;
+  // one online-softmax step over 64 keys (32 per lane, both halves)
+  auto online = [&](const f32x16* s, float& m, float& l) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[u][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+    const float m_new = fmaxf(m, mx);
+    const float alpha = (m_new == m) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    float lt = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float lk = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) lk += __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][e], c2, -m));
+      lt += lk;
+    }
+    l = l * alpha + lt;
+  };
+
+  // ---- sweep 1: each query's normaliser
+  f32x16 a1[2], a2[2];
+  float m1 = -INFINITY, l1 = 0.f, m2 = -INFINITY, l2 = 0.f;
+  for (int j = 0; j < tiles; ++j) {
+    stage(j);
+#pragma unroll
+    for (int kb0 = 0; kb0 < KB; kb0 += 2) {
+      scores2(a1, a2, j, kb0);
+      online(a1, m1, l1);
+      online(a2, m2, l2);
+    }
+  }
+  l1 += __shfl_xor(l1, 32);
+  l2 += __shfl_xor(l2, 32);
+  const float L1 = m1 + log2f(l1), L2 = m2 + log2f(l2);
+
+  // ---- sweep 2: the three inner products of the probability rows
+  float d12 = 0.f, d11 = 0.f, d22 = 0.f;
+  for (int j = 0; j < tiles; ++j) {
+    stage(j);
+    float t12 = 0.f, t11 = 0.f, t22 = 0.f;
+#pragma unroll
+    for (int kb0 = 0; kb0 < KB; kb0 += 2) {
+      scores2(a1, a2, j, kb0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(a1[u][e], c2, -L1));
+          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(a2[u][e], c2, -L2));
+          t12 = __builtin_fmaf(p1, p2, t12);
+          t11 = __builtin_fmaf(p1, p1, t11);
+          t22 = __builtin_fmaf(p2, p2, t22);
+        }
+    }
+    d12 += t12;
+    d11 += t11;
+    d22 += t22;
+  }
+  // both halves of a column, then the wave's 32 columns, then the waves
+  d12 += __shfl_xor(d12, 32);
+  d11 += __shfl_xor(d11, 32);
+  d22 += __shfl_xor(d22, 32);
+  if (!col_ok) d12 = d11 = d22 = 0.f;
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) {
+    d12 += __shfl_xor(d12, off);
+    d11 += __shfl_xor(d11, off);
+    d22 += __shfl_xor(d22, off);
+  }
+  if (lane == 0) {
+    red[wave][0] = d12;
+    red[wave][1] = d11;
+    red[wave][2] = d22;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float t12 = 0.f, t11 = 0.f, t22 = 0.f;
+    for (int w = 0; w < nthreads / 64; ++w) {
+      t12 += red[w][0];
+      t11 += red[w][1];
+      t22 += red[w][2];
+    }
+    *cos_out = t12 / sqrtf(t11 * t22);
+  }
+}
+
+__global__ void repetitive_heads_kernel(int32_t B, int32_t H, int32_t T, int32_t gh,
+                                        int32_t stride, const float* __restrict__ cos,
+                                        double gamma, uint8_t* __restrict__ flags) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  double total = 0.0;
+  int64_t n = 0;
+  for (int b = 0; b < B; ++b)
+    for (int f = 0; f < T; ++f)
+      for (int y = 0; y < gh; ++y) {
+        if (stride * (y / stride) == y) continue;
+        total += (double)cos[(((int64_t)b * H + h) * T + f) * gh + y];
+        ++n;
+      }
+  flags[h] = (n == 0 || total / (double)n >= gamma) ? 1 : 0;
+}
+
+__global__ void __launch_bounds__(256)
+anchor_rows_kernel(int64_t BH, int32_t N, int32_t cpr, int32_t gh, int32_t gw, int32_t stride,
+                   int32_t na, int broadcast, const i32x4* __restrict__ src,
+                   i32x4* __restrict__ dst) {
+  const int P = gh * gw;
+  const int T = N / P;
+  const int per_frame_a = na * gw;
+  const int rows = broadcast ? N : T * per_frame_a;  // destination rows per head
+  const int64_t total = BH * rows * cpr;
+  const int64_t stride_g = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += stride_g) {
+    const int64_t r = idx / cpr;
+    const int c = (int)(idx - r * cpr);
+    const int64_t bh = r / rows;
+    const int dn = (int)(r - bh * rows);
+    int sn;
+    if (!broadcast) {  // dst row dn = compact index: (frame, anchor number, x)
+      const int f = dn / per_frame_a, rem = dn - f * per_frame_a;
+      const int ai = rem / gw, x = rem - ai * gw;
+      sn = f * P + ai * stride * gw + x;
+    } else {           // dst row dn = token (f, y, x) <- compact (f, y / s, x)
+      const int f = dn / P, rem = dn - f * P;
+      const int y = rem / gw, x = rem - y * gw;
+      sn = f * per_frame_a + (y / stride) * gw + x;
+    }
+    dst[(bh * N + dn) * cpr + c] = src[(bh * N + sn) * cpr + c];
+  }
+}
+
+template <int D, bool F32IN>
+int launch_cos(const RowCosLaunch& a, hipStream_t s) {
+  const int waves = (a.gw + 31) / 32;
+  dim3 grid(a.T * a.gh, a.H, a.B);
+  hipLaunchKernelGGL((row_cosine_kernel<D, F32IN>), grid, dim3(64 * waves), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_row_cosines(const RowCosLaunch& a, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (a.d == 64) return a.dtype == 1 ? launch_cos<64, true>(a, s) : launch_cos<64, false>(a, s);
+  return a.dtype == 1 ? launch_cos<128, true>(a, s) : launch_cos<128, false>(a, s);
+}
+
+int launch_repetitive_heads(int32_t B, int32_t H, int32_t T, int32_t gh, int32_t stride,
+                            const float* cos, double gamma, uint8_t* flags, void* stream) {
+  hipLaunchKernelGGL(repetitive_heads_kernel, dim3((H + 63) / 64), dim3(64), 0,
+                     (hipStream_t)stream, B, H, T, gh, stride, cos, gamma, flags);
+  return hipGetLastError();
+}
+
+int launch_anchor_rows(int64_t BH, int32_t N, int32_t row_bytes, int32_t gh, int32_t gw,
+                       int32_t stride, int broadcast, const void* src, void* dst, void* stream) {
+  const int32_t cpr = row_bytes / 16;
+  const int32_t na = (gh + stride - 1) / stride;
+  const int32_t T = N / (gh * gw);
+  const int64_t rows = broadcast ? (int64_t)N : (int64_t)T * na * gw;
+  const int64_t total = BH * rows * cpr;
+  if (total == 0) return hipSuccess;
+  int64_t grid = (total + 255) / 256;
+  if (grid > 1 << 20) grid = 1 << 20;
+  hipLaunchKernelGGL(anchor_rows_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
+                     BH, N, cpr, gh, gw, stride, na, broadcast,
+                     reinterpret_cast<const i32x4*>(src), reinterpret_cast<i32x4*>(dst));
+  return hipGetLastError();
+}
+
+}  // namespace bsattn

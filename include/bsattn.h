@@ -52,7 +52,8 @@ typedef enum {
   BSATTN_MASK_STATIC_RANDOM = 1, /* seeded stand-in for a calibrated static mask */
   BSATTN_MASK_DENSE = 2,         /* all tiles active (full attention) */
   BSATTN_MASK_WINDOW_ANCHOR_EXPANDED = 3, /* LVSA window grown to a frame budget + anchors */
-  BSATTN_MASK_BLOCK_DIAGONAL = 4          /* SQuad passes: square blocks of block_tiles tiles */
+  BSATTN_MASK_BLOCK_DIAGONAL = 4,         /* SQuad passes: square blocks of block_tiles tiles */
+  BSATTN_MASK_DENSE_ROWS = 5              /* query tiles < query_tiles dense, the rest empty */
 } bsattn_mask_kind;
 
 /* Token geometry of the video latent.  N = frames*grid_h*grid_w; the number
@@ -92,7 +93,11 @@ typedef struct {
  *   is softmax attention inside disjoint groups of tokens): cell (i, j) is
  *   active when i / block_tiles == j / block_tiles (integer division), so
  *   runs of block_tiles * tile consecutive tokens attend only among
- *   themselves.  The frame layout is irrelevant to this mode. */
+ *   themselves.  The frame layout is irrelevant to this mode.
+ * DENSE_ROWS (CalibAtt page, "B. Fase di Inferenza": a repetitive head
+ *   computes its anchor rows only): query tiles i < query_tiles read every
+ *   key tile, the others none, for anchor rows packed at the front of Q
+ *   (bsattn_anchor_rows). */
 typedef struct {
   int32_t kind;           /* bsattn_mask_kind */
   int32_t window;         /* w >= 0, in frames */
@@ -104,6 +109,7 @@ typedef struct {
   int32_t mask_heads;     /* Hm >= 1: number of mask slices (1 = shared by all heads) */
   int32_t budget;         /* WINDOW_ANCHOR_EXPANDED: C >= 0 frames per query frame */
   int32_t block_tiles;    /* BLOCK_DIAGONAL: b >= 1 tiles per diagonal block */
+  int32_t query_tiles;    /* DENSE_ROWS: >= 0 query tiles with every key tile */
 } bsattn_mask_params;
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
@@ -124,8 +130,8 @@ BSATTN_API int32_t bsattn_num_tiles(int64_t tokens, int32_t tile);
  *         every byte is written (0 or 1).
  * Errors: INVALID_ARG on null pointers, non-positive sizes, window < 0,
  * num_anchors outside [0, T], budget < 0 (expanded mode), block_tiles < 1
- * (block-diagonal mode), thresh24 > 2^24, mask_heads < 1, an unknown kind,
- * or Hm*Tq*Tk >= 2^31. */
+ * (block-diagonal mode), query_tiles < 0 (dense-rows mode), thresh24 > 2^24,
+ * mask_heads < 1, an unknown kind, or Hm*Tq*Tk >= 2^31. */
 BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
                                  const bsattn_mask_params* params,
                                  uint8_t* mask, void* stream);
@@ -185,6 +191,56 @@ BSATTN_API int bsattn_fwd(int32_t B, int32_t H, int32_t N, int32_t d,
 BSATTN_API int bsattn_window_reorder(int32_t B, int32_t H, int32_t N, int32_t d, int32_t w,
                                      int32_t dtype, const void* src, void* dst, int32_t inverse,
                                      void* stream);
+
+/* ---- Spatial repetition (CalibAtt page, "A. Fase di Calibrazione" step 3
+ * and "B. Fase di Inferenza").  In a repetitive head the spatial rows of a
+ * frame attend alike: attention is computed for the anchor rows only (every
+ * stride-th latent row, y = 0, s, 2s, ...) and copied to the rows between.
+ * Tokens are frame-major, n = f*P + y*grid_w + x, N = T*grid_h*grid_w; row
+ * y copies from its anchor a(y) = s*floor(y/s). */
+
+/* Row similarity (calibration):
+ *   cos[b, h, f, y] = sum_x <p_(y,x), p_(a,x)> /
+ *                     sqrt(sum_x |p_(y,x)|^2 * sum_x |p_(a,x)|^2),
+ * p_n the full-attention softmax probabilities of query n over all N keys
+ * (scale <= 0 selects 1/sqrt(d)); anchor rows get 1.
+ *   q, k: device [B, H, N, d], dtype BF16 (or F32 rounded to bf16).
+ *   cos:  device float [B, H, T, grid_h], written.
+ * Supported: d in {64, 128}, grid_w <= 256.  B*H*T == 0 is a no-op.
+ * Errors: INVALID_ARG (null pointers, sizes, B or H > 65535, unaligned q or
+ * k, non-finite scale), UNSUPPORTED (d, dtype, grid_w), HIP. */
+BSATTN_API int bsattn_row_cosines(int32_t B, int32_t H, int32_t T, int32_t grid_h,
+                                  int32_t grid_w, int32_t d, int32_t stride, int32_t dtype,
+                                  const void* q, const void* k, float* cos, float scale,
+                                  void* stream);
+
+/* Repetitive heads (calibration): flags[h] = 1 when the mean of cos over the
+ * prompts b, frames f and non-anchor rows y (float64, summed in that
+ * order) is >= gamma, or when no row is a non-anchor row.
+ *   cos:   device float [B, H, T, grid_h] (as written by bsattn_row_cosines).
+ *   flags: device uint8 [H], written.
+ * Errors: INVALID_ARG (negative sizes, grid_h or stride < 1, null pointers,
+ * non-finite gamma), HIP. */
+BSATTN_API int bsattn_repetitive_heads(int32_t B, int32_t H, int32_t T, int32_t grid_h,
+                                       int32_t stride, const float* cos, double gamma,
+                                       uint8_t* flags, void* stream);
+
+/* Anchor-row gather and broadcast (inference), on [B, H, N, d] buffers:
+ *   broadcast == 0: dst rows 0 .. Na-1 (Na = T * ceil(grid_h/stride) *
+ *                   grid_w) receive the anchor rows' tokens, frame by frame,
+ *                   row by row; dst rows >= Na are not written.
+ *   broadcast != 0: every row n of dst receives src row c(n), the packed
+ *                   index of n's anchor-row token (src rows < Na are read).
+ * With the gathered Q, a DENSE_ROWS mask of ceil(Na/tile) query tiles and
+ * bsattn_fwd, then the broadcast of its output, a repetitive head costs
+ * Na/N of full attention.
+ *   src, dst: distinct device buffers, element type `dtype`, 16-byte aligned,
+ *             rows of d elements a multiple of 16 bytes (any such d).
+ * Errors: INVALID_ARG (null or aliased buffers, sizes, row length),
+ * UNSUPPORTED (dtype), HIP. */
+BSATTN_API int bsattn_anchor_rows(int32_t B, int32_t H, int32_t T, int32_t grid_h,
+                                  int32_t grid_w, int32_t d, int32_t stride, int32_t dtype,
+                                  const void* src, void* dst, int32_t broadcast, void* stream);
 
 /* ---- Static-mask calibration (CalibAtt page, "A. Fase di Calibrazione").
  * The calibration runs full attention on a few prompts, measures how much

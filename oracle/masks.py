@@ -53,6 +53,10 @@ Dense mode: every tile active (the full-attention baseline).
 Block-diagonal mode (SQuad page, 1. Operatore di Attenzione SQuad: each of
 its two passes attends inside disjoint groups of consecutive tokens): tile
 pair (i, j) is active when i and j lie in the same run of b tiles.
+
+Dense-rows mode (CalibAtt page, B. Fase di Inferenza: a repetitive head
+computes its anchor rows only, packed at the front): query tiles below
+query_tiles read every key tile, the others none.
 """
 from __future__ import annotations
 
@@ -227,10 +231,10 @@ def tile_mask(kind: int, frames: int, grid_h: int, grid_w: int, tile: int,
               window: int = 0, num_anchors: int = 0, rotation: int = 0,
               seed: int = 0, thresh24: int = 0, force_diagonal: int = 0,
               mask_heads: int = 1, budget: int = 0,
-              block_tiles: int = 1) -> np.ndarray:
+              block_tiles: int = 1, query_tiles: int = 0) -> np.ndarray:
     """uint8 [Hm, Tq, Tk] tile mask for kind 0 (window + anchors),
-    1 (static random), 2 (dense), 3 (expanded window + anchors) or
-    4 (block diagonal)."""
+    1 (static random), 2 (dense), 3 (expanded window + anchors),
+    4 (block diagonal) or 5 (dense rows)."""
     N = frames * grid_h * grid_w
     nt = -(-N // tile)
     if kind == 0:
@@ -244,6 +248,12 @@ def tile_mask(kind: int, frames: int, grid_h: int, grid_w: int, tile: int,
         return tile_mask_dense(mask_heads, nt, nt)
     if kind == 4:
         return tile_mask_block_diagonal(mask_heads, nt, nt, block_tiles)
+    if kind == 5:
+        if query_tiles < 0:
+            raise ValueError("query_tiles must be >= 0")
+        M = np.zeros((mask_heads, nt, nt), dtype=np.uint8)
+        M[:, :query_tiles, :] = 1
+        return M
     if kind == 3:
         M = tile_mask_expanded(frames, grid_h, grid_w, tile, window,
                                num_anchors, rotation, budget)

@@ -21,7 +21,8 @@ def oracle_mask(w, rotation=None):
                             seed=s.seed, thresh24=s.thresh24,
                             force_diagonal=s.force_diagonal,
                             mask_heads=s.mask_heads, budget=s.budget,
-                            block_tiles=s.block_tiles)
+                            block_tiles=s.block_tiles,
+                            query_tiles=s.query_tiles)
 
 
 def gpu_mask_csr(w, device="cuda"):

@@ -111,7 +111,9 @@ def test_build_mask_rejects_bad_arguments():
     assert call(params=bs.MaskParams(3, 1, 5, 0, 0, 0, 0, 1, 5)) == bs.ERR_INVALID_ARG
     # block diagonal: at least one tile per block
     assert call(params=bs.MaskParams(4, 0, 0, 0, 0, 0, 0, 1, 0, 0)) == bs.ERR_INVALID_ARG
-    assert call(params=bs.MaskParams(5, 0, 0, 0, 0, 0, 0, 1, 0, 1)) == bs.ERR_INVALID_ARG
+    assert call(params=bs.MaskParams(6, 0, 0, 0, 0, 0, 0, 1, 0, 1)) == bs.ERR_INVALID_ARG
+    # dense rows: a non-negative tile count
+    assert call(params=bs.MaskParams(5, 0, 0, 0, 0, 0, 0, 1, 0, 1, -1)) == bs.ERR_INVALID_ARG
     assert call(params=bs.MaskParams(0, -1, 1, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
     assert call(params=bs.MaskParams(0, 1, 5, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
     assert call(params=bs.MaskParams(1, 0, 0, 0, 0, (1 << 24) + 1, 0, 1)) == \
@@ -207,3 +209,27 @@ def test_window_reorder_rejects_bad_arguments():
     assert R(1, 1, 12, 128, 4, 3, p, p2, 0, None) == bs.ERR_UNSUPPORTED
     assert R(1, 1, 12, 128, 4, 0, ctypes.c_void_p(65), p2, 0, None) == bs.ERR_INVALID_ARG
     assert R(0, 1, 12, 128, 4, 0, None, None, 0, None) == bs.OK
+
+
+def test_repetition_calls_reject_bad_arguments():
+    L = bs.lib()
+    p, p2 = ctypes.c_void_p(64), ctypes.c_void_p(128)
+    C = L.bsattn_row_cosines
+    assert C(1, 1, 2, 4, 8, 128, 0, 0, p, p, p, 0.0, None) == bs.ERR_INVALID_ARG   # stride 0
+    assert C(1, 1, 2, 4, 300, 128, 2, 0, p, p, p, 0.0, None) == bs.ERR_UNSUPPORTED  # grid_w
+    assert C(1, 1, 2, 4, 8, 96, 2, 0, p, p, p, 0.0, None) == bs.ERR_UNSUPPORTED
+    assert C(1, 1, 2, 4, 8, 128, 2, 0, p, p, None, 0.0, None) == bs.ERR_INVALID_ARG
+    assert C(1, 1, 2, 4, 8, 128, 2, 0, p, p, p, float("nan"), None) == bs.ERR_INVALID_ARG
+    assert C(0, 1, 2, 4, 8, 128, 2, 0, None, None, None, 0.0, None) == bs.OK
+    R = L.bsattn_repetitive_heads
+    assert R(1, 2, 3, 4, 0, p, 0.9, p, None) == bs.ERR_INVALID_ARG
+    assert R(1, 2, 3, 4, 2, None, 0.9, p, None) == bs.ERR_INVALID_ARG
+    assert R(1, 2, 3, 4, 2, p, float("inf"), p, None) == bs.ERR_INVALID_ARG
+    assert R(1, 0, 3, 4, 2, None, 0.9, None, None) == bs.OK
+    A = L.bsattn_anchor_rows
+    assert A(1, 1, 2, 4, 8, 128, 2, 0, p, p, 0, None) == bs.ERR_INVALID_ARG        # aliased
+    assert A(1, 1, 2, 4, 8, 128, 2, 0, None, p2, 0, None) == bs.ERR_INVALID_ARG
+    assert A(1, 1, 2, 0, 8, 128, 2, 0, p, p2, 0, None) == bs.ERR_INVALID_ARG
+    assert A(1, 1, 2, 4, 8, 128, 2, 5, p, p2, 0, None) == bs.ERR_UNSUPPORTED
+    assert A(1, 1, 2, 4, 8, 4, 2, 0, p, p2, 0, None) == bs.ERR_INVALID_ARG        # 8-byte rows
+    assert A(1, 1, 0, 4, 8, 128, 2, 0, None, None, 0, None) == bs.OK

@@ -334,3 +334,12 @@ def test_block_diagonal_by_hand():
     assert (oracle.tile_mask(4, 1, 1, 300, 64, block_tiles=5)[0] == 1).all()
     with pytest.raises(ValueError):
         oracle.tile_mask(4, 1, 1, 300, 64, block_tiles=0)
+
+
+def test_dense_rows_by_hand():
+    got = oracle.tile_mask(5, 1, 1, 300, 64, query_tiles=2)[0]
+    want = np.zeros((5, 5), dtype=np.uint8)
+    want[:2] = 1
+    np.testing.assert_array_equal(got, want)
+    assert (oracle.tile_mask(5, 1, 1, 300, 64, query_tiles=0) == 0).all()
+    assert (oracle.tile_mask(5, 1, 1, 300, 64, query_tiles=9) == 1).all()

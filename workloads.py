@@ -26,6 +26,7 @@ MASK_STATIC_RANDOM = 1
 MASK_DENSE = 2
 MASK_WINDOW_ANCHOR_EXPANDED = 3
 MASK_BLOCK_DIAGONAL = 4
+MASK_DENSE_ROWS = 5
 
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
@@ -51,6 +52,7 @@ class MaskSpec:
     mask_heads: int = 1      # Hm: 1 (shared by all heads) or H
     budget: int = 0          # C, frames per query frame (expanded windows)
     block_tiles: int = 1     # tiles per diagonal block (block-diagonal mode)
+    query_tiles: int = 0     # dense query tiles (dense-rows mode)
 
 
 @dataclass(frozen=True)
