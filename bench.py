@@ -15,8 +15,9 @@ Printed: ONE JSON line with
 plus the forward-only time, the same kernel at density 1.0 and the speedup,
 a density sweep, the path with LVSA expanded windows on the 84-frame
 long-video shape, the static-mask calibration (block energies, selection,
-agreement) with the forward on the calibrated mask, and SQuad's two-pass
-attention against dense attention of the same shape.
+agreement) with the forward on the calibrated mask, SQuad's two-pass
+attention against dense attention of the same shape, and spatial
+repetition (row cosines, head decision, attention on anchor rows).
 """
 from __future__ import annotations
 
@@ -287,6 +288,69 @@ def squad_leg(bs, W, torch, dev, calls: int):
             "speedup_vs_dense": round(dense_ms / total, 2)}
 
 
+def repetition_leg(bs, W, torch, dev, calls: int):
+    """Spatial repetition at the video shape (21 x 30 x 52, 12 heads, six of
+    them with repeating rows): row cosines and the head decision at stride
+    2, gamma 0.9; then attention of all heads computed on anchor rows only
+    against dense attention of the same shape."""
+    w = W.WORKLOADS[2]
+    stride, gamma = 2, 0.9
+    q, k = W.make_qk_row_repetitive(w, rep_heads=6, device=dev)
+    v = torch.randn(q.shape, generator=torch.Generator().manual_seed(9)).to(
+        torch.bfloat16).to(dev)
+    stream = torch.cuda.current_stream()
+    cos = torch.empty((w.B, w.H, w.frames, w.grid_h), dtype=torch.float32, device=dev)
+    flags = torch.empty(w.H, dtype=torch.uint8, device=dev)
+    bs.row_cosines(q, k, w.frames, w.grid_h, w.grid_w, stride, cos)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    bs.row_cosines(q, k, w.frames, w.grid_h, w.grid_w, stride, cos, stream=stream)
+    ev[1].record(stream)
+    bs.repetitive_heads(cos, stride, gamma, flags, stream=stream)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    cos_ms = ev[0].elapsed_time(ev[1])
+    nonanchor = w.grid_h - (-(-w.grid_h // stride))
+    # two sweeps x two queries x (non-anchor rows x grid_w) x N keys x 2d
+    cos_flops = 2 * 2 * w.B * w.H * w.frames * nonanchor * w.grid_w * w.N * 2.0 * w.d
+    bs.repeated_attention(q, k, v, w.frames, w.grid_h, w.grid_w, stride, w.tile)
+    re = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for a, b in re:
+        a.record(stream)
+        bs.repeated_attention(q, k, v, w.frames, w.grid_h, w.grid_w, stride, w.tile,
+                              stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    rep_ms = float(np.median([a.elapsed_time(b) for a, b in re]))
+    dm = bs.make_mask(w.frames, w.grid_h, w.grid_w, w.tile, device=dev, kind=W.MASK_DENSE)
+    drp, dci = bs.make_csr(dm)
+    o = torch.empty_like(q)
+    bs.fwd(q, k, v, o, drp, dci, w.tile)
+    de = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for a, b in de:
+        a.record(stream)
+        bs.fwd(q, k, v, o, drp, dci, w.tile, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = float(np.median([a.elapsed_time(b) for a, b in de]))
+    c = cos.cpu().numpy()
+    na = w.frames * (-(-w.grid_h // stride)) * w.grid_w
+    return {"workload": w.name + "_rows_repeat_in_6_of_12_heads", "stride": stride,
+            "gamma": gamma,
+            "row_cosines_ms": round(cos_ms, 3),
+            "row_cosines_tflops": round(cos_flops / (cos_ms * 1e-3) / 1e12, 1),
+            "heads_ms": round(ev[1].elapsed_time(ev[2]), 4),
+            "flags": flags.cpu().tolist(),
+            "mean_cos_repeating_heads": round(float(c[:, :6, :, 1::2].mean()), 4),
+            "mean_cos_other_heads": round(float(c[:, 6:, :, 1::2].mean()), 4),
+            "anchor_fraction": round(na / w.N, 4),
+            "repeated_attention_ms": round(rep_ms, 4),
+            "dense_ms": round(dense_ms, 4),
+            "speedup_vs_dense": round(dense_ms / rep_ms, 2)}
+
+
 def cpu_baseline(w, q, k, v, mask_np, tiles: int, workers: int):
     """The oracle as it stands, on `tiles` evenly spaced query tiles (every
     row of them, every head) at rotation 0; TFLOP/s credited like the GPU
@@ -344,6 +408,8 @@ def main():
                          "(0 = skip)")
     ap.add_argument("--squad", type=int, default=6,
                     help="timed calls of the SQuad two-pass leg (0 = skip)")
+    ap.add_argument("--repetition", type=int, default=5,
+                    help="timed calls of the spatial-repetition leg (0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB "
                          "(byte-counter calibration under a profiler)")
@@ -463,6 +529,9 @@ def main():
 
     squad = squad_leg(bs, W, torch, dev, args.squad) if args.squad > 0 else None
 
+    repetition = repetition_leg(bs, W, torch, dev, args.repetition) \
+        if args.repetition > 0 else None
+
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -535,6 +604,7 @@ def main():
         "expanded_windows": expanded,
         "calibration": calib,
         "squad": squad,
+        "repetition": repetition,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -165,6 +165,24 @@ def make_qk_frame_local(w: Workload, strength: float = 1.0,
     return (q.to(w.torch_dtype()).to(device), k.to(w.torch_dtype()).to(device))
 
 
+def make_qk_row_repetitive(w: Workload, rep_heads: int, noise: float = 0.1,
+                           seed: Optional[int] = None, device: str = "cpu"):
+    """Q and K where, in heads 0 .. rep_heads-1, every spatial row of a frame
+    repeats one per-frame row of queries plus N(0, noise^2) noise (the rows
+    of a frame then attend alike); the other heads are i.i.d. N(0, 1).  K is
+    i.i.d. N(0, 1).  Rounded to the workload's dtype."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    q = torch.randn((w.B, w.H, w.N, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.H, w.N, w.d), generator=g, dtype=torch.float32)
+    if rep_heads > 0:
+        row = torch.randn((w.B, rep_heads, w.frames, 1, w.grid_w, w.d), generator=g)
+        jit = noise * torch.randn((w.B, rep_heads, w.frames, w.grid_h, w.grid_w, w.d),
+                                  generator=g)
+        q[:, :rep_heads] = (row + jit).reshape(w.B, rep_heads, w.N, w.d)
+    return (q.to(w.torch_dtype()).to(device), k.to(w.torch_dtype()).to(device))
+
+
 def make_energies(rows: int, tk: int, seed: int, zero_frac: float = 0.1,
                   tie_frac: float = 0.1) -> torch.Tensor:
     """Synthetic float32 block energies [rows, tk] >= 0: heavy-tailed values
