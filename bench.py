@@ -37,6 +37,7 @@ METRIC = "block-sparse attn fwd TFLOP/s (active blocks) + ms/call at 32760 token
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (no sparsity)
 HEADLINE = 2                # the 32 760-token video workload
 TRAFFIC_SUMMARY = "fwd_bf16_t128_d128.video_21x30x52_window_anchor.traffic.txt"
+MFMA_SUMMARY = "fwd_bf16_t128_d128.video_21x30x52_window_anchor.mfma.txt"
 
 
 def active_flops(mask_np: np.ndarray, w) -> float:
@@ -551,10 +552,9 @@ def main():
     # HBM bytes per launch from the committed PMC summary, if it was taken on
     # this kernel source
     from block_sparse_attention_bsattn_amd import rocprof_summary
-    traffic = rocprof_summary.read_traffic(
-        os.path.join(ROOT, "profiles", TRAFFIC_SUMMARY),
-        os.path.join(ROOT, "block_sparse_attention_bsattn_amd", "csrc",
-                     "fwd_bf16_t128.hip"))
+    src = os.path.join(ROOT, "block_sparse_attention_bsattn_amd", "csrc", "fwd_bf16_t128.hip")
+    traffic = rocprof_summary.read_traffic(os.path.join(ROOT, "profiles", TRAFFIC_SUMMARY), src)
+    mfma = rocprof_summary.read_mfma(os.path.join(ROOT, "profiles", MFMA_SUMMARY), src)
 
     out = {
         "metric": METRIC,
@@ -583,6 +583,9 @@ def main():
             "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": None if traffic is None else round(traffic["total"]),
             "traffic_unit": "bytes/launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
+            "traffic_gbs": None if traffic is None else
+            round(traffic["total"] / (float(fwd_ms.mean()) * 1e-3) / 1e9, 1),
+            "mfma_busy_rocprof": None if mfma is None else round(mfma["busy"], 4),
             "kernel": "fwd_bf16_t128_d128",
             "fwd_ms_mean": round(float(fwd_ms.mean()), 4),
             "active_tflop_per_launch": round(fwd_flops_mean / 1e12, 4),

@@ -1,9 +1,12 @@
 """Turn rocprofv3 CSV output into the short text summaries kept in profiles/.
 
-Two summaries:
+Three summaries:
 
   stats    per-kernel call count and durations from a ``--kernel-trace
            --stats`` run (the ``*_kernel_stats.csv`` file);
+  mfma     the matrix-core busy fraction and executed bf16 MFMA work of one
+           kernel from one ``--pmc`` run (SQ_VALU_MFMA_BUSY_CYCLES,
+           GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_BF16);
   traffic  HBM bytes per launch of one kernel from two ``--pmc`` runs, one
            with FETCH_SIZE and one with WRITE_SIZE (KiB per dispatch).  Both
            counters are scaled by what they read for a plain device copy of
@@ -136,6 +139,67 @@ def read_traffic(path: str, source: str):
             "total": float(kv["traffic_bytes_per_launch"])}
 
 
+def mfma_summary(pmc_dir, kernel, simds, xcds, source, command):
+    """Matrix-core busy fraction per launch of one kernel: the summed
+    SQ_VALU_MFMA_BUSY_CYCLES of all SIMDs over (kernel cycles x SIMDs), the
+    MfmaUtil expression rocprofv3 lists.  The CSV's GRBM_GUI_ACTIVE is the
+    sum over the XCDs' instances (about 8 x the kernel's cycles), so the
+    kernel's cycles are that sum / xcds.  Also the bf16 MFMA work executed
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOPs)."""
+    busy = dict(_counter_by_dispatch(pmc_dir, "SQ_VALU_MFMA_BUSY_CYCLES"))
+    gui = dict(_counter_by_dispatch(pmc_dir, "GRBM_GUI_ACTIVE"))
+    mops = dict(_counter_by_dispatch(pmc_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
+    utils, flops = [], []
+    for name, dv in busy.items():
+        if kernel not in name:
+            continue
+        g = {d: v for d, v in gui.get(name, [])}
+        m = {d: v for d, v in mops.get(name, [])}
+        for d, b in dv:
+            if g.get(d):
+                utils.append(b / (g[d] / xcds * simds))
+            if d in m:
+                flops.append(m[d] * 512.0)
+    if not utils:
+        raise KeyError(f"no dispatch of a kernel matching {kernel!r}")
+    lines = [
+        "# Matrix-core busy fraction from rocprofv3 PMC counters", "",
+        f"kernel: {kernel}",
+        f"source: {os.path.relpath(source)}",
+        f"source_sha256: {source_sha256(source)}",
+        f"command: {command}",
+        "counters: SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs), GRBM_GUI_ACTIVE, "
+        "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+        f"simds: {simds}",
+        f"xcds (GRBM_GUI_ACTIVE instances summed in the CSV): {xcds}",
+        f"launches: {len(utils)}",
+        f"mfma_busy_fraction_mean: {statistics.mean(utils):.4f}",
+        f"mfma_busy_fraction_min: {min(utils):.4f}",
+        f"mfma_busy_fraction_max: {max(utils):.4f}",
+        f"bf16_mfma_flops_per_launch: {statistics.mean(flops):.4e}" if flops else
+        "bf16_mfma_flops_per_launch: n/a",
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def read_mfma(path: str, source: str):
+    """The MFMA summary as a dict, or None when missing or taken on another
+    version of the kernel source."""
+    if not os.path.exists(path) or not os.path.exists(source):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_sha256(source):
+        return None
+    out = {"busy": float(kv["mfma_busy_fraction_mean"])}
+    f = kv.get("bf16_mfma_flops_per_launch", "n/a")
+    out["flops"] = None if f == "n/a" else float(f)
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -152,9 +216,19 @@ def main(argv=None):
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
     t.add_argument("--out", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--pmc-dir", required=True)
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--simds", type=int, default=1024)
+    m.add_argument("--xcds", type=int, default=8)
+    m.add_argument("--source", required=True)
+    m.add_argument("--command", required=True)
+    m.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         text = stats_summary(a.csv_dir, a.command)
+    elif a.cmd == "mfma":
+        text = mfma_summary(a.pmc_dir, a.kernel, a.simds, a.xcds, a.source, a.command)
     else:
         text = traffic_summary(a.fetch_dir, a.write_dir, a.kernel, a.copy_mib,
                                a.source, a.command_fetch, a.command_write)
