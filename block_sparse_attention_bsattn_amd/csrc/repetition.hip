@@ -6,8 +6,10 @@
 // Tokens are frame-major, n = f*P + y*gw + x (P = gh*gw); the anchor of row
 // y is a(y) = s*floor(y/s) for the stride s.
 //
-// row_cosine_kernel: one workgroup per spatial row (f, y), one wave per 32
-// columns x.  Lane (x, half) holds two queries, q1 = (f, y, x) and its
+// row_cosine_kernel: one wave per 32 columns x of a non-anchor spatial row
+// (f, y), as many consecutive non-anchor rows per workgroup as 8 waves
+// hold, so each staged K tile serves several rows (anchor rows get 1 from a
+// small kernel of their own).  Lane (x, half) holds two queries, q1 = (f, y, x) and its
 // anchor q2 = (f, a(y), x), and 64 keys of each 128-key tile, as in the
 // forward's S^T = K Q^T mapping; each K operand read from LDS feeds the
 // MFMAs of both queries, 64 keys at a time.  Sweep 1 gives each query's
@@ -68,23 +70,35 @@ row_cosine_kernel(RowCosLaunch a) {
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int row = blockIdx.x;  // f * gh + y
+  // rows_per_wg consecutive non-anchor rows share each staged K tile; wpr
+  // waves per row.  Non-anchor row j of the head: frame j / nna, and the
+  // (j % nna)-th row of the frame that is not a multiple of the stride.
+  const int wpr = (a.gw + 31) / 32;
+  const int rows_per_wg = (nthreads / 64) / wpr;
+  const int nna = a.gh - (a.gh + a.stride - 1) / a.stride;  // non-anchor rows per frame
+  const int rows_total = a.T * nna;
+  const int rsub = wave / wpr;
+  auto row_of = [&](int j, int& fr, int& yr) {
+    fr = j / nna;
+    const int jj = j - fr * nna;
+    yr = (jj / (a.stride - 1)) * a.stride + 1 + jj % (a.stride - 1);
+  };
+  const int jrow = blockIdx.x * rows_per_wg + rsub;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int f = row / a.gh, y = row - f * a.gh;
+  int f = 0, y = 1;
+  if (jrow < rows_total) row_of(jrow, f, y);
   const int ya = a.stride * (y / a.stride);
-  float* const cos_out = a.cos + ((int64_t)b * a.H + h) * a.T * a.gh + row;
-  if (ya == y) {
-    if (tid == 0) *cos_out = 1.0f;
-    return;
-  }
+  // wave-uniform: this wave has a row
+  const bool active = jrow < rows_total;
+  float* const cos_base = a.cos + ((int64_t)b * a.H + h) * a.T * a.gh;
   const int N = a.N;
   const int P = a.gh * a.gw;
   const int64_t head_row = ((int64_t)b * a.H + h) * N;
-  const int x = wave * 32 + l32;
-  const bool col_ok = x < a.gw;
+  const int x = (wave - rsub * wpr) * 32 + l32;
+  const bool col_ok = active && x < a.gw;
   const int n1 = f * P + y * a.gw + x;
   const int n2 = f * P + ya * a.gw + x;
 
@@ -185,6 +199,7 @@ row_cosine_kernel(RowCosLaunch a) {
   float m1 = -INFINITY, l1 = 0.f, m2 = -INFINITY, l2 = 0.f;
   for (int j = 0; j < tiles; ++j) {
     stage(j);
+    if (!active) continue;
 #pragma unroll
     for (int kb0 = 0; kb0 < KB; kb0 += 2) {
       scores2(a1, a2, j, kb0);
@@ -200,6 +215,7 @@ row_cosine_kernel(RowCosLaunch a) {
   float d12 = 0.f, d11 = 0.f, d22 = 0.f;
   for (int j = 0; j < tiles; ++j) {
     stage(j);
+    if (!active) continue;
     float t12 = 0.f, t11 = 0.f, t22 = 0.f;
 #pragma unroll
     for (int kb0 = 0; kb0 < KB; kb0 += 2) {
@@ -236,14 +252,29 @@ row_cosine_kernel(RowCosLaunch a) {
     red[wave][2] = d22;
   }
   __syncthreads();
-  if (tid == 0) {
-    float t12 = 0.f, t11 = 0.f, t22 = 0.f;
-    for (int w = 0; w < nthreads / 64; ++w) {
-      t12 += red[w][0];
-      t11 += red[w][1];
-      t22 += red[w][2];
+  // one thread per row of this workgroup
+  if (tid < rows_per_wg) {
+    const int j = blockIdx.x * rows_per_wg + tid;
+    if (j < rows_total) {
+      int fr, yr;
+      row_of(j, fr, yr);
+      float t12 = 0.f, t11 = 0.f, t22 = 0.f;
+      for (int w = tid * wpr; w < (tid + 1) * wpr; ++w) {
+        t12 += red[w][0];
+        t11 += red[w][1];
+        t22 += red[w][2];
+      }
+      cos_base[fr * a.gh + yr] = t12 / sqrtf(t11 * t22);
     }
-    *cos_out = t12 / sqrtf(t11 * t22);
+  }
+}
+
+// anchor rows: cosine 1 by definition
+__global__ void anchor_cos_kernel(int64_t rows, int32_t gh, int32_t stride, float* cos) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int y = (int)(i % gh);
+    if (stride * (y / stride) == y) cos[i] = 1.0f;
   }
 }
 
@@ -296,9 +327,18 @@ anchor_rows_kernel(int64_t BH, int32_t N, int32_t cpr, int32_t gh, int32_t gw, i
 
 template <int D, bool F32IN>
 int launch_cos(const RowCosLaunch& a, hipStream_t s) {
-  const int waves = (a.gw + 31) / 32;
-  dim3 grid(a.T * a.gh, a.H, a.B);
-  hipLaunchKernelGGL((row_cosine_kernel<D, F32IN>), grid, dim3(64 * waves), 0, s, a);
+  const int64_t all_rows = (int64_t)a.B * a.H * a.T * a.gh;
+  int64_t cgrid = (all_rows + 255) / 256;
+  if (cgrid > 1 << 16) cgrid = 1 << 16;
+  hipLaunchKernelGGL(anchor_cos_kernel, dim3((unsigned)cgrid), dim3(256), 0, s, all_rows, a.gh,
+                     a.stride, a.cos);
+  const int nna = a.gh - (a.gh + a.stride - 1) / a.stride;
+  if (nna == 0) return hipGetLastError();
+  const int wpr = (a.gw + 31) / 32;      // waves per row, <= 8
+  const int rows_per_wg = 8 / wpr;       // up to 8 waves per workgroup
+  const int rows = a.T * nna;
+  dim3 grid((rows + rows_per_wg - 1) / rows_per_wg, a.H, a.B);
+  hipLaunchKernelGGL((row_cosine_kernel<D, F32IN>), grid, dim3(64 * wpr * rows_per_wg), 0, s, a);
   return hipGetLastError();
 }
 
