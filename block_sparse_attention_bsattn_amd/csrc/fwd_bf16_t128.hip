@@ -76,6 +76,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
@@ -92,6 +93,7 @@ constexpr int TILE_BYTES = BT * ROW_BYTES;  // 32 KB
 constexpr float TAU = 8.0f;                 // lazy-rescale threshold (log2 units)
 constexpr int NXCD = 8;
 constexpr int PF = 4;                       // MFMA operand read-ahead (steps)
+constexpr int LPT_CHUNK = 128;              // workgroups ordered longest-first together
 
 // Lambdas are forced inline: an outlined lambda would reach its captures
 // through memory and turn every buffer resource into a waterfall loop.
@@ -163,7 +165,6 @@ __device__ __forceinline__ void fetch_load_i(int i, __amdgpu_buffer_rsrc_t rs, l
 // one statement that the wave skips as a whole when `skip` is nonzero: no
 // branch is visible to the compiler, so the statement can be pinned between
 // blocks of other work.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void dma_burst4(const i32x4& rs, uint32_t m0, const uint32_t* voff,
                                            uint32_t soff, uint32_t skip) {
   asm volatile(
@@ -230,10 +231,54 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // ---- XCD-aware remap of the 1-D grid onto (batch*head, query-tile pair)
   const uint32_t G = gridDim.x, hw = blockIdx.x;
   const uint32_t q8 = G / NXCD, r8 = G % NXCD, xcd = hw % NXCD, slot = hw / NXCD;
-  const uint32_t logical =
-      (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + slot;
+  const uint32_t lo = xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8;
+  const uint32_t cnt = q8 + (xcd < r8 ? 1u : 0u);
   // one workgroup per query-tile pair (qt0, qt0 + 1)
   const uint32_t pairs = (uint32_t)(a.tiles + 1) >> 1;
+  // Longest first: the XCD's range is cut into chunks of LPT_CHUNK
+  // workgroups, and inside a chunk the workgroup dispatched k-th takes the
+  // pair with the k-th longest pair of lists (ties by position).  Pair
+  // lengths vary with how a tile pair meets the frames; walked in position
+  // order the last long pairs would run alone at the end of the launch.
+  // Each workgroup ranks its chunk itself (row_ptr differences, one item
+  // per thread, ranks by broadcast LDS reads); a malformed row_ptr only
+  // changes the order, which stays a permutation.
+  uint32_t logical;
+  {
+    int* const keys = reinterpret_cast<int*>(kslots);
+    int* const pick = keys + LPT_CHUNK;
+    const uint32_t c0 = (slot / LPT_CHUNK) * LPT_CHUNK;
+    const int cn = (int)min(cnt - c0, (uint32_t)LPT_CHUNK);
+    if (tid < LPT_CHUNK) {
+      int key = -1;  // past the chunk: never counted below
+      if (tid < cn) {
+        const uint32_t item = lo + c0 + (uint32_t)tid;
+        const int bhi = (int)(item / pairs);
+        const int qt = 2 * (int)(item % pairs);
+        const int hr = (a.mask_heads == 1 ? 0 : bhi % a.H) * a.tiles;
+        const int64_t len = (int64_t)a.row_ptr[hr + min(qt + 2, a.tiles)] - a.row_ptr[hr + qt];
+        key = (int)min(max(len, (int64_t)0), (int64_t)2 * a.tiles);
+      }
+      keys[tid] = key;
+    }
+    __syncthreads();
+    if (tid < cn) {
+      const int mine = keys[tid];
+      int rank = 0;
+      const i32x4* const k4 = reinterpret_cast<const i32x4*>(keys);
+#pragma unroll
+      for (int u4 = 0; u4 < LPT_CHUNK / 4; ++u4) {
+        const i32x4 kv = k4[u4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          rank += (kv[e] > mine || (kv[e] == mine && 4 * u4 + e < tid)) ? 1 : 0;
+      }
+      if (rank == (int)(slot - c0)) *pick = (int)(lo + c0) + tid;
+    }
+    __syncthreads();
+    logical = (uint32_t)__builtin_amdgcn_readfirstlane(*pick);
+    __syncthreads();  // the LDS is refilled by tile fetches below
+  }
   const int bh = (int)(logical / pairs);
   const int qt0 = 2 * (int)(logical % pairs);
   const int h = bh % a.H;
