@@ -93,7 +93,7 @@ constexpr int TILE_BYTES = BT * ROW_BYTES;  // 32 KB
 constexpr float TAU = 8.0f;                 // lazy-rescale threshold (log2 units)
 constexpr int NXCD = 8;
 constexpr int PF = 4;                       // MFMA operand read-ahead (steps)
-constexpr int LPT_CHUNK = 128;              // workgroups ordered longest-first together
+constexpr int LPT_CHUNK = 32;               // workgroups ordered longest-first together
 
 // Lambdas are forced inline: an outlined lambda would reach its captures
 // through memory and turn every buffer resource into a waterfall loop.
@@ -240,6 +240,9 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // pair with the k-th longest pair of lists (ties by position).  Pair
   // lengths vary with how a tile pair meets the frames; walked in position
   // order the last long pairs would run alone at the end of the launch.
+  // A chunk of about one workgroup per CU of the XCD keeps the pairs in
+  // flight together close in position, so they share key tiles in the L2
+  // (larger chunks spread them: more L2 misses, measured slower).
   // Each workgroup ranks its chunk itself (row_ptr differences, one item
   // per thread, ranks by broadcast LDS reads); a malformed row_ptr only
   // changes the order, which stays a permutation.
