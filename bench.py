@@ -380,8 +380,18 @@ def cpu_baseline(w, q, k, v, mask_np, tiles: int, workers: int):
         oracle.block_sparse_attention_rows(qc, kc, vc, mask_np, w.tile, rows,
                                            workers=workers)
     dt = time.perf_counter() - t0
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model,
+            "blas_threads_per_worker": 1 if threadpool_limits is not None else None,
             "sample": f"{len(rows)} query rows ({tiles} of {w.num_tiles} query "
                       f"tiles) x {w.B * w.H} heads at rotation 0, float64 NumPy, "
                       f"{dt:.1f} s"}
