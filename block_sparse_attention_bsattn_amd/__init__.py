@@ -13,7 +13,7 @@ The calls mirror include/bsattn.h:
     window_reorder(src, dst, w, inverse)                -> bsattn_window_reorder
     row_cosines(q, k, ..., cos)                         -> bsattn_row_cosines
     repetitive_heads(cos, stride, gamma, flags)         -> bsattn_repetitive_heads
-    anchor_rows(src, dst, ..., broadcast)               -> bsattn_anchor_rows
+    anchor_rows(src, dst, ..., broadcast, block_rows)   -> bsattn_anchor_rows
 
 plus small helpers that allocate the outputs with torch (make_mask,
 make_csr, attention, calibrate, squad, repeated_attention).  There is no fallback: if libbsattn.so is missing or a
@@ -42,6 +42,7 @@ MASK_DENSE = 2
 MASK_WINDOW_ANCHOR_EXPANDED = 3
 MASK_BLOCK_DIAGONAL = 4
 MASK_DENSE_ROWS = 5
+MASK_DENSE_ROWS_SPREAD = 6
 
 # Every symbol include/bsattn.h exports.
 EXPORTS = ("bsattn_version", "bsattn_status_string", "bsattn_last_error",
@@ -111,7 +112,7 @@ def lib() -> ctypes.CDLL:
     L.bsattn_repetitive_heads.restype = ctypes.c_int
     L.bsattn_repetitive_heads.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.c_double, u8p, vp]
     L.bsattn_anchor_rows.restype = ctypes.c_int
-    L.bsattn_anchor_rows.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, i32, vp]
+    L.bsattn_anchor_rows.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, i32, i32, vp]
     L.bsattn_block_energy.restype = ctypes.c_int
     L.bsattn_block_energy.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp,
                                       ctypes.c_float, vp]
@@ -287,9 +288,11 @@ def repetitive_heads(cos, stride, gamma, flags, stream=None):
     return flags
 
 
-def anchor_rows(src, dst, frames, grid_h, grid_w, stride, broadcast=False, stream=None):
+def anchor_rows(src, dst, frames, grid_h, grid_w, stride, broadcast=False, block_rows=0,
+                stream=None):
     """bsattn_anchor_rows between [B, H, N, d] buffers (gather, or broadcast
-    with broadcast=True)."""
+    with broadcast=True); block_rows > 0 spreads the packed anchor rows in
+    blocks of that many rows."""
     if src.dim() != 4 or tuple(dst.shape) != tuple(src.shape) or dst.dtype != src.dtype:
         raise ValueError("src and dst must share shape [B, H, N, d] and dtype")
     B, H, N, d = src.shape
@@ -297,7 +300,7 @@ def anchor_rows(src, dst, frames, grid_h, grid_w, stride, broadcast=False, strea
         raise ValueError("N must equal frames * grid_h * grid_w")
     st = lib().bsattn_anchor_rows(B, H, frames, grid_h, grid_w, d, stride, _dtype_code(src),
                                   _ptr(src, "src", src.dtype), _ptr(dst, "dst", src.dtype),
-                                  int(bool(broadcast)), _stream(stream))
+                                  int(bool(broadcast)), int(block_rows), _stream(stream))
     _check(st, "bsattn_anchor_rows")
     return dst
 
@@ -446,21 +449,25 @@ def squad(q, k, v, w: int, tile: int, scale: float = 0.0, stream=None):
 def repeated_attention(q, k, v, frames, grid_h, grid_w, stride, tile, scale=0.0,
                        stream=None):
     """Attention of a repetitive head through the library's calls: the
-    anchor rows' queries are packed to the front, full attention runs for
-    those query tiles only (DENSE_ROWS mask), and every row takes its
-    anchor row's output."""
+    anchor rows' queries are gathered into blocks of two query tiles spread
+    evenly over the sequence, full attention runs for those query tiles only
+    (DENSE_ROWS_SPREAD mask), and every row takes its anchor row's output."""
     import torch
     B, H, N, d = q.shape
     na = frames * (-(-grid_h // stride)) * grid_w
+    ta = -(-na // tile)
+    bt = 2
+    block_rows = bt * tile
     qa = torch.zeros_like(q)
-    anchor_rows(q, qa, frames, grid_h, grid_w, stride, stream=stream)
+    anchor_rows(q, qa, frames, grid_h, grid_w, stride, block_rows=block_rows, stream=stream)
     mask = make_mask(frames, grid_h, grid_w, tile, device=q.device, stream=stream,
-                     kind=MASK_DENSE_ROWS, query_tiles=-(-na // tile))
+                     kind=MASK_DENSE_ROWS_SPREAD, query_tiles=ta, block_tiles=bt)
     rp, ci = make_csr(mask, stream=stream)
     oa = torch.empty_like(q)
     fwd(qa, k, v, oa, rp, ci, tile, scale=scale, stream=stream)
     out = torch.empty_like(q)
-    anchor_rows(oa, out, frames, grid_h, grid_w, stride, broadcast=True, stream=stream)
+    anchor_rows(oa, out, frames, grid_h, grid_w, stride, broadcast=True, block_rows=block_rows,
+                stream=stream)
     return out
 
 

@@ -77,7 +77,7 @@ BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
   const int64_t tokens = per_frame * L.frames;
   if (tokens > INT32_MAX)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: more than 2^31-1 tokens");
-  if (M.kind < BSATTN_MASK_WINDOW_ANCHOR || M.kind > BSATTN_MASK_DENSE_ROWS)
+  if (M.kind < BSATTN_MASK_WINDOW_ANCHOR || M.kind > BSATTN_MASK_DENSE_ROWS_SPREAD)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: unknown mask kind %d", M.kind);
   if (M.mask_heads < 1)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: mask_heads must be >= 1");
@@ -94,11 +94,23 @@ BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: budget must be >= 0");
   if (M.kind == BSATTN_MASK_BLOCK_DIAGONAL && M.block_tiles < 1)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: block_tiles must be >= 1");
-  if (M.kind == BSATTN_MASK_DENSE_ROWS && M.query_tiles < 0)
+  const bool dense_rows =
+      M.kind == BSATTN_MASK_DENSE_ROWS || M.kind == BSATTN_MASK_DENSE_ROWS_SPREAD;
+  if (dense_rows && M.query_tiles < 0)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: query_tiles must be >= 0");
   if (M.kind == BSATTN_MASK_STATIC_RANDOM && M.thresh24 > (1u << 24))
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: thresh24 exceeds 2^24");
   const int32_t tiles = bsattn_num_tiles(tokens, L.tile);
+  if (M.kind == BSATTN_MASK_DENSE_ROWS_SPREAD) {
+    if (M.block_tiles < 1)
+      return fail(BSATTN_ERR_INVALID_ARG, "build_mask: block_tiles must be >= 1");
+    const int64_t rg = ((int64_t)M.query_tiles + M.block_tiles - 1) / M.block_tiles;
+    const int64_t pg = ((int64_t)tiles + M.block_tiles - 1) / M.block_tiles;
+    if (rg > pg)
+      return fail(BSATTN_ERR_INVALID_ARG,
+                  "build_mask: %d query tiles in blocks of %d do not fit %lld block slots",
+                  M.query_tiles, M.block_tiles, (long long)pg);
+  }
   const int64_t cells = (int64_t)M.mask_heads * tiles * tiles;
   if (cells >= kMaxCells)
     return fail(BSATTN_ERR_INVALID_ARG, "build_mask: mask has >= 2^31 cells");
@@ -118,8 +130,10 @@ BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
                  : 0;
   a.num_anchors = M.num_anchors;
   a.rotation = ((M.rotation % L.frames) + L.frames) % L.frames;
-  a.block_tiles = M.kind == BSATTN_MASK_BLOCK_DIAGONAL ? M.block_tiles : 1;
-  a.query_tiles = M.kind == BSATTN_MASK_DENSE_ROWS ? M.query_tiles : 0;
+  a.block_tiles = (M.kind == BSATTN_MASK_BLOCK_DIAGONAL || M.kind == BSATTN_MASK_DENSE_ROWS_SPREAD)
+                     ? M.block_tiles
+                     : 1;
+  a.query_tiles = dense_rows ? M.query_tiles : 0;
   a.seed = M.seed;
   a.thresh24 = M.thresh24;
   a.force_diagonal = M.force_diagonal != 0;
@@ -282,11 +296,22 @@ BSATTN_API int bsattn_repetitive_heads(int32_t B, int32_t H, int32_t T, int32_t 
 
 BSATTN_API int bsattn_anchor_rows(int32_t B, int32_t H, int32_t T, int32_t grid_h,
                                   int32_t grid_w, int32_t d, int32_t stride, int32_t dtype,
-                                  const void* src, void* dst, int32_t broadcast, void* stream) {
+                                  const void* src, void* dst, int32_t broadcast,
+                                  int32_t block_rows, void* stream) {
   const int st = check_grid("anchor_rows", B, H, T, grid_h, grid_w, d, stride, dtype, false);
   if (st != BSATTN_OK) return st;
   if ((d * (dtype == BSATTN_DTYPE_BF16 ? 2 : 4)) % 16 != 0)
     return fail(BSATTN_ERR_INVALID_ARG, "anchor_rows: rows must be 16-byte multiples");
+  if (block_rows < 0)
+    return fail(BSATTN_ERR_INVALID_ARG, "anchor_rows: block_rows must be >= 0");
+  if (block_rows > 0) {
+    const int64_t n = (int64_t)T * grid_h * grid_w;
+    const int64_t packed = (int64_t)T * ((grid_h + stride - 1) / stride) * grid_w;
+    if ((packed + block_rows - 1) / block_rows > (n + block_rows - 1) / block_rows)
+      return fail(BSATTN_ERR_INVALID_ARG,
+                  "anchor_rows: %lld anchor rows in blocks of %d do not fit %lld block slots",
+                  (long long)packed, block_rows, (long long)((n + block_rows - 1) / block_rows));
+  }
   if ((int64_t)B * H * T == 0) return ok();
   if (!src || !dst || src == dst)
     return fail(BSATTN_ERR_INVALID_ARG, "anchor_rows: null or aliased buffers");
@@ -294,8 +319,8 @@ BSATTN_API int bsattn_anchor_rows(int32_t B, int32_t H, int32_t T, int32_t grid_
     return fail(BSATTN_ERR_INVALID_ARG, "anchor_rows: buffers must be 16-byte aligned");
   const int32_t row_bytes = d * (dtype == BSATTN_DTYPE_BF16 ? 2 : 4);
   return hip_status(bsattn::launch_anchor_rows((int64_t)B * H, T * grid_h * grid_w, row_bytes,
-                                               grid_h, grid_w, stride, broadcast != 0, src, dst,
-                                               stream),
+                                               grid_h, grid_w, stride, broadcast != 0,
+                                               block_rows, src, dst, stream),
                     "anchor_rows");
 }
 

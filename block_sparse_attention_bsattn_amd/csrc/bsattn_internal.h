@@ -12,8 +12,8 @@ struct MaskLaunch {
   int32_t tq, tk, mask_heads;
   int32_t window, num_anchors, rotation;  // window <= frames, rotation in [0, frames)
   int32_t budget;                         // expanded mode: min(C, frames)
-  int32_t block_tiles;                    // block-diagonal mode
-  int32_t query_tiles;                    // dense-rows mode
+  int32_t block_tiles;                    // block-diagonal and spread dense-rows modes
+  int32_t query_tiles;                    // dense-rows modes
   uint64_t seed;
   uint32_t thresh24;
   int32_t force_diagonal;
@@ -67,7 +67,8 @@ int launch_row_cosines(const RowCosLaunch& a, void* stream);
 int launch_repetitive_heads(int32_t B, int32_t H, int32_t T, int32_t gh, int32_t stride,
                             const float* cos, double gamma, uint8_t* flags, void* stream);
 int launch_anchor_rows(int64_t BH, int32_t N, int32_t row_bytes, int32_t gh, int32_t gw,
-                       int32_t stride, int broadcast, const void* src, void* dst, void* stream);
+                       int32_t stride, int broadcast, int32_t block_rows, const void* src,
+                       void* dst, void* stream);
 
 // static-mask calibration
 int launch_block_energy(const EnergyLaunch& a, void* stream);

@@ -30,6 +30,15 @@
 // computes its anchor rows only, packed into the first query tiles): query
 // tiles below query_tiles read every key tile, the others none.
 //
+// Spread dense-rows mode (same passage, with the anchor rows laid out in
+// blocks spread evenly over the sequence): the query_tiles anchor tiles form
+// Rg = ceil(query_tiles / block_tiles) blocks of block_tiles tiles (the last
+// one possibly shorter); block g sits at block slot floor(g * Pg / Rg) of the
+// Pg = ceil(Tq / block_tiles) slots (the rows bsattn_anchor_rows writes for
+// block_rows = block_tiles * tile).  The slot of g strictly increases with g
+// (Rg <= Pg), so slot b holds block g = ceil(b * Rg / Pg) exactly when
+// floor(g * Pg / Rg) == b; with Rg < Pg no block reaches the last slot.
+//
 // Static mode (CalibAtt page, "B. Fase di Inferenza": the block lists are
 // precomputed and deterministic) draws one SplitMix64 value per cell
 // c = (h*Tq + i)*Tk + j: the (c+1)-th output of the generator seeded with
@@ -123,6 +132,17 @@ __global__ void build_mask_kernel(MaskLaunch a, uint8_t* __restrict__ mask) {
       on = (i / a.block_tiles) == (j / a.block_tiles);
     } else if (a.kind == 5) {
       on = i < a.query_tiles;
+    } else if (a.kind == 6) {
+      const int64_t bt = a.block_tiles;
+      const int64_t rg = (a.query_tiles + bt - 1) / bt, pg = (a.tq + bt - 1) / bt;
+      const int64_t b = i / bt;
+      if (b < pg && rg > 0) {
+        const int64_t g = (b * rg + pg - 1) / pg;
+        if (g < rg && (g * pg) / rg == b) {
+          const int64_t size = g < rg - 1 ? bt : a.query_tiles - (rg - 1) * bt;
+          on = (i - b * bt) < size;
+        }
+      }
     } else if (a.kind == 1) {
       const uint64_t z = splitmix64_at(a.seed, (uint64_t)c + 1);
       on = ((uint32_t)(z >> 40) < a.thresh24) || (a.force_diagonal && i == j);

@@ -26,8 +26,13 @@
 // same decision.
 //
 // anchor_rows_kernel: an HBM-bound row copy.  Gather packs the anchor rows'
-// tokens (frame by frame, row by row) into the first Na rows of a buffer;
-// broadcast gives every token its anchor row's value from such a buffer.
+// tokens (frame by frame, row by row) into Na rows of a buffer; broadcast
+// gives every token its anchor row's value from such a buffer.  The packed
+// index a sits at buffer row a, or, spread in blocks of block_rows rows, at
+// row floor(g * Pg / Rg) * block_rows + a mod block_rows with g = a /
+// block_rows, Rg = ceil(Na / block_rows) and Pg = ceil(N / block_rows).  With
+// Rg < Pg no block reaches the last (possibly partial) slot; with Rg == Pg
+// the layout is the packed one; so every row written lies below N.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -297,8 +302,14 @@ __global__ void repetitive_heads_kernel(int32_t B, int32_t H, int32_t T, int32_t
 
 __global__ void __launch_bounds__(256)
 anchor_rows_kernel(int64_t BH, int32_t N, int32_t cpr, int32_t gh, int32_t gw, int32_t stride,
-                   int32_t na, int broadcast, const i32x4* __restrict__ src,
-                   i32x4* __restrict__ dst) {
+                   int32_t na, int broadcast, int32_t block_rows, int32_t rg, int32_t pg,
+                   const i32x4* __restrict__ src, i32x4* __restrict__ dst) {
+  // buffer row of packed index p
+  auto place = [&](int p) {
+    if (block_rows == 0) return p;
+    const int g = p / block_rows;
+    return (int)(((int64_t)g * pg) / rg) * block_rows + (p - g * block_rows);
+  };
   const int P = gh * gw;
   const int T = N / P;
   const int per_frame_a = na * gw;
@@ -321,7 +332,9 @@ anchor_rows_kernel(int64_t BH, int32_t N, int32_t cpr, int32_t gh, int32_t gw, i
       const int y = rem / gw, x = rem - y * gw;
       sn = f * per_frame_a + (y / stride) * gw + x;
     }
-    dst[(bh * N + dn) * cpr + c] = src[(bh * N + sn) * cpr + c];
+    const int drow = broadcast ? dn : place(dn);
+    const int srow = broadcast ? place(sn) : sn;
+    dst[(bh * N + drow) * cpr + c] = src[(bh * N + srow) * cpr + c];
   }
 }
 
@@ -358,17 +371,21 @@ int launch_repetitive_heads(int32_t B, int32_t H, int32_t T, int32_t gh, int32_t
 }
 
 int launch_anchor_rows(int64_t BH, int32_t N, int32_t row_bytes, int32_t gh, int32_t gw,
-                       int32_t stride, int broadcast, const void* src, void* dst, void* stream) {
+                       int32_t stride, int broadcast, int32_t block_rows, const void* src,
+                       void* dst, void* stream) {
   const int32_t cpr = row_bytes / 16;
   const int32_t na = (gh + stride - 1) / stride;
   const int32_t T = N / (gh * gw);
+  const int32_t packed = T * na * gw;
+  const int32_t rg = block_rows > 0 ? (packed + block_rows - 1) / block_rows : 1;
+  const int32_t pg = block_rows > 0 ? (N + block_rows - 1) / block_rows : 1;
   const int64_t rows = broadcast ? (int64_t)N : (int64_t)T * na * gw;
   const int64_t total = BH * rows * cpr;
   if (total == 0) return hipSuccess;
   int64_t grid = (total + 255) / 256;
   if (grid > 1 << 20) grid = 1 << 20;
   hipLaunchKernelGGL(anchor_rows_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
-                     BH, N, cpr, gh, gw, stride, na, broadcast,
+                     BH, N, cpr, gh, gw, stride, na, broadcast, block_rows, rg, pg,
                      reinterpret_cast<const i32x4*>(src), reinterpret_cast<i32x4*>(dst));
   return hipGetLastError();
 }

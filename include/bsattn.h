@@ -53,7 +53,8 @@ typedef enum {
   BSATTN_MASK_DENSE = 2,         /* all tiles active (full attention) */
   BSATTN_MASK_WINDOW_ANCHOR_EXPANDED = 3, /* LVSA window grown to a frame budget + anchors */
   BSATTN_MASK_BLOCK_DIAGONAL = 4,         /* SQuad passes: square blocks of block_tiles tiles */
-  BSATTN_MASK_DENSE_ROWS = 5              /* query tiles < query_tiles dense, the rest empty */
+  BSATTN_MASK_DENSE_ROWS = 5,             /* query tiles < query_tiles dense, the rest empty */
+  BSATTN_MASK_DENSE_ROWS_SPREAD = 6       /* query_tiles dense tiles in blocks spread evenly */
 } bsattn_mask_kind;
 
 /* Token geometry of the video latent.  N = frames*grid_h*grid_w; the number
@@ -97,7 +98,17 @@ typedef struct {
  * DENSE_ROWS (CalibAtt page, "B. Fase di Inferenza": a repetitive head
  *   computes its anchor rows only): query tiles i < query_tiles read every
  *   key tile, the others none, for anchor rows packed at the front of Q
- *   (bsattn_anchor_rows). */
+ *   (bsattn_anchor_rows with block_rows = 0).
+ * DENSE_ROWS_SPREAD (same passage): the Ta = query_tiles dense query tiles
+ *   come in Rg = ceil(Ta / block_tiles) blocks of block_tiles tiles, the
+ *   last one holding the Ta - (Rg - 1) * block_tiles left over; of the
+ *   Pg = ceil(Tq / block_tiles) block slots, block g takes slot
+ *   floor(g * Pg / Rg), i.e. query tiles from floor(g * Pg / Rg) *
+ *   block_tiles on.  Those tiles read every key tile, all others none.
+ *   Rg <= Pg is required.  This is the layout bsattn_anchor_rows writes with
+ *   block_rows = block_tiles * tile; the dense tiles then spread evenly over
+ *   each head, and bsattn_fwd's workgroups load the GPU evenly (packed at
+ *   the front, half of every head's workgroups would have no work). */
 typedef struct {
   int32_t kind;           /* bsattn_mask_kind */
   int32_t window;         /* w >= 0, in frames */
@@ -108,8 +119,9 @@ typedef struct {
   int32_t force_diagonal; /* STATIC_RANDOM */
   int32_t mask_heads;     /* Hm >= 1: number of mask slices (1 = shared by all heads) */
   int32_t budget;         /* WINDOW_ANCHOR_EXPANDED: C >= 0 frames per query frame */
-  int32_t block_tiles;    /* BLOCK_DIAGONAL: b >= 1 tiles per diagonal block */
-  int32_t query_tiles;    /* DENSE_ROWS: >= 0 query tiles with every key tile */
+  int32_t block_tiles;    /* BLOCK_DIAGONAL: b >= 1 tiles per diagonal block;
+                             DENSE_ROWS_SPREAD: >= 1 tiles per block */
+  int32_t query_tiles;    /* DENSE_ROWS(_SPREAD): >= 0 query tiles with every key tile */
 } bsattn_mask_params;
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
@@ -130,7 +142,8 @@ BSATTN_API int32_t bsattn_num_tiles(int64_t tokens, int32_t tile);
  *         every byte is written (0 or 1).
  * Errors: INVALID_ARG on null pointers, non-positive sizes, window < 0,
  * num_anchors outside [0, T], budget < 0 (expanded mode), block_tiles < 1
- * (block-diagonal mode), query_tiles < 0 (dense-rows mode), thresh24 > 2^24,
+ * (block-diagonal and spread dense-rows modes), query_tiles < 0 (dense-rows
+ * modes), spread blocks that do not fit (Rg > Pg), thresh24 > 2^24,
  * mask_heads < 1, an unknown kind, or Hm*Tq*Tk >= 2^31. */
 BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
                                  const bsattn_mask_params* params,
@@ -225,22 +238,29 @@ BSATTN_API int bsattn_repetitive_heads(int32_t B, int32_t H, int32_t T, int32_t 
                                        int32_t stride, const float* cos, double gamma,
                                        uint8_t* flags, void* stream);
 
-/* Anchor-row gather and broadcast (inference), on [B, H, N, d] buffers:
- *   broadcast == 0: dst rows 0 .. Na-1 (Na = T * ceil(grid_h/stride) *
- *                   grid_w) receive the anchor rows' tokens, frame by frame,
- *                   row by row; dst rows >= Na are not written.
- *   broadcast != 0: every row n of dst receives src row c(n), the packed
- *                   index of n's anchor-row token (src rows < Na are read).
- * With the gathered Q, a DENSE_ROWS mask of ceil(Na/tile) query tiles and
+/* Anchor-row gather and broadcast (inference), on [B, H, N, d] buffers.
+ * The anchor rows' tokens, frame by frame, row by row, have packed indices
+ * a = 0 .. Na-1 (Na = T * ceil(grid_h/stride) * grid_w); packed index a is
+ * stored at buffer row a when block_rows == 0, else at row
+ *   floor(g * Pg / Rg) * block_rows + (a mod block_rows),
+ *   g = a / block_rows, Rg = ceil(Na / block_rows), Pg = ceil(N / block_rows)
+ * (blocks of block_rows rows spread evenly; every such row lies below N).
+ *   broadcast == 0: the anchor tokens are written to their buffer rows of
+ *                   dst; the other rows of dst are not written.
+ *   broadcast != 0: every row n of dst receives the src buffer row of n's
+ *                   anchor-row token.
+ * With the gathered Q, a DENSE_ROWS mask of ceil(Na/tile) query tiles (or,
+ * for block_rows = b * tile, a DENSE_ROWS_SPREAD mask with block_tiles = b),
  * bsattn_fwd, then the broadcast of its output, a repetitive head costs
- * Na/N of full attention.
+ * about Na/N of full attention.
  *   src, dst: distinct device buffers, element type `dtype`, 16-byte aligned,
  *             rows of d elements a multiple of 16 bytes (any such d).
- * Errors: INVALID_ARG (null or aliased buffers, sizes, row length),
- * UNSUPPORTED (dtype), HIP. */
+ * Errors: INVALID_ARG (null or aliased buffers, sizes, row length,
+ * block_rows < 0), UNSUPPORTED (dtype), HIP. */
 BSATTN_API int bsattn_anchor_rows(int32_t B, int32_t H, int32_t T, int32_t grid_h,
                                   int32_t grid_w, int32_t d, int32_t stride, int32_t dtype,
-                                  const void* src, void* dst, int32_t broadcast, void* stream);
+                                  const void* src, void* dst, int32_t broadcast,
+                                  int32_t block_rows, void* stream);
 
 /* ---- Static-mask calibration (CalibAtt page, "A. Fase di Calibrazione").
  * The calibration runs full attention on a few prompts, measures how much

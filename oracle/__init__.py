@@ -45,13 +45,15 @@ from .masks import (anchor_frames, window_frames, frame_set, frame_mask,
                     frame_mask_expanded, tile_mask_expanded,
                     tile_frame_range, tile_mask_window_anchor,
                     splitmix64_stream, static_hash24, tile_mask_static,
-                    tile_mask_dense, tile_mask_block_diagonal, tile_mask)
+                    tile_mask_dense, tile_mask_block_diagonal, tile_mask,
+                    tile_mask_dense_rows_spread)
 from .csr import tile_csr
 from .calibration import (block_energy, block_energy_rows, select_row,
                           select_mask, aggregate)
 from .repetition import (anchor_row, row_cosines, repetitive_heads,
                          anchor_count, gather_anchor_rows,
-                         broadcast_anchor_rows, repeated_attention)
+                         broadcast_anchor_rows, repeated_attention,
+                         anchor_buffer_rows)
 from .squad import (squad_local, squad_attention, squad_attention_rows,
                     window_major_to_position_major,
                     position_major_to_window_major)
@@ -63,10 +65,12 @@ __all__ = [
     "tile_mask_expanded",
     "tile_frame_range", "tile_mask_window_anchor", "splitmix64_stream",
     "static_hash24", "tile_mask_static", "tile_mask_dense", "tile_mask_block_diagonal", "tile_mask",
+    "tile_mask_dense_rows_spread",
     "tile_csr", "block_sparse_attention", "block_sparse_attention_rows",
     "block_energy", "block_energy_rows", "select_row", "select_mask",
     "aggregate", "squad_local", "squad_attention", "squad_attention_rows",
     "window_major_to_position_major", "position_major_to_window_major",
     "anchor_row", "row_cosines", "repetitive_heads", "anchor_count",
     "gather_anchor_rows", "broadcast_anchor_rows", "repeated_attention",
+    "anchor_buffer_rows",
 ]

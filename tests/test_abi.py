@@ -111,9 +111,14 @@ def test_build_mask_rejects_bad_arguments():
     assert call(params=bs.MaskParams(3, 1, 5, 0, 0, 0, 0, 1, 5)) == bs.ERR_INVALID_ARG
     # block diagonal: at least one tile per block
     assert call(params=bs.MaskParams(4, 0, 0, 0, 0, 0, 0, 1, 0, 0)) == bs.ERR_INVALID_ARG
-    assert call(params=bs.MaskParams(6, 0, 0, 0, 0, 0, 0, 1, 0, 1)) == bs.ERR_INVALID_ARG
+    assert call(params=bs.MaskParams(7, 0, 0, 0, 0, 0, 0, 1, 0, 1)) == bs.ERR_INVALID_ARG
     # dense rows: a non-negative tile count
     assert call(params=bs.MaskParams(5, 0, 0, 0, 0, 0, 0, 1, 0, 1, -1)) == bs.ERR_INVALID_ARG
+    # spread dense rows: also at least one tile per block, and blocks that fit
+    assert call(params=bs.MaskParams(6, 0, 0, 0, 0, 0, 0, 1, 0, 1, -1)) == bs.ERR_INVALID_ARG
+    assert call(params=bs.MaskParams(6, 0, 0, 0, 0, 0, 0, 1, 0, 0, 2)) == bs.ERR_INVALID_ARG
+    assert call(params=bs.MaskParams(6, 0, 0, 0, 0, 0, 0, 1, 0, 2, 1 << 20)) == \
+        bs.ERR_INVALID_ARG
     assert call(params=bs.MaskParams(0, -1, 1, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
     assert call(params=bs.MaskParams(0, 1, 5, 0, 0, 0, 0, 1)) == bs.ERR_INVALID_ARG
     assert call(params=bs.MaskParams(1, 0, 0, 0, 0, (1 << 24) + 1, 0, 1)) == \
@@ -227,9 +232,10 @@ def test_repetition_calls_reject_bad_arguments():
     assert R(1, 2, 3, 4, 2, p, float("inf"), p, None) == bs.ERR_INVALID_ARG
     assert R(1, 0, 3, 4, 2, None, 0.9, None, None) == bs.OK
     A = L.bsattn_anchor_rows
-    assert A(1, 1, 2, 4, 8, 128, 2, 0, p, p, 0, None) == bs.ERR_INVALID_ARG        # aliased
-    assert A(1, 1, 2, 4, 8, 128, 2, 0, None, p2, 0, None) == bs.ERR_INVALID_ARG
-    assert A(1, 1, 2, 0, 8, 128, 2, 0, p, p2, 0, None) == bs.ERR_INVALID_ARG
-    assert A(1, 1, 2, 4, 8, 128, 2, 5, p, p2, 0, None) == bs.ERR_UNSUPPORTED
-    assert A(1, 1, 2, 4, 8, 4, 2, 0, p, p2, 0, None) == bs.ERR_INVALID_ARG        # 8-byte rows
-    assert A(1, 1, 0, 4, 8, 128, 2, 0, None, None, 0, None) == bs.OK
+    assert A(1, 1, 2, 4, 8, 128, 2, 0, p, p, 0, 0, None) == bs.ERR_INVALID_ARG     # aliased
+    assert A(1, 1, 2, 4, 8, 128, 2, 0, None, p2, 0, 0, None) == bs.ERR_INVALID_ARG
+    assert A(1, 1, 2, 0, 8, 128, 2, 0, p, p2, 0, 0, None) == bs.ERR_INVALID_ARG
+    assert A(1, 1, 2, 4, 8, 128, 2, 5, p, p2, 0, 0, None) == bs.ERR_UNSUPPORTED
+    assert A(1, 1, 2, 4, 8, 4, 2, 0, p, p2, 0, 0, None) == bs.ERR_INVALID_ARG     # 8-byte rows
+    assert A(1, 1, 2, 4, 8, 128, 2, 0, p, p2, 0, -1, None) == bs.ERR_INVALID_ARG  # block_rows
+    assert A(1, 1, 0, 4, 8, 128, 2, 0, None, None, 0, 0, None) == bs.OK

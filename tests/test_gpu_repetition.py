@@ -107,9 +107,46 @@ def test_dense_rows_masks(N, tile, qt):
     check_mask_csr(w, mask, rp, ci)
 
 
-@pytest.mark.parametrize("T,gh,gw,d,s,tile,H", [(2, 6, 16, 128, 2, 128, 2),
+@pytest.mark.parametrize("N,tile,qt,bt", [(1024, 128, 3, 2), (2000, 64, 7, 3), (1000, 128, 3, 2),
+                                          (640, 64, 0, 1), (640, 64, 10, 1), (32760, 128, 128, 2),
+                                          (131040, 128, 342, 2)])
+def test_spread_dense_rows_masks(N, tile, qt, bt):
+    w = W.small_workload(frames=1, grid_h=1, grid_w=N, tile=tile,
+                         mask=W.MaskSpec(W.MASK_DENSE_ROWS_SPREAD, query_tiles=qt,
+                                         block_tiles=bt))
+    mask, rp, ci = gpu_mask_csr(w)
+    check_mask_csr(w, mask, rp, ci)
+
+
+@pytest.mark.parametrize("T,gh,gw,d,s,br,dt", [(2, 5, 3, 128, 2, 4, torch.bfloat16),
+                                               (21, 30, 52, 128, 2, 256, torch.bfloat16),
+                                               (3, 7, 4, 64, 3, 5, torch.float32),
+                                               (4, 9, 10, 64, 3, 128, torch.bfloat16)])
+def test_anchor_rows_spread_bit_exact(T, gh, gw, d, s, br, dt):
+    """Gather into blocks of br rows spread over the buffer, and the
+    broadcast back from that layout."""
+    N = T * gh * gw
+    x = torch.randn(2, 3, N, d, generator=torch.Generator().manual_seed(N + br)).to(dt)
+    ga = torch.zeros_like(x).cuda()
+    bs.anchor_rows(x.cuda(), ga, T, gh, gw, s, block_rows=br)
+    bc = torch.empty_like(ga)
+    bs.anchor_rows(ga, bc, T, gh, gw, s, broadcast=True, block_rows=br)
+    torch.cuda.synchronize()
+    na = T * oracle.anchor_count(gh, s) * gw
+    rows = oracle.anchor_buffer_rows(na, N, br)
+    want_g = oracle.gather_anchor_rows(x.float().numpy(), T, gh, gw, s)
+    got = ga.cpu().float().numpy()
+    assert np.array_equal(got[:, :, rows], want_g)
+    rest = np.setdiff1d(np.arange(N), rows)
+    assert (got[:, :, rest] == 0).all()                      # other rows untouched
+    want_b = oracle.broadcast_anchor_rows(want_g, T, gh, gw, s)
+    assert np.array_equal(bc.cpu().float().numpy(), want_b)
+
+
+@pytest.mark.parametrize("T,gh,gw,d,s,tile,H", [(2, 6, 16, 128, 2, 128, 2),   # packed
                                                 (3, 5, 20, 64, 2, 64, 1),
-                                                (2, 9, 32, 128, 3, 64, 2)])
+                                                (2, 9, 32, 128, 3, 64, 2),     # spread
+                                                (6, 12, 20, 128, 3, 128, 2)])
 def test_repeated_attention_full_parity(T, gh, gw, d, s, tile, H):
     N = T * gh * gw
     g = torch.Generator().manual_seed(N + s)

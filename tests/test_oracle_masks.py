@@ -343,3 +343,33 @@ def test_dense_rows_by_hand():
     np.testing.assert_array_equal(got, want)
     assert (oracle.tile_mask(5, 1, 1, 300, 64, query_tiles=0) == 0).all()
     assert (oracle.tile_mask(5, 1, 1, 300, 64, query_tiles=9) == 1).all()
+
+
+def test_dense_rows_spread_by_hand():
+    """Spread dense rows, enumerated by hand from the rule (block g of the
+    query_tiles dense tiles starts at tile floor(g * Pg / Rg) * block_tiles,
+    Pg = ceil(Tq / block_tiles) block slots)."""
+    def dense_rows(N, tile, ta, bt):
+        m = oracle.tile_mask(6, 1, 1, N, tile, query_tiles=ta, block_tiles=bt)[0]
+        assert all(r.all() or not r.any() for r in m)     # whole rows on or off
+        return m.any(axis=1).nonzero()[0].tolist()
+    # 9 tiles, 3 dense in blocks of 2: Rg = 2 over Pg = 5 slots -> slots 0, 2
+    assert dense_rows(9 * 64, 64, 3, 2) == [0, 1, 4]
+    # 6 tiles, 2 dense, blocks of 1: Rg = 2 over Pg = 6 -> slots 0, 3
+    assert dense_rows(6 * 64, 64, 2, 1) == [0, 3]
+    # 8 tiles, 4 dense in blocks of 2: slots 0, 2
+    assert dense_rows(8 * 64, 64, 4, 2) == [0, 1, 4, 5]
+    # 1000 tokens, tile 128: 8 tiles (the last partial), Pg = 4, Rg = 2 ->
+    # slots 0, 2
+    assert dense_rows(1000, 128, 3, 2) == [0, 1, 4]
+    # 5 tiles, all dense in blocks of 2: Rg = Pg = 3, packed
+    assert dense_rows(5 * 64, 64, 5, 2) == [0, 1, 2, 3, 4]
+    # as many blocks as slots: the front-packed layout of the plain mode
+    np.testing.assert_array_equal(oracle.tile_mask(6, 1, 1, 5 * 64, 64, query_tiles=4,
+                                                   block_tiles=2),
+                                  oracle.tile_mask(5, 1, 1, 5 * 64, 64, query_tiles=4))
+    assert dense_rows(8 * 64, 64, 0, 2) == []
+    with pytest.raises(ValueError):       # 4 blocks, 3 slots
+        oracle.tile_mask(6, 1, 1, 5 * 64, 64, query_tiles=7, block_tiles=2)
+    with pytest.raises(ValueError):
+        oracle.tile_mask(6, 1, 1, 5 * 64, 64, query_tiles=1, block_tiles=0)

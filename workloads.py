@@ -27,6 +27,7 @@ MASK_DENSE = 2
 MASK_WINDOW_ANCHOR_EXPANDED = 3
 MASK_BLOCK_DIAGONAL = 4
 MASK_DENSE_ROWS = 5
+MASK_DENSE_ROWS_SPREAD = 6
 
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
