@@ -219,10 +219,11 @@ def calibration(bs, W, torch, dev, calls: int):
 
 
 def squad_leg(bs, W, torch, dev, calls: int):
-    """SQuad's two-pass attention at 65 536 tokens (w = 256): the local pass,
-    the reorders of Q, K and the local output, the global pass and the
-    inverse reorder, each timed with events on the launch stream; then the
-    same kernel as dense attention for the comparison the page draws."""
+    """SQuad's two-pass attention at 65 536 tokens (w = 256): the local pass
+    and the global pass on the grouped view (bsattn_fwd_grouped), each timed
+    with events on the launch stream; next to it the same operator through
+    explicit reorders of Q, K and the local output and back; then the same
+    kernel as dense attention for the comparison the page draws."""
     w = W.SQUAD
     win = W.SQUAD_W
     G = w.N // win
@@ -243,6 +244,18 @@ def squad_leg(bs, W, torch, dev, calls: int):
         rp, ci = masks[win // w.tile]
         bs.fwd(q, k, v, o_l, rp, ci, w.tile, stream=stream)
         mark(1)
+        rp, ci = masks[G // w.tile]
+        bs.fwd_grouped(q, k, o_l, out, rp, ci, win, stream=stream)
+        mark(2)
+
+    def run_reordered(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        rp, ci = masks[win // w.tile]
+        bs.fwd(q, k, v, o_l, rp, ci, w.tile, stream=stream)
+        mark(1)
         bs.window_reorder(q, qp, win, stream=stream)
         bs.window_reorder(k, kp, win, stream=stream)
         bs.window_reorder(o_l, op, win, stream=stream)
@@ -254,16 +267,20 @@ def squad_leg(bs, W, torch, dev, calls: int):
         mark(4)
 
     run()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(calls)]
-    for e in evs:
+    run_reordered()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(calls)]
+    evr = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(calls)]
+    for e, er in zip(evs, evr):
         run(e)
+        run_reordered(er)
     torch.cuda.synchronize()
-    part = lambda a, b: float(np.median([e[a].elapsed_time(e[b]) for e in evs]))
+    part = lambda es, a, b: float(np.median([e[a].elapsed_time(e[b]) for e in es]))
     flops_local = 4.0 * w.d * w.N * win * w.B * w.H
     flops_global = 4.0 * w.d * w.N * G * w.B * w.H
     reorder_bytes = 4 * 2 * w.B * w.H * w.N * w.d * 2   # 4 reorders, read + write
-    l_ms, r_ms, g_ms, i_ms = part(0, 1), part(1, 2), part(2, 3), part(3, 4)
-    total = part(0, 4)
+    l_ms, g_ms, total = part(evs, 0, 1), part(evs, 1, 2), part(evs, 0, 2)
+    r_ms, rg_ms, i_ms = part(evr, 1, 2), part(evr, 2, 3), part(evr, 3, 4)
+    total_r = part(evr, 0, 4)
     # dense attention of the same shape with the same kernel
     dm = bs.make_mask(*layout, device=dev, kind=W.MASK_DENSE)
     drp, dci = bs.make_csr(dm)
@@ -280,9 +297,11 @@ def squad_leg(bs, W, torch, dev, calls: int):
     return {"workload": w.name, "window": win, "groups": G,
             "ms_total": round(total, 4),
             "local_ms": round(l_ms, 4), "local_tflops": round(flops_local / (l_ms * 1e-3) / 1e12, 1),
-            "global_ms": round(g_ms, 4), "global_tflops": round(flops_global / (g_ms * 1e-3) / 1e12, 1),
-            "reorder_ms": round(r_ms + i_ms, 4),
-            "reorder_gbs": round(reorder_bytes / ((r_ms + i_ms) * 1e-3) / 1e9, 1),
+            "global_grouped_ms": round(g_ms, 4),
+            "global_grouped_tflops": round(flops_global / (g_ms * 1e-3) / 1e12, 1),
+            "reordered_path": {"ms_total": round(total_r, 4), "global_ms": round(rg_ms, 4),
+                               "reorder_ms": round(r_ms + i_ms, 4),
+                               "reorder_gbs": round(reorder_bytes / ((r_ms + i_ms) * 1e-3) / 1e9, 1)},
             "attention_tflop": round((flops_local + flops_global) / 1e12, 4),
             "dense_tflop": round(dense_flops / 1e12, 3),
             "dense_ms": round(dense_ms, 3),

@@ -7,6 +7,7 @@ The calls mirror include/bsattn.h:
     build_mask(layout, params, mask)                    -> bsattn_build_mask
     compact(mask, row_ptr, col_idx)                     -> bsattn_compact
     fwd(q, k, v, o, row_ptr, col_idx, tile, ...)        -> bsattn_fwd
+    fwd_grouped(q, k, v, o, row_ptr, col_idx, w, ...)   -> bsattn_fwd_grouped
     block_energy(q, k, energy, tile, ...)               -> bsattn_block_energy
     select_blocks(energy, eps, mask)                    -> bsattn_select_blocks
     aggregate_masks(masks, rho, out)                    -> bsattn_aggregate_masks
@@ -47,7 +48,7 @@ MASK_DENSE_ROWS_SPREAD = 6
 # Every symbol include/bsattn.h exports.
 EXPORTS = ("bsattn_version", "bsattn_status_string", "bsattn_last_error",
            "bsattn_num_tiles", "bsattn_build_mask", "bsattn_compact",
-           "bsattn_fwd", "bsattn_window_reorder", "bsattn_row_cosines",
+           "bsattn_fwd", "bsattn_fwd_grouped", "bsattn_window_reorder", "bsattn_row_cosines",
            "bsattn_repetitive_heads", "bsattn_anchor_rows", "bsattn_block_energy",
            "bsattn_select_blocks",
            "bsattn_aggregate_masks", "bsattn_mfma_ceiling")
@@ -104,6 +105,9 @@ def lib() -> ctypes.CDLL:
     L.bsattn_fwd.restype = ctypes.c_int
     L.bsattn_fwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                              i32, i32p, i32p, ctypes.c_float, vp]
+    L.bsattn_fwd_grouped.restype = ctypes.c_int
+    L.bsattn_fwd_grouped.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                     i32, i32p, i32p, i32, ctypes.c_float, vp]
     L.bsattn_window_reorder.restype = ctypes.c_int
     L.bsattn_window_reorder.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i32, vp]
     L.bsattn_row_cosines.restype = ctypes.c_int
@@ -234,6 +238,30 @@ def fwd(q, k, v, o, row_ptr, col_idx, tile: int, mask_heads: int = 1,
                           _ptr(col_idx, "col_idx", torch.int32), float(scale),
                           _stream(stream))
     _check(st, "bsattn_fwd")
+    return o
+
+
+def fwd_grouped(q, k, v, o, row_ptr, col_idx, w: int, mask_heads: int = 1,
+                lse=None, scale: float = 0.0, stream=None):
+    """bsattn_fwd_grouped: the forward over the position-major order of the
+    windows of w tokens (bf16, d 128, tile 128), on window-major buffers."""
+    import torch
+    if q.dtype != torch.bfloat16 or q.dim() != 4:
+        raise ValueError("q must be bf16 [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must have the shape and dtype of q")
+    if lse is not None and tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must have shape [B, H, N]")
+    st = lib().bsattn_fwd_grouped(B, H, N, d, 128, DTYPE_BF16, _ptr(q, "q", q.dtype),
+                                  _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype),
+                                  _ptr(o, "o", q.dtype),
+                                  _ptr(lse, "lse", torch.float32, allow_none=True),
+                                  mask_heads, _ptr(row_ptr, "row_ptr", torch.int32),
+                                  _ptr(col_idx, "col_idx", torch.int32), int(w), float(scale),
+                                  _stream(stream))
+    _check(st, "bsattn_fwd_grouped")
     return o
 
 
@@ -414,12 +442,15 @@ def calibrate(q, k, tile, eps, rho, scale=0.0, stream=None):
     return mask, energy, sel
 
 
-def squad(q, k, v, w: int, tile: int, scale: float = 0.0, stream=None):
+def squad(q, k, v, w: int, tile: int, scale: float = 0.0, stream=None, grouped=None):
     """SQuad's two-pass attention through the library's calls: the local
-    pass (block-diagonal mask, w / tile tiles per block) gives O_L; Q, K and
-    O_L are reordered to position-major; the global pass (block-diagonal,
-    G / tile tiles per block, G = N / w) runs with O_L as values; the result
-    is reordered back.  Needs w and N / w to be multiples of tile."""
+    pass (block-diagonal mask, w / tile tiles per block) gives O_L; the
+    global pass (block-diagonal, G / tile tiles per block, G = N / w) runs
+    over the position-major order with O_L as values.  For bf16, d 128 and
+    tile 128 the global pass reads and writes the window-major buffers
+    through bsattn_fwd_grouped; otherwise (or with grouped=False) Q, K and
+    O_L are reordered to position-major and the result back.  Needs w and
+    N / w to be multiples of tile."""
     import torch
     B, H, N, d = q.shape
     if w % tile or N % w or (N // w) % tile:
@@ -436,6 +467,14 @@ def squad(q, k, v, w: int, tile: int, scale: float = 0.0, stream=None):
         return o
 
     o_local = pass_(q, k, v, w // tile)
+    if grouped is None:
+        grouped = q.dtype == torch.bfloat16 and d == 128 and tile == 128
+    if grouped:
+        mask = make_mask(*layout, device=q.device, stream=stream,
+                         kind=MASK_BLOCK_DIAGONAL, block_tiles=G // tile)
+        rp, ci = make_csr(mask, stream=stream)
+        out = torch.empty_like(q)
+        return fwd_grouped(q, k, o_local, out, rp, ci, w, scale=scale, stream=stream)
     qp, kp, op = torch.empty_like(q), torch.empty_like(k), torch.empty_like(o_local)
     window_reorder(q, qp, w, stream=stream)
     window_reorder(k, kp, w, stream=stream)

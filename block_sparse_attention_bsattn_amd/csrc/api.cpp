@@ -153,37 +153,40 @@ BSATTN_API int bsattn_compact(int32_t rows, int32_t Tk, const uint8_t* mask,
                     "compact");
 }
 
-BSATTN_API int bsattn_fwd(int32_t B, int32_t H, int32_t N, int32_t d,
-                          int32_t tile, int32_t dtype, const void* q,
-                          const void* k, const void* v, void* o, float* lse,
-                          int32_t mask_heads, const int32_t* row_ptr,
-                          const int32_t* col_idx, float scale, void* stream) {
+// Validation shared by the two forward entry points; fills `a` on success.
+// A no-op call (B*H*N == 0) returns OK with *noop set.
+static int fwd_args(const char* who, int32_t B, int32_t H, int32_t N, int32_t d, int32_t tile,
+                    int32_t dtype, const void* q, const void* k, const void* v, void* o,
+                    float* lse, int32_t mask_heads, const int32_t* row_ptr,
+                    const int32_t* col_idx, float scale, bsattn::FwdLaunch& a, bool* noop) {
+  *noop = false;
   if (B < 0 || H < 0 || N < 0 || d < 0)
-    return fail(BSATTN_ERR_INVALID_ARG, "fwd: B, H, N and d must be >= 0");
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: B, H, N and d must be >= 0", who);
   if (d != 64 && d != 128)
-    return fail(BSATTN_ERR_UNSUPPORTED, "fwd: head dim %d (supported: 64, 128)", d);
+    return fail(BSATTN_ERR_UNSUPPORTED, "%s: head dim %d (supported: 64, 128)", who, d);
   if (tile != 64 && tile != 128)
-    return fail(BSATTN_ERR_UNSUPPORTED, "fwd: tile %d (supported: 64, 128)", tile);
+    return fail(BSATTN_ERR_UNSUPPORTED, "%s: tile %d (supported: 64, 128)", who, tile);
   if (dtype != BSATTN_DTYPE_BF16 && dtype != BSATTN_DTYPE_F32)
-    return fail(BSATTN_ERR_UNSUPPORTED, "fwd: dtype %d", dtype);
-  if ((int64_t)B * H * N == 0) return ok();
+    return fail(BSATTN_ERR_UNSUPPORTED, "%s: dtype %d", who, dtype);
+  if ((int64_t)B * H * N == 0) {
+    *noop = true;
+    return BSATTN_OK;
+  }
   if (B > 65535 || H > 65535)
-    return fail(BSATTN_ERR_INVALID_ARG, "fwd: B and H must be <= 65535");
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: B and H must be <= 65535", who);
   if (mask_heads != 1 && mask_heads != H)
-    return fail(BSATTN_ERR_INVALID_ARG, "fwd: mask_heads %d must be 1 or H=%d",
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: mask_heads %d must be 1 or H=%d", who,
                 mask_heads, H);
   if (!q || !k || !v || !o || !row_ptr || !col_idx)
-    return fail(BSATTN_ERR_INVALID_ARG, "fwd: null pointer");
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: null pointer", who);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(BSATTN_ERR_INVALID_ARG, "fwd: q, k, v, o must be 16-byte aligned");
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: q, k, v, o must be 16-byte aligned", who);
   if (!(scale == scale) || isinf(scale))
-    return fail(BSATTN_ERR_INVALID_ARG, "fwd: scale must be finite");
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: scale must be finite", who);
   const int32_t tiles = bsattn_num_tiles(N, tile);
   const int64_t cells = (int64_t)mask_heads * tiles * tiles;
   if (cells >= kMaxCells)
-    return fail(BSATTN_ERR_INVALID_ARG, "fwd: tile mask has >= 2^31 cells");
-
-  bsattn::FwdLaunch a;
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: tile mask has >= 2^31 cells", who);
   a.B = B;
   a.H = H;
   a.N = N;
@@ -202,7 +205,46 @@ BSATTN_API int bsattn_fwd(int32_t B, int32_t H, int32_t N, int32_t d,
   a.col_cap = cells;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
   a.scale_log2 = sc * 1.4426950408889634f;
+  a.window = 0;
+  return BSATTN_OK;
+}
+
+BSATTN_API int bsattn_fwd(int32_t B, int32_t H, int32_t N, int32_t d,
+                          int32_t tile, int32_t dtype, const void* q,
+                          const void* k, const void* v, void* o, float* lse,
+                          int32_t mask_heads, const int32_t* row_ptr,
+                          const int32_t* col_idx, float scale, void* stream) {
+  bsattn::FwdLaunch a;
+  bool noop;
+  const int st = fwd_args("fwd", B, H, N, d, tile, dtype, q, k, v, o, lse, mask_heads, row_ptr,
+                          col_idx, scale, a, &noop);
+  if (st != BSATTN_OK) return st;
+  if (noop) return ok();
   return hip_status(bsattn::launch_fwd(a, stream), "fwd");
+}
+
+BSATTN_API int bsattn_fwd_grouped(int32_t B, int32_t H, int32_t N, int32_t d, int32_t tile,
+                                  int32_t dtype, const void* q, const void* k, const void* v,
+                                  void* o, float* lse, int32_t mask_heads,
+                                  const int32_t* row_ptr, const int32_t* col_idx,
+                                  int32_t window, float scale, void* stream) {
+  bsattn::FwdLaunch a;
+  bool noop;
+  const int st = fwd_args("fwd_grouped", B, H, N, d, tile, dtype, q, k, v, o, lse, mask_heads,
+                          row_ptr, col_idx, scale, a, &noop);
+  if (st != BSATTN_OK) return st;
+  if (d != 128 || tile != 128 || dtype != BSATTN_DTYPE_BF16)
+    return fail(BSATTN_ERR_UNSUPPORTED, "fwd_grouped: bf16, d 128 and tile 128 only");
+  if (window < 1)
+    return fail(BSATTN_ERR_INVALID_ARG, "fwd_grouped: window must be >= 1");
+  if (noop) return ok();
+  if (N % window != 0 || (N / window) % 128 != 0)
+    return fail(BSATTN_ERR_INVALID_ARG,
+                "fwd_grouped: N=%d must be window=%d times a multiple of 128", N, window);
+  if ((int64_t)N * 256 >= ((int64_t)1 << 31))
+    return fail(BSATTN_ERR_INVALID_ARG, "fwd_grouped: N * 256 bytes must stay below 2^31");
+  a.window = window;
+  return hip_status(bsattn::launch_fwd(a, stream), "fwd_grouped");
 }
 
 BSATTN_API int bsattn_window_reorder(int32_t B, int32_t H, int32_t N, int32_t d, int32_t w,

@@ -32,6 +32,7 @@ struct FwdLaunch {
   int32_t tiles;      // Tq = Tk
   int64_t col_cap;    // entries of col_idx that may be read
   float scale_log2;   // softmax scale * log2(e)
+  int32_t window;     // 0, or w > 0: the grouped view (bf16 / d 128 / tile 128 only)
 };
 
 // Each returns a hipError_t value (0 = success).

@@ -131,25 +131,24 @@ __device__ __forceinline__ int list_len(sconst_i32 row_ptr, int64_t cap, int mro
   return e0 > b0 ? (int)(e0 - b0) : 0;
 }
 
-// Load i (0..7) of a tile fetch: 1 KB of the tile into LDS; the immediate
-// offset 1024 (i % 4) applies to both the global and the LDS address.
+// Load i (0..3) of the first half of a tile fetch: 1 KB of the tile (rows
+// 4i .. 4i+3 of the wave's 16) into LDS.  The immediate offset 1024 i
+// applies to both the global and the LDS address; `step` adds to the global
+// one what rows 4i lie further apart than 1024 bytes (0 for contiguous rows).
 template <int I>
 __device__ __forceinline__ void fetch_load(__amdgpu_buffer_rsrc_t rs, lds_char_t* buf, int wg,
-                                           uint32_t voff, uint32_t toff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(buf + (8 * wg + 4 * (I >> 2)) * 1024),
-                                           16, voff, toff + 4096 * (I >> 2), 1024 * (I & 3), 0);
+                                           uint32_t voff, uint32_t toff, uint32_t step) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(buf + 8 * wg * 1024), 16, voff,
+                                           toff + I * step, 1024 * I, 0);
 }
 __device__ __forceinline__ void fetch_load_i(int i, __amdgpu_buffer_rsrc_t rs, lds_char_t* buf,
-                                             int wg, const uint32_t* ld_off, uint32_t toff) {
+                                             int wg, const uint32_t* ld_off, uint32_t toff,
+                                             uint32_t step) {
   switch (i) {  // resolved at compile time: every caller's loop is unrolled
-    case 0: fetch_load<0>(rs, buf, wg, ld_off[0], toff); break;
-    case 1: fetch_load<1>(rs, buf, wg, ld_off[1], toff); break;
-    case 2: fetch_load<2>(rs, buf, wg, ld_off[2], toff); break;
-    case 3: fetch_load<3>(rs, buf, wg, ld_off[3], toff); break;
-    case 4: fetch_load<4>(rs, buf, wg, ld_off[0], toff); break;
-    case 5: fetch_load<5>(rs, buf, wg, ld_off[1], toff); break;
-    case 6: fetch_load<6>(rs, buf, wg, ld_off[2], toff); break;
-    default: fetch_load<7>(rs, buf, wg, ld_off[3], toff); break;
+    case 0: fetch_load<0>(rs, buf, wg, ld_off[0], toff, step); break;
+    case 1: fetch_load<1>(rs, buf, wg, ld_off[1], toff, step); break;
+    case 2: fetch_load<2>(rs, buf, wg, ld_off[2], toff, step); break;
+    default: fetch_load<3>(rs, buf, wg, ld_off[3], toff, step); break;
   }
 }
 
@@ -181,6 +180,29 @@ __device__ __forceinline__ void dma_burst4(const i32x4& rs, uint32_t m0, const u
         "{m0}"(m0)
       : "memory", "scc");
 }
+// The same four loads when consecutive rows of a tile lie `row stride`
+// bytes apart in memory (the grouped view): load k takes the scalar offset
+// soff + k * step, step = 4 * row stride - 1024, so that with the immediate
+// 1024 k it reaches rows 4k further on while the LDS address still advances
+// by 1024 k from the one M0.
+__device__ __forceinline__ void dma_burst4_strided(const i32x4& rs, uint32_t m0,
+                                                   const uint32_t* voff, uint32_t soff,
+                                                   uint32_t step, uint32_t skip) {
+  const uint32_t s1 = soff + step, s2 = soff + 2 * step, s3 = soff + 3 * step;
+  asm volatile(
+      "s_cmp_eq_u32 %0, 0\n\t"
+      "s_cbranch_scc0 .Lbsattn_skips_%=\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %5, %6 offen offset:0 lds\n\t"
+      "buffer_load_dwordx4 %2, %5, %7 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %3, %5, %8 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %4, %5, %9 offen offset:3072 lds\n"
+      ".Lbsattn_skips_%=:"
+      :
+      : "s"(skip), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rs), "s"(soff),
+        "s"(s1), "s"(s2), "s"(s3), "{m0}"(m0)
+      : "memory", "scc");
+}
 __device__ __forceinline__ i32x4 raw_rsrc(const void* base, int nbytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   i32x4 r;
@@ -206,6 +228,12 @@ __device__ __forceinline__ bool ent_in(int e, int grp) {
   return e >= 0 && ((e >> (30 - grp)) & 1);
 }
 
+// GRP: the grouped view (a.window = w > 0, G = N / w a multiple of 128):
+// attention runs over the position-major order of the windows of w tokens,
+// position p = r * G + c standing for buffer row c * w + r, so tile t is the
+// 128 buffer rows from row0(t) = (128 t mod G) * w + 128 t / G on at stride
+// w.  Every address below goes through that map; the arithmetic is the same.
+template <bool GRP>
 __global__ void __launch_bounds__(512, 1)
 fwd_bf16_t128_d128(FwdLaunch a) {
   // K slots [0, 32K) and [32K, 64K) of a 64 KB-aligned array, so one XOR of
@@ -287,6 +315,12 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   const int h = bh % a.H;
   const int N = a.N;
   const int64_t head_row = (int64_t)bh * N;
+  const int gw = GRP ? a.window : 1;
+  const int gG = GRP ? N / a.window : 1;
+  // buffer row of the first row of position-major tile t; rows of a tile are
+  // RS bytes apart
+  auto row0 = [&](int t) INLINE { return GRP ? ((t * BT) % gG) * gw + (t * BT) / gG : t * BT; };
+  const uint32_t RS = (uint32_t)gw * ROW_BYTES;
 
   // ---- active lists of both groups, merged on the fly (scalar, identical
   // in every wave)
@@ -379,7 +413,8 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   bf16x8 qf[8];
   auto load_q = [&](int tq) INLINE {
     const int qr = tq * BT + wg * 32 + l32;
-    const __bf16* qptr = reinterpret_cast<const __bf16*>(a.q) + (head_row + qr) * D + half * 8;
+    const int64_t qb = GRP ? (int64_t)row0(tq) + (int64_t)(wg * 32 + l32) * gw : qr;
+    const __bf16* qptr = reinterpret_cast<const __bf16*>(a.q) + (head_row + qb) * D + half * 8;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       if (tq < a.tiles && qr < N) {
@@ -411,10 +446,10 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   for (int i4 = 0; i4 < 4; ++i4) {
     const int r = 32 * wg + (lane >> 4);
     const int c = (lane & 15) ^ (((lane >> 4) << 2) | i4);
-    ld_off[i4] = (uint32_t)(r * ROW_BYTES + c * 16);
+    ld_off[i4] = (uint32_t)r * RS + (uint32_t)(c * 16);
   }
   auto tile_off = [&](int j) INLINE {
-    return (j >= 0 && j < a.tiles) ? (uint32_t)j * TILE_BYTES : 0x80000000u;
+    return (j >= 0 && j < a.tiles) ? (uint32_t)row0(j) * ROW_BYTES : 0x80000000u;
   };
 
   // Per-lane LDS read addresses of slot 0 (K) and slot 1 (V) (base folded in
@@ -637,7 +672,11 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       const uint32_t buf = (part < 2 ? kbuf : vbuf) + (uint32_t)(8 * wg * 1024);
       const uint32_t to = part < 2 ? tko : tvo;
       // loads 4(part%2) .. +3: rows 16(part%2) .. of this wave's 32-row share
-      dma_burst4(rs, buf + (part & 1) * 4096, ld_off, to + (part & 1) * 4096, skip);
+      if constexpr (GRP)
+        dma_burst4_strided(rs, buf + (part & 1) * 4096, ld_off, to + (part & 1) * 16 * RS,
+                           4 * RS - 1024, skip);
+      else
+        dma_burst4(rs, buf + (part & 1) * 4096, ld_off, to + (part & 1) * 4096, skip);
       __builtin_amdgcn_sched_barrier(0);
     };
     if (do_sm) {
@@ -659,7 +698,8 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       const uint32_t t0 = tile_off(ent_tile(e));
       lds_char_t* dst = kl + (grp * 4) * 1024;  // group g loads rows 16g.. of each 64-row half
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fetch_load_i(i, krs, dst, wg, ld_off, t0 + grp * 4096);
+      for (int i = 0; i < 4; ++i)
+        fetch_load_i(i, krs, dst, wg, ld_off, t0 + grp * 16 * RS, GRP ? 4 * RS - 1024 : 0);
     }
     // as a builtin, so the compiler knows every load before the loop is done
     // and inserts no wait of its own inside it
@@ -672,7 +712,8 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   auto store_o = [&](int tq, float inv, int db0, int ndb) INLINE {
     const int qr = tq * BT + wg * 32 + l32;
     if (tq < a.tiles && qr < N) {
-      __bf16* op = reinterpret_cast<__bf16*>(a.o) + (head_row + qr) * D;
+      const int64_t qb = GRP ? (int64_t)row0(tq) + (int64_t)(wg * 32 + l32) * gw : qr;
+      __bf16* op = reinterpret_cast<__bf16*>(a.o) + (head_row + qb) * D;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         if (db < db0 || db >= db0 + ndb) continue;
@@ -690,8 +731,9 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   };
   auto store_lse = [&](int tq, float mm, float ll) INLINE {
     const int qr = tq * BT + wg * 32 + l32;
+    const int64_t qb = GRP ? (int64_t)row0(tq) + (int64_t)(wg * 32 + l32) * gw : qr;
     if (tq < a.tiles && qr < N && a.lse != nullptr && half == 0)
-      a.lse[head_row + qr] = ll > 0.f ? (mm + log2f(ll)) * 0.69314718055994531f : -INFINITY;
+      a.lse[head_row + qb] = ll > 0.f ? (mm + log2f(ll)) * 0.69314718055994531f : -INFINITY;
   };
   auto l_over_halves = [&]() INLINE {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l),
@@ -910,8 +952,12 @@ fwd_bf16_t128_d128(FwdLaunch a) {
 int launch_fwd_bf16_t128_d128(const FwdLaunch& a, void* stream) {
   // one workgroup per (batch*head, query-tile pair), in either mode
   const int64_t blocks = (int64_t)a.B * a.H * ((a.tiles + 1) / 2);
-  hipLaunchKernelGGL(fwd_bf16_t128_d128, dim3((unsigned)blocks), dim3(512), 0,
-                     (hipStream_t)stream, a);
+  if (a.window > 0)
+    hipLaunchKernelGGL(fwd_bf16_t128_d128<true>, dim3((unsigned)blocks), dim3(512), 0,
+                       (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(fwd_bf16_t128_d128<false>, dim3((unsigned)blocks), dim3(512), 0,
+                       (hipStream_t)stream, a);
   return hipGetLastError();
 }
 

@@ -188,6 +188,27 @@ BSATTN_API int bsattn_fwd(int32_t B, int32_t H, int32_t N, int32_t d,
                           int32_t mask_heads, const int32_t* row_ptr,
                           const int32_t* col_idx, float scale, void* stream);
 
+/* The forward on the grouped view of the tokens: SQuad's global pass
+ * (SQuad page, "1. Operatore di Attenzione SQuad": the tokens at the same
+ * position inside every window of w tokens attend to one another).  With
+ * G = N / window, position-major index p = r * G + c (window c, position r)
+ * stands for buffer row n(p) = c * window + r.  The call computes, for every
+ * p, O[n(p)] = softmax(scale * q[n(p)] K^T) V over the keys n(p') whose
+ * position-major tiles p' / 128 are active for tile p / 128 in the CSR,
+ * which therefore describes the position-major order (for SQuad's global
+ * pass: a block-diagonal mask of G / 128 tiles per block).  It equals
+ * bsattn_window_reorder of q, k and v, then bsattn_fwd, then the inverse
+ * reorder of o (and lse), bit for bit, without the reorders' traffic.
+ * Arguments as bsattn_fwd, plus window (w >= 1).  Supported: bf16, d = 128,
+ * tile = 128, N a multiple of w with G a multiple of 128.
+ * Errors: as bsattn_fwd; UNSUPPORTED for other dtypes or sizes, INVALID_ARG
+ * for window < 1 or N not of that form. */
+BSATTN_API int bsattn_fwd_grouped(int32_t B, int32_t H, int32_t N, int32_t d, int32_t tile,
+                                  int32_t dtype, const void* q, const void* k, const void* v,
+                                  void* o, float* lse, int32_t mask_heads,
+                                  const int32_t* row_ptr, const int32_t* col_idx,
+                                  int32_t window, float scale, void* stream);
+
 /* Reorder token rows between window-major and position-major order (SQuad
  * page, "1. Operatore di Attenzione SQuad": the global pass groups the
  * tokens at the same position inside every window).  With G = N / w:

@@ -88,6 +88,33 @@ def test_fwd_rejects_bad_arguments_without_launching():
     assert bs.lib().bsattn_last_error() == b""
 
 
+def _fwd_grouped(**kw):
+    args = dict(B=1, H=2, N=32768, d=128, tile=128, dtype=0, q=64, k=64, v=64, o=64,
+                lse=None, mask_heads=1, row_ptr=64, col_idx=64, window=256, scale=0.0)
+    args.update(kw)
+    L = bs.lib()
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.bsattn_fwd_grouped(args["B"], args["H"], args["N"], args["d"], args["tile"],
+                                args["dtype"], p(args["q"]), p(args["k"]), p(args["v"]),
+                                p(args["o"]), p(args["lse"]), args["mask_heads"],
+                                p(args["row_ptr"]), p(args["col_idx"]), args["window"],
+                                args["scale"], None)
+
+
+def test_fwd_grouped_rejects_bad_arguments_without_launching():
+    assert _fwd_grouped(d=64) == bs.ERR_UNSUPPORTED
+    assert _fwd_grouped(tile=64) == bs.ERR_UNSUPPORTED
+    assert _fwd_grouped(dtype=1) == bs.ERR_UNSUPPORTED
+    assert _fwd_grouped(window=0) == bs.ERR_INVALID_ARG
+    assert _fwd_grouped(N=32760, window=256) == bs.ERR_INVALID_ARG   # not a multiple of w
+    assert _fwd_grouped(N=1000, window=10) == bs.ERR_INVALID_ARG     # G = 100
+    assert b"multiple of 128" in bs.lib().bsattn_last_error()
+    assert _fwd_grouped(q=None) == bs.ERR_INVALID_ARG
+    assert _fwd_grouped(mask_heads=3) == bs.ERR_INVALID_ARG
+    assert _fwd_grouped(B=0, q=None, k=None, v=None, o=None, row_ptr=None,
+                        col_idx=None) == bs.OK
+
+
 def test_build_mask_rejects_bad_arguments():
     L = bs.lib()
     ok_layout = bs.Layout(4, 8, 8, 64)

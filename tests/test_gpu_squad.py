@@ -70,3 +70,56 @@ def test_squad_rejects_misaligned_windows():
     q = torch.zeros(1, 1, 1000, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
         bs.squad(q, q, q, 100, 64)
+
+
+@pytest.mark.parametrize("N,w,H,mask", [(32768, 256, 2, "block"), (16384, 128, 2, "block"),
+                                        (16384, 1, 1, "static"), (32768, 256, 12, "static_h"),
+                                        (65536, 512, 1, "dense"), (16384, 128, 3, "empty")])
+def test_fwd_grouped_equals_reorder_fwd_reorder(N, w, H, mask):
+    """bsattn_fwd_grouped gives, bit for bit, what the window reorder of q,
+    k and v, bsattn_fwd and the inverse reorder of o and lse give, for
+    block-diagonal (SQuad's global pass), static (one mask and one per
+    head), dense and empty masks; w = 1 is the identity view."""
+    g = torch.Generator().manual_seed(N + w + H)
+    q, k, v = (torch.randn(1, H, N, 128, generator=g).to(torch.bfloat16).cuda()
+               for _ in range(3))
+    G = N // w
+    T = N // 128
+    hm = H if mask == "static_h" else 1
+    if mask == "block":
+        m = bs.make_mask(1, 1, N, 128, kind=W.MASK_BLOCK_DIAGONAL, block_tiles=G // 128)
+    elif mask in ("static", "static_h"):
+        m = bs.make_mask(1, 1, N, 128, kind=W.MASK_STATIC_RANDOM, seed=7,
+                         thresh24=W.thresh24_for_density(0.2), force_diagonal=1, mask_heads=hm)
+    elif mask == "dense":
+        m = bs.make_mask(1, 1, N, 128, kind=W.MASK_DENSE)
+    else:
+        m = torch.zeros(1, T, T, dtype=torch.uint8, device="cuda")
+    rp, ci = bs.make_csr(m)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    bs.fwd_grouped(q, k, v, o, rp, ci, w, mask_heads=hm, lse=lse)
+    qp, kp, vp = (torch.empty_like(x) for x in (q, k, v))
+    for src, dst in ((q, qp), (k, kp), (v, vp)):
+        bs.window_reorder(src, dst, w)
+    op = torch.empty_like(q)
+    lp = torch.empty_like(lse)
+    bs.fwd(qp, kp, vp, op, rp, ci, 128, mask_heads=hm, lse=lp)
+    ref = torch.empty_like(op)
+    bs.window_reorder(op, ref, w, inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref)
+    lref = lp.view(1, H, w, G).transpose(2, 3).reshape(1, H, N)   # position-major -> buffer
+    assert torch.equal(lse, lref)
+    if mask == "empty":
+        assert (o == 0).all() and torch.isinf(lse).all()
+
+
+def test_squad_grouped_equals_reordered_path():
+    w = W.SQUAD
+    q, k, v = W.make_qkv(w)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    a = bs.squad(q, k, v, W.SQUAD_W, w.tile, grouped=True)
+    b = bs.squad(q, k, v, W.SQUAD_W, w.tile, grouped=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
