@@ -94,6 +94,8 @@ constexpr float TAU = 8.0f;                 // lazy-rescale threshold (log2 unit
 constexpr int NXCD = 8;
 constexpr int PF = 4;                       // MFMA operand read-ahead (steps)
 constexpr int LPT_CHUNK = 32;               // workgroups ordered longest-first together
+constexpr int DEAL_MAX = 4096;              // per-head masks: items ranked globally (LDS keys)
+constexpr int DEAL_TILES = 4095;            // ... and key bins 0 .. 2 * tiles in 32 KB of LDS
 
 // Lambdas are forced inline: an outlined lambda would reach its captures
 // through memory and turn every buffer resource into a waterfall loop.
@@ -274,8 +276,107 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // Each workgroup ranks its chunk itself (row_ptr differences, one item
   // per thread, ranks by broadcast LDS reads); a malformed row_ptr only
   // changes the order, which stays a permutation.
+  // Per-head masks (Hm = H) differ from head to head, so the contiguous XCD
+  // ranges carry unequal work and a long pair late in a range ends the
+  // launch alone.  There every workgroup ranks all items instead (counting
+  // sort on the list length, ties by position) and the ranks are dealt to
+  // the XCDs round by round in snake order (round s: ranks 8s .. 8s+7 to
+  // XCDs 0..7, reversed on odd rounds; the last, partial round in order),
+  // so every XCD gets an even share, longest first.
   uint32_t logical;
-  {
+  bool deal = a.mask_heads > 1 && G <= (uint32_t)DEAL_MAX && a.tiles <= DEAL_TILES;
+  int* const keys_d = reinterpret_cast<int*>(kslots);  // G list lengths
+  int* const misc = keys_d + DEAL_MAX;                 // scan partials and results
+  int* const cnt_b = reinterpret_cast<int*>(vslots);   // items per length
+  if (deal) {
+    // dealt only when the heads' masks differ in size by over an eighth:
+    // with even heads (a random static mask) the contiguous ranges' shared
+    // key tiles in the L2 are worth more than the balance
+    if (tid < 2) misc[540 + tid] = tid == 0 ? 0x7FFFFFFF : 0;
+    __syncthreads();
+    int hmin = 0x7FFFFFFF, hmax = 0;
+    for (int h = tid; h < a.H; h += 512) {
+      const int64_t nnz = (int64_t)a.row_ptr[(h + 1) * a.tiles] - a.row_ptr[h * a.tiles];
+      const int v = (int)min(max(nnz, (int64_t)0), (int64_t)0x3FFFFFFF);
+      hmin = min(hmin, v);
+      hmax = max(hmax, v);
+    }
+    atomicMin(&misc[540], hmin);
+    atomicMax(&misc[541], hmax);
+    __syncthreads();
+    deal = 8 * (int64_t)misc[541] > 9 * (int64_t)misc[540];
+  }
+  if (deal) {
+    const int nb = 2 * a.tiles + 1;
+    for (int b = tid; b < nb; b += 512) cnt_b[b] = 0;
+    __syncthreads();
+    for (uint32_t i = (uint32_t)tid; i < G; i += 512) {
+      const uint32_t bhi = i / pairs;
+      const int qt = 2 * (int)(i % pairs);
+      const int hr = (int)(bhi % (uint32_t)a.H) * a.tiles;
+      const int64_t len = (int64_t)a.row_ptr[hr + min(qt + 2, a.tiles)] - a.row_ptr[hr + qt];
+      const int key = (int)min(max(len, (int64_t)0), (int64_t)2 * a.tiles);
+      keys_d[i] = key;
+      atomicAdd(&cnt_b[key], 1);
+    }
+    __syncthreads();
+    int* const keys = keys_d;
+    int* const start_b = cnt_b + 8192;                 // items longer than each length
+    // start_b[b] = items with a length above b: thread t sums its run of
+    // bins taken from the top, the runs' sums are scanned, then spread
+    const int per = (nb + 511) / 512;
+    const int q0 = min(tid * per, nb), q1 = min(q0 + per, nb);
+    int sum = 0;
+    for (int qq = q0; qq < q1; ++qq) sum += cnt_b[nb - 1 - qq];
+    misc[tid] = sum;
+    __syncthreads();
+    for (int dd = 1; dd < 512; dd <<= 1) {
+      const int add = tid >= dd ? misc[tid - dd] : 0;
+      __syncthreads();
+      misc[tid] += add;
+      __syncthreads();
+    }
+    int run = tid > 0 ? misc[tid - 1] : 0;
+    for (int qq = q0; qq < q1; ++qq) {
+      const int b = nb - 1 - qq;
+      start_b[b] = run;
+      run += cnt_b[b];
+    }
+    __syncthreads();
+    const uint32_t rounds = G / NXCD;
+    const int rho = (int)(slot < rounds ? slot * NXCD + ((slot & 1) ? NXCD - 1 - xcd : xcd) : hw);
+    for (int b = tid; b < nb; b += 512) {
+      const int c = cnt_b[b], st = start_b[b];
+      if (c > 0 && rho >= st && rho < st + c) {
+        misc[512] = b;
+        misc[513] = rho - st;
+      }
+    }
+    __syncthreads();
+    const int kstar = misc[512], ostar = misc[513];
+    // the ostar-th item in index order among those of length kstar
+    const uint64_t below = (1ull << lane) - 1;
+    int base = 0;
+    for (uint32_t i0 = 0; i0 < G; i0 += 512) {
+      const uint32_t i = i0 + (uint32_t)tid;
+      const bool f = i < G && keys[i] == kstar;
+      const uint64_t bal = __ballot(f);
+      if (lane == 0) misc[520 + wave] = __popcll(bal);
+      __syncthreads();
+      int wpre = 0, tot = 0;
+      for (int wv = 0; wv < 8; ++wv) {
+        const int c = misc[520 + wv];
+        wpre += wv < wave ? c : 0;
+        tot += c;
+      }
+      if (f && base + wpre + __popcll(bal & below) == ostar) misc[530] = (int)i;
+      base += tot;
+      __syncthreads();  // the wave counts are rewritten by the next block
+      if (base > ostar) break;
+    }
+    logical = (uint32_t)__builtin_amdgcn_readfirstlane(misc[530]);
+    __syncthreads();  // the LDS is refilled by tile fetches below
+  } else {
     int* const keys = reinterpret_cast<int*>(kslots);
     int* const pick = keys + LPT_CHUNK;
     const uint32_t c0 = (slot / LPT_CHUNK) * LPT_CHUNK;
