@@ -60,7 +60,12 @@
 //     other group's MFMA stream they would stall the softmax.
 //   * Workgroups are remapped so each XCD (own L2) walks a contiguous range
 //     of (head, query-tile pair); neighbouring query tiles share most of
-//     their key tiles.
+//     their key tiles.  Inside a range the longest pairs go first (per chunk
+//     of 32); per-head masks with uneven heads are instead dealt over the
+//     XCDs globally, longest first.
+//   * A second instance reads and writes through the grouped view of the
+//     tokens (SQuad's global pass: the position-major order of windows of w
+//     tokens) instead of contiguous rows; only the addresses differ.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
