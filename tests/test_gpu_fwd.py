@@ -207,6 +207,26 @@ def test_full_size_sampled_rows(cfg, stride):
                  lse_tolerance(q, k, m_ref, w.tile, rows, workers=16))
 
 
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_full_size_every_row(cfg):
+    """The 32 760-token workloads (window/anchor at rotation 0; static per
+    head) compared element by element on every output row and head, in the
+    launch configuration the bench times."""
+    from threadpoolctl import threadpool_limits
+    w = W.WORKLOADS[cfg]
+    q, k, v, mask, rp, ci, o, lse = run_gpu(w)
+    m_ref = check_mask_csr(w, mask, rp, ci)
+    rows = np.arange(w.N)
+    # 16 oracle workers, one BLAS thread each (no oversubscription)
+    with threadpool_limits(limits=1):
+        o_ref, lse_ref = oracle.block_sparse_attention(q.cpu(), k.cpu(), v.cpu(), m_ref,
+                                                       w.tile, workers=16)
+        print(f"  oracle done for {w.name}", flush=True)
+        tol = lse_tolerance(q, k, m_ref, w.tile, rows, workers=16)
+    assert_close(f"{w.name} (all {w.N} rows x {w.B * w.H} heads)", to64(o), o_ref,
+                 to64(lse), lse_ref, tol)
+
+
 def test_tuned_kernel_pair_and_split_lists_and_bad_indices():
     """bf16 / d 128 / tile 128 (the tuned kernel) on hand-built lists whose
     query-tile pairs have identical, disjoint, empty, nearly identical and
