@@ -92,8 +92,18 @@ def block_sparse_attention_rows(q, k, v, mask, tile: int, rows,
         lse[b, h, c0:c0 + len(ids)] = lc
 
     if workers > 1:
-        with ThreadPoolExecutor(workers) as ex:
-            list(ex.map(run, jobs))
+        # one BLAS thread per worker thread: the workers already fill the
+        # cores, and nested BLAS threads would oversubscribe them
+        try:
+            from threadpoolctl import threadpool_limits
+        except ImportError:  # pragma: no cover
+            threadpool_limits = None
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+                list(ex.map(run, jobs))
+        else:  # pragma: no cover
+            with ThreadPoolExecutor(workers) as ex:
+                list(ex.map(run, jobs))
     else:
         for job in jobs:
             run(job)
