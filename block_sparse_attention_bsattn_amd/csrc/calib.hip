@@ -70,7 +70,7 @@ block_energy_kernel(EnergyLaunch a) {
   constexpr int KP = D + 8;            // K row pitch in LDS (bf16)
   constexpr int PER = BT * D / 8 / NT; // 8-element chunks of a tile per thread
   __shared__ __bf16 Ks[BT * KP];
-  __shared__ float wsum[NW];
+  __shared__ float wsum[2][NW];  // per-wave tile sums, by tile parity
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -193,10 +193,20 @@ block_energy_kernel(EnergyLaunch a) {
   l += __shfl_xor(l, 32);
   const float L = m + log2f(l);  // log2 of the row's normaliser (in x units)
 
-  // ---- sweep 2: probabilities summed per key tile
+  // ---- sweep 2: probabilities summed per key tile.  The waves' sums of
+  // tile j are added (and E written) by thread 0 after the next tile's
+  // first barrier, so no barrier of its own is needed.
+  float* const erow = a.energy + (((int64_t)b * a.H + h) * T + qt) * T;
+  auto write_tile = [&](int j) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t += wsum[j & 1][w];
+    erow[j] = t;
+  };
   fetch(0);
   for (int j = 0; j < T; ++j) {
     __syncthreads();
+    if (tid == 0 && j > 0) write_tile(j - 1);
     stage();
     __syncthreads();
     fetch(j + 1);
@@ -212,15 +222,10 @@ block_energy_kernel(EnergyLaunch a) {
     if (!row_ok) ps = 0.f;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off);
-    if (lane == 0) wsum[wave] = ps;
-    __syncthreads();
-    if (tid == 0) {
-      float t = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) t += wsum[w];
-      a.energy[(((int64_t)b * a.H + h) * T + qt) * T + j] = t;
-    }
+    if (lane == 0) wsum[j & 1][wave] = ps;
   }
+  __syncthreads();
+  if (tid == 0 && T > 0) write_tile(T - 1);
 }
 
 template <int BT, int D, bool F32IN>
