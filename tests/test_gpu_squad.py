@@ -72,16 +72,19 @@ def test_squad_rejects_misaligned_windows():
         bs.squad(q, q, q, 100, 64)
 
 
-@pytest.mark.parametrize("N,w,H,mask", [(32768, 256, 2, "block"), (16384, 128, 2, "block"),
-                                        (16384, 1, 1, "static"), (32768, 256, 12, "static_h"),
-                                        (65536, 512, 1, "dense"), (16384, 128, 3, "empty")])
-def test_fwd_grouped_equals_reorder_fwd_reorder(N, w, H, mask):
+@pytest.mark.parametrize("N,w,H,B,mask", [(32768, 256, 2, 1, "block"), (16384, 128, 2, 2, "block"),
+                                          (16384, 1, 1, 1, "static"),
+                                          (32768, 256, 12, 1, "static_h"),
+                                          (16384, 64, 3, 2, "static_h"),
+                                          (65536, 512, 1, 1, "dense"),
+                                          (16384, 128, 3, 1, "empty")])
+def test_fwd_grouped_equals_reorder_fwd_reorder(N, w, H, B, mask):
     """bsattn_fwd_grouped gives, bit for bit, what the window reorder of q,
     k and v, bsattn_fwd and the inverse reorder of o and lse give, for
     block-diagonal (SQuad's global pass), static (one mask and one per
     head), dense and empty masks; w = 1 is the identity view."""
-    g = torch.Generator().manual_seed(N + w + H)
-    q, k, v = (torch.randn(1, H, N, 128, generator=g).to(torch.bfloat16).cuda()
+    g = torch.Generator().manual_seed(N + w + H + B)
+    q, k, v = (torch.randn(B, H, N, 128, generator=g).to(torch.bfloat16).cuda()
                for _ in range(3))
     G = N // w
     T = N // 128
@@ -109,7 +112,7 @@ def test_fwd_grouped_equals_reorder_fwd_reorder(N, w, H, mask):
     bs.window_reorder(op, ref, w, inverse=True)
     torch.cuda.synchronize()
     assert torch.equal(o, ref)
-    lref = lp.view(1, H, w, G).transpose(2, 3).reshape(1, H, N)   # position-major -> buffer
+    lref = lp.view(B, H, w, G).transpose(2, 3).reshape(B, H, N)   # position-major -> buffer
     assert torch.equal(lse, lref)
     if mask == "empty":
         assert (o == 0).all() and torch.isinf(lse).all()
