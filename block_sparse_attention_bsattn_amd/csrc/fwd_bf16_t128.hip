@@ -485,34 +485,43 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // after the other, both groups on the same tile, taking alternate list
   // entries.  A split phase costs about 1.6 pair phases (each staged tile
   // serves half the rows, and a fetch has one phase to land instead of
-  // two), so split mode is taken below 40 % estimated overlap, and always
-  // when one list is empty.  The overlap is estimated on the first 8
-  // entries of both lists; the choice affects speed only.
+  // two).  With I entries common to both lists, pair mode runs
+  // n0 + n1 - I phases and split mode about 0.8 (n0 + n1) pair-phase
+  // equivalents, so split mode is taken when 5 I < n0 + n1, and always when
+  // one list is empty.  I is counted exactly, all threads at once: list B's
+  // tiles set bits of a bitmap in the (still unused) V slots, then list A's
+  // entries test them.  The choice affects speed only.
   bool split;
   {
-    constexpr int KS = 8;
-    const int ks_ = min(min(n0, n1), KS);
-    int va[KS], vb[KS];
-#pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      va[i] = n0 > 0 ? col_idx[jb0 + min(i, n0 - 1)] : 0;
-      vb[i] = n1 > 0 ? col_idx[jb1 + min(i, n1 - 1)] : 0;
-    }
-    int ia = 0, ib = 0, match = 0;
-#pragma unroll
-    for (int st = 0; st < 2 * KS; ++st) {
-      int x = va[0], y = vb[0];
-#pragma unroll
-      for (int i = 1; i < KS; ++i) {
-        x = ia == i ? va[i] : x;
-        y = ib == i ? vb[i] : y;
+    uint32_t* const bits = reinterpret_cast<uint32_t*>(vslots);
+    constexpr int BW = 2 * TILE_BYTES / 4 - 1;  // bitmap words; the last one counts
+    uint32_t* const common = bits + BW;
+    const int nw = (a.tiles + 31) >> 5;
+    const int nthr = (int)blockDim.x;
+    if (n0 > 0 && n1 > 0 && nw <= BW) {
+      for (int c = tid; c < nw; c += nthr) bits[c] = 0u;
+      if (tid == 0) *common = 0u;
+      __syncthreads();
+      for (int i = tid; i < n1; i += nthr) {
+        const int t = col_idx[jb1 + i];
+        if (t >= 0 && t < a.tiles) atomicOr(&bits[t >> 5], 1u << (t & 31));
       }
-      const bool live = ia < ks_ && ib < ks_;
-      match += (live && x == y) ? 1 : 0;
-      ia += (live && x <= y) ? 1 : 0;
-      ib += (live && y <= x) ? 1 : 0;
+      __syncthreads();
+      int hits = 0;
+      for (int i = tid; i < n0; i += nthr) {
+        const int t = col_idx[jb0 + i];
+        hits += (t >= 0 && t < a.tiles && ((bits[t >> 5] >> (t & 31)) & 1u)) ? 1 : 0;
+      }
+      // sum over the wave, then one LDS add per wave
+      for (int o = 32; o > 0; o >>= 1) hits += __shfl_xor(hits, o, 64);
+      if (lane == 0 && hits > 0) atomicAdd(common, (uint32_t)hits);
+      __syncthreads();
+      const int shared_n = __builtin_amdgcn_readfirstlane((int)*common);
+      split = 5 * shared_n < n0 + n1;
+      __syncthreads();  // the V slots are refilled by tile fetches below
+    } else {
+      split = n0 == 0 || n1 == 0;
     }
-    split = ks_ == 0 || 5 * match < 2 * ks_;
   }
 
   // ---- Q^T operand: lane holds q[row l%32][8 d values], 8 chunks of 16 d
