@@ -331,8 +331,8 @@ def repetition_leg(bs, W, torch, dev, calls: int):
     torch.cuda.synchronize()
     cos_ms = ev[0].elapsed_time(ev[1])
     nonanchor = w.grid_h - (-(-w.grid_h // stride))
-    # two sweeps x two queries x (non-anchor rows x grid_w) x N keys x 2d
-    cos_flops = 2 * 2 * w.B * w.H * w.frames * nonanchor * w.grid_w * w.N * 2.0 * w.d
+    # one sweep x two queries x (non-anchor rows x grid_w) x N keys x 2d
+    cos_flops = 2 * w.B * w.H * w.frames * nonanchor * w.grid_w * w.N * 2.0 * w.d
     bs.repeated_attention(q, k, v, w.frames, w.grid_h, w.grid_w, stride, w.tile)
     re = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(calls)]

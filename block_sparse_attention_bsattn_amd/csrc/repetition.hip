@@ -12,10 +12,12 @@
 // small kernel of their own).  Lane (x, half) holds two queries, q1 = (f, y, x) and its
 // anchor q2 = (f, a(y), x), and 64 keys of each 128-key tile, as in the
 // forward's S^T = K Q^T mapping; each K operand read from LDS feeds the
-// MFMAs of both queries, 64 keys at a time.  Sweep 1 gives each query's
-// normaliser (online max and sum, per-step partial sums); sweep 2 recomputes
-// both score rows and accumulates, per column, sum_k p1 p2, sum_k p1^2 and
-// sum_k p2^2.
+// MFMAs of both queries, 64 keys at a time.  One sweep over the keys keeps,
+// per query, an online max m and, relative to it, the normaliser
+// z = sum_k e (e = 2^(s log2(e) scale - m)) and, per column, the raw sums
+// sum_k e1 e2, sum_k e1^2 and sum_k e2^2, all rescaled when a max grows;
+// dividing by z1 z2, z1^2 and z2^2 at the end gives sum_k p1 p2,
+// sum_k p1^2 and sum_k p2^2 of the probability rows.
 // The workgroup adds its columns (shuffles, then LDS) and writes
 //   cos(y) = sum_x <p1, p2> / sqrt(sum_x |p1|^2 * sum_x |p2|^2);
 // anchor rows get exactly 1.  No N x N matrix is ever stored.
@@ -177,73 +179,66 @@ row_cosine_kernel(RowCosLaunch a) {
     }
   };
   const float c2 = a.scale_log2;
-  // one online-softmax step over 64 keys (32 per lane, both halves)
-  auto online = [&](const f32x16* s, float& m, float& l) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[u][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
-    const float m_new = fmaxf(m, mx);
-    const float alpha = (m_new == m) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
-    float lt = 0.f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      float lk = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) lk += __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][e], c2, -m));
-      lt += lk;
-    }
-    l = l * alpha + lt;
-  };
-
-  // ---- sweep 1: each query's normaliser
+  // per lane (one query column, one half of the keys): max m, normaliser z
+  // and the raw sums, relative to m; both halves share m
   f32x16 a1[2], a2[2];
-  float m1 = -INFINITY, l1 = 0.f, m2 = -INFINITY, l2 = 0.f;
+  float m1 = -INFINITY, z1 = 0.f, m2 = -INFINITY, z2 = 0.f;
+  float s12 = 0.f, s11 = 0.f, s22 = 0.f;
   for (int j = 0; j < tiles; ++j) {
     stage(j);
     if (!active) continue;
 #pragma unroll
     for (int kb0 = 0; kb0 < KB; kb0 += 2) {
       scores2(a1, a2, j, kb0);
-      online(a1, m1, l1);
-      online(a2, m2, l2);
-    }
-  }
-  l1 += __shfl_xor(l1, 32);
-  l2 += __shfl_xor(l2, 32);
-  const float L1 = m1 + log2f(l1), L2 = m2 + log2f(l2);
-
-  // ---- sweep 2: the three inner products of the probability rows
-  float d12 = 0.f, d11 = 0.f, d22 = 0.f;
-  for (int j = 0; j < tiles; ++j) {
-    stage(j);
-    if (!active) continue;
-    float t12 = 0.f, t11 = 0.f, t22 = 0.f;
-#pragma unroll
-    for (int kb0 = 0; kb0 < KB; kb0 += 2) {
-      scores2(a1, a2, j, kb0);
+      float mx1 = -INFINITY, mx2 = -INFINITY;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(a1[u][e], c2, -L1));
-          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(a2[u][e], c2, -L2));
-          t12 = __builtin_fmaf(p1, p2, t12);
-          t11 = __builtin_fmaf(p1, p1, t11);
-          t22 = __builtin_fmaf(p2, p2, t22);
+          mx1 = fmaxf(mx1, a1[u][e]);
+          mx2 = fmaxf(mx2, a2[u][e]);
         }
+      mx1 = fmaxf(mx1, __shfl_xor(mx1, 32)) * c2;
+      mx2 = fmaxf(mx2, __shfl_xor(mx2, 32)) * c2;
+      // key 0 is in the first step, so m is finite from then on
+      const float n1 = fmaxf(m1, mx1), n2 = fmaxf(m2, mx2);
+      const float al1 = (n1 == m1) ? 1.f : __builtin_amdgcn_exp2f(m1 - n1);
+      const float al2 = (n2 == m2) ? 1.f : __builtin_amdgcn_exp2f(m2 - n2);
+      m1 = n1;
+      m2 = n2;
+      z1 *= al1;
+      z2 *= al2;
+      s12 *= al1 * al2;
+      s11 *= al1 * al1;
+      s22 *= al2 * al2;
+      float t1 = 0.f, t2 = 0.f, t12 = 0.f, t11 = 0.f, t22 = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(a1[u][e], c2, -m1));
+          const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(a2[u][e], c2, -m2));
+          t1 += e1;
+          t2 += e2;
+          t12 = __builtin_fmaf(e1, e2, t12);
+          t11 = __builtin_fmaf(e1, e1, t11);
+          t22 = __builtin_fmaf(e2, e2, t22);
+        }
+      z1 += t1;
+      z2 += t2;
+      s12 += t12;
+      s11 += t11;
+      s22 += t22;
     }
-    d12 += t12;
-    d11 += t11;
-    d22 += t22;
   }
-  // both halves of a column, then the wave's 32 columns, then the waves
-  d12 += __shfl_xor(d12, 32);
-  d11 += __shfl_xor(d11, 32);
-  d22 += __shfl_xor(d22, 32);
+  // both halves of a column (same m), then the probability-row sums
+  z1 += __shfl_xor(z1, 32);
+  z2 += __shfl_xor(z2, 32);
+  s12 += __shfl_xor(s12, 32);
+  s11 += __shfl_xor(s11, 32);
+  s22 += __shfl_xor(s22, 32);
+  float d12 = s12 / (z1 * z2), d11 = s11 / (z1 * z1), d22 = s22 / (z2 * z2);
+  // then the wave's 32 columns, then the waves
   if (!col_ok) d12 = d11 = d22 = 0.f;
 #pragma unroll
   for (int off = 16; off >= 1; off >>= 1) {
