@@ -48,6 +48,32 @@ def test_row_cosines(B, H, T, gh, gw, d, s, dt):
     assert (got[:, :, :, anchors] == 1.0).all()
 
 
+@pytest.mark.parametrize("scale", [0.0, 0.25])
+def test_row_cosines_rising_scores(scale):
+    """Keys ordered so that every query's scores grow with the key index: the
+    running max of each query rises at almost every 64-key step, so the
+    normalisers and inner products are rescaled many times over the sweep
+    (and, at scale 0.25, the softmax is sharp)."""
+    B, H, T, gh, gw, d, s = 1, 2, 3, 5, 40, 128, 2
+    N = T * gh * gw
+    g = torch.Generator().manual_seed(2024)
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    q = torch.randn(B, H, N, d, generator=g) * 0.5 + 2.0 * u
+    ramp = torch.linspace(-8.0, 8.0, N).reshape(1, 1, N, 1)
+    k = torch.randn(B, H, N, d, generator=g) * 0.5 + ramp * u
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    cos = torch.empty(B, H, T, gh, dtype=torch.float32, device="cuda")
+    bs.row_cosines(q.cuda(), k.cuda(), T, gh, gw, s, cos, scale=scale)
+    torch.cuda.synchronize()
+    want = oracle.row_cosines(q, k, T, gh, gw, s, scale=scale if scale > 0 else None)
+    got = cos.cpu().numpy()
+    err = float(np.abs(got - want).max())
+    print(f"cos rising scores scale {scale}: max|dcos| {err:.2e} "
+          f"range [{float(want.min()):.3f}, {float(want.max()):.3f}]", flush=True)
+    assert err <= COS_TOL
+
+
 def test_row_cosines_of_repeated_rows_are_one():
     B, H, T, gh, gw, d = 1, 2, 2, 6, 24, 128
     q, k = _qk(B, H, T, gh, gw, d, 7)
