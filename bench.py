@@ -322,14 +322,16 @@ def repetition_leg(bs, W, torch, dev, calls: int):
     cos = torch.empty((w.B, w.H, w.frames, w.grid_h), dtype=torch.float32, device=dev)
     flags = torch.empty(w.H, dtype=torch.uint8, device=dev)
     bs.row_cosines(q, k, w.frames, w.grid_h, w.grid_w, stride, cos)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    ev[0].record(stream)
-    bs.row_cosines(q, k, w.frames, w.grid_h, w.grid_w, stride, cos, stream=stream)
-    ev[1].record(stream)
-    bs.repetitive_heads(cos, stride, gamma, flags, stream=stream)
-    ev[2].record(stream)
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(calls)]
+    for ev in cev:
+        ev[0].record(stream)
+        bs.row_cosines(q, k, w.frames, w.grid_h, w.grid_w, stride, cos, stream=stream)
+        ev[1].record(stream)
+        bs.repetitive_heads(cos, stride, gamma, flags, stream=stream)
+        ev[2].record(stream)
     torch.cuda.synchronize()
-    cos_ms = ev[0].elapsed_time(ev[1])
+    cos_ms = float(np.median([ev[0].elapsed_time(ev[1]) for ev in cev]))
+    heads_ms = float(np.median([ev[1].elapsed_time(ev[2]) for ev in cev]))
     nonanchor = w.grid_h - (-(-w.grid_h // stride))
     # one sweep x two queries x (non-anchor rows x grid_w) x N keys x 2d
     cos_flops = 2 * w.B * w.H * w.frames * nonanchor * w.grid_w * w.N * 2.0 * w.d
@@ -361,7 +363,7 @@ def repetition_leg(bs, W, torch, dev, calls: int):
             "gamma": gamma,
             "row_cosines_ms": round(cos_ms, 3),
             "row_cosines_tflops": round(cos_flops / (cos_ms * 1e-3) / 1e12, 1),
-            "heads_ms": round(ev[1].elapsed_time(ev[2]), 4),
+            "heads_ms": round(heads_ms, 4),
             "flags": flags.cpu().tolist(),
             "mean_cos_repeating_heads": round(float(c[:, :6, :, 1::2].mean()), 4),
             "mean_cos_other_heads": round(float(c[:, 6:, :, 1::2].mean()), 4),
@@ -369,6 +371,79 @@ def repetition_leg(bs, W, torch, dev, calls: int):
             "repeated_attention_ms": round(rep_ms, 4),
             "dense_ms": round(dense_ms, 4),
             "speedup_vs_dense": round(dense_ms / rep_ms, 2)}
+
+
+# Time at half the bf16 dense peak for each workload's active-block work: the
+# target each record is read against.
+def configs_leg(bs, W, torch, dev, calls: int):
+    """Every 32 760- and 131 040-token workload on its own: mask build,
+    compaction and forward (median of `calls` event-timed calls each, on the
+    launch stream), active TFLOP, TFLOP/s and fraction of the bf16 peak, at
+    rotation 0; then the LVSA page's linear-cost claim ("Complessita") as
+    forward time per active tile-head at 131 040 tokens against 32 760."""
+    stream = torch.cuda.current_stream()
+    recs = {}
+    for key in (2, 3, 4, 5):
+        w = W.WORKLOADS[key]
+        q, k, v = W.make_qkv(w, device=dev)
+        o = torch.empty_like(q)
+        Tn = w.num_tiles
+        Hm = w.mask.mask_heads
+        mask = torch.empty((Hm, Tn, Tn), dtype=torch.uint8, device=dev)
+        row_ptr = torch.empty(Hm * Tn + 1, dtype=torch.int32, device=dev)
+        col_idx = torch.empty(Hm * Tn * Tn, dtype=torch.int32, device=dev)
+        layout = (w.frames, w.grid_h, w.grid_w, w.tile)
+        params = bs.mask_params_of(w.mask)
+
+        def run(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            bs.build_mask(layout, mask, stream=stream, **params)
+            if ev is not None:
+                ev[1].record(stream)
+            bs.compact(mask, row_ptr, col_idx, stream=stream)
+            if ev is not None:
+                ev[2].record(stream)
+            bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, mask_heads=Hm, stream=stream)
+            if ev is not None:
+                ev[3].record(stream)
+
+        run()
+        torch.cuda.synchronize()
+        m_np = mask.cpu().numpy()
+        flops = active_flops(m_np, w)
+        tiles = int(m_np.sum()) * (w.H if Hm == 1 else 1) * w.B
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(calls)]
+        for e in evs:
+            run(e)
+        torch.cuda.synchronize()
+        part = lambda a, b: float(np.median([e[a].elapsed_time(e[b]) for e in evs]))
+        f_ms = part(2, 3)
+        tflops = flops / (f_ms * 1e-3) / 1e12
+        recs[w.name] = {
+            "B": w.B, "H": w.H, "N": w.N, "mask_heads": Hm,
+            "density": round(float(m_np.mean()), 4),
+            "active_tile_heads": tiles,
+            "active_tflop": round(flops / 1e12, 4),
+            "build_mask_us": round(part(0, 1) * 1e3, 2),
+            "compact_us": round(part(1, 2) * 1e3, 2),
+            "fwd_ms_median": round(f_ms, 4),
+            "fwd_tflops": round(tflops, 1),
+            "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "ms_at_half_peak": round(flops / (0.5 * PEAK_BF16_TFLOPS * 1e12) * 1e3, 3),
+            "us_per_active_tile_head": round(f_ms * 1e3 / tiles, 5),
+        }
+        del q, k, v, o, mask, row_ptr, col_idx
+        torch.cuda.empty_cache()
+    short, long_ = recs[W.WORKLOADS[2].name], recs[W.WORKLOADS[4].name]
+    recs["linear_cost_check"] = {
+        "what": "forward time per active tile-head, 131 040 tokens (+-2 + 4 anchors) "
+                "over 32 760 tokens (+-1 + 2 anchors); 1.0 = cost linear in active tiles",
+        "ratio": round(long_["us_per_active_tile_head"] / short["us_per_active_tile_head"], 4),
+        "tokens_ratio": round(long_["N"] / short["N"], 3),
+        "time_ratio": round(long_["fwd_ms_median"] / short["fwd_ms_median"], 3),
+    }
+    return recs
 
 
 def cpu_baseline(w, q, k, v, mask_np, tiles: int, workers: int):
@@ -409,7 +484,7 @@ def cpu_baseline(w, q, k, v, mask_np, tiles: int, workers: int):
     except OSError:
         pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers,
-            "kind": "oracle", "cpu_model": cpu_model,
+            "threads_used": workers, "kind": "oracle", "cpu_model": cpu_model,
             "blas_threads_per_worker": 1 if threadpool_limits is not None else None,
             "sample": f"{len(rows)} query rows ({tiles} of {w.num_tiles} query "
                       f"tiles) x {w.B * w.H} heads at rotation 0, float64 NumPy, "
@@ -440,6 +515,9 @@ def main():
                     help="timed calls of the SQuad two-pass leg (0 = skip)")
     ap.add_argument("--repetition", type=int, default=5,
                     help="timed calls of the spatial-repetition leg (0 = skip)")
+    ap.add_argument("--configs", type=int, default=10,
+                    help="timed calls per workload of the per-config records "
+                         "(0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB "
                          "(byte-counter calibration under a profiler)")
@@ -562,6 +640,8 @@ def main():
     repetition = repetition_leg(bs, W, torch, dev, args.repetition) \
         if args.repetition > 0 else None
 
+    configs = configs_leg(bs, W, torch, dev, args.configs) if args.configs > 0 else None
+
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -575,8 +655,12 @@ def main():
     if args.cpu_tiles > 0:
         bs.build_mask(layout, mask, **bs.mask_params_of(w.with_rotation(0).mask))
         torch.cuda.synchronize()
-        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        # the pool takes every core this process may run on, up to the 16
+        # threads a one-GPU machine grants a job
+        host = len(os.sched_getaffinity(0))
+        workers = max(1, min(16, host))
         cpu = cpu_baseline(w, q, k, v, mask.cpu().numpy(), args.cpu_tiles, workers)
+        cpu["host_cores_visible"] = host
 
     # HBM bytes per launch from the committed PMC summary, if it was taken on
     # this kernel source
@@ -632,6 +716,7 @@ def main():
         round(dense_flops / (dense_ms * 1e-3) / 1e12, 3),
         "speedup_vs_density_1": None if dense_ms is None else
         round(dense_ms / float(fwd_ms.mean()), 3),
+        "configs": configs,
         "density_sweep": sweep,
         "expanded_windows": expanded,
         "calibration": calib,

@@ -3,7 +3,9 @@
 Three summaries:
 
   stats    per-kernel call count and durations from a ``--kernel-trace
-           --stats`` run (the ``*_kernel_stats.csv`` file);
+           --stats`` run (the ``*_kernel_stats.csv`` file), with the mean and
+           median over every launch after a kernel's first from the
+           per-dispatch trace (``*_kernel_trace.csv``);
   mfma     the matrix-core busy fraction and executed bf16 MFMA work of one
            kernel from one ``--pmc`` run (SQ_VALU_MFMA_BUSY_CYCLES,
            GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_BF16);
@@ -48,19 +50,47 @@ def source_sha256(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def _warm_durations(csv_dir: str):
+    """{kernel name: [duration ns of each dispatch after the first]} from the
+    per-dispatch kernel trace, or {} when the trace is missing.  The first
+    launch of a kernel in a process pays one-time costs (code object load,
+    cold caches) that the steady state does not."""
+    try:
+        path = _one(os.path.join(csv_dir, "**", "*kernel_trace.csv"))
+    except FileNotFoundError:
+        return {}
+    per: dict = {}
+    for r in csv.DictReader(open(path)):
+        if not {"Kernel_Name", "Start_Timestamp", "End_Timestamp"} <= r.keys():
+            return {}
+        per.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out = {}
+    for name, lst in per.items():
+        lst.sort()
+        out[name] = [d for _, d in lst[1:]]
+    return out
+
+
 def stats_summary(csv_dir: str, command: str, top: int = 12) -> str:
     path = _one(os.path.join(csv_dir, "**", "*kernel_stats.csv"))
     rows = list(csv.DictReader(open(path)))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    warm = _warm_durations(csv_dir)
     lines = ["# rocprofv3 kernel-trace statistics", "",
              f"command: {command}", "",
-             f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} "
-             f"{'total_ms':>10} {'pct':>6}  kernel"]
+             "warm_avg_us / warm_med_us: every launch after a kernel's first "
+             "(from the per-dispatch trace)", "",
+             f"{'calls':>6} {'avg_us':>10} {'warm_avg_us':>12} {'warm_med_us':>12} "
+             f"{'min_us':>10} {'max_us':>10} {'total_ms':>10} {'pct':>6}  kernel"]
     for r in rows[:top]:
         name = r["Name"]
+        wd = warm.get(name, [])
+        wa = f"{statistics.mean(wd) / 1e3:12.2f}" if wd else f"{'n/a':>12}"
+        wm = f"{statistics.median(wd) / 1e3:12.2f}" if wd else f"{'n/a':>12}"
         if len(name) > 90:
             name = name[:87] + "..."
-        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {wa} {wm} "
                      f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
                      f"{float(r['TotalDurationNs']) / 1e6:10.3f} "
                      f"{float(r['Percentage']):6.2f}  {name}")

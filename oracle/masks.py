@@ -239,8 +239,8 @@ def tile_mask(kind: int, frames: int, grid_h: int, grid_w: int, tile: int,
               mask_heads: int = 1, budget: int = 0,
               block_tiles: int = 1, query_tiles: int = 0) -> np.ndarray:
     """uint8 [Hm, Tq, Tk] tile mask for kind 0 (window + anchors),
-    1 (static random), 2 (dense), 3 (expanded window + anchors),
-    4 (block diagonal), 5 (dense rows) or 6 (spread dense rows)."""
+    1 (static random), 2 (dense), 3 (expanded window + anchors) or
+    4 (block diagonal)."""
     N = frames * grid_h * grid_w
     nt = -(-N // tile)
     if kind == 0:
@@ -254,39 +254,8 @@ def tile_mask(kind: int, frames: int, grid_h: int, grid_w: int, tile: int,
         return tile_mask_dense(mask_heads, nt, nt)
     if kind == 4:
         return tile_mask_block_diagonal(mask_heads, nt, nt, block_tiles)
-    if kind == 5:
-        if query_tiles < 0:
-            raise ValueError("query_tiles must be >= 0")
-        M = np.zeros((mask_heads, nt, nt), dtype=np.uint8)
-        M[:, :query_tiles, :] = 1
-        return M
     if kind == 3:
         M = tile_mask_expanded(frames, grid_h, grid_w, tile, window,
                                num_anchors, rotation, budget)
         return np.repeat(M[None], mask_heads, axis=0)
-    if kind == 6:
-        return tile_mask_dense_rows_spread(mask_heads, N, tile, query_tiles,
-                                           block_tiles)
     raise ValueError(f"unknown mask kind {kind}")
-
-
-def tile_mask_dense_rows_spread(Hm: int, N: int, tile: int, query_tiles: int,
-                                block_tiles: int) -> np.ndarray:
-    """Spread dense-rows mode on N tokens in tiles of `tile`: the dense query
-    tiles of block g (g = 0 .. Rg-1) start at tile floor(g * Pg / Rg) *
-    block_tiles."""
-    if query_tiles < 0 or block_tiles < 1:
-        raise ValueError("query_tiles >= 0 and block_tiles >= 1 required")
-    Tq = -(-N // tile)
-    rg = -(-query_tiles // block_tiles)
-    pg = -(-Tq // block_tiles)
-    if rg > pg:
-        raise ValueError("the blocks do not fit the block slots")
-    M = np.zeros((Hm, Tq, Tq), dtype=np.uint8)
-    placed = 0
-    for g in range(rg):
-        size = min(block_tiles, query_tiles - placed)
-        start = (g * pg // rg) * block_tiles
-        M[:, start:start + size, :] = 1
-        placed += size
-    return M

@@ -120,28 +120,6 @@ def broadcast_anchor_rows(xa, frames: int, grid_h: int, grid_w: int,
     return xa[..., idx, :]
 
 
-def anchor_buffer_rows(na: int, n: int, block_rows: int) -> np.ndarray:
-    """Buffer row of each packed anchor index a = 0 .. na-1: a itself when
-    block_rows is 0; otherwise the packed rows are cut into blocks of
-    block_rows (the last one shorter if need be) and block g starts at row
-    floor(g * Pg / Rg) * block_rows, Rg = ceil(na / block_rows) blocks over
-    Pg = ceil(n / block_rows) block slots."""
-    if na > n:
-        raise ValueError("more anchor rows than rows")
-    if block_rows == 0:
-        return np.arange(na, dtype=np.int64)
-    rg = -(-na // block_rows)
-    pg = -(-n // block_rows)
-    if rg > pg:
-        raise ValueError("the blocks do not fit the block slots")
-    rows = []
-    for g in range(rg):
-        start = (g * pg // rg) * block_rows
-        size = min(block_rows, na - g * block_rows)
-        rows.extend(range(start, start + size))
-    return np.asarray(rows, dtype=np.int64)
-
-
 def repeated_attention(q, k, v, frames: int, grid_h: int, grid_w: int,
                        stride: int, scale: float | None = None) -> np.ndarray:
     """Full attention for the anchor-row queries, copied to their rows."""

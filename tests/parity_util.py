@@ -14,7 +14,16 @@ MEAN_ABS = 1e-3
 
 
 def oracle_mask(w, rotation=None):
+    """The expected tile mask of workload w: the oracle's, or for the anchor-
+    row layouts (dense-rows kinds, not masks of the method) the library's
+    stated layout contract."""
     s = w.mask
+    if s.kind in (5, 6):
+        from layout_contract import dense_rows_mask, spread_dense_rows_mask
+        if s.kind == 5:
+            return dense_rows_mask(s.mask_heads, w.N, w.tile, s.query_tiles)
+        return spread_dense_rows_mask(s.mask_heads, w.N, w.tile, s.query_tiles,
+                                      s.block_tiles)
     return oracle.tile_mask(s.kind, w.frames, w.grid_h, w.grid_w, w.tile,
                             window=s.window, num_anchors=s.num_anchors,
                             rotation=s.rotation if rotation is None else rotation,
@@ -33,7 +42,8 @@ def gpu_mask_csr(w, device="cuda"):
 
 
 def check_mask_csr(w, mask, row_ptr, col_idx):
-    """Bit-exact comparison of the GPU mask and CSR with the oracle's."""
+    """Bit-exact comparison of the GPU mask and CSR with the oracle's (the
+    layout contract's for the dense-rows kinds)."""
     m_ref = oracle_mask(w)
     m = mask.cpu().numpy()
     assert m.shape == m_ref.shape
@@ -84,6 +94,22 @@ def lse_tolerance(q, k, mask, tile, rows=None, workers=8):
     q64 = q.detach().cpu().to(torch.float64).numpy()[:, :, rows]
     scale = 1.0 / np.sqrt(q.shape[-1])
     return LSE_BASE + 2.0 ** -9 * scale * (np.abs(q64) * np.abs(kbar)).sum(-1)
+
+
+def oracle_rows_and_lse_tol(q, k, v, mask, tile, rows=None, workers=16):
+    """The oracle's O and LSE for the query rows `rows` (all rows if None),
+    and the per-row LSE bound of `lse_tolerance`, from one oracle pass: the
+    attention weights do not depend on the values, so attending over the
+    values [V | K] gives O in the first d columns and kbar in the rest."""
+    N, d = q.shape[2], q.shape[3]
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    vk = torch.cat([v.cpu(), k.cpu()], dim=-1)
+    o2, lse = oracle.block_sparse_attention_rows(q.cpu(), k.cpu(), vk, mask, tile,
+                                                 rows, workers=workers)
+    q64 = q.detach().cpu().to(torch.float64).numpy()[:, :, rows]
+    scale = 1.0 / np.sqrt(d)
+    tol = LSE_BASE + 2.0 ** -9 * scale * (np.abs(q64) * np.abs(o2[..., d:])).sum(-1)
+    return o2[..., :d], lse, tol
 
 
 def assert_close(name, o_gpu, o_ref, lse_gpu=None, lse_ref=None,

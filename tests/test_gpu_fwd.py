@@ -1,9 +1,10 @@
 """GPU forward against the float64 oracle.
 
-Small workloads are compared on every output element; the full-size video
-workloads, in the launch configuration the benchmark times, on sampled query
-rows that the oracle computes one by one (every query tile's first and last
-row plus seeded random rows, for every head)."""
+Small workloads are compared on every output element.  The full-size video
+workloads run in the launch configuration the benchmark times: the
+32 760-token ones are compared on every row and head, the 131 040-token ones
+on sampled rows of every query tile (its first and last row plus seeded
+random rows, for every head)."""
 import zlib
 
 import numpy as np
@@ -14,7 +15,8 @@ import block_sparse_attention_bsattn_amd as bs
 import oracle
 import workloads as W
 from parity_util import (assert_close, check_mask_csr, gpu_mask_csr,
-                         lse_tolerance, oracle_mask, to64)
+                         lse_tolerance, oracle_mask, oracle_rows_and_lse_tol,
+                         to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -176,55 +178,59 @@ def test_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def sample_rows(w, per_tile_random=1, seed=0):
+def sample_rows(w, per_tile, seed=0):
+    """`per_tile` rows of every query tile: its first and last row and
+    per_tile - 2 further distinct rows drawn at random (all rows of a tile
+    shorter than that)."""
     g = np.random.default_rng(seed)
-    rows = set()
+    rows = []
     for i in range(w.num_tiles):
         lo = i * w.tile
         hi = min(lo + w.tile, w.N) - 1
-        rows.update((lo, hi))
-        rows.update(int(x) for x in g.integers(lo, hi + 1, per_tile_random))
-    return np.array(sorted(rows))
+        inner = np.arange(lo + 1, hi)
+        k = max(0, min(per_tile - 2, len(inner)))
+        pick = g.choice(inner, size=k, replace=False) if k else []
+        rows.extend(sorted({lo, hi, *map(int, pick)}))
+    return np.array(rows)
 
 
-@pytest.mark.parametrize("cfg,stride", [(2, 1), (3, 1), (4, 4), (5, 2),
-                                        ("expanded", 8)])
-def test_full_size_sampled_rows(cfg, stride):
-    """Full-size workload on the GPU; the oracle computes sampled rows (every
-    `stride`-th query tile's first and last row plus one random row)."""
+# Rows per query tile at the 131 040-token shapes: every query tile (so both
+# tiles of every query-tile pair, and both groups of the tuned kernel) is
+# checked, with its first and last row.
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg,per_tile,rotation", [(4, 16, 0), (4, 4, 37),
+                                                   ("expanded", 8, 0)])
+def test_full_size_sampled_rows(cfg, per_tile, rotation):
+    """Full-size 131 040-token workload on the GPU (launch configuration of
+    the benchmark); the oracle computes `per_tile` rows of every query tile
+    for every head."""
     w = W.EXPANDED if cfg == "expanded" else W.WORKLOADS[cfg]
+    w = w.with_rotation(rotation)
     q, k, v, mask, rp, ci, o, lse = run_gpu(w)
     m_ref = check_mask_csr(w, mask, rp, ci)
-    rows = sample_rows(w)
-    keep = (rows // w.tile) % stride == 0
-    keep |= rows >= (w.num_tiles - 1) * w.tile       # always the ragged tail
-    rows = rows[keep]
-    o_ref, lse_ref = oracle.block_sparse_attention_rows(
-        q.cpu(), k.cpu(), v.cpu(), m_ref, w.tile, rows, workers=16)
+    rows = sample_rows(w, per_tile, seed=rotation)
+    assert len(set((rows // w.tile).tolist())) == w.num_tiles
+    o_ref, lse_ref, tol = oracle_rows_and_lse_tol(q, k, v, m_ref, w.tile, rows)
     idx = torch.from_numpy(rows).cuda()
-    assert_close(f"{w.name} ({len(rows)} rows x {w.B * w.H} heads)",
-                 to64(o[:, :, idx]), o_ref, to64(lse[:, :, idx]), lse_ref,
-                 lse_tolerance(q, k, m_ref, w.tile, rows, workers=16))
+    assert_close(f"{w.name} r{rotation} ({len(rows)} rows: {per_tile} of every "
+                 f"query tile, x {w.B * w.H} heads)",
+                 to64(o[:, :, idx]), o_ref, to64(lse[:, :, idx]), lse_ref, tol)
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
-def test_full_size_every_row(cfg):
-    """The 32 760-token workloads (window/anchor at rotation 0; static per
-    head) compared element by element on every output row and head, in the
-    launch configuration the bench times."""
-    from threadpoolctl import threadpool_limits
-    w = W.WORKLOADS[cfg]
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg,rotation", [(2, 0), (2, 10), (3, 0), (5, 0)])
+def test_full_size_every_row(cfg, rotation):
+    """The 32 760-token workloads (window/anchor at rotations 0 and 10;
+    static per head; dense with 40 heads) compared element by element on
+    every output row and head, in the launch configuration the bench
+    times."""
+    w = W.WORKLOADS[cfg].with_rotation(rotation)
     q, k, v, mask, rp, ci, o, lse = run_gpu(w)
     m_ref = check_mask_csr(w, mask, rp, ci)
-    rows = np.arange(w.N)
-    # 16 oracle workers, one BLAS thread each (no oversubscription)
-    with threadpool_limits(limits=1):
-        o_ref, lse_ref = oracle.block_sparse_attention(q.cpu(), k.cpu(), v.cpu(), m_ref,
-                                                       w.tile, workers=16)
-        print(f"  oracle done for {w.name}", flush=True)
-        tol = lse_tolerance(q, k, m_ref, w.tile, rows, workers=16)
-    assert_close(f"{w.name} (all {w.N} rows x {w.B * w.H} heads)", to64(o), o_ref,
-                 to64(lse), lse_ref, tol)
+    o_ref, lse_ref, tol = oracle_rows_and_lse_tol(q, k, v, m_ref, w.tile)
+    print(f"  oracle done for {w.name} r{rotation}", flush=True)
+    assert_close(f"{w.name} r{rotation} (all {w.N} rows x {w.B * w.H} heads)", to64(o),
+                 o_ref, to64(lse), lse_ref, tol)
 
 
 def test_tuned_kernel_pair_and_split_lists_and_bad_indices():

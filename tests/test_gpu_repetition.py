@@ -9,6 +9,7 @@ import torch
 import block_sparse_attention_bsattn_amd as bs
 import oracle
 import workloads as W
+from layout_contract import anchor_buffer_rows
 from parity_util import assert_close, check_mask_csr, gpu_mask_csr, to64
 
 pytestmark = pytest.mark.gpu
@@ -159,7 +160,7 @@ def test_anchor_rows_spread_bit_exact(T, gh, gw, d, s, br, dt):
     bs.anchor_rows(ga, bc, T, gh, gw, s, broadcast=True, block_rows=br)
     torch.cuda.synchronize()
     na = T * oracle.anchor_count(gh, s) * gw
-    rows = oracle.anchor_buffer_rows(na, N, br)
+    rows = anchor_buffer_rows(na, N, br)
     want_g = oracle.gather_anchor_rows(x.float().numpy(), T, gh, gw, s)
     got = ga.cpu().float().numpy()
     assert np.array_equal(got[:, :, rows], want_g)

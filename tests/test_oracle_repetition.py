@@ -112,28 +112,3 @@ def test_repeated_attention():
     for y in range(gh):
         np.testing.assert_allclose(o[:, :, :, y], f[:, :, :, 2 * (y // 2)], rtol=1e-12,
                                    atol=1e-13)
-
-
-def test_anchor_buffer_rows_by_hand():
-    """The spread layout of the packed anchor rows, by hand, and its
-    agreement with the spread dense-rows mask."""
-    np.testing.assert_array_equal(oracle.anchor_buffer_rows(5, 12, 0), np.arange(5))
-    # 5 rows in blocks of 2 over ceil(12 / 2) = 6 slots: Rg = 3 -> slots 0, 2, 4
-    np.testing.assert_array_equal(oracle.anchor_buffer_rows(5, 12, 2), [0, 1, 4, 5, 8])
-    # 4 rows in blocks of 2 over ceil(11 / 2) = 6 slots: slots 0, 3 (the
-    # partial last slot, rows 10 .. 11, stays unused)
-    np.testing.assert_array_equal(oracle.anchor_buffer_rows(4, 11, 2), [0, 1, 6, 7])
-    # as many blocks as slots: packed at the front
-    np.testing.assert_array_equal(oracle.anchor_buffer_rows(7, 7, 2), np.arange(7))
-    with pytest.raises(ValueError):
-        oracle.anchor_buffer_rows(8, 7, 2)   # more anchor rows than rows
-    # rows are distinct, increasing and inside the buffer
-    for na, n, b in [(300, 768, 128), (16380, 32760, 256), (1, 256, 256), (17, 40, 4)]:
-        r = oracle.anchor_buffer_rows(na, n, b)
-        assert len(r) == na and (np.diff(r) > 0).all() and r[-1] < n
-    # the tiles the spread rows occupy are the spread mask's dense tiles:
-    # 300 rows, tile 64, blocks of 2 tiles (128 rows), 768 tokens
-    rows = oracle.anchor_buffer_rows(300, 768, 128)
-    tiles = sorted(set((rows // 64).tolist()))
-    m = oracle.tile_mask(6, 1, 1, 768, 64, query_tiles=-(-300 // 64), block_tiles=2)[0]
-    assert tiles == m.any(axis=1).nonzero()[0].tolist() == [0, 1, 4, 5, 8]
