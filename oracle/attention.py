@@ -57,23 +57,25 @@ def block_sparse_attention_rows(q, k, v, mask, tile: int, rows,
                                 chunk: int = 128):
     """Oracle outputs for the query rows `rows` (same for every (b, h)).
 
-    q, k, v: [B, H, N, d]; mask: uint8 [Hm, Tq, Tk] with Hm in {1, H}.
-    Returns (o [B, H, len(rows), d], lse [B, H, len(rows)]), float64.
+    q, k: [B, H, N, d]; v: [B, H, N, dv] (dv = d for attention itself; any
+    dv gives the same weights applied to other values); mask: uint8
+    [Hm, Tq, Tk] with Hm in {1, H}.
+    Returns (o [B, H, len(rows), dv], lse [B, H, len(rows)]), float64.
     """
     q = _as_f64(q)
     k = _as_f64(k)
     v = _as_f64(v)
     mask = np.asarray(mask)
     B, H, N, d = q.shape
-    if k.shape != (B, H, N, d) or v.shape != (B, H, N, d):
-        raise ValueError("q, k, v must share the shape [B, H, N, d]")
+    if k.shape != (B, H, N, d) or v.ndim != 4 or v.shape[:3] != (B, H, N):
+        raise ValueError("q and k must share the shape [B, H, N, d], v [B, H, N, dv]")
     Hm = mask.shape[0]
     if Hm not in (1, H):
         raise ValueError("mask must have 1 or H head slices")
     if scale is None or scale <= 0:
         scale = 1.0 / math.sqrt(d)
     rows = np.asarray(rows, dtype=np.int64)
-    o = np.zeros((B, H, len(rows), d), dtype=np.float64)
+    o = np.zeros((B, H, len(rows), v.shape[3]), dtype=np.float64)
     lse = np.full((B, H, len(rows)), -np.inf)
 
     jobs = []

@@ -205,3 +205,20 @@ def test_bf16_inputs_read_exactly():
     f = lambda x: x.to(torch.float64).numpy()
     np.testing.assert_allclose(o, _sdpa64(f(q), f(k), f(v)), rtol=1e-12,
                                atol=1e-12)
+
+
+def test_values_of_another_width_share_the_weights():
+    """The weights do not depend on the values: attending over [V | K] gives
+    the attention output with V in the first d columns and with V := K in
+    the rest (the parity tests' LSE bound uses the second)."""
+    g = torch.Generator().manual_seed(11)
+    q, k, v = (torch.randn(1, 2, 200, 16, generator=g, dtype=torch.float64) for _ in range(3))
+    m = (torch.rand(2, 4, 4, generator=g) < 0.6).to(torch.uint8).numpy()
+    m[:, 0, :] = 0                                   # an empty row too
+    o1, l1 = oracle.block_sparse_attention(q, k, v, m, 64)
+    o2, l2 = oracle.block_sparse_attention(q, k, k, m, 64)
+    o3, l3 = oracle.block_sparse_attention(q, k, torch.cat([v, k], -1), m, 64)
+    np.testing.assert_array_equal(l1, l3)
+    np.testing.assert_array_equal(l2, l3)
+    np.testing.assert_allclose(o3[..., :16], o1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(o3[..., 16:], o2, rtol=0, atol=1e-13)
