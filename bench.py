@@ -4,7 +4,9 @@ One step = one pass of the whole path over one synthetic batch at the
 32 760-token video shape (B=1, H=12, d=128, 21 frames of 30x52 latents, bf16,
 128x128 tiles): build the window(+-1 frame) + 2 rotating-anchor mask for
 rotation r = (layer + step) mod 21 (layer 0), compact it into active-tile
-lists, run the fused forward.  Inputs are resident in HBM before timing.
+lists, build the forward's work plan from them, run the fused forward
+through the plan (--planned 0: the forward without a plan).  Inputs are
+resident in HBM before timing.
 
 Printed: ONE JSON line with
   value        active-block TFLOP/s of the whole step (mask + lists + forward),
@@ -50,10 +52,24 @@ def active_flops(mask_np: np.ndarray, w) -> float:
     return float(4.0 * w.d * w.B * heads_per_slice * per_slice.sum())
 
 
+def forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, tile, Hm, planned, stream):
+    """A callable that runs one forward on fixed lists: through a plan built
+    here once (bsattn_fwd_plan; the lists are static) when planned, else
+    bsattn_fwd."""
+    if not planned or tile != 128 or q.dtype != torch.bfloat16 or q.shape[-1] != 128:
+        return lambda: bs.fwd(q, k, v, o, row_ptr, col_idx, tile, mask_heads=Hm, stream=stream)
+    B, H, N, _ = q.shape
+    plan = torch.empty(bs.fwd_plan_bytes(B, H, N, tile, Hm), dtype=torch.uint8,
+                       device=q.device)
+    bs.fwd_plan(row_ptr, col_idx, B, H, N, plan, tile, Hm, stream=stream)
+    return lambda: bs.fwd_planned(q, k, v, o, row_ptr, col_idx, plan, mask_heads=Hm,
+                                  stream=stream)
+
+
 SWEEP_P = (0.05, 0.1, 0.2, 0.3, 0.5, 0.7, 1.0)
 
 
-def density_sweep(bs, W, torch, dev, q, k, v, o, calls: int = 5):
+def density_sweep(bs, W, torch, dev, q, k, v, o, calls: int = 5, planned: bool = True):
     """The forward on the 32 760-token shape with per-head static random
     masks (seed 3, diagonal forced) at several densities: median ms per call
     against active TFLOP, and a least-squares line through them."""
@@ -75,13 +91,14 @@ def density_sweep(bs, W, torch, dev, q, k, v, o, calls: int = 5):
         bs.compact(mask, row_ptr, col_idx)
         m_np = mask.cpu().numpy()
         flops = active_flops(m_np, base)
-        bs.fwd(q, k, v, o, row_ptr, col_idx, base.tile, mask_heads=Hm)
+        run = forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, base.tile, Hm, planned,
+                         stream)
+        run()
         evs = [(torch.cuda.Event(enable_timing=True),
                 torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
         for a, b in evs:
             a.record(stream)
-            bs.fwd(q, k, v, o, row_ptr, col_idx, base.tile, mask_heads=Hm,
-                   stream=stream)
+            run()
             b.record(stream)
         torch.cuda.synchronize()
         ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
@@ -203,6 +220,16 @@ def calibration(bs, W, torch, dev, calls: int):
         b.record(stream)
     torch.cuda.synchronize()
     f_ms = float(np.median([a.elapsed_time(b) for a, b in fe]))
+    runp = forward_fn(bs, torch, q[:1], k[:1], v, o, rp, ci, w.tile, w.H, True, stream)
+    runp()
+    fp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for a, b in fp:
+        a.record(stream)
+        runp()
+        b.record(stream)
+    torch.cuda.synchronize()
+    fp_ms = float(np.median([a.elapsed_time(b) for a, b in fp]))
     from dataclasses import replace
     w1 = replace(w, B=1)
     f_flops = active_flops(m_np, w1)
@@ -215,7 +242,9 @@ def calibration(bs, W, torch, dev, calls: int):
             "aggregate_us": round(part(2, 3) * 1e3, 1),
             "calibrated_density": round(float(m_np.mean()), 4),
             "fwd_ms_on_calibrated_mask": round(f_ms, 4),
-            "fwd_tflops_on_calibrated_mask": round(f_flops / (f_ms * 1e-3) / 1e12, 1)}
+            "fwd_tflops_on_calibrated_mask": round(f_flops / (f_ms * 1e-3) / 1e12, 1),
+            "planned_fwd_ms_on_calibrated_mask": round(fp_ms, 4),
+            "planned_fwd_tflops_on_calibrated_mask": round(f_flops / (fp_ms * 1e-3) / 1e12, 1)}
 
 
 def squad_leg(bs, W, torch, dev, calls: int):
@@ -266,8 +295,33 @@ def squad_leg(bs, W, torch, dev, calls: int):
         bs.window_reorder(og, out, win, inverse=True, stream=stream)
         mark(4)
 
+    # the same two passes through work plans (built once: the masks are static)
+    plans = {}
+    for b, view in ((win // w.tile, 0), (G // w.tile, win)):
+        rp, ci = masks[b]
+        pl = torch.empty(bs.fwd_plan_bytes(w.B, w.H, w.N, w.tile, 1), dtype=torch.uint8,
+                         device=dev)
+        bs.fwd_plan(rp, ci, w.B, w.H, w.N, pl, w.tile, 1, stream=stream)
+        plans[view] = (rp, ci, pl)
+
+    def run_planned(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        rp, ci, pl = plans[0]
+        bs.fwd_planned(q, k, v, o_l, rp, ci, pl, stream=stream)
+        mark(1)
+        rp, ci, pl = plans[win]
+        bs.fwd_planned(q, k, o_l, out, rp, ci, pl, window=win, stream=stream)
+        mark(2)
+
     run()
     run_reordered()
+    run_planned()
+    evp = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(calls)]
+    for e in evp:
+        run_planned(e)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(calls)]
     evr = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(calls)]
     for e, er in zip(evs, evr):
@@ -294,7 +348,13 @@ def squad_leg(bs, W, torch, dev, calls: int):
     torch.cuda.synchronize()
     dense_ms = float(np.median([a.elapsed_time(b) for a, b in de]))
     dense_flops = 4.0 * w.d * w.N * w.N * w.B * w.H
+    p_l, p_g, p_t = part(evp, 0, 1), part(evp, 1, 2), part(evp, 0, 2)
     return {"workload": w.name, "window": win, "groups": G,
+            "planned_path": {"ms_total": round(p_t, 4), "local_ms": round(p_l, 4),
+                             "local_tflops": round(flops_local / (p_l * 1e-3) / 1e12, 1),
+                             "global_grouped_ms": round(p_g, 4),
+                             "global_grouped_tflops":
+                                 round(flops_global / (p_g * 1e-3) / 1e12, 1)},
             "ms_total": round(total, 4),
             "local_ms": round(l_ms, 4), "local_tflops": round(flops_local / (l_ms * 1e-3) / 1e12, 1),
             "global_grouped_ms": round(g_ms, 4),
@@ -375,7 +435,7 @@ def repetition_leg(bs, W, torch, dev, calls: int):
 
 # Time at half the bf16 dense peak for each workload's active-block work: the
 # target each record is read against.
-def configs_leg(bs, W, torch, dev, calls: int):
+def configs_leg(bs, W, torch, dev, calls: int, planned: bool = True):
     """Every 32 760- and 131 040-token workload on its own: mask build,
     compaction and forward (median of `calls` event-timed calls each, on the
     launch stream), active TFLOP, TFLOP/s and fraction of the bf16 peak, at
@@ -395,6 +455,9 @@ def configs_leg(bs, W, torch, dev, calls: int):
         layout = (w.frames, w.grid_h, w.grid_w, w.tile)
         params = bs.mask_params_of(w.mask)
 
+        plan = torch.empty(bs.fwd_plan_bytes(w.B, w.H, w.N, w.tile, Hm), dtype=torch.uint8,
+                           device=dev) if planned else None
+
         def run(ev=None):
             if ev is not None:
                 ev[0].record(stream)
@@ -404,21 +467,29 @@ def configs_leg(bs, W, torch, dev, calls: int):
             bs.compact(mask, row_ptr, col_idx, stream=stream)
             if ev is not None:
                 ev[2].record(stream)
-            bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, mask_heads=Hm, stream=stream)
+            if planned:
+                bs.fwd_plan(row_ptr, col_idx, w.B, w.H, w.N, plan, w.tile, Hm, stream=stream)
             if ev is not None:
                 ev[3].record(stream)
+            if planned:
+                bs.fwd_planned(q, k, v, o, row_ptr, col_idx, plan, mask_heads=Hm,
+                               stream=stream)
+            else:
+                bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, mask_heads=Hm, stream=stream)
+            if ev is not None:
+                ev[4].record(stream)
 
         run()
         torch.cuda.synchronize()
         m_np = mask.cpu().numpy()
         flops = active_flops(m_np, w)
         tiles = int(m_np.sum()) * (w.H if Hm == 1 else 1) * w.B
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(calls)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(calls)]
         for e in evs:
             run(e)
         torch.cuda.synchronize()
         part = lambda a, b: float(np.median([e[a].elapsed_time(e[b]) for e in evs]))
-        f_ms = part(2, 3)
+        f_ms = part(3, 4)
         tflops = flops / (f_ms * 1e-3) / 1e12
         recs[w.name] = {
             "B": w.B, "H": w.H, "N": w.N, "mask_heads": Hm,
@@ -427,6 +498,7 @@ def configs_leg(bs, W, torch, dev, calls: int):
             "active_tflop": round(flops / 1e12, 4),
             "build_mask_us": round(part(0, 1) * 1e3, 2),
             "compact_us": round(part(1, 2) * 1e3, 2),
+            "plan_us": round(part(2, 3) * 1e3, 2) if planned else None,
             "fwd_ms_median": round(f_ms, 4),
             "fwd_tflops": round(tflops, 1),
             "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -515,6 +587,12 @@ def main():
                     help="timed calls of the SQuad two-pass leg (0 = skip)")
     ap.add_argument("--repetition", type=int, default=5,
                     help="timed calls of the spatial-repetition leg (0 = skip)")
+    ap.add_argument("--planned", type=int, default=1,
+                    help="forward through a work plan (bsattn_fwd_plan + "
+                         "bsattn_fwd_planned; 0 = bsattn_fwd)")
+    ap.add_argument("--unplanned-calls", type=int, default=10,
+                    help="timed calls of bsattn_fwd beside the planned forward "
+                         "(0 = skip)")
     ap.add_argument("--configs", type=int, default=10,
                     help="timed calls per workload of the per-config records "
                          "(0 = skip)")
@@ -554,9 +632,15 @@ def main():
         bs.build_mask(layout, mask, **bs.mask_params_of(w.with_rotation(r).mask))
         flops_by_r[r] = active_flops(mask.cpu().numpy(), w)
 
+    # the planned forward's plan buffer, sized for any list set of this
+    # shape (allocated once, outside the timed steps)
+    plan = torch.empty(bs.fwd_plan_bytes(w.B, w.H, w.N, w.tile, Hm), dtype=torch.uint8,
+                       device=dev) if args.planned else None
+
     def step(s, ev=None):
-        """One pass of the path; ev = 4 events bracketing mask build,
-        compaction and the forward on the launch stream."""
+        """One pass of the path; ev = 5 events bracketing mask build,
+        compaction, the plan (planned forward only) and the forward on the
+        launch stream."""
         r = s % T  # (layer + step) mod T with layer 0
         if ev is not None:
             ev[0].record(stream)
@@ -567,17 +651,23 @@ def main():
         bs.compact(mask, row_ptr, col_idx, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, mask_heads=Hm,
-               stream=stream)
+        if args.planned:
+            bs.fwd_plan(row_ptr, col_idx, w.B, w.H, w.N, plan, w.tile, Hm, stream=stream)
         if ev is not None:
             ev[3].record(stream)
+        if args.planned:
+            bs.fwd_planned(q, k, v, o, row_ptr, col_idx, plan, mask_heads=Hm, stream=stream)
+        else:
+            bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, mask_heads=Hm, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
         return flops_by_r[r]
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
               for _ in range(args.steps)]
     total_flops = 0.0
     torch.cuda.synchronize()
@@ -586,9 +676,24 @@ def main():
         total_flops += step(args.warmup + s, events[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    fwd_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+    fwd_ms = np.array([e[3].elapsed_time(e[4]) for e in events])
     mask_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     compact_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    plan_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+
+    # the same forward without a plan (one workgroup per query-tile pair),
+    # on the lists of the last step
+    unplanned_ms = None
+    if args.planned and args.unplanned_calls > 0:
+        ue = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.unplanned_calls)]
+        bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, mask_heads=Hm, stream=stream)
+        for a_, b_ in ue:
+            a_.record(stream)
+            bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, mask_heads=Hm, stream=stream)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        unplanned_ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in ue]))
     ms_per_step = elapsed * 1e3 / args.steps
     value = total_flops / elapsed / 1e12
     fwd_flops_mean = total_flops / args.steps
@@ -617,18 +722,21 @@ def main():
         bs.build_mask(layout, mask, kind=W.MASK_DENSE, mask_heads=Hm)
         bs.compact(mask, row_ptr, col_idx)
         dense_flops = active_flops(mask.cpu().numpy(), w)
-        bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, mask_heads=Hm)
+        run = forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, w.tile, Hm,
+                         bool(args.planned), stream)
+        run()
         dev_ev = [(torch.cuda.Event(enable_timing=True),
                    torch.cuda.Event(enable_timing=True))
                   for _ in range(args.dense_calls)]
         for a, b in dev_ev:
             a.record(stream)
-            bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, mask_heads=Hm)
+            run()
             b.record(stream)
         torch.cuda.synchronize()
         dense_ms = float(np.median([a.elapsed_time(b) for a, b in dev_ev]))
 
-    sweep = density_sweep(bs, W, torch, dev, q, k, v, o) if args.sweep else None
+    sweep = density_sweep(bs, W, torch, dev, q, k, v, o, planned=bool(args.planned)) \
+        if args.sweep else None
 
     expanded = expanded_windows(bs, W, torch, dev, args.expanded) \
         if args.expanded > 0 else None
@@ -640,7 +748,8 @@ def main():
     repetition = repetition_leg(bs, W, torch, dev, args.repetition) \
         if args.repetition > 0 else None
 
-    configs = configs_leg(bs, W, torch, dev, args.configs) if args.configs > 0 else None
+    configs = configs_leg(bs, W, torch, dev, args.configs, bool(args.planned)) \
+        if args.configs > 0 else None
 
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -686,7 +795,8 @@ def main():
             "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
             "tile": w.tile, "frames": w.frames, "grid": [w.grid_h, w.grid_w],
             "mask": "window +-1 frame + 2 anchors rotating (layer+step) mod 21",
-            "step": "build_mask + compact + fwd",
+            "step": "build_mask + compact + fwd_plan + fwd_planned" if args.planned
+                    else "build_mask + compact + fwd",
         },
         "roofline": {
             "bound": "mfma",
@@ -699,7 +809,8 @@ def main():
             "traffic_gbs": None if traffic is None else
             round(traffic["total"] / (float(fwd_ms.mean()) * 1e-3) / 1e9, 1),
             "mfma_busy_rocprof": None if mfma is None else round(mfma["busy"], 4),
-            "kernel": "fwd_bf16_t128_d128",
+            "kernel": "fwd_bf16_t128_d128<false, true>" if args.planned
+                      else "fwd_bf16_t128_d128<false, false>",
             "fwd_ms_mean": round(float(fwd_ms.mean()), 4),
             "active_tflop_per_launch": round(fwd_flops_mean / 1e12, 4),
             "mfma_ceiling_measured": None if ceiling is None else round(ceiling, 1),
@@ -710,6 +821,8 @@ def main():
         "fwd_ms_median": round(float(np.median(fwd_ms)), 4),
         "build_mask_us": round(float(np.median(mask_ms)) * 1e3, 2),
         "compact_us": round(float(np.median(compact_ms)) * 1e3, 2),
+        "plan_us": round(float(np.median(plan_ms)) * 1e3, 2) if args.planned else None,
+        "fwd_unplanned_ms_median": None if unplanned_ms is None else round(unplanned_ms, 4),
         "density": None if dense_flops is None else round(fwd_flops_mean / dense_flops, 4),
         "dense_fwd_ms": None if dense_ms is None else round(dense_ms, 4),
         "dense_tflops": None if dense_ms is None else

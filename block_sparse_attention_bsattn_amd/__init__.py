@@ -8,6 +8,9 @@ The calls mirror include/bsattn.h:
     compact(mask, row_ptr, col_idx)                     -> bsattn_compact
     fwd(q, k, v, o, row_ptr, col_idx, tile, ...)        -> bsattn_fwd
     fwd_grouped(q, k, v, o, row_ptr, col_idx, w, ...)   -> bsattn_fwd_grouped
+    fwd_plan_bytes(B, H, N, tile, ...)                  -> bsattn_fwd_plan_bytes
+    fwd_plan(row_ptr, col_idx, B, H, N, tile, plan)     -> bsattn_fwd_plan
+    fwd_planned(q, k, v, o, row_ptr, col_idx, plan, ..) -> bsattn_fwd_planned
     block_energy(q, k, energy, tile, ...)               -> bsattn_block_energy
     select_blocks(energy, eps, mask)                    -> bsattn_select_blocks
     aggregate_masks(masks, rho, out)                    -> bsattn_aggregate_masks
@@ -17,7 +20,7 @@ The calls mirror include/bsattn.h:
     anchor_rows(src, dst, ..., broadcast, block_rows)   -> bsattn_anchor_rows
 
 plus small helpers that allocate the outputs with torch (make_mask,
-make_csr, attention, calibrate, squad, repeated_attention).  There is no fallback: if libbsattn.so is missing or a
+make_csr, make_plan, attention, calibrate, squad, repeated_attention).  There is no fallback: if libbsattn.so is missing or a
 call fails, an exception is raised.
 """
 from __future__ import annotations
@@ -48,7 +51,8 @@ MASK_DENSE_ROWS_SPREAD = 6
 # Every symbol include/bsattn.h exports.
 EXPORTS = ("bsattn_version", "bsattn_status_string", "bsattn_last_error",
            "bsattn_num_tiles", "bsattn_build_mask", "bsattn_compact",
-           "bsattn_fwd", "bsattn_fwd_grouped", "bsattn_window_reorder", "bsattn_row_cosines",
+           "bsattn_fwd", "bsattn_fwd_grouped", "bsattn_fwd_plan_bytes", "bsattn_fwd_plan",
+           "bsattn_fwd_planned", "bsattn_window_reorder", "bsattn_row_cosines",
            "bsattn_repetitive_heads", "bsattn_anchor_rows", "bsattn_block_energy",
            "bsattn_select_blocks",
            "bsattn_aggregate_masks", "bsattn_mfma_ceiling")
@@ -108,6 +112,15 @@ def lib() -> ctypes.CDLL:
     L.bsattn_fwd_grouped.restype = ctypes.c_int
     L.bsattn_fwd_grouped.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                      i32, i32p, i32p, i32, ctypes.c_float, vp]
+    L.bsattn_fwd_plan_bytes.restype = ctypes.c_int64
+    L.bsattn_fwd_plan_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int64, i32]
+    L.bsattn_fwd_plan.restype = ctypes.c_int
+    L.bsattn_fwd_plan.argtypes = [i32, i32, i32, i32, i32, i32p, i32p, i32, vp,
+                                  ctypes.c_int64, vp]
+    L.bsattn_fwd_planned.restype = ctypes.c_int
+    L.bsattn_fwd_planned.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                     i32, i32p, i32p, vp, ctypes.c_int64, i32, i32,
+                                     ctypes.c_float, vp]
     L.bsattn_window_reorder.restype = ctypes.c_int
     L.bsattn_window_reorder.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i32, vp]
     L.bsattn_row_cosines.restype = ctypes.c_int
@@ -262,6 +275,66 @@ def fwd_grouped(q, k, v, o, row_ptr, col_idx, w: int, mask_heads: int = 1,
                                   _ptr(col_idx, "col_idx", torch.int32), int(w), float(scale),
                                   _stream(stream))
     _check(st, "bsattn_fwd_grouped")
+    return o
+
+
+def fwd_plan_bytes(B: int, H: int, N: int, tile: int = 128, mask_heads: int = 1,
+                   nnz_bound: int = -1, workers: int = 0) -> int:
+    """bsattn_fwd_plan_bytes: size of a plan buffer for these sizes."""
+    n = lib().bsattn_fwd_plan_bytes(B, H, N, tile, mask_heads, int(nnz_bound), workers)
+    if n < 0:
+        _check(int(n), "bsattn_fwd_plan_bytes")
+    return int(n)
+
+
+def fwd_plan(row_ptr, col_idx, B: int, H: int, N: int, plan, tile: int = 128,
+             mask_heads: int = 1, workers: int = 0, stream=None):
+    """bsattn_fwd_plan of a CSR into the uint8 device tensor `plan`."""
+    import torch
+    st = lib().bsattn_fwd_plan(B, H, N, tile, mask_heads,
+                               _ptr(row_ptr, "row_ptr", torch.int32),
+                               _ptr(col_idx, "col_idx", torch.int32), workers,
+                               _ptr(plan, "plan", torch.uint8), plan.numel(),
+                               _stream(stream))
+    _check(st, "bsattn_fwd_plan")
+    return plan
+
+
+def make_plan(row_ptr, col_idx, B: int, H: int, N: int, tile: int = 128,
+              mask_heads: int = 1, workers: int = 0, nnz_bound: Optional[int] = None,
+              stream=None):
+    """A plan tensor sized for the CSR (its entry count read from row_ptr
+    unless nnz_bound is given) and built by bsattn_fwd_plan."""
+    import torch
+    if nnz_bound is None:
+        nnz_bound = int(row_ptr[-1].item())
+    nb = fwd_plan_bytes(B, H, N, tile, mask_heads, nnz_bound, workers)
+    plan = torch.empty(nb, dtype=torch.uint8, device=row_ptr.device)
+    return fwd_plan(row_ptr, col_idx, B, H, N, plan, tile, mask_heads, workers, stream)
+
+
+def fwd_planned(q, k, v, o, row_ptr, col_idx, plan, mask_heads: int = 1, lse=None,
+                workers: int = 0, window: int = 0, scale: float = 0.0, stream=None):
+    """bsattn_fwd_planned: the forward through a plan from fwd_plan (bf16,
+    d 128, tile 128; window > 0 for the grouped view)."""
+    import torch
+    if q.dtype != torch.bfloat16 or q.dim() != 4:
+        raise ValueError("q must be bf16 [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must have the shape and dtype of q")
+    if lse is not None and tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must have shape [B, H, N]")
+    st = lib().bsattn_fwd_planned(B, H, N, d, 128, DTYPE_BF16, _ptr(q, "q", q.dtype),
+                                  _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype),
+                                  _ptr(o, "o", q.dtype),
+                                  _ptr(lse, "lse", torch.float32, allow_none=True),
+                                  mask_heads, _ptr(row_ptr, "row_ptr", torch.int32),
+                                  _ptr(col_idx, "col_idx", torch.int32),
+                                  _ptr(plan, "plan", torch.uint8), plan.numel(), workers,
+                                  int(window), float(scale), _stream(stream))
+    _check(st, "bsattn_fwd_planned")
     return o
 
 
@@ -423,6 +496,22 @@ def attention(q, k, v, row_ptr, col_idx, tile, mask_heads=1, want_lse=False,
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     fwd(q, k, v, o, row_ptr, col_idx, tile, mask_heads=mask_heads, lse=lse,
         scale=scale, stream=stream)
+    return (o, lse) if want_lse else o
+
+
+def attention_planned(q, k, v, row_ptr, col_idx, plan=None, mask_heads=1, want_lse=False,
+                      workers=0, window=0, scale=0.0, stream=None):
+    """As attention(), through a plan (built here from the CSR when None)."""
+    import torch
+    B, H, N, _ = q.shape
+    if plan is None:
+        plan = make_plan(row_ptr, col_idx, B, H, N, 128, mask_heads, workers, stream=stream)
+    o = torch.empty_like(q)
+    lse = None
+    if want_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fwd_planned(q, k, v, o, row_ptr, col_idx, plan, mask_heads=mask_heads, lse=lse,
+                workers=workers, window=window, scale=scale, stream=stream)
     return (o, lse) if want_lse else o
 
 

@@ -206,6 +206,8 @@ static int fwd_args(const char* who, int32_t B, int32_t H, int32_t N, int32_t d,
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
   a.scale_log2 = sc * 1.4426950408889634f;
   a.window = 0;
+  a.plan = nullptr;
+  a.pl = bsattn::PlanLayout{};
   return BSATTN_OK;
 }
 
@@ -245,6 +247,116 @@ BSATTN_API int bsattn_fwd_grouped(int32_t B, int32_t H, int32_t N, int32_t d, in
     return fail(BSATTN_ERR_INVALID_ARG, "fwd_grouped: N * 256 bytes must stay below 2^31");
   a.window = window;
   return hip_status(bsattn::launch_fwd(a, stream), "fwd_grouped");
+}
+
+// ---- planned forward
+
+// Validation shared by the three planned calls; fills *workers (0 selects
+// the device's compute units, rounded down to a multiple of 8).
+static int plan_args(const char* who, int32_t B, int32_t H, int32_t N, int32_t tile,
+                     int32_t mask_heads, int32_t* workers) {
+  if (B < 0 || H < 0 || N < 0)
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: B, H and N must be >= 0", who);
+  if (tile != 128)
+    return fail(BSATTN_ERR_UNSUPPORTED, "%s: tile %d (the planned path: 128)", who, tile);
+  if (mask_heads != 1 && mask_heads != H)
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: mask_heads %d must be 1 or H=%d", who,
+                mask_heads, H);
+  const int32_t tiles = bsattn_num_tiles(N, tile);
+  if (tiles > bsattn::kPlanMaxTiles)
+    return fail(BSATTN_ERR_UNSUPPORTED, "%s: %d tiles (at most %d)", who, tiles,
+                bsattn::kPlanMaxTiles);
+  if ((int64_t)B * H > 65535)
+    return fail(BSATTN_ERR_UNSUPPORTED, "%s: B*H must be <= 65535", who);
+  int32_t w = *workers;
+  if (w == 0) {
+    const int cu = bsattn::device_compute_units();
+    if (cu < 1) return fail(BSATTN_ERR_HIP, "%s: cannot query the device", who);
+    w = cu - cu % bsattn::kPlanXcds;
+    const int most = bsattn::kPlanXcds * bsattn::kPlanMaxWorkersPerXcd;
+    if (w > most) w = most;
+    if (w < bsattn::kPlanXcds) w = bsattn::kPlanXcds;
+  }
+  if (w < bsattn::kPlanXcds || w % bsattn::kPlanXcds != 0 ||
+      w > bsattn::kPlanXcds * bsattn::kPlanMaxWorkersPerXcd)
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: workers %d must be a multiple of %d in [%d, %d]",
+                who, w, bsattn::kPlanXcds, bsattn::kPlanXcds,
+                bsattn::kPlanXcds * bsattn::kPlanMaxWorkersPerXcd);
+  *workers = w;
+  return BSATTN_OK;
+}
+
+// The plan layout for a buffer of plan_bytes bytes (the step capacity is
+// whatever follows the fixed part); INVALID_ARG when it is too small.
+static int plan_fit(const char* who, int32_t B, int32_t H, int32_t N, int32_t mask_heads,
+                    int32_t workers, const void* plan, int64_t plan_bytes,
+                    bsattn::PlanLayout& L) {
+  L = bsattn::plan_layout(B, H, N, 128, mask_heads, 0, workers);
+  if (!plan) return fail(BSATTN_ERR_INVALID_ARG, "%s: null plan", who);
+  if (!aligned16(plan)) return fail(BSATTN_ERR_INVALID_ARG, "%s: plan not 16-byte aligned", who);
+  if (plan_bytes < L.bytes)
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: plan_bytes %lld below the minimum %lld", who,
+                (long long)plan_bytes, (long long)L.bytes);
+  L.step_cap = (plan_bytes - L.off_steps) / 8;
+  L.bytes = plan_bytes;
+  return BSATTN_OK;
+}
+
+BSATTN_API int64_t bsattn_fwd_plan_bytes(int32_t B, int32_t H, int32_t N, int32_t tile,
+                                         int32_t mask_heads, int64_t nnz_bound,
+                                         int32_t workers) {
+  const int st = plan_args("fwd_plan_bytes", B, H, N, tile, mask_heads, &workers);
+  if (st != BSATTN_OK) return st;
+  const int32_t tiles = bsattn_num_tiles(N, tile);
+  const int64_t full = (int64_t)mask_heads * tiles * tiles;
+  if (nnz_bound < 0 || nnz_bound > full) nnz_bound = full;
+  ok();
+  return bsattn::plan_layout(B, H, N, tile, mask_heads, nnz_bound, workers).bytes;
+}
+
+BSATTN_API int bsattn_fwd_plan(int32_t B, int32_t H, int32_t N, int32_t tile,
+                               int32_t mask_heads, const int32_t* row_ptr,
+                               const int32_t* col_idx, int32_t workers, void* plan,
+                               int64_t plan_bytes, void* stream) {
+  int st = plan_args("fwd_plan", B, H, N, tile, mask_heads, &workers);
+  if (st != BSATTN_OK) return st;
+  if ((int64_t)B * H * N == 0) return ok();
+  if (!row_ptr || !col_idx) return fail(BSATTN_ERR_INVALID_ARG, "fwd_plan: null CSR");
+  bsattn::PlanLayout L;
+  st = plan_fit("fwd_plan", B, H, N, mask_heads, workers, plan, plan_bytes, L);
+  if (st != BSATTN_OK) return st;
+  const int64_t cap = (int64_t)mask_heads * L.tiles * L.tiles;
+  return hip_status(bsattn::launch_fwd_plan(L, row_ptr, col_idx, cap, (char*)plan, stream),
+                    "fwd_plan");
+}
+
+BSATTN_API int bsattn_fwd_planned(int32_t B, int32_t H, int32_t N, int32_t d, int32_t tile,
+                                  int32_t dtype, const void* q, const void* k, const void* v,
+                                  void* o, float* lse, int32_t mask_heads,
+                                  const int32_t* row_ptr, const int32_t* col_idx,
+                                  const void* plan, int64_t plan_bytes, int32_t workers,
+                                  int32_t window, float scale, void* stream) {
+  bsattn::FwdLaunch a;
+  bool noop;
+  int st = fwd_args("fwd_planned", B, H, N, d, tile, dtype, q, k, v, o, lse, mask_heads,
+                    row_ptr, col_idx, scale, a, &noop);
+  if (st != BSATTN_OK) return st;
+  if (d != 128 || tile != 128 || dtype != BSATTN_DTYPE_BF16)
+    return fail(BSATTN_ERR_UNSUPPORTED, "fwd_planned: bf16, d 128 and tile 128 only");
+  st = plan_args("fwd_planned", B, H, N, tile, mask_heads, &workers);
+  if (st != BSATTN_OK) return st;
+  if (window < 0) return fail(BSATTN_ERR_INVALID_ARG, "fwd_planned: window must be >= 0");
+  if (noop) return ok();
+  if (window > 0 && (N % window != 0 || (N / window) % 128 != 0))
+    return fail(BSATTN_ERR_INVALID_ARG,
+                "fwd_planned: N=%d must be window=%d times a multiple of 128", N, window);
+  if ((int64_t)N * 256 >= ((int64_t)1 << 31))
+    return fail(BSATTN_ERR_INVALID_ARG, "fwd_planned: N * 256 bytes must stay below 2^31");
+  st = plan_fit("fwd_planned", B, H, N, mask_heads, workers, plan, plan_bytes, a.pl);
+  if (st != BSATTN_OK) return st;
+  a.plan = static_cast<const char*>(plan);
+  a.window = window;
+  return hip_status(bsattn::launch_fwd(a, stream), "fwd_planned");
 }
 
 BSATTN_API int bsattn_window_reorder(int32_t B, int32_t H, int32_t N, int32_t d, int32_t w,

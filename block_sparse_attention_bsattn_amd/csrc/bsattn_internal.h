@@ -19,6 +19,38 @@ struct MaskLaunch {
   int32_t force_diagonal;
 };
 
+// Work plan of the planned forward (bf16, d 128, tile 128): built on the
+// device from the CSR lists by launch_fwd_plan, read by the planned forward.
+// All offsets are in bytes from the start of the caller's plan buffer.
+struct PlanLayout {
+  int32_t B, H, N, tiles, mask_heads, workers, pairs;
+  int64_t items;      // B * H * pairs
+  int64_t step_cap;   // capacity of the step array (8-byte entries)
+  int64_t off_wstep;  // int32 [workers + 1]: each worker's range of the step array
+  int64_t off_witem;  // int32 [2 * workers]: each worker's (first, count) in witems
+  int64_t off_wcnt;   // int32 [workers]: steps of each worker's pair stream
+  int64_t off_witems; // int32 [items]: item words in each worker's order (bit 31: split mode)
+  int64_t off_pinfo;  // int32x4 [mask_heads * pairs]: union, common, n0, n1 per list pair
+  int64_t off_itmp;   // int32x4 [items]: worker, step offset, sequence number
+  int64_t off_steps;  // int32x2 [step_cap]: (entry word, item word)
+  int64_t bytes;
+};
+constexpr int32_t kPlanMagic = 0x42535031;
+// header: magic, B, H, N, tiles, Hm, workers, pairs, then the section
+// offsets / 16 (wstep, witem, wcnt, witems, pinfo, itmp, steps) and the step
+// capacity (clamped to 2^31 - 1)
+constexpr int kPlanHeaderInts = 16;
+constexpr int kPlanXcds = 8;
+constexpr int kPlanMaxTiles = 4096;
+constexpr int kPlanMaxWorkersPerXcd = 64;
+// Item words: (b * H + h) << 15 | pair, pair = query-tile pair index.
+constexpr int kPlanPairBits = 15;
+
+PlanLayout plan_layout(int32_t B, int32_t H, int32_t N, int32_t tile, int32_t mask_heads,
+                       int64_t nnz_bound, int32_t workers);
+// compute units of the current device (-1 on a runtime error)
+int device_compute_units();
+
 struct FwdLaunch {
   int32_t B, H, N, d, tile, dtype;
   const void* q;
@@ -33,6 +65,9 @@ struct FwdLaunch {
   int64_t col_cap;    // entries of col_idx that may be read
   float scale_log2;   // softmax scale * log2(e)
   int32_t window;     // 0, or w > 0: the grouped view (bf16 / d 128 / tile 128 only)
+  // planned forward only (plan == nullptr otherwise)
+  const char* plan;
+  PlanLayout pl;
 };
 
 // Each returns a hipError_t value (0 = success).
@@ -48,6 +83,9 @@ struct EnergyLaunch {
 int launch_build_mask(const MaskLaunch& a, uint8_t* mask, void* stream);
 int launch_compact(int32_t rows, int32_t tk, const uint8_t* mask,
                    int32_t* row_ptr, int32_t* col_idx, void* stream);
+// the work plan of the planned forward (three launches)
+int launch_fwd_plan(const PlanLayout& L, const int32_t* row_ptr, const int32_t* col_idx,
+                    int64_t col_cap, char* plan, void* stream);
 int launch_fwd(const FwdLaunch& a, void* stream);
 // tuned instance: bf16, head dim 128, 128x128 tiles, N * 256 < 2^31
 int launch_fwd_bf16_t128_d128(const FwdLaunch& a, void* stream);

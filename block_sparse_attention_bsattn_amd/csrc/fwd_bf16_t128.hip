@@ -240,7 +240,9 @@ __device__ __forceinline__ bool ent_in(int e, int grp) {
 // position p = r * G + c standing for buffer row c * w + r, so tile t is the
 // 128 buffer rows from row0(t) = (128 t mod G) * w + 128 t / G on at stride
 // w.  Every address below goes through that map; the arithmetic is the same.
-template <bool GRP>
+// PLANNED: one persistent workgroup per worker of a work plan (see the
+// pipelined stream below) instead of one workgroup per query-tile pair.
+template <bool GRP, bool PLANNED>
 __global__ void __launch_bounds__(512, 1)
 fwd_bf16_t128_d128(FwdLaunch a) {
   // K slots [0, 32K) and [32K, 64K) of a 64 KB-aligned array, so one XOR of
@@ -263,13 +265,15 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   lds_char_t* const kl = uniform_lds((lds_char_t*)kslots);
   lds_char_t* const vl = uniform_lds((lds_char_t*)vslots);
 
+  // one workgroup per query-tile pair (qt0, qt0 + 1)
+  const uint32_t pairs = (uint32_t)(a.tiles + 1) >> 1;
+  uint32_t logical = 0;
+  if constexpr (!PLANNED) {
   // ---- XCD-aware remap of the 1-D grid onto (batch*head, query-tile pair)
   const uint32_t G = gridDim.x, hw = blockIdx.x;
   const uint32_t q8 = G / NXCD, r8 = G % NXCD, xcd = hw % NXCD, slot = hw / NXCD;
   const uint32_t lo = xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8;
   const uint32_t cnt = q8 + (xcd < r8 ? 1u : 0u);
-  // one workgroup per query-tile pair (qt0, qt0 + 1)
-  const uint32_t pairs = (uint32_t)(a.tiles + 1) >> 1;
   // Longest first: the XCD's range is cut into chunks of LPT_CHUNK
   // workgroups, and inside a chunk the workgroup dispatched k-th takes the
   // pair with the k-th longest pair of lists (ties by position).  Pair
@@ -288,7 +292,6 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // the XCDs round by round in snake order (round s: ranks 8s .. 8s+7 to
   // XCDs 0..7, reversed on odd rounds; the last, partial round in order),
   // so every XCD gets an even share, longest first.
-  uint32_t logical;
   bool deal = a.mask_heads > 1 && G <= (uint32_t)DEAL_MAX && a.tiles <= DEAL_TILES;
   int* const keys_d = reinterpret_cast<int*>(kslots);  // G list lengths
   int* const misc = keys_d + DEAL_MAX;                 // scan partials and results
@@ -416,11 +419,14 @@ fwd_bf16_t128_d128(FwdLaunch a) {
     logical = (uint32_t)__builtin_amdgcn_readfirstlane(*pick);
     __syncthreads();  // the LDS is refilled by tile fetches below
   }
-  const int bh = (int)(logical / pairs);
-  const int qt0 = 2 * (int)(logical % pairs);
-  const int h = bh % a.H;
+  }  // !PLANNED
+  // the work item: (batch*head, query-tile pair); the planned stream moves
+  // from item to item
+  int bh = (int)(logical / pairs);
+  int qt0 = 2 * (int)(logical % pairs);
+  int h = bh % a.H;
   const int N = a.N;
-  const int64_t head_row = (int64_t)bh * N;
+  int64_t head_row = (int64_t)bh * N;
   const int gw = GRP ? a.window : 1;
   const int gG = GRP ? N / a.window : 1;
   // buffer row of the first row of position-major tile t; rows of a tile are
@@ -432,10 +438,14 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // in every wave)
   const sconst_i32 row_ptr = (sconst_i32)(uintptr_t)a.row_ptr;
   const sconst_i32 col_idx = (sconst_i32)(uintptr_t)a.col_idx;
-  const int hrow = (a.mask_heads == 1 ? 0 : h) * a.tiles;
-  int jb0 = 0, jb1 = 0;
-  const int n0 = list_len(row_ptr, a.col_cap, hrow + qt0, jb0);
-  const int n1 = qt0 + 1 < a.tiles ? list_len(row_ptr, a.col_cap, hrow + qt0 + 1, jb1) : 0;
+  int jb0 = 0, jb1 = 0, n0 = 0, n1 = 0;
+  // the two lists of query tiles qt0 and qt0 + 1 of head h
+  auto item_lists = [&]() INLINE {
+    const int hrow = (a.mask_heads == 1 ? 0 : h) * a.tiles;
+    n0 = list_len(row_ptr, a.col_cap, hrow + qt0, jb0);
+    n1 = qt0 + 1 < a.tiles ? list_len(row_ptr, a.col_cap, hrow + qt0 + 1, jb1) : 0;
+  };
+  if constexpr (!PLANNED) item_lists();
   // Each list keeps its validated head c (index i) and the raw entry at
   // index i + 1, loaded one step ahead: a value is validated only when it
   // becomes the head, by which time its scalar load has long completed.
@@ -491,8 +501,8 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // one list is empty.  I is counted exactly, all threads at once: list B's
   // tiles set bits of a bitmap in the (still unused) V slots, then list A's
   // entries test them.  The choice affects speed only.
-  bool split;
-  {
+  bool split = false;
+  if constexpr (!PLANNED) {
     uint32_t* const bits = reinterpret_cast<uint32_t*>(vslots);
     constexpr int BW = 2 * TILE_BYTES / 4 - 1;  // bitmap words; the last one counts
     uint32_t* const common = bits + BW;
@@ -525,11 +535,13 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   }
 
   // ---- Q^T operand: lane holds q[row l%32][8 d values], 8 chunks of 16 d
+  // (hr = the head's first row, b*H*N + h*N), scaled by scale*log2(e) and
+  // rounded to bf16
   bf16x8 qf[8];
-  auto load_q = [&](int tq) INLINE {
+  auto load_q = [&](int64_t hr, int tq) INLINE {
     const int qr = tq * BT + wg * 32 + l32;
     const int64_t qb = GRP ? (int64_t)row0(tq) + (int64_t)(wg * 32 + l32) * gw : qr;
-    const __bf16* qptr = reinterpret_cast<const __bf16*>(a.q) + (head_row + qb) * D + half * 8;
+    const __bf16* qptr = reinterpret_cast<const __bf16*>(a.q) + (hr + qb) * D + half * 8;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       if (tq < a.tiles && qr < N) {
@@ -543,14 +555,21 @@ fwd_bf16_t128_d128(FwdLaunch a) {
     }
   };
 
-  // ---- buffer resources for this head's K and V rows
-  const char* kbase = reinterpret_cast<const char*>(a.k) + head_row * ROW_BYTES;
-  const char* vbase = reinterpret_cast<const char*>(a.v) + head_row * ROW_BYTES;
+  // ---- buffer resources for a head's K and V rows (hr = its first row)
   const int nbytes = N * ROW_BYTES;
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, nbytes, 0x00020000);
-  const i32x4 krs4 = raw_rsrc(kbase, nbytes);
-  const i32x4 vrs4 = raw_rsrc(vbase, nbytes);
+  auto k_rsrc = [&](int64_t hr) INLINE {
+    return raw_rsrc(reinterpret_cast<const char*>(a.k) + hr * ROW_BYTES, nbytes);
+  };
+  auto v_rsrc = [&](int64_t hr) INLINE {
+    return raw_rsrc(reinterpret_cast<const char*>(a.v) + hr * ROW_BYTES, nbytes);
+  };
+  auto k_brsrc = [&](int64_t hr) INLINE {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(a.k) + hr * ROW_BYTES), (short)0, nbytes,
+        0x00020000);
+  };
+  i32x4 krs4 = k_rsrc(head_row);
+  i32x4 vrs4 = v_rsrc(head_row);
 
   // Direct-load offsets.  Load i (0..7) of wave wg fills LDS bytes
   // [(8 wg + i) * 1024, +1024) of a slot: rows 32 wg + 4i + (0..3).  Lane l
@@ -778,12 +797,12 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // about 64 B per clock per CU, and issuing all 16 loads at once would
   // stall the wave until the queue had room.
   auto vector_phase = [&](bool do_sm, int j, int tk, int tv, uint32_t kbuf, uint32_t vbuf,
-                          uint32_t skip) INLINE {
+                          uint32_t skip, const i32x4& rsk, const i32x4& rsv) INLINE {
     const uint32_t tko = tile_off(tk), tvo = tile_off(tv);
     // part 0: K loads 0-3; 1: K loads 4-7; 2: V loads 0-3; 3: V loads 4-7
     // (part is a constant after unrolling)
     auto fetch_part = [&](int part) INLINE {
-      const i32x4& rs = part < 2 ? krs4 : vrs4;
+      const i32x4& rs = part < 2 ? rsk : rsv;
       const uint32_t buf = (part < 2 ? kbuf : vbuf) + (uint32_t)(8 * wg * 1024);
       const uint32_t to = part < 2 ? tko : tvo;
       // loads 4(part%2) .. +3: rows 16(part%2) .. of this wave's 32-row share
@@ -808,7 +827,7 @@ fwd_bf16_t128_d128(FwdLaunch a) {
 
   // K of entry e (a key tile) into K slot 0, loaded by all 8 waves (4 KB
   // each), then a full wait and a barrier
-  auto load_first_k = [&](int e) INLINE {
+  auto load_first_k = [&](int e, const __amdgpu_buffer_rsrc_t& krs) INLINE {
     if (e != NONE) {
       const uint32_t t0 = tile_off(ent_tile(e));
       lds_char_t* dst = kl + (grp * 4) * 1024;  // group g loads rows 16g.. of each 64-row half
@@ -824,11 +843,11 @@ fwd_bf16_t128_d128(FwdLaunch a) {
 
   // O = O^T / l for this wave's rows of query tile tq (rows past N not
   // written); db0 .. db0 + ndb - 1 are the 32-wide d blocks written
-  auto store_o = [&](int tq, float inv, int db0, int ndb) INLINE {
+  auto store_o = [&](int64_t hr, int tq, float inv, int db0, int ndb) INLINE {
     const int qr = tq * BT + wg * 32 + l32;
     if (tq < a.tiles && qr < N) {
       const int64_t qb = GRP ? (int64_t)row0(tq) + (int64_t)(wg * 32 + l32) * gw : qr;
-      __bf16* op = reinterpret_cast<__bf16*>(a.o) + (head_row + qb) * D;
+      __bf16* op = reinterpret_cast<__bf16*>(a.o) + (hr + qb) * D;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         if (db < db0 || db >= db0 + ndb) continue;
@@ -844,11 +863,11 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       }
     }
   };
-  auto store_lse = [&](int tq, float mm, float ll) INLINE {
+  auto store_lse = [&](int64_t hr, int tq, float mm, float ll) INLINE {
     const int qr = tq * BT + wg * 32 + l32;
     const int64_t qb = GRP ? (int64_t)row0(tq) + (int64_t)(wg * 32 + l32) * gw : qr;
     if (tq < a.tiles && qr < N && a.lse != nullptr && half == 0)
-      a.lse[head_row + qb] = ll > 0.f ? (mm + log2f(ll)) * 0.69314718055994531f : -INFINITY;
+      a.lse[hr + qb] = ll > 0.f ? (mm + log2f(ll)) * 0.69314718055994531f : -INFINITY;
   };
   auto l_over_halves = [&]() INLINE {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l),
@@ -857,10 +876,22 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   };
 
   int e_m1, e_0, e_1, e_2;
+  auto reset_state = [&]() INLINE {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) nm[e] = 0.f;
+  };
+
+  if constexpr (!PLANNED) {
   if (!split) {
     // ================= pair mode =================
     const int qt = qt0 + grp;
-    load_q(qt);
+    load_q(head_row, qt);
     init_lists(jb0, n0, jb1, n1);
     kr = kr_slot0;
     vr[0] = vr0_slot0 ^ (uint32_t)TILE_BYTES;
@@ -874,7 +905,7 @@ fwd_bf16_t128_d128(FwdLaunch a) {
     e_2 = next_entry();
 
     // ---- prologue: K_0 into slot 0
-    load_first_k(e_0);
+    load_first_k(e_0, k_brsrc(head_row));
 
     // Every wave alternates matrix and vector phases; group 1 starts with a
     // vector phase (phase 0) and so is one phase behind.  Pair w = phases
@@ -912,7 +943,7 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       }
       vector_phase(ent_in(es, grp), ent_tile(es), tk, tv,
                    kl32 + (uint32_t)(((w + 1) & 1) * TILE_BYTES),
-                   vl32 + (uint32_t)((w & 1) * TILE_BYTES), skip);
+                   vl32 + (uint32_t)((w & 1) * TILE_BYTES), skip, krs4, vrs4);
     };
     if (grp == 1 && e_0 != NONE) {
       // phase 0 (with no entry at all there is none: group 0 runs no
@@ -936,9 +967,171 @@ fwd_bf16_t128_d128(FwdLaunch a) {
 
     // ---- epilogue: O = O^T / l
     l_over_halves();
-    store_o(qt, l > 0.f ? 1.f / l : 0.f, 0, 4);
-    store_lse(qt, m, l);
+    store_o(head_row, qt, l > 0.f ? 1.f / l : 0.f, 0, 4);
+    store_lse(head_row, qt, m, l);
+  }
   } else {
+    // ================= planned: one persistent workgroup per worker =================
+    // The worker's pair-mode items form one stream of steps (each item's
+    // union list, item after item), walked exactly as one item's list in
+    // pair mode above, with no drain between items: when the next entry
+    // begins a new item, the vector phase ends by loading and scaling that
+    // item's Q rows (Q is free once the old item's last S is done) and
+    // clearing the -m bias; when the current entry begins a new item, the
+    // vector phase first writes the old item's O and LSE (its last P V ran
+    // in the matrix phase just ended) and clears O, m and l.  K and V tiles
+    // are fetched from the head of the item each entry belongs to.  Then
+    // the worker's split-mode items run one after the other as above.
+    const sconst_i32 hdr = (sconst_i32)(uintptr_t)a.plan;
+    const int wk = (int)blockIdx.x;
+    const int BH = a.B * a.H;
+    if (hdr[0] != kPlanMagic || hdr[1] != a.B || hdr[2] != a.H || hdr[3] != N ||
+        hdr[4] != a.tiles || hdr[5] != a.mask_heads || hdr[6] != (int)gridDim.x ||
+        hdr[7] != (int)pairs)
+      return;  // a plan made for other arguments (uniform: nothing ran yet)
+    const int64_t cap = a.pl.step_cap;
+    const sconst_i32 wstep = (sconst_i32)(uintptr_t)(a.plan + a.pl.off_wstep);
+    int sb = wstep[wk], se = wstep[wk + 1];
+    sb = max(sb, 0);
+    se = (int)min((int64_t)se, cap);
+    if (se < sb) se = sb;
+    typedef const __attribute__((address_space(4))) uint64_t* sconst_u64;
+    const sconst_u64 steps = (sconst_u64)(uintptr_t)(a.plan + a.pl.off_steps);
+    // item word -> the head's first row, and this group's query tile
+    auto item_hr = [&](int iw) INLINE {
+      return (int64_t)min((int)((uint32_t)iw >> kPlanPairBits), BH - 1) * N;
+    };
+    auto item_qt = [&](int iw) INLINE {
+      return 2 * min(iw & ((1 << kPlanPairBits) - 1), (int)pairs - 1) + grp;
+    };
+    int i_m1 = -1, i_0 = -1, i_1 = -1, i_2 = -1;  // item words of the window
+    if (sb < se) {
+      int sidx = sb;
+      const int slast = se - 1;
+      uint64_t look = steps[sb];  // the next step, loaded one call ahead
+      auto next_step = [&](int& iw) INLINE {
+        const bool have = sidx < se;
+        const uint64_t cur = look;
+        ++sidx;
+        look = steps[min(sidx, slast)];
+        iw = have ? (int)(uint32_t)(cur >> 32) : -1;
+        return have ? (int)((uint32_t)cur & 0x7FFFFFFFu) : NONE;
+      };
+      e_m1 = NONE;
+      e_0 = next_step(i_0);
+      e_1 = next_step(i_1);
+      e_2 = next_step(i_2);
+      int cur = i_0;  // the item whose O this group accumulates
+      int64_t cur_hr = item_hr(cur);
+      int cur_qt = item_qt(cur);
+      load_q(cur_hr, cur_qt);
+      kr = kr_slot0;
+      vr[0] = vr0_slot0 ^ (uint32_t)TILE_BYTES;
+      vr[1] = vr1_slot0 ^ (uint32_t)TILE_BYTES;
+      int w = 0;
+      load_first_k(e_0, k_brsrc(item_hr(i_0)));
+      auto advance = [&]() INLINE {
+        e_m1 = e_0;
+        i_m1 = i_0;
+        e_0 = e_1;
+        i_0 = i_1;
+        e_1 = e_2;
+        i_1 = i_2;
+        e_2 = next_step(i_2);
+        flip_slots();
+      };
+      const uint32_t skip = __builtin_amdgcn_readfirstlane(grp != 1 ? 1u : 0u);
+      auto run_vector_phase = [&](bool in_loop) INLINE {
+        const int es = in_loop ? e_0 : NONE;
+        const int tk = ent_tile(in_loop ? e_2 : e_1);
+        const int ik = in_loop ? i_2 : i_1;
+        const int tv = ent_tile(in_loop ? e_1 : e_0);
+        const int iv = in_loop ? i_1 : i_0;
+        bool bnd = false, nxt = false;
+        int ncur = 0, nq = 0;
+        if (in_loop) {
+          bnd = e_0 != NONE && e_m1 != NONE && i_0 != i_m1;
+          nxt = e_1 != NONE && i_1 != i_0;
+          ncur = i_0;
+          nq = i_1;
+          advance();
+          ++w;
+        }
+        if (bnd) {
+          l_over_halves();
+          store_o(cur_hr, cur_qt, l > 0.f ? 1.f / l : 0.f, 0, 4);
+          store_lse(cur_hr, cur_qt, m, l);
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+          m = -INFINITY;
+          l = 0.f;
+          cur = ncur;
+          cur_hr = item_hr(cur);
+          cur_qt = item_qt(cur);
+        }
+        vector_phase(ent_in(es, grp), ent_tile(es), tk, tv,
+                     kl32 + (uint32_t)(((w + 1) & 1) * TILE_BYTES),
+                     vl32 + (uint32_t)((w & 1) * TILE_BYTES), skip, k_rsrc(item_hr(ik)),
+                     v_rsrc(item_hr(iv)));
+        if (nxt) {
+          // the new item's Q, loaded and scaled here so that no load of it
+          // is pending in the matrix phases (group 1 also waits here for
+          // this phase's tile fetches, once per item)
+          load_q(item_hr(nq), item_qt(nq));
+#pragma unroll
+          for (int e = 0; e < 16; ++e) nm[e] = 0.f;
+        }
+      };
+      if (grp == 1) {
+        run_vector_phase(false);  // phase 0
+        BARRIER();
+      }
+      while (e_0 != NONE || e_m1 != NONE) {
+        matrix_phase(ent_in(e_m1, grp), ent_in(e_0, grp));
+        if (grp == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        BARRIER();
+        if (grp == 1 && !(e_1 != NONE || e_0 != NONE)) break;
+        run_vector_phase(true);
+        BARRIER();
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      l_over_halves();
+      store_o(cur_hr, cur_qt, l > 0.f ? 1.f / l : 0.f, 0, 4);
+      store_lse(cur_hr, cur_qt, m, l);
+    }
+  }
+
+  // ================= split-mode items =================
+  // Not planned: this workgroup's pair, when its mode is split.  Planned:
+  // the worker's split-mode items, one after the other (both groups have
+  // passed the same barriers in the stream, and no LDS read or tile fetch
+  // is in flight).
+  int ib = 0, ic = split ? 1 : 0;
+  if constexpr (PLANNED) {
+    const sconst_i32 witem = (sconst_i32)(uintptr_t)(a.plan + a.pl.off_witem);
+    const int64_t items = a.pl.items;
+    ib = (int)min(max((int64_t)witem[2 * blockIdx.x], (int64_t)0), items);
+    ic = (int)min(max((int64_t)witem[2 * blockIdx.x + 1], (int64_t)0), items - ib);
+  }
+#pragma unroll 1
+  for (int t = 0; t < ic; ++t) {
+    if constexpr (PLANNED) {
+      const sconst_i32 witems = (sconst_i32)(uintptr_t)(a.plan + a.pl.off_witems);
+      const int iw = witems[ib + t];
+      if (iw >= 0) continue;  // a pair-mode item: done in the stream
+      const int BH = a.B * a.H;
+      const int wd = iw & 0x7FFFFFFF;
+      bh = min(wd >> kPlanPairBits, BH - 1);
+      qt0 = 2 * min(wd & ((1 << kPlanPairBits) - 1), (int)pairs - 1);
+      h = bh % a.H;
+      head_row = (int64_t)bh * N;
+      krs4 = k_rsrc(head_row);
+      vrs4 = v_rsrc(head_row);
+      item_lists();
+      reset_state();
+    }
     // ================= split mode =================
     // Both groups work on one query tile (the same 128 rows, the same Q),
     // entry e of its list going to group e % 2.  Phase p: group p % 2 runs
@@ -964,7 +1157,7 @@ fwd_bf16_t128_d128(FwdLaunch a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) nm[e] = 0.f;
       }
-      load_q(tq);
+      load_q(head_row, tq);
       init_lists(tt == 0 ? jb0 : jb1, tt == 0 ? n0 : n1, 0, 0);
       kr = kr_slot0 ^ (uint32_t)(grp * TILE_BYTES);
       vr[0] = vr0_slot0 ^ (uint32_t)(grp * TILE_BYTES);
@@ -974,7 +1167,7 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       e_m1 = NONE;
       e_0 = next_entry();
       e_1 = next_entry();
-      load_first_k(e_0);
+      load_first_k(e_0, k_brsrc(head_row));
       const uint32_t kown = kl32 + (uint32_t)(grp * TILE_BYTES);
       const uint32_t vown = vl32 + (uint32_t)(grp * TILE_BYTES);
       // n + 2 phases (p = 0 .. n+1); group g runs its matrix phases at
@@ -991,7 +1184,8 @@ fwd_bf16_t128_d128(FwdLaunch a) {
         // the softmax always runs: with no entry (j = -1) every score is
         // masked to -inf, so P = 0 and m, l and O stay as they are (a
         // runtime choice here costs the register allocator dearly)
-        vector_phase(true, ent_tile(e_m1), ent_tile(e_1), ent_tile(e_m1), kown, vown, 0u);
+        vector_phase(true, ent_tile(e_m1), ent_tile(e_1), ent_tile(e_m1), kown, vown, 0u, krs4,
+                     vrs4);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         BARRIER();
         split_advance();
@@ -1052,10 +1246,10 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       if (grp == 0) keep_half(0); else keep_half(2);
       const float lt = l * a0 + lpn * a1;
       if (grp == 0)
-        store_o(tq, lt > 0.f ? 1.f / lt : 0.f, 0, 2);
+        store_o(head_row, tq, lt > 0.f ? 1.f / lt : 0.f, 0, 2);
       else
-        store_o(tq, lt > 0.f ? 1.f / lt : 0.f, 2, 2);
-      if (grp == 0) store_lse(tq, mt, lt);
+        store_o(head_row, tq, lt > 0.f ? 1.f / lt : 0.f, 2, 2);
+      if (grp == 0) store_lse(head_row, tq, mt, lt);
       // the exchange area is the next tile's K slot 0
       BARRIER();
     }
@@ -1065,14 +1259,24 @@ fwd_bf16_t128_d128(FwdLaunch a) {
 }  // namespace
 
 int launch_fwd_bf16_t128_d128(const FwdLaunch& a, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (a.plan != nullptr) {
+    // one persistent workgroup per worker of the plan
+    const dim3 grid((unsigned)a.pl.workers);
+    if (a.window > 0)
+      hipLaunchKernelGGL((fwd_bf16_t128_d128<true, true>), grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_bf16_t128_d128<false, true>), grid, dim3(512), 0, s, a);
+    return hipGetLastError();
+  }
   // one workgroup per (batch*head, query-tile pair), in either mode
   const int64_t blocks = (int64_t)a.B * a.H * ((a.tiles + 1) / 2);
   if (a.window > 0)
-    hipLaunchKernelGGL(fwd_bf16_t128_d128<true>, dim3((unsigned)blocks), dim3(512), 0,
-                       (hipStream_t)stream, a);
+    hipLaunchKernelGGL((fwd_bf16_t128_d128<true, false>), dim3((unsigned)blocks), dim3(512), 0,
+                       s, a);
   else
-    hipLaunchKernelGGL(fwd_bf16_t128_d128<false>, dim3((unsigned)blocks), dim3(512), 0,
-                       (hipStream_t)stream, a);
+    hipLaunchKernelGGL((fwd_bf16_t128_d128<false, false>), dim3((unsigned)blocks), dim3(512), 0,
+                       s, a);
   return hipGetLastError();
 }
 

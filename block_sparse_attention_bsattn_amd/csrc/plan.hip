@@ -1,0 +1,440 @@
+// Work plan of the planned block-sparse forward (bf16, d 128, 128x128 tiles).
+//
+// The active lists are static inputs of the forward (CalibAtt page, "B. Fase
+// di Inferenza": the kernel follows precomputed per-block lists and takes no
+// decision itself), so everything the forward's workgroups would otherwise
+// work out for themselves at every launch is worked out once per list set:
+// which query-tile pairs go to which worker (one persistent workgroup per
+// compute unit), in which order, and the merged key-tile list of every pair.
+//
+// A work item is one (batch, head, query-tile pair p) -- query tiles 2p and
+// 2p + 1.  Its two groups of four waves own one query tile each and walk the
+// union of the two active lists (pair mode), or, when the lists have little
+// in common, the two tiles are processed one after the other (split mode):
+// split mode when 5 I < n0 + n1 (I common tiles of lists of n0 and n1
+// entries), and always when one list is empty.
+//
+// Three launches:
+//   1. pairs:  one wave per (mask slice, pair): the two lists become bitmaps
+//              in LDS; the union and common tile counts are popcounts.
+//   2. assign: one wave per XCD.  Items are cut into eight contiguous ranges
+//              of equal estimated cost (neighbouring pairs of a head share
+//              key tiles, which the XCD's L2 then serves), and each range is
+//              spread over the XCD's workers (worker w runs on XCD w % 8):
+//              64 items at a time are ranked by cost, longest first, and
+//              dealt a round at a time, the longest to the least-loaded
+//              worker.  Records each item's worker, its place in the
+//              worker's order and the offset of its steps in the worker's
+//              pair-mode stream.
+//   3. steps:  one wave per item: the worker's item list, and for a pair-mode
+//              item its union list in ascending key-tile order, one step per
+//              tile, (tile | group 0 needs it << 30 | group 1 needs it << 29,
+//              item word).  An empty union is one step with no tile.
+//
+// Outputs depend only on the lists: the forward computes every item the same
+// way whichever worker runs it.  Every read of the CSR is clamped to its
+// capacity and every write to the plan's own capacity.
+#include <hip/hip_runtime.h>
+
+#include "bsattn_internal.h"
+
+namespace bsattn {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWords = kPlanMaxTiles / 32;  // bitmap words per list
+constexpr int kBadTile = 0x0FFFFFFE;        // a step with no key tile
+
+struct PlanArgs {
+  PlanLayout L;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int64_t col_cap;
+  char* plan;
+};
+
+__device__ __forceinline__ int32_t* P32(const PlanArgs& a, int64_t off) {
+  return reinterpret_cast<int32_t*>(a.plan + off);
+}
+
+// list of CSR row r: first entry and length, clamped to the capacity
+__device__ __forceinline__ int list_of(const PlanArgs& a, int r, int64_t& begin) {
+  int64_t b0 = a.row_ptr[r], e0 = a.row_ptr[r + 1];
+  if (b0 < 0) b0 = 0;
+  if (e0 > a.col_cap) e0 = a.col_cap;
+  begin = b0;
+  return e0 > b0 ? (int)(e0 - b0) : 0;
+}
+
+// The two lists of pair p in mask slice s as bitmaps in this wave's LDS
+// words (bm[0..kWords) for tile 2p, bm[kWords..2 kWords) for tile 2p + 1);
+// entries outside [0, tiles) are left out.  Returns the raw list lengths.
+// Called by every wave of the workgroup (it holds workgroup barriers); a
+// wave with use == false builds empty bitmaps.
+__device__ void lists_to_bitmaps(const PlanArgs& a, bool use, int s, int p, uint32_t* bm,
+                                 int lane, int& n0, int& n1) {
+  const int tiles = a.L.tiles;
+  for (int wd = lane; wd < 2 * kWords; wd += kWave) bm[wd] = 0u;
+  __syncthreads();
+  n0 = n1 = 0;
+  int64_t b0 = 0, b1 = 0;
+  if (use) {
+    const int r0 = s * tiles + 2 * p;
+    n0 = list_of(a, r0, b0);
+    n1 = 2 * p + 1 < tiles ? list_of(a, r0 + 1, b1) : 0;
+  }
+  for (int e = lane; e < n0; e += kWave) {
+    const int t = a.col_idx[b0 + e];
+    if (t >= 0 && t < tiles) atomicOr(&bm[t >> 5], 1u << (t & 31));
+  }
+  for (int e = lane; e < n1; e += kWave) {
+    const int t = a.col_idx[b1 + e];
+    if (t >= 0 && t < tiles) atomicOr(&bm[kWords + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+}
+
+// the 64 tiles 64 lane .. 64 lane + 63 of both bitmaps
+__device__ __forceinline__ void lane_words(const uint32_t* bm, int lane, uint64_t& wa,
+                                           uint64_t& wb) {
+  const int w0 = 2 * lane;
+  wa = (uint64_t)bm[w0] | ((uint64_t)bm[w0 + 1] << 32);
+  wb = (uint64_t)bm[kWords + w0] | ((uint64_t)bm[kWords + w0 + 1] << 32);
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ---- 1. per (mask slice, pair): union and common tile counts
+__global__ void __launch_bounds__(256) plan_pairs_kernel(PlanArgs a) {
+  __shared__ uint32_t bms[4][2 * kWords];
+  const int lane = threadIdx.x % kWave;
+  const int wv = threadIdx.x / kWave;
+  const int64_t sp = (int64_t)blockIdx.x * 4 + wv;
+  const PlanLayout& L = a.L;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    int32_t* h = P32(a, 0);
+    h[0] = kPlanMagic;
+    h[1] = L.B;
+    h[2] = L.H;
+    h[3] = L.N;
+    h[4] = L.tiles;
+    h[5] = L.mask_heads;
+    h[6] = L.workers;
+    h[7] = L.pairs;
+    // the sections, in units of 16 bytes, and the step capacity (for readers
+    // of the plan other than the forward)
+    h[8] = (int32_t)(L.off_wstep / 16);
+    h[9] = (int32_t)(L.off_witem / 16);
+    h[10] = (int32_t)(L.off_wcnt / 16);
+    h[11] = (int32_t)(L.off_witems / 16);
+    h[12] = (int32_t)(L.off_pinfo / 16);
+    h[13] = (int32_t)(L.off_itmp / 16);
+    h[14] = (int32_t)(L.off_steps / 16);
+    h[15] = (int32_t)min(L.step_cap, (int64_t)0x7FFFFFFF);
+  }
+  const bool use = sp < (int64_t)L.mask_heads * L.pairs;
+  const int s = use ? (int)(sp / L.pairs) : 0, p = use ? (int)(sp % L.pairs) : 0;
+  int n0, n1;
+  lists_to_bitmaps(a, use, s, p, bms[wv], lane, n0, n1);
+  uint64_t wa, wb;
+  lane_words(bms[wv], lane, wa, wb);
+  const int u = wave_sum(__popcll(wa | wb));
+  const int common = wave_sum(__popcll(wa & wb));
+  if (use && lane == 0) {
+    int32_t* pi = P32(a, L.off_pinfo) + 4 * sp;
+    pi[0] = u;
+    pi[1] = common;
+    pi[2] = n0;
+    pi[3] = n1;
+  }
+}
+
+struct ItemCost {
+  int cost;   // estimated work, in fifths of a pair-mode step
+  int steps;  // steps in the worker's pair-mode stream (0 in split mode)
+  int split;
+};
+
+__device__ __forceinline__ ItemCost item_cost(const PlanArgs& a, int64_t i) {
+  const PlanLayout& L = a.L;
+  const int64_t bh = i / L.pairs;
+  const int p = (int)(i - bh * L.pairs);
+  const int s = L.mask_heads == 1 ? 0 : (int)(bh % L.H);
+  const int32_t* pi = P32(a, L.off_pinfo) + 4 * ((int64_t)s * L.pairs + p);
+  const int u = pi[0], common = pi[1], n0 = pi[2], n1 = pi[3];
+  ItemCost c;
+  // the forward's own rule: split mode unless the lists largely coincide
+  c.split = (n0 == 0 || n1 == 0 || 5 * common < n0 + n1) ? 1 : 0;
+  // a split-mode step serves half the rows of a pair-mode one and runs
+  // about 0.8 as long; each item also pays a fixed set-up (pair mode: the
+  // hand-over to the next item; split mode: a drained start and the
+  // combine of the two groups)
+  c.steps = c.split ? 0 : max(u, 1);
+  c.cost = c.split ? 4 * (n0 + n1) + 30 : 5 * (c.steps + 1);
+  return c;
+}
+
+// ---- 2. per XCD: the item range and its deal over the XCD's workers
+__global__ void __launch_bounds__(kWave) plan_assign_kernel(PlanArgs a) {
+  __shared__ int sorted[kWave];
+  __shared__ int s_cost[kWave], s_steps[kWave];
+  const int lane = threadIdx.x;
+  const int x = blockIdx.x;  // XCD
+  const PlanLayout& L = a.L;
+  const int64_t G = L.items;
+  const int R = L.workers / kPlanXcds;  // workers of this XCD: w = x + 8 j
+
+  // item i goes to XCD floor(8 (2 prefix(i) + cost(i)) / (2 C)): contiguous
+  // ranges of about equal cost
+  const int64_t per = (G + kWave - 1) / kWave;
+  const int64_t c0 = min((int64_t)lane * per, G), c1 = min(c0 + per, G);
+  int64_t sum = 0;
+  for (int64_t i = c0; i < c1; ++i) sum += item_cost(a, i).cost;
+  int64_t pre = sum;  // inclusive scan over lanes
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int64_t t = __shfl_up(pre, o, kWave);
+    if (lane >= o) pre += t;
+  }
+  const int64_t total = __shfl(pre, kWave - 1, kWave);
+  int64_t run = pre - sum;
+  int64_t below = 0, upto = 0;  // items of this lane's chunk on XCDs < x, <= x
+  for (int64_t i = c0; i < c1; ++i) {
+    const int c = item_cost(a, i).cost;
+    const int64_t xi = total > 0 ? min((int64_t)kPlanXcds - 1,
+                                       (kPlanXcds * (2 * run + c)) / (2 * total))
+                                 : 0;
+    below += xi < x ? 1 : 0;
+    upto += xi <= x ? 1 : 0;
+    run += c;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    below += __shfl_xor(below, o, kWave);
+    upto += __shfl_xor(upto, o, kWave);
+  }
+  const int64_t lo = below, hi = upto;
+
+  // deal [lo, hi) over the R workers; lane j < R keeps worker j's load,
+  // item count and pair-mode steps
+  int64_t load = 0;
+  int cnt = 0, nsteps = 0;
+  for (int64_t b0 = lo; b0 < hi; b0 += kWave) {
+    const int64_t i = b0 + lane;
+    const bool valid = i < hi;
+    ItemCost ic;
+    ic.cost = 0;
+    ic.steps = 0;
+    ic.split = 0;
+    if (valid) ic = item_cost(a, i);
+    // longest first, ties by position
+    const int64_t key = valid ? ((int64_t)ic.cost << 32) | (uint32_t)(0xFFFF - lane) : -1;
+    int rank = 0;
+    for (int l2 = 0; l2 < kWave; ++l2) {
+      const int64_t k2 = __shfl(key, l2, kWave);
+      rank += k2 > key ? 1 : 0;
+    }
+    if (valid) {
+      sorted[rank] = lane;
+      s_cost[lane] = ic.cost;
+      s_steps[lane] = ic.steps + (ic.split << 30);
+    }
+    __syncthreads();
+    const int nvalid = (int)min((int64_t)kWave, hi - b0);
+    for (int r0 = 0; r0 < nvalid; r0 += R) {
+      const int k = min(R, nvalid - r0);
+      // rank of worker j by load (ties by index)
+      int wr = 0;
+      for (int j2 = 0; j2 < R; ++j2) {
+        const int64_t l2 = __shfl(load, j2, kWave);
+        wr += (l2 < load || (l2 == load && j2 < lane)) ? 1 : 0;
+      }
+      if (lane < R && wr < k) {
+        const int src = sorted[r0 + wr];
+        const int64_t item = b0 + src;
+        const int st = s_steps[src];
+        const int w = x + kPlanXcds * lane;
+        int32_t* it = P32(a, L.off_itmp) + 4 * item;
+        it[0] = w;
+        it[1] = nsteps;
+        it[2] = cnt;
+        it[3] = st >> 30;  // split
+        load += s_cost[src];
+        nsteps += st & 0x3FFFFFFF;
+        cnt += 1;
+      }
+    }
+    __syncthreads();
+  }
+  // worker j's items take witems[lo + (items of workers < j), ...)
+  int pc = lane < R ? cnt : 0;
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(pc, o, kWave);
+    if (lane >= o) pc += t;
+  }
+  if (lane < R) {
+    const int w = x + kPlanXcds * lane;
+    P32(a, L.off_witem)[2 * w] = (int)(lo + pc - cnt);
+    P32(a, L.off_witem)[2 * w + 1] = cnt;
+    P32(a, L.off_wcnt)[w] = nsteps;
+  }
+}
+
+// ---- 3. per item: the worker's item list and the pair's merged steps
+__global__ void __launch_bounds__(256) plan_steps_kernel(PlanArgs a) {
+  __shared__ uint32_t bms[4][2 * kWords];
+  __shared__ int64_t wbase[kPlanXcds * kPlanMaxWorkersPerXcd + 1];
+  __shared__ int64_t part[256];
+  const PlanLayout& L = a.L;
+  const int W = L.workers;  // at most 512: two per thread
+  const int tid = threadIdx.x;
+  // every workgroup scans the workers' stream lengths
+  {
+    const int32_t* wc = P32(a, L.off_wcnt);
+    const int64_t v0 = 2 * tid < W ? wc[2 * tid] : 0;
+    const int64_t v1 = 2 * tid + 1 < W ? wc[2 * tid + 1] : 0;
+    part[tid] = v0 + v1;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const int64_t t = tid >= o ? part[tid - o] : 0;
+      __syncthreads();
+      part[tid] += t;
+      __syncthreads();
+    }
+    const int64_t ex = part[tid] - v0 - v1;
+    if (2 * tid < W) wbase[2 * tid] = ex;
+    if (2 * tid + 1 < W) wbase[2 * tid + 1] = ex + v0;
+    if (tid == 255) wbase[W] = part[255];
+    __syncthreads();
+  }
+  if (blockIdx.x == 0) {
+    for (int w = tid; w <= W; w += blockDim.x)
+      P32(a, L.off_wstep)[w] = (int32_t)min(wbase[w], L.step_cap);
+  }
+  const int lane = tid % kWave;
+  const int wv = tid / kWave;
+  int2* steps = reinterpret_cast<int2*>(a.plan + L.off_steps);
+  for (int64_t i0 = (int64_t)blockIdx.x * 4; i0 < L.items; i0 += (int64_t)gridDim.x * 4) {
+    const int64_t i = i0 + wv;
+    bool use = i < L.items;
+    int w = 0, off = 0, seq = 0, split = 1;
+    if (use) {
+      const int32_t* it = P32(a, L.off_itmp) + 4 * i;
+      w = it[0];
+      off = it[1];
+      seq = it[2];
+      split = it[3];
+      use = w >= 0 && w < W;  // every item is dealt; kept as a guard
+    }
+    const int64_t bh = use ? i / L.pairs : 0;
+    const int p = use ? (int)(i - bh * L.pairs) : 0;
+    const int word = (int)((bh << kPlanPairBits) | p);
+    if (use && lane == 0) {
+      const int32_t* wi = P32(a, L.off_witem) + 2 * w;
+      if (seq < wi[1]) P32(a, L.off_witems)[wi[0] + seq] = word | (split << 31);
+    }
+    const bool merge = use && !split;
+    const int s = L.mask_heads == 1 ? 0 : (int)(bh % L.H);
+    int n0, n1;
+    lists_to_bitmaps(a, merge, s, p, bms[wv], lane, n0, n1);
+    if (!merge) continue;  // (no barrier below)
+    uint64_t wa, wb;
+    lane_words(bms[wv], lane, wa, wb);
+    const uint64_t un = wa | wb;
+    const int mine = __popcll(un);
+    int pos = mine;  // inclusive scan over lanes, then exclusive
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t = __shfl_up(pos, o, kWave);
+      if (lane >= o) pos += t;
+    }
+    const int u = __shfl(pos, kWave - 1, kWave);
+    pos -= mine;
+    const int64_t base = wbase[w] + off;
+    if (u == 0) {
+      if (lane == 0 && base < L.step_cap) steps[base] = make_int2(kBadTile, word);
+      continue;
+    }
+    uint64_t m = un;
+    while (m) {
+      const int b = __builtin_ctzll(m);
+      m &= m - 1;
+      const int t = 64 * lane + b;
+      const int e = t | (int)(((wa >> b) & 1) << 30) | (int)(((wb >> b) & 1) << 29);
+      const int64_t at = base + pos;
+      if (at < L.step_cap) steps[at] = make_int2(e, word);
+      ++pos;
+    }
+  }
+}
+
+}  // namespace
+
+PlanLayout plan_layout(int32_t B, int32_t H, int32_t N, int32_t tile, int32_t mask_heads,
+                       int64_t nnz_bound, int32_t workers) {
+  PlanLayout L;
+  L.B = B;
+  L.H = H;
+  L.N = N;
+  L.tiles = (int32_t)(((int64_t)N + tile - 1) / tile);
+  L.mask_heads = mask_heads;
+  L.workers = workers;
+  L.pairs = (L.tiles + 1) / 2;
+  L.items = (int64_t)B * H * L.pairs;
+  // each pair's steps number at most n0 + n1 (at least 1); per head, the
+  // lists of a mask slice are used once per batch entry and per head that
+  // shares the slice
+  const int64_t share = mask_heads > 0 ? (int64_t)H / mask_heads : 0;
+  L.step_cap = (int64_t)B * share * (nnz_bound + (int64_t)mask_heads * L.pairs);
+  auto up16 = [](int64_t v) { return (v + 15) & ~(int64_t)15; };
+  int64_t off = up16(kPlanHeaderInts * 4);
+  L.off_wstep = off;
+  off = up16(off + 4 * ((int64_t)workers + 1));
+  L.off_witem = off;
+  off = up16(off + 8 * (int64_t)workers);
+  L.off_wcnt = off;
+  off = up16(off + 4 * (int64_t)workers);
+  L.off_witems = off;
+  off = up16(off + 4 * L.items);
+  L.off_pinfo = off;
+  off = up16(off + 16 * (int64_t)mask_heads * L.pairs);
+  L.off_itmp = off;
+  off = up16(off + 16 * L.items);
+  L.off_steps = off;
+  off = up16(off + 8 * L.step_cap);
+  L.bytes = off;
+  return L;
+}
+
+int device_compute_units() {
+  int dev = 0, cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -1;
+  return cu;
+}
+
+int launch_fwd_plan(const PlanLayout& L, const int32_t* row_ptr, const int32_t* col_idx,
+                    int64_t col_cap, char* plan, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  PlanArgs a;
+  a.L = L;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.col_cap = col_cap;
+  a.plan = plan;
+  const int64_t sp = (int64_t)L.mask_heads * L.pairs;
+  hipLaunchKernelGGL(plan_pairs_kernel, dim3((unsigned)((sp + 3) / 4 > 0 ? (sp + 3) / 4 : 1)),
+                     dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(plan_assign_kernel, dim3(kPlanXcds), dim3(kWave), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t blocks = (L.items + 3) / 4;
+  const unsigned grid = (unsigned)(blocks < 1 ? 1 : (blocks > 65536 ? 65536 : blocks));
+  hipLaunchKernelGGL(plan_steps_kernel, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace bsattn

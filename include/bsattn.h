@@ -10,7 +10,8 @@
  * a tile mask says which key tiles each query tile reads, and only those
  * tiles are computed.  The output O has the shape of Q.
  *
- * Pipeline: bsattn_build_mask -> bsattn_compact -> bsattn_fwd.  A static mask
+ * Pipeline: bsattn_build_mask -> bsattn_compact -> bsattn_fwd (or
+ * bsattn_fwd_plan once per list set, then bsattn_fwd_planned).  A static mask
  * can instead be calibrated: bsattn_block_energy -> bsattn_select_blocks ->
  * bsattn_aggregate_masks, then bsattn_compact -> bsattn_fwd.
  *
@@ -163,7 +164,10 @@ BSATTN_API int bsattn_build_mask(const bsattn_layout* layout,
 BSATTN_API int bsattn_compact(int32_t rows, int32_t Tk, const uint8_t* mask,
                               int32_t* row_ptr, int32_t* col_idx, void* stream);
 
-/* Block-sparse attention forward.
+/* Block-sparse attention forward: softmax attention of every query row over
+ * the keys of its query tile's active key tiles only (CalibAtt page, "B. Fase
+ * di Inferenza": only the selected 128x128 blocks are computed; LVSA page,
+ * "Meccanismo Core": each query attends to its frame set A(t)).
  *   q, k, v: device [B, H, N, d] contiguous, element type `dtype`
  *            (BF16 or F32; F32 inputs are rounded to bf16 for the matrix
  *            products, which accumulate in fp32).
@@ -207,6 +211,61 @@ BSATTN_API int bsattn_fwd_grouped(int32_t B, int32_t H, int32_t N, int32_t d, in
                                   int32_t dtype, const void* q, const void* k, const void* v,
                                   void* o, float* lse, int32_t mask_heads,
                                   const int32_t* row_ptr, const int32_t* col_idx,
+                                  int32_t window, float scale, void* stream);
+
+/* ---- Planned forward.  The active lists are fixed inputs of the forward
+ * (CalibAtt page, "B. Fase di Inferenza": inference follows per-block lists
+ * worked out beforehand, with no decision left to the attention kernel), so
+ * the work schedule is worked out once per list set too: which query-tile
+ * pairs each worker (one persistent workgroup per compute unit) computes, in
+ * which order, and every pair's merged key-tile list.  The planned forward
+ * then moves from one pair to the next without draining its pipeline: the
+ * same arithmetic, item by item, as bsattn_fwd (bitwise-identical O and
+ * LSE), with the per-workgroup set-up of bsattn_fwd gone.
+ *
+ * Supported: bf16, d = 128, tile = 128, Tq <= 4096, B*H <= 65535.  Workers
+ * is a multiple of 8 in [8, 512] (worker w is taken to run on XCD w % 8);
+ * 0 selects the current device's compute units (256 on MI355X). */
+
+/* Bytes of a plan buffer for these sizes: a fixed part, plus 8 bytes per
+ * step; the steps number at most B * (H / mask_heads) * (nnz_bound +
+ * mask_heads * ceil(Tq / 2)), nnz_bound an upper bound on the CSR's entries
+ * (< 0 or above mask_heads*Tq*Tk selects mask_heads*Tq*Tk).  Returns the
+ * size (> 0), or a negative bsattn_status (sizes as for bsattn_fwd_plan). */
+BSATTN_API int64_t bsattn_fwd_plan_bytes(int32_t B, int32_t H, int32_t N, int32_t tile,
+                                         int32_t mask_heads, int64_t nnz_bound,
+                                         int32_t workers);
+
+/* Build the plan of a CSR (as written by bsattn_compact for rows =
+ * mask_heads*Tq, Tk = Tq = ceil(N / tile)) into `plan`: device memory of
+ * plan_bytes bytes, 16-byte aligned, owned by the caller; its contents are
+ * the library's own (three launches on `stream`).  Key-tile indices outside
+ * [0, Tk) are left out; entries beyond the plan's step capacity (a
+ * plan_bytes below what bsattn_fwd_plan_bytes gives for the CSR's entry
+ * count) are dropped, and the forward then misses them.  The plan stays
+ * valid as long as the CSR does not change.
+ * Errors: INVALID_ARG (sizes, mask_heads not in {1, H}, null or unaligned
+ * pointers, plan_bytes below the fixed part, bad workers), UNSUPPORTED
+ * (tile, Tq, B*H), HIP.  B*H*N == 0 is a no-op. */
+BSATTN_API int bsattn_fwd_plan(int32_t B, int32_t H, int32_t N, int32_t tile,
+                               int32_t mask_heads, const int32_t* row_ptr,
+                               const int32_t* col_idx, int32_t workers, void* plan,
+                               int64_t plan_bytes, void* stream);
+
+/* The forward through a plan: arguments as bsattn_fwd, plus the plan buffer
+ * (plan, plan_bytes and workers as given to bsattn_fwd_plan, whose CSR must
+ * be row_ptr / col_idx) and window: 0 for contiguous tokens, w > 0 for the
+ * grouped view of bsattn_fwd_grouped.  Launches `workers` workgroups.  The
+ * kernel checks the plan's header (B, H, N, Tq, mask_heads, workers); a
+ * plan built for other sizes makes it return without writing O or LSE.
+ * Errors: as bsattn_fwd and bsattn_fwd_plan; UNSUPPORTED for other dtypes,
+ * head dims or tiles; INVALID_ARG for window < 0 or N not of the grouped
+ * form. */
+BSATTN_API int bsattn_fwd_planned(int32_t B, int32_t H, int32_t N, int32_t d, int32_t tile,
+                                  int32_t dtype, const void* q, const void* k, const void* v,
+                                  void* o, float* lse, int32_t mask_heads,
+                                  const int32_t* row_ptr, const int32_t* col_idx,
+                                  const void* plan, int64_t plan_bytes, int32_t workers,
                                   int32_t window, float scale, void* stream);
 
 /* Reorder token rows between window-major and position-major order (SQuad

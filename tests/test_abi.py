@@ -266,3 +266,67 @@ def test_repetition_calls_reject_bad_arguments():
     assert A(1, 1, 2, 4, 8, 4, 2, 0, p, p2, 0, 0, None) == bs.ERR_INVALID_ARG     # 8-byte rows
     assert A(1, 1, 2, 4, 8, 128, 2, 0, p, p2, 0, -1, None) == bs.ERR_INVALID_ARG  # block_rows
     assert A(1, 1, 0, 4, 8, 128, 2, 0, None, None, 0, 0, None) == bs.OK
+
+
+def _plan_bytes(**kw):
+    args = dict(B=1, H=12, N=32760, tile=128, mask_heads=1, nnz=-1, workers=256)
+    args.update(kw)
+    return bs.lib().bsattn_fwd_plan_bytes(args["B"], args["H"], args["N"], args["tile"],
+                                          args["mask_heads"], args["nnz"], args["workers"])
+
+
+def test_fwd_plan_bytes():
+    full = _plan_bytes()
+    assert full > 0
+    # 8 bytes per step, B * (H / mask_heads) steps per CSR entry
+    assert _plan_bytes(nnz=1002) - _plan_bytes(nnz=1000) == 2 * 8 * 12
+    assert _plan_bytes(nnz=1002, mask_heads=12) - _plan_bytes(nnz=1000, mask_heads=12) == 16
+    assert _plan_bytes(nnz=10**12) == full             # clamped to Hm * Tq * Tk
+    assert _plan_bytes(nnz=256 * 256) == full
+    assert _plan_bytes(tile=64) == bs.ERR_UNSUPPORTED
+    assert _plan_bytes(N=4097 * 128) == bs.ERR_UNSUPPORTED   # Tq > 4096
+    assert _plan_bytes(mask_heads=5) == bs.ERR_INVALID_ARG
+    assert _plan_bytes(workers=100) == bs.ERR_INVALID_ARG    # not a multiple of 8
+    assert _plan_bytes(workers=1024) == bs.ERR_INVALID_ARG
+    assert _plan_bytes(B=100, H=1000) == bs.ERR_UNSUPPORTED  # B*H > 65535
+    assert _plan_bytes(N=-1) == bs.ERR_INVALID_ARG
+
+
+def _planned(**kw):
+    args = dict(B=1, H=2, N=4096, d=128, tile=128, dtype=0, q=64, k=64, v=64, o=64,
+                lse=None, mask_heads=1, row_ptr=64, col_idx=64, plan=64,
+                plan_bytes=1 << 30, workers=256, window=0, scale=0.0)
+    args.update(kw)
+    L = bs.lib()
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.bsattn_fwd_planned(args["B"], args["H"], args["N"], args["d"], args["tile"],
+                                args["dtype"], p(args["q"]), p(args["k"]), p(args["v"]),
+                                p(args["o"]), p(args["lse"]), args["mask_heads"],
+                                p(args["row_ptr"]), p(args["col_idx"]), p(args["plan"]),
+                                args["plan_bytes"], args["workers"], args["window"],
+                                args["scale"], None)
+
+
+def test_fwd_planned_and_plan_reject_bad_arguments_without_launching():
+    assert _planned(d=64) == bs.ERR_UNSUPPORTED
+    assert _planned(tile=64) == bs.ERR_UNSUPPORTED
+    assert _planned(dtype=1) == bs.ERR_UNSUPPORTED
+    assert _planned(window=-1) == bs.ERR_INVALID_ARG
+    assert _planned(window=10) == bs.ERR_INVALID_ARG        # N not w * 128 k
+    assert _planned(plan=None) == bs.ERR_INVALID_ARG
+    assert _planned(plan=72) == bs.ERR_INVALID_ARG          # unaligned
+    assert _planned(plan_bytes=64) == bs.ERR_INVALID_ARG    # below the fixed part
+    assert b"plan_bytes" in bs.lib().bsattn_last_error()
+    assert _planned(workers=12) == bs.ERR_INVALID_ARG
+    assert _planned(mask_heads=3) == bs.ERR_INVALID_ARG
+    assert _planned(q=None) == bs.ERR_INVALID_ARG
+    assert _planned(B=0, q=None, k=None, v=None, o=None) == bs.OK
+    L = bs.lib()
+    p = ctypes.c_void_p
+    assert L.bsattn_fwd_plan(1, 2, 4096, 128, 1, p(64), p(64), 256, p(64), 64,
+                             None) == bs.ERR_INVALID_ARG
+    assert L.bsattn_fwd_plan(1, 2, 4096, 128, 1, None, p(64), 256, p(64), 1 << 30,
+                             None) == bs.ERR_INVALID_ARG
+    assert L.bsattn_fwd_plan(1, 2, 4096, 64, 1, p(64), p(64), 256, p(64), 1 << 30,
+                             None) == bs.ERR_UNSUPPORTED
+    assert L.bsattn_fwd_plan(0, 2, 4096, 128, 1, None, None, 256, None, 0, None) == bs.OK

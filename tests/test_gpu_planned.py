@@ -1,0 +1,286 @@
+"""The planned forward (bsattn_fwd_plan + bsattn_fwd_planned).
+
+The plan is integer work and is compared bit for bit with what the CSR
+fixes: every query-tile pair dealt to exactly one worker, its mode by the
+forward's own rule, and for a pair-mode item its merged key-tile list in
+ascending order with the right group flags.  The planned forward computes
+every item with the same arithmetic as bsattn_fwd, so its O and LSE must be
+bitwise equal to bsattn_fwd's; at full size it is also compared with the
+float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_bsattn_amd as bs
+import oracle
+import workloads as W
+from parity_util import (assert_close, check_mask_csr, gpu_mask_csr,
+                         oracle_rows_and_lse_tol, to64)
+
+pytestmark = pytest.mark.gpu
+
+PAIR_BITS = 15
+BAD_TILE = 0x0FFFFFFE
+
+
+def read_plan(plan, items):
+    a = plan.cpu().numpy().view(np.int32)
+    h = a[:16]
+    W_ = int(h[6])
+    sec = {k: int(h[8 + i]) * 4 for i, k in enumerate(
+        ("wstep", "witem", "wcnt", "witems", "pinfo", "itmp", "steps"))}
+    cap = int(h[15])
+    return dict(
+        header=h,
+        workers=W_,
+        wstep=a[sec["wstep"]:sec["wstep"] + W_ + 1],
+        witem=a[sec["witem"]:sec["witem"] + 2 * W_].reshape(W_, 2),
+        witems=a[sec["witems"]:sec["witems"] + items],
+        steps=a[sec["steps"]:sec["steps"] + 2 * cap].reshape(cap, 2),
+    )
+
+
+def expected_items(rp, ci, B, H, N, Hm):
+    """Per item (b*H + h) * pairs + p: (split, list of (tile, need0, need1))
+    from the CSR, by the rule the forward uses."""
+    tiles = -(-N // 128)
+    pairs = (tiles + 1) // 2
+    out = {}
+    cache = {}
+    for s in range(Hm):
+        for p in range(pairs):
+            r0 = s * tiles + 2 * p
+            la = ci[rp[r0]:rp[r0 + 1]].tolist()
+            lb = ci[rp[r0 + 1]:rp[r0 + 2]].tolist() if 2 * p + 1 < tiles else []
+            a = {t for t in la if 0 <= t < tiles}
+            b = {t for t in lb if 0 <= t < tiles}
+            n0, n1 = len(la), len(lb)
+            split = n0 == 0 or n1 == 0 or 5 * len(a & b) < n0 + n1
+            cache[s, p] = (split, [(t, t in a, t in b) for t in sorted(a | b)])
+    for bh in range(B * H):
+        s = 0 if Hm == 1 else bh % H
+        for p in range(pairs):
+            out[bh * pairs + p] = cache[s, p]
+    return out, pairs
+
+
+def check_plan(plan, rp, ci, B, H, N, Hm):
+    rp = rp.cpu().numpy()
+    ci = ci.cpu().numpy()
+    exp, pairs = expected_items(rp, ci, B, H, N, Hm)
+    P = read_plan(plan, len(exp))
+    h = P["header"]
+    assert (h[0], h[1], h[2], h[3], h[5], h[7]) == (0x42535031, B, H, N, Hm, pairs)
+    seen = np.zeros(len(exp), dtype=np.int64)
+    pos = 0
+    for w in range(P["workers"]):
+        first, cnt = P["witem"][w]
+        assert P["wstep"][w] == pos, f"worker {w}: stream not contiguous"
+        stream = []
+        for t in range(cnt):
+            iw = int(P["witems"][first + t])
+            split = iw < 0
+            iw &= 0x7FFFFFFF
+            bh, p = iw >> PAIR_BITS, iw & ((1 << PAIR_BITS) - 1)
+            i = bh * pairs + p
+            seen[i] += 1
+            esplit, union = exp[i]
+            assert split == esplit, f"item {i}: mode"
+            if not split:
+                if union:
+                    stream += [(t_ | (n0 << 30) | (n1 << 29), iw) for t_, n0, n1 in union]
+                else:
+                    stream.append((BAD_TILE, iw))
+        got = P["steps"][pos:pos + len(stream)]
+        assert [tuple(x) for x in got.tolist()] == stream, f"worker {w}: steps"
+        pos += len(stream)
+        assert P["wstep"][w + 1] == pos
+    assert (seen == 1).all(), "every item exactly once"
+    return P
+
+
+def run_both(q, k, v, rp, ci, Hm, workers=0, window=0):
+    B, H, N, _ = q.shape
+    plan = bs.make_plan(rp, ci, B, H, N, 128, Hm, workers)
+    o_p, l_p = bs.attention_planned(q, k, v, rp, ci, plan, mask_heads=Hm, want_lse=True,
+                                    workers=workers, window=window)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if window:
+        bs.fwd_grouped(q, k, v, o, rp, ci, window, mask_heads=Hm, lse=lse)
+    else:
+        bs.fwd(q, k, v, o, rp, ci, 128, mask_heads=Hm, lse=lse)
+    torch.cuda.synchronize()
+    return plan, o_p, l_p, o, lse
+
+
+def assert_bitwise(name, o_p, l_p, o, lse):
+    same_o = torch.equal(o_p, o)
+    same_l = torch.equal(l_p.view(torch.int32), lse.view(torch.int32))
+    if not (same_o and same_l):
+        d = (o_p.float() - o.float()).abs().max().item()
+        pytest.fail(f"{name}: planned differs from bsattn_fwd (max |dO| {d:.3e}, "
+                    f"O equal {same_o}, LSE equal {same_l})")
+    print(f"{name}: bitwise equal", flush=True)
+
+
+def _small(T, gh, gw, H, B, mask, seed):
+    return W.small_workload(frames=T, grid_h=gh, grid_w=gw, tile=128, d=128, H=H, B=B,
+                            mask=mask, seed=seed, name=f"planned_{T}x{gh}x{gw}")
+
+
+SMALL = [
+    ("window_odd_tiles", _small(7, 9, 13, 2, 1, W.MaskSpec(W.MASK_WINDOW_ANCHOR, window=1,
+                                                             num_anchors=2, rotation=3), 1)),
+    ("window_b2", _small(5, 8, 16, 3, 2, W.MaskSpec(W.MASK_WINDOW_ANCHOR, window=0,
+                                                     num_anchors=1, rotation=1), 2)),
+    ("static_perhead", _small(6, 10, 13, 3, 2, W.MaskSpec(
+        W.MASK_STATIC_RANDOM, seed=9, thresh24=W.thresh24_for_density(0.4), force_diagonal=1,
+        mask_heads=3), 3)),
+    ("static_sparse_empty_rows", _small(6, 10, 13, 2, 1, W.MaskSpec(
+        W.MASK_STATIC_RANDOM, seed=4, thresh24=W.thresh24_for_density(0.12), force_diagonal=0,
+        mask_heads=2), 4)),
+    ("dense", _small(4, 8, 9, 2, 1, W.MaskSpec(W.MASK_DENSE), 5)),
+    ("expanded", _small(12, 6, 11, 2, 1, W.MaskSpec(W.MASK_WINDOW_ANCHOR_EXPANDED, window=0,
+                                                     num_anchors=3, rotation=7, budget=5), 6)),
+    ("one_tile", _small(1, 5, 7, 2, 1, W.MaskSpec(W.MASK_DENSE), 7)),
+]
+
+
+@pytest.mark.parametrize("workers", [0, 8, 64])
+@pytest.mark.parametrize("name,w", SMALL, ids=[c[0] for c in SMALL])
+def test_small_plan_and_bitwise(name, w, workers):
+    mask, rp, ci = gpu_mask_csr(w)
+    m_ref = check_mask_csr(w, mask, rp, ci)
+    q, k, v = W.make_qkv(w, device="cuda")
+    Hm = w.mask.mask_heads
+    plan, o_p, l_p, o, lse = run_both(q, k, v, rp, ci, Hm, workers)
+    check_plan(plan, rp, ci, w.B, w.H, w.N, Hm)
+    assert_bitwise(f"{name} workers={workers}", o_p, l_p, o, lse)
+    if workers == 0:
+        o_ref, l_ref, tol = oracle_rows_and_lse_tol(q, k, v, m_ref, 128, workers=8)
+        assert_close(f"{name} planned", to64(o_p), o_ref, to64(l_p), l_ref, tol)
+
+
+def test_lists_with_out_of_range_entries_and_empty_pairs():
+    """Hand-built lists (identical, disjoint, one or both empty, random) with
+    key-tile indices outside [0, Tk) mixed in: the plan leaves them out, and
+    the planned forward equals bsattn_fwd, which skips them."""
+    w = W.small_workload(frames=16, grid_h=8, grid_w=16, tile=128, d=128, H=2)
+    Tn = w.num_tiles
+    g = np.random.default_rng(77)
+    lists = {0: [0, 3, 5, 9, 15], 1: [0, 3, 5, 9, 15], 2: [1, 2, 3, 4, 5, 6, 7, 8],
+             3: [1, 2, 3, 4, 5, 6, 7, 8], 4: [0, 2, 4, 6], 5: [1, 3, 7, 11, 13], 6: [],
+             7: [6, 7, 8], 8: [1, 2, 3, 4, 5, 9], 9: [2, 3, 4, 5, 9, 10], 10: [], 11: []}
+    for i in range(12, 16):
+        lists[i] = sorted(g.choice(Tn, size=int(g.integers(1, 9)), replace=False).tolist())
+    rows, cols = [0], []
+    for r in range(2 * Tn):
+        js = list(lists[r % Tn] if r < Tn else lists[(r + 4) % Tn])
+        if r % 3 == 0:
+            js = js + [Tn]
+        if r % 4 == 1:
+            js = [-1] + js
+        if r % 5 == 2:
+            js = js + [1 << 20]
+        cols += js
+        rows.append(len(cols))
+    rp = torch.tensor(rows, dtype=torch.int32, device="cuda")
+    ci = torch.tensor(cols + [0], dtype=torch.int32, device="cuda")
+    q, k, v = W.make_qkv(w, device="cuda")
+    for workers in (0, 8):
+        plan, o_p, l_p, o, lse = run_both(q, k, v, rp, ci, 2, workers)
+        check_plan(plan, rp, ci, 1, 2, w.N, 2)
+        assert_bitwise(f"hand-built lists workers={workers}", o_p, l_p, o, lse)
+
+
+@pytest.mark.parametrize("N,H,B,seed", [(1300, 5, 1, 1), (32760, 4, 1, 3)])
+def test_uneven_per_head_masks(N, H, B, seed):
+    g = torch.Generator().manual_seed(seed)
+    T = -(-N // 128)
+    dens = torch.linspace(0.05, 0.95, H)
+    m = (torch.rand(H, T, T, generator=g) < dens[:, None, None]).to(torch.uint8)
+    m[0, : max(1, T // 8)] = 1
+    m[:, torch.arange(T), torch.arange(T)] = 1
+    q, k, v = (torch.randn(B, H, N, 128, generator=g).to(torch.bfloat16).cuda()
+               for _ in range(3))
+    rp, ci = bs.make_csr(m.cuda())
+    plan, o_p, l_p, o, lse = run_both(q, k, v, rp, ci, H)
+    check_plan(plan, rp, ci, B, H, N, H)
+    assert_bitwise(f"uneven heads N={N}", o_p, l_p, o, lse)
+
+
+@pytest.mark.parametrize("cfg,rotation", [(2, 0), (2, 5), (3, 0), (4, 0), (5, 0),
+                                          ("expanded", 2)])
+def test_full_size_plan_and_bitwise(cfg, rotation):
+    """Every full-size workload in the launch configuration the bench
+    times: the plan against the CSR, and the planned forward bitwise equal
+    to bsattn_fwd."""
+    w = (W.EXPANDED if cfg == "expanded" else W.WORKLOADS[cfg]).with_rotation(rotation)
+    mask, rp, ci = gpu_mask_csr(w)
+    q, k, v = W.make_qkv(w, device="cuda")
+    Hm = w.mask.mask_heads
+    plan, o_p, l_p, o, lse = run_both(q, k, v, rp, ci, Hm)
+    check_plan(plan, rp, ci, w.B, w.H, w.N, Hm)
+    assert_bitwise(f"{w.name} r{rotation}", o_p, l_p, o, lse)
+
+
+@pytest.mark.timeout(900)
+def test_full_size_planned_against_the_oracle():
+    """The 32 760-token window/anchor workload at rotation 7, planned, on
+    every row and head against the float64 oracle."""
+    w = W.WORKLOADS[2].with_rotation(7)
+    mask, rp, ci = gpu_mask_csr(w)
+    m_ref = check_mask_csr(w, mask, rp, ci)
+    q, k, v = W.make_qkv(w, device="cuda")
+    o, lse = bs.attention_planned(q, k, v, rp, ci, want_lse=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref, tol = oracle_rows_and_lse_tol(q, k, v, m_ref, 128)
+    assert_close(f"{w.name} r7 planned (all rows)", to64(o), o_ref, to64(lse), l_ref, tol)
+
+
+def test_grouped_view_planned_equals_fwd_grouped():
+    """SQuad's global pass through a plan on the grouped view: bitwise equal
+    to bsattn_fwd_grouped."""
+    N, win, H = 16384, 128, 3
+    G = N // win
+    m = bs.make_mask(1, 1, N, 128, device="cuda", kind=W.MASK_BLOCK_DIAGONAL,
+                     block_tiles=G // 128)
+    rp, ci = bs.make_csr(m)
+    g = torch.Generator().manual_seed(12)
+    q, k, v = (torch.randn(1, H, N, 128, generator=g).to(torch.bfloat16).cuda()
+               for _ in range(3))
+    plan, o_p, l_p, o, lse = run_both(q, k, v, rp, ci, 1, window=win)
+    assert_bitwise("grouped view", o_p, l_p, o, lse)
+
+
+def test_never_read_tiles_are_never_fetched():
+    """K/V tiles no query tile reads are NaN; the planned output stays
+    finite and bitwise equal to the unpoisoned one."""
+    w = W.small_workload(frames=9, grid_h=10, grid_w=26, tile=128, d=128, H=2,
+                         mask=W.MaskSpec(W.MASK_WINDOW_ANCHOR, window=0, num_anchors=0))
+    Tn = w.num_tiles
+    m = np.zeros((1, Tn, Tn), dtype=np.uint8)
+    m[0, :, :4] = 1
+    rp, ci = bs.make_csr(torch.from_numpy(m).cuda())
+    q, k, v = W.make_qkv(w, device="cuda")
+    plan = bs.make_plan(rp, ci, 1, 2, w.N)
+    o1, l1 = bs.attention_planned(q, k, v, rp, ci, plan, want_lse=True)
+    kp, vp = k.clone(), v.clone()
+    kp[:, :, 4 * 128:] = float("nan")
+    vp[:, :, 4 * 128:] = float("nan")
+    o2, l2 = bs.attention_planned(q, kp, vp, rp, ci, plan, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o2.float()).all()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_plan_for_other_sizes_writes_nothing():
+    w = W.small_workload(frames=4, grid_h=8, grid_w=16, tile=128, d=128, H=2)
+    mask, rp, ci = gpu_mask_csr(w)
+    q, k, v = W.make_qkv(w, device="cuda")
+    plan = bs.make_plan(rp, ci, 1, 3, w.N)        # built for H = 3
+    o = torch.full_like(q, 7.0)
+    bs.fwd_planned(q, k, v, o, rp, ci, plan)
+    torch.cuda.synchronize()
+    assert (o == 7.0).all()
