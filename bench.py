@@ -4,9 +4,10 @@ One step = one pass of the whole path over one synthetic batch at the
 32 760-token video shape (B=1, H=12, d=128, 21 frames of 30x52 latents, bf16,
 128x128 tiles): build the window(+-1 frame) + 2 rotating-anchor mask for
 rotation r = (layer + step) mod 21 (layer 0), compact it into active-tile
-lists, build the forward's work plan from them, run the fused forward
-through the plan (--planned 0: the forward without a plan).  Inputs are
-resident in HBM before timing.
+lists, run the fused forward (--planned 1: build the forward's work plan
+from the lists every step and run the forward through it).  Inputs are
+resident in HBM before timing.  Static masks (the density sweep, the
+calibrated and SQuad masks) are planned once and timed through their plan.
 
 Printed: ONE JSON line with
   value        active-block TFLOP/s of the whole step (mask + lists + forward),
@@ -490,6 +491,18 @@ def configs_leg(bs, W, torch, dev, calls: int, planned: bool = True):
         torch.cuda.synchronize()
         part = lambda a, b: float(np.median([e[a].elapsed_time(e[b]) for e in evs]))
         f_ms = part(3, 4)
+        # the other forward on the same lists
+        runo = forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, w.tile, Hm, not planned,
+                          stream)
+        runo()
+        eo = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(calls)]
+        for a_, b_ in eo:
+            a_.record(stream)
+            runo()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        o_ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in eo]))
         tflops = flops / (f_ms * 1e-3) / 1e12
         recs[w.name] = {
             "B": w.B, "H": w.H, "N": w.N, "mask_heads": Hm,
@@ -504,6 +517,10 @@ def configs_leg(bs, W, torch, dev, calls: int, planned: bool = True):
             "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
             "ms_at_half_peak": round(flops / (0.5 * PEAK_BF16_TFLOPS * 1e12) * 1e3, 3),
             "us_per_active_tile_head": round(f_ms * 1e3 / tiles, 5),
+            ("fwd_unplanned_ms_median" if planned else "fwd_planned_ms_median"):
+                round(o_ms, 4),
+            ("fwd_unplanned_tflops" if planned else "fwd_planned_tflops"):
+                round(flops / (o_ms * 1e-3) / 1e12, 1),
         }
         del q, k, v, o, mask, row_ptr, col_idx
         torch.cuda.empty_cache()
@@ -587,12 +604,12 @@ def main():
                     help="timed calls of the SQuad two-pass leg (0 = skip)")
     ap.add_argument("--repetition", type=int, default=5,
                     help="timed calls of the spatial-repetition leg (0 = skip)")
-    ap.add_argument("--planned", type=int, default=1,
-                    help="forward through a work plan (bsattn_fwd_plan + "
-                         "bsattn_fwd_planned; 0 = bsattn_fwd)")
-    ap.add_argument("--unplanned-calls", type=int, default=10,
-                    help="timed calls of bsattn_fwd beside the planned forward "
-                         "(0 = skip)")
+    ap.add_argument("--planned", type=int, default=0,
+                    help="headline step: forward through a work plan rebuilt every "
+                         "step (bsattn_fwd_plan + bsattn_fwd_planned); 0 = bsattn_fwd")
+    ap.add_argument("--other-calls", type=int, default=10,
+                    help="timed calls of the other forward (planned or not) on the "
+                         "last step's lists (0 = skip)")
     ap.add_argument("--configs", type=int, default=10,
                     help="timed calls per workload of the per-config records "
                          "(0 = skip)")
@@ -681,19 +698,21 @@ def main():
     compact_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     plan_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
 
-    # the same forward without a plan (one workgroup per query-tile pair),
-    # on the lists of the last step
-    unplanned_ms = None
-    if args.planned and args.unplanned_calls > 0:
+    # the other forward on the lists of the last step: without a plan (one
+    # workgroup per query-tile pair) or through one (built once here)
+    other_ms = None
+    if args.other_calls > 0:
+        run = forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, w.tile, Hm,
+                         not args.planned, stream)
+        run()
         ue = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.unplanned_calls)]
-        bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, mask_heads=Hm, stream=stream)
+              for _ in range(args.other_calls)]
         for a_, b_ in ue:
             a_.record(stream)
-            bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, mask_heads=Hm, stream=stream)
+            run()
             b_.record(stream)
         torch.cuda.synchronize()
-        unplanned_ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in ue]))
+        other_ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in ue]))
     ms_per_step = elapsed * 1e3 / args.steps
     value = total_flops / elapsed / 1e12
     fwd_flops_mean = total_flops / args.steps
@@ -735,7 +754,7 @@ def main():
         torch.cuda.synchronize()
         dense_ms = float(np.median([a.elapsed_time(b) for a, b in dev_ev]))
 
-    sweep = density_sweep(bs, W, torch, dev, q, k, v, o, planned=bool(args.planned)) \
+    sweep = density_sweep(bs, W, torch, dev, q, k, v, o, planned=True) \
         if args.sweep else None
 
     expanded = expanded_windows(bs, W, torch, dev, args.expanded) \
@@ -822,7 +841,8 @@ def main():
         "build_mask_us": round(float(np.median(mask_ms)) * 1e3, 2),
         "compact_us": round(float(np.median(compact_ms)) * 1e3, 2),
         "plan_us": round(float(np.median(plan_ms)) * 1e3, 2) if args.planned else None,
-        "fwd_unplanned_ms_median": None if unplanned_ms is None else round(unplanned_ms, 4),
+        ("fwd_unplanned_ms_median" if args.planned else "fwd_planned_ms_median"):
+            None if other_ms is None else round(other_ms, 4),
         "density": None if dense_flops is None else round(fwd_flops_mean / dense_flops, 4),
         "dense_fwd_ms": None if dense_ms is None else round(dense_ms, 4),
         "dense_tflops": None if dense_ms is None else

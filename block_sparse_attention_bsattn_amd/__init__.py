@@ -30,7 +30,8 @@ import os
 from typing import Optional, Sequence
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libbsattn.so")
+# BSATTN_LIB may name another build of the same library (for A/B timing)
+LIB_PATH = os.environ.get("BSATTN_LIB") or os.path.join(_PKG, "libbsattn.so")
 
 OK = 0
 ERR_INVALID_ARG = -1

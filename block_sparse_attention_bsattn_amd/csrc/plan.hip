@@ -17,7 +17,7 @@
 // Three launches:
 //   1. pairs:  one wave per (mask slice, pair): the two lists become bitmaps
 //              in LDS; the union and common tile counts are popcounts.
-//   2. assign: one wave per XCD.  Items are cut into eight contiguous ranges
+//   2. assign: one workgroup per XCD.  Items are cut into eight contiguous ranges
 //              of equal estimated cost (neighbouring pairs of a head share
 //              key tiles, which the XCD's L2 then serves), and each range is
 //              spread over the XCD's workers (worker w runs on XCD w % 8):
@@ -158,11 +158,9 @@ struct ItemCost {
   int split;
 };
 
-__device__ __forceinline__ ItemCost item_cost(const PlanArgs& a, int64_t i) {
+// cost of the item of (mask slice s, pair p)
+__device__ __forceinline__ ItemCost item_cost_sp(const PlanArgs& a, int s, int p) {
   const PlanLayout& L = a.L;
-  const int64_t bh = i / L.pairs;
-  const int p = (int)(i - bh * L.pairs);
-  const int s = L.mask_heads == 1 ? 0 : (int)(bh % L.H);
   const int32_t* pi = P32(a, L.off_pinfo) + 4 * ((int64_t)s * L.pairs + p);
   const int u = pi[0], common = pi[1], n0 = pi[2], n1 = pi[3];
   ItemCost c;
@@ -177,107 +175,183 @@ __device__ __forceinline__ ItemCost item_cost(const PlanArgs& a, int64_t i) {
   return c;
 }
 
+// The assign kernel keeps every (mask slice, pair)'s cost in LDS when they
+// fit (cost, and steps | split << 30), else reads them from the plan.
+constexpr int kLdsPairs = 4096;
+
+struct CostTable {
+  const int* cost;   // LDS, or null
+  const int* steps;
+  __device__ __forceinline__ ItemCost get(const PlanArgs& a, int s, int p) const {
+    if (cost == nullptr) return item_cost_sp(a, s, p);
+    const int sp = s * a.L.pairs + p;
+    ItemCost c;
+    c.cost = cost[sp];
+    c.steps = steps[sp] & 0x3FFFFFFF;
+    c.split = steps[sp] >> 30;
+    return c;
+  }
+  __device__ __forceinline__ ItemCost item(const PlanArgs& a, int i) const {
+    const int bh = i / a.L.pairs;
+    return get(a, a.L.mask_heads == 1 ? 0 : bh % a.L.H, i - bh * a.L.pairs);
+  }
+};
+
 // ---- 2. per XCD: the item range and its deal over the XCD's workers
-__global__ void __launch_bounds__(kWave) plan_assign_kernel(PlanArgs a) {
+constexpr int kAssignThreads = 256;
+
+__global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a) {
+  __shared__ int64_t part[kAssignThreads];
+  __shared__ __attribute__((aligned(16))) uint32_t keys[kWave];
   __shared__ int sorted[kWave];
   __shared__ int s_cost[kWave], s_steps[kWave];
-  const int lane = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) int64_t s_load[kPlanMaxWorkersPerXcd];
+  __shared__ int t_cost[kLdsPairs], t_steps[kLdsPairs];
+  const int tid = threadIdx.x;
   const int x = blockIdx.x;  // XCD
   const PlanLayout& L = a.L;
-  const int64_t G = L.items;
+  const int G = (int)L.items;
   const int R = L.workers / kPlanXcds;  // workers of this XCD: w = x + 8 j
-
-  // item i goes to XCD floor(8 (2 prefix(i) + cost(i)) / (2 C)): contiguous
-  // ranges of about equal cost
-  const int64_t per = (G + kWave - 1) / kWave;
-  const int64_t c0 = min((int64_t)lane * per, G), c1 = min(c0 + per, G);
-  int64_t sum = 0;
-  for (int64_t i = c0; i < c1; ++i) sum += item_cost(a, i).cost;
-  int64_t pre = sum;  // inclusive scan over lanes
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int64_t t = __shfl_up(pre, o, kWave);
-    if (lane >= o) pre += t;
-  }
-  const int64_t total = __shfl(pre, kWave - 1, kWave);
-  int64_t run = pre - sum;
-  int64_t below = 0, upto = 0;  // items of this lane's chunk on XCDs < x, <= x
-  for (int64_t i = c0; i < c1; ++i) {
-    const int c = item_cost(a, i).cost;
-    const int64_t xi = total > 0 ? min((int64_t)kPlanXcds - 1,
-                                       (kPlanXcds * (2 * run + c)) / (2 * total))
-                                 : 0;
-    below += xi < x ? 1 : 0;
-    upto += xi <= x ? 1 : 0;
-    run += c;
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    below += __shfl_xor(below, o, kWave);
-    upto += __shfl_xor(upto, o, kWave);
-  }
-  const int64_t lo = below, hi = upto;
-
-  // deal [lo, hi) over the R workers; lane j < R keeps worker j's load,
-  // item count and pair-mode steps
-  int64_t load = 0;
-  int cnt = 0, nsteps = 0;
-  for (int64_t b0 = lo; b0 < hi; b0 += kWave) {
-    const int64_t i = b0 + lane;
-    const bool valid = i < hi;
-    ItemCost ic;
-    ic.cost = 0;
-    ic.steps = 0;
-    ic.split = 0;
-    if (valid) ic = item_cost(a, i);
-    // longest first, ties by position
-    const int64_t key = valid ? ((int64_t)ic.cost << 32) | (uint32_t)(0xFFFF - lane) : -1;
-    int rank = 0;
-    for (int l2 = 0; l2 < kWave; ++l2) {
-      const int64_t k2 = __shfl(key, l2, kWave);
-      rank += k2 > key ? 1 : 0;
-    }
-    if (valid) {
-      sorted[rank] = lane;
-      s_cost[lane] = ic.cost;
-      s_steps[lane] = ic.steps + (ic.split << 30);
+  const int nsp = L.mask_heads * L.pairs;
+  CostTable tab;
+  tab.cost = nullptr;
+  tab.steps = nullptr;
+  if (nsp <= kLdsPairs) {
+    for (int sp = tid; sp < nsp; sp += kAssignThreads) {
+      const ItemCost c = item_cost_sp(a, sp / L.pairs, sp % L.pairs);
+      t_cost[sp] = c.cost;
+      t_steps[sp] = c.steps | (c.split << 30);
     }
     __syncthreads();
-    const int nvalid = (int)min((int64_t)kWave, hi - b0);
+    tab.cost = t_cost;
+    tab.steps = t_steps;
+  }
+
+  // item i goes to XCD floor(8 (2 prefix(i) + cost(i)) / (2 C)): contiguous
+  // ranges of about equal cost.  Thread t sums a contiguous chunk, walking
+  // (head, pair) incrementally.
+  const int per = (G + kAssignThreads - 1) / kAssignThreads;
+  const int c0 = min(tid * per, G), c1 = min(c0 + per, G);
+  const int bh0 = c0 / L.pairs;
+  const int p0 = c0 - bh0 * L.pairs;
+  const int h0 = bh0 % L.H;
+  int64_t sum = 0;
+  {
+    int p = p0, h = h0;
+    for (int i = c0; i < c1; ++i) {
+      sum += tab.get(a, L.mask_heads == 1 ? 0 : h, p).cost;
+      if (++p == L.pairs) {
+        p = 0;
+        if (++h == L.H) h = 0;
+      }
+    }
+  }
+  part[tid] = sum;
+  __syncthreads();
+  for (int o = 1; o < kAssignThreads; o <<= 1) {
+    const int64_t t = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += t;
+    __syncthreads();
+  }
+  const int64_t total = part[kAssignThreads - 1];
+  int64_t run = part[tid] - sum;
+  int below = 0, upto = 0;  // items of this chunk on XCDs < x, <= x
+  {
+    int p = p0, h = h0;
+    for (int i = c0; i < c1; ++i) {
+      const int c = tab.get(a, L.mask_heads == 1 ? 0 : h, p).cost;
+      const int64_t xi = total > 0 ? min((int64_t)kPlanXcds - 1,
+                                         (kPlanXcds * (2 * run + c)) / (2 * total))
+                                   : 0;
+      below += xi < x ? 1 : 0;
+      upto += xi <= x ? 1 : 0;
+      run += c;
+      if (++p == L.pairs) {
+        p = 0;
+        if (++h == L.H) h = 0;
+      }
+    }
+  }
+  __syncthreads();
+  part[tid] = ((int64_t)below << 32) | (uint32_t)upto;
+  __syncthreads();
+  for (int o = kAssignThreads / 2; o > 0; o >>= 1) {
+    if (tid < o) part[tid] += part[tid + o];
+    __syncthreads();
+  }
+  const int lo = (int)(part[0] >> 32), hi = (int)(part[0] & 0xFFFFFFFF);
+  if (tid < R) s_load[tid] = 0;
+
+  // deal [lo, hi) over the R workers, 64 items at a time; thread j < R
+  // keeps worker j's item count and pair-mode steps (its load in LDS)
+  int cnt = 0, nsteps = 0;
+  for (int b0 = lo; b0 < hi; b0 += kWave) {
+    const int nvalid = min(kWave, hi - b0);
+    uint32_t key = 0;
+    if (tid < nvalid) {
+      const ItemCost ic = tab.item(a, b0 + tid);
+      // longest first, ties by position; 0 marks an empty slot
+      key = ((uint32_t)min(ic.cost, (1 << 25) - 1) << 6 | (uint32_t)(kWave - 1 - tid)) + 1;
+      s_cost[tid] = ic.cost;
+      s_steps[tid] = ic.steps + (ic.split << 30);
+    }
+    if (tid < kWave) keys[tid] = key;
+    __syncthreads();
+    if (tid < nvalid) {
+      int rank = 0;
+      const uint4* k4 = reinterpret_cast<const uint4*>(keys);
+#pragma unroll
+      for (int j = 0; j < kWave / 4; ++j) {
+        const uint4 kv = k4[j];
+        rank += (kv.x > key) + (kv.y > key) + (kv.z > key) + (kv.w > key);
+      }
+      sorted[rank] = tid;
+    }
+    __syncthreads();
     for (int r0 = 0; r0 < nvalid; r0 += R) {
       const int k = min(R, nvalid - r0);
-      // rank of worker j by load (ties by index)
-      int wr = 0;
-      for (int j2 = 0; j2 < R; ++j2) {
-        const int64_t l2 = __shfl(load, j2, kWave);
-        wr += (l2 < load || (l2 == load && j2 < lane)) ? 1 : 0;
+      int wr = R;
+      int64_t mine = 0;
+      if (tid < R) {
+        // rank of worker j by load (ties by index)
+        mine = s_load[tid];
+        wr = 0;
+        for (int j2 = 0; j2 < R; ++j2) {
+          const int64_t l2 = s_load[j2];
+          wr += (l2 < mine || (l2 == mine && j2 < tid)) ? 1 : 0;
+        }
       }
-      if (lane < R && wr < k) {
+      __syncthreads();
+      if (tid < R && wr < k) {
         const int src = sorted[r0 + wr];
-        const int64_t item = b0 + src;
+        const int item = b0 + src;
         const int st = s_steps[src];
-        const int w = x + kPlanXcds * lane;
-        int32_t* it = P32(a, L.off_itmp) + 4 * item;
-        it[0] = w;
+        int32_t* it = P32(a, L.off_itmp) + 4 * (int64_t)item;
+        it[0] = x + kPlanXcds * tid;
         it[1] = nsteps;
         it[2] = cnt;
         it[3] = st >> 30;  // split
-        load += s_cost[src];
+        s_load[tid] = mine + s_cost[src];
         nsteps += st & 0x3FFFFFFF;
         cnt += 1;
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
   // worker j's items take witems[lo + (items of workers < j), ...)
-  int pc = lane < R ? cnt : 0;
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(pc, o, kWave);
-    if (lane >= o) pc += t;
-  }
-  if (lane < R) {
-    const int w = x + kPlanXcds * lane;
-    P32(a, L.off_witem)[2 * w] = (int)(lo + pc - cnt);
-    P32(a, L.off_witem)[2 * w + 1] = cnt;
-    P32(a, L.off_wcnt)[w] = nsteps;
+  if (tid < kWave) {
+    int pc = tid < R ? cnt : 0;
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t = __shfl_up(pc, o, kWave);
+      if (tid >= o) pc += t;
+    }
+    if (tid < R) {
+      const int w = x + kPlanXcds * tid;
+      P32(a, L.off_witem)[2 * w] = lo + pc - cnt;
+      P32(a, L.off_witem)[2 * w + 1] = cnt;
+      P32(a, L.off_wcnt)[w] = nsteps;
+    }
   }
 }
 
@@ -381,11 +455,13 @@ PlanLayout plan_layout(int32_t B, int32_t H, int32_t N, int32_t tile, int32_t ma
   L.workers = workers;
   L.pairs = (L.tiles + 1) / 2;
   L.items = (int64_t)B * H * L.pairs;
-  // each pair's steps number at most n0 + n1 (at least 1); per head, the
-  // lists of a mask slice are used once per batch entry and per head that
-  // shares the slice
+  // each pair's steps number at most n0 + n1 and at most Tk (at least 1);
+  // per head, the lists of a mask slice are used once per batch entry and
+  // per head that shares the slice
   const int64_t share = mask_heads > 0 ? (int64_t)H / mask_heads : 0;
-  L.step_cap = (int64_t)B * share * (nnz_bound + (int64_t)mask_heads * L.pairs);
+  const int64_t by_lists = (int64_t)B * share * (nnz_bound + (int64_t)mask_heads * L.pairs);
+  const int64_t by_tiles = L.items * (int64_t)(L.tiles > 1 ? L.tiles : 1);
+  L.step_cap = by_lists < by_tiles ? by_lists : by_tiles;
   auto up16 = [](int64_t v) { return (v + 15) & ~(int64_t)15; };
   int64_t off = up16(kPlanHeaderInts * 4);
   L.off_wstep = off;
@@ -428,7 +504,7 @@ int launch_fwd_plan(const PlanLayout& L, const int32_t* row_ptr, const int32_t* 
                      dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(plan_assign_kernel, dim3(kPlanXcds), dim3(kWave), 0, s, a);
+  hipLaunchKernelGGL(plan_assign_kernel, dim3(kPlanXcds), dim3(kAssignThreads), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t blocks = (L.items + 3) / 4;

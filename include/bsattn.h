@@ -228,10 +228,11 @@ BSATTN_API int bsattn_fwd_grouped(int32_t B, int32_t H, int32_t N, int32_t d, in
  * 0 selects the current device's compute units (256 on MI355X). */
 
 /* Bytes of a plan buffer for these sizes: a fixed part, plus 8 bytes per
- * step; the steps number at most B * (H / mask_heads) * (nnz_bound +
- * mask_heads * ceil(Tq / 2)), nnz_bound an upper bound on the CSR's entries
- * (< 0 or above mask_heads*Tq*Tk selects mask_heads*Tq*Tk).  Returns the
- * size (> 0), or a negative bsattn_status (sizes as for bsattn_fwd_plan). */
+ * step; the steps number at most the smaller of B * (H / mask_heads) *
+ * (nnz_bound + mask_heads * ceil(Tq / 2)) and B * H * ceil(Tq / 2) * Tk,
+ * nnz_bound an upper bound on the CSR's entries (< 0 or above
+ * mask_heads*Tq*Tk selects mask_heads*Tq*Tk).  Returns the size (> 0), or a
+ * negative bsattn_status (sizes as for bsattn_fwd_plan). */
 BSATTN_API int64_t bsattn_fwd_plan_bytes(int32_t B, int32_t H, int32_t N, int32_t tile,
                                          int32_t mask_heads, int64_t nnz_bound,
                                          int32_t workers);
