@@ -11,6 +11,7 @@ The calls mirror include/bsattn.h:
     fwd_plan_bytes(B, H, N, tile, ...)                  -> bsattn_fwd_plan_bytes
     fwd_plan(row_ptr, col_idx, B, H, N, tile, plan)     -> bsattn_fwd_plan
     fwd_planned(q, k, v, o, row_ptr, col_idx, plan, ..) -> bsattn_fwd_planned
+    fwd_noalloc(q, k, v, o, row_ptr, col_idx, tile, ...) -> bsattn_fwd_noalloc
     block_energy(q, k, energy, tile, ...)               -> bsattn_block_energy
     select_blocks(energy, eps, mask)                    -> bsattn_select_blocks
     aggregate_masks(masks, rho, out)                    -> bsattn_aggregate_masks
@@ -53,7 +54,8 @@ MASK_DENSE_ROWS_SPREAD = 6
 EXPORTS = ("bsattn_version", "bsattn_status_string", "bsattn_last_error",
            "bsattn_num_tiles", "bsattn_build_mask", "bsattn_compact",
            "bsattn_fwd", "bsattn_fwd_grouped", "bsattn_fwd_plan_bytes", "bsattn_fwd_plan",
-           "bsattn_fwd_planned", "bsattn_window_reorder", "bsattn_row_cosines",
+           "bsattn_fwd_planned", "bsattn_fwd_noalloc", "bsattn_window_reorder",
+           "bsattn_row_cosines",
            "bsattn_repetitive_heads", "bsattn_anchor_rows", "bsattn_block_energy",
            "bsattn_select_blocks",
            "bsattn_aggregate_masks", "bsattn_mfma_ceiling")
@@ -122,6 +124,9 @@ def lib() -> ctypes.CDLL:
     L.bsattn_fwd_planned.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                      i32, i32p, i32p, vp, ctypes.c_int64, i32, i32,
                                      ctypes.c_float, vp]
+    L.bsattn_fwd_noalloc.restype = ctypes.c_int
+    L.bsattn_fwd_noalloc.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                     i32, i32p, i32p, ctypes.c_float, vp]
     L.bsattn_window_reorder.restype = ctypes.c_int
     L.bsattn_window_reorder.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i32, vp]
     L.bsattn_row_cosines.restype = ctypes.c_int
@@ -336,6 +341,31 @@ def fwd_planned(q, k, v, o, row_ptr, col_idx, plan, mask_heads: int = 1, lse=Non
                                   _ptr(plan, "plan", torch.uint8), plan.numel(), workers,
                                   int(window), float(scale), _stream(stream))
     _check(st, "bsattn_fwd_planned")
+    return o
+
+
+def fwd_noalloc(q, k, v, o, row_ptr, col_idx, tile: int, mask_heads: int = 1,
+                lse=None, scale: float = 0.0, stream=None):
+    """bsattn_fwd_noalloc: bsattn_fwd's result without any allocation (the
+    plan lives in the library's own device array)."""
+    import torch
+    dt = _dtype_code(q)
+    if q.dim() != 4:
+        raise ValueError("q must have shape [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must have the shape and dtype of q")
+    if lse is not None and tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must have shape [B, H, N]")
+    st = lib().bsattn_fwd_noalloc(B, H, N, d, tile, dt, _ptr(q, "q", q.dtype),
+                                  _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype),
+                                  _ptr(o, "o", q.dtype),
+                                  _ptr(lse, "lse", torch.float32, allow_none=True),
+                                  mask_heads, _ptr(row_ptr, "row_ptr", torch.int32),
+                                  _ptr(col_idx, "col_idx", torch.int32), float(scale),
+                                  _stream(stream))
+    _check(st, "bsattn_fwd_noalloc")
     return o
 
 

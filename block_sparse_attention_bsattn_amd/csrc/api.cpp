@@ -359,6 +359,45 @@ BSATTN_API int bsattn_fwd_planned(int32_t B, int32_t H, int32_t N, int32_t d, in
   return hip_status(bsattn::launch_fwd(a, stream), "fwd_planned");
 }
 
+BSATTN_API int bsattn_fwd_noalloc(int32_t B, int32_t H, int32_t N, int32_t d, int32_t tile,
+                                  int32_t dtype, const void* q, const void* k, const void* v,
+                                  void* o, float* lse, int32_t mask_heads,
+                                  const int32_t* row_ptr, const int32_t* col_idx, float scale,
+                                  void* stream) {
+  bsattn::FwdLaunch a;
+  bool noop;
+  int st = fwd_args("fwd_noalloc", B, H, N, d, tile, dtype, q, k, v, o, lse, mask_heads,
+                    row_ptr, col_idx, scale, a, &noop);
+  if (st != BSATTN_OK) return st;
+  if (noop) return ok();
+  // shapes outside the planned path run bsattn_fwd's kernels, which use no
+  // memory beyond their arguments
+  const bool planned = d == 128 && tile == 128 && dtype == BSATTN_DTYPE_BF16 &&
+                       a.tiles <= bsattn::kPlanMaxTiles && (int64_t)B * H <= 65535 &&
+                       (int64_t)N * 256 < ((int64_t)1 << 31);
+  if (!planned) return hip_status(bsattn::launch_fwd(a, stream), "fwd_noalloc");
+  int32_t workers = 0;
+  st = plan_args("fwd_noalloc", B, H, N, tile, mask_heads, &workers);
+  if (st != BSATTN_OK) return st;
+  const int64_t full = (int64_t)mask_heads * a.tiles * a.tiles;
+  bsattn::PlanLayout L = bsattn::plan_layout(B, H, N, tile, mask_heads, full, workers);
+  if (L.bytes > bsattn::kNoAllocScratchBytes)
+    return fail(BSATTN_ERR_INVALID_ARG,
+                "fwd_noalloc: a plan for B=%d H=%d N=%d mask_heads=%d needs %lld bytes, above "
+                "the library's %lld-byte device scratch (use bsattn_fwd_plan with a buffer "
+                "of the caller's)",
+                B, H, N, mask_heads, (long long)L.bytes,
+                (long long)bsattn::kNoAllocScratchBytes);
+  char* plan = nullptr;
+  int e = bsattn::noalloc_scratch(&plan);
+  if (e != 0) return hip_status(e, "fwd_noalloc: device scratch");
+  e = bsattn::launch_fwd_plan(L, row_ptr, col_idx, full, plan, stream);
+  if (e != 0) return hip_status(e, "fwd_noalloc: plan");
+  a.plan = plan;
+  a.pl = L;
+  return hip_status(bsattn::launch_fwd(a, stream), "fwd_noalloc");
+}
+
 BSATTN_API int bsattn_window_reorder(int32_t B, int32_t H, int32_t N, int32_t d, int32_t w,
                                      int32_t dtype, const void* src, void* dst, int32_t inverse,
                                      void* stream) {

@@ -50,6 +50,11 @@ PlanLayout plan_layout(int32_t B, int32_t H, int32_t N, int32_t tile, int32_t ma
                        int64_t nnz_bound, int32_t workers);
 // compute units of the current device (-1 on a runtime error)
 int device_compute_units();
+// The allocation-free forward's plan: a static device array of this many
+// bytes per GPU; noalloc_scratch gives the current device's address (a
+// hipError_t value, 0 = success).
+constexpr int64_t kNoAllocScratchBytes = (int64_t)64 << 20;
+int noalloc_scratch(char** ptr);
 
 struct FwdLaunch {
   int32_t B, H, N, d, tile, dtype;

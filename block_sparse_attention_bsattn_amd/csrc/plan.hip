@@ -36,6 +36,8 @@
 // capacity and every write to the plan's own capacity.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "bsattn_internal.h"
 
 namespace bsattn {
@@ -480,6 +482,35 @@ PlanLayout plan_layout(int32_t B, int32_t H, int32_t N, int32_t tile, int32_t ma
   off = up16(off + 8 * L.step_cap);
   L.bytes = off;
   return L;
+}
+
+// ---- the allocation-free forward: the plan lives in this file-scope
+// device array (one per GPU, held until the process ends) instead of a
+// caller's buffer.  Host code never uses the array's name as an address:
+// each device's address comes from hipGetSymbolAddress, taken once per
+// device with that device current, on the first call there.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+char* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+int noalloc_scratch(char** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 int device_compute_units() {

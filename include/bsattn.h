@@ -269,6 +269,26 @@ BSATTN_API int bsattn_fwd_planned(int32_t B, int32_t H, int32_t N, int32_t d, in
                                   const void* plan, int64_t plan_bytes, int32_t workers,
                                   int32_t window, float scale, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * result as bsattn_fwd, bitwise, with arguments as bsattn_fwd.  For bf16,
+ * d = 128, tile = 128 (Tq <= 4096, B*H <= 65535) it plans the lists
+ * (bsattn_fwd_plan, three launches) into a static device array of the
+ * library's own and runs bsattn_fwd_planned from it; every other supported
+ * shape runs bsattn_fwd's kernels, which need no memory beyond the
+ * arguments.  It calls no allocator.  The array holds 64 MiB per GPU, kept
+ * until the process ends (the plan for B = 1, H = 12, 131 072 tokens needs
+ * about 50 MiB); a plan larger than that is rejected with INVALID_ARG
+ * before anything is enqueued.  Every call on a GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (on different streams) race,
+ * so order them on one stream.  Errors: as bsattn_fwd; INVALID_ARG for a
+ * plan above the array's size; HIP. */
+BSATTN_API int bsattn_fwd_noalloc(int32_t B, int32_t H, int32_t N, int32_t d, int32_t tile,
+                                  int32_t dtype, const void* q, const void* k, const void* v,
+                                  void* o, float* lse, int32_t mask_heads,
+                                  const int32_t* row_ptr, const int32_t* col_idx, float scale,
+                                  void* stream);
+
 /* Reorder token rows between window-major and position-major order (SQuad
  * page, "1. Operatore di Attenzione SQuad": the global pass groups the
  * tokens at the same position inside every window).  With G = N / w:
