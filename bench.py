@@ -6,8 +6,10 @@ One step = one pass of the whole path over one synthetic batch at the
 rotation r = (layer + step) mod 21 (layer 0), compact it into active-tile
 lists, run the fused forward (--planned 1: build the forward's work plan
 from the lists every step and run the forward through it).  Inputs are
-resident in HBM before timing.  Static masks (the density sweep, the
-calibrated and SQuad masks) are planned once and timed through their plan.
+resident in HBM before timing.  SQuad's passes (two key tiles per query
+tile, where the per-workgroup set-up of bsattn_fwd dominates) run through
+work plans built once; elsewhere both forwards are reported, timed
+interleaved call by call.
 
 Printed: ONE JSON line with
   value        active-block TFLOP/s of the whole step (mask + lists + forward),
@@ -65,6 +67,23 @@ def forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, tile, Hm, planned, strea
     bs.fwd_plan(row_ptr, col_idx, B, H, N, plan, tile, Hm, stream=stream)
     return lambda: bs.fwd_planned(q, k, v, o, row_ptr, col_idx, plan, mask_heads=Hm,
                                   stream=stream)
+
+
+def time_interleaved(torch, stream, fns, calls: int):
+    """Median event time (ms) of each callable, the callables run in turn
+    call after call, so that all see the same clock (the chip's clock
+    drifts by several per cent as a run heats it)."""
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(calls)] for _ in fns]
+    for f in fns:
+        f()
+    for c in range(calls):
+        for f, ev in zip(fns, evs):
+            ev[c][0].record(stream)
+            f()
+            ev[c][1].record(stream)
+    torch.cuda.synchronize()
+    return [float(np.median([a.elapsed_time(b) for a, b in ev])) for ev in evs]
 
 
 SWEEP_P = (0.05, 0.1, 0.2, 0.3, 0.5, 0.7, 1.0)
@@ -212,25 +231,9 @@ def calibration(bs, W, torch, dev, calls: int):
         torch.bfloat16).to(dev)
     rp, ci = bs.make_csr(mask)
     o = torch.empty_like(v)
-    bs.fwd(q[:1], k[:1], v, o, rp, ci, w.tile, mask_heads=w.H)
-    fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(calls)]
-    for a, b in fe:
-        a.record(stream)
-        bs.fwd(q[:1], k[:1], v, o, rp, ci, w.tile, mask_heads=w.H, stream=stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    f_ms = float(np.median([a.elapsed_time(b) for a, b in fe]))
+    runu = forward_fn(bs, torch, q[:1], k[:1], v, o, rp, ci, w.tile, w.H, False, stream)
     runp = forward_fn(bs, torch, q[:1], k[:1], v, o, rp, ci, w.tile, w.H, True, stream)
-    runp()
-    fp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(calls)]
-    for a, b in fp:
-        a.record(stream)
-        runp()
-        b.record(stream)
-    torch.cuda.synchronize()
-    fp_ms = float(np.median([a.elapsed_time(b) for a, b in fp]))
+    f_ms, fp_ms = time_interleaved(torch, stream, [runu, runp], max(calls, 5))
     from dataclasses import replace
     w1 = replace(w, B=1)
     f_flops = active_flops(m_np, w1)
@@ -491,18 +494,10 @@ def configs_leg(bs, W, torch, dev, calls: int, planned: bool = True):
         torch.cuda.synchronize()
         part = lambda a, b: float(np.median([e[a].elapsed_time(e[b]) for e in evs]))
         f_ms = part(3, 4)
-        # the other forward on the same lists
-        runo = forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, w.tile, Hm, not planned,
-                          stream)
-        runo()
-        eo = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(calls)]
-        for a_, b_ in eo:
-            a_.record(stream)
-            runo()
-            b_.record(stream)
-        torch.cuda.synchronize()
-        o_ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in eo]))
+        # both forwards on the same lists, interleaved
+        run_u = forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, w.tile, Hm, False, stream)
+        run_p = forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, w.tile, Hm, True, stream)
+        u_ms, p_ms = time_interleaved(torch, stream, [run_u, run_p], calls)
         tflops = flops / (f_ms * 1e-3) / 1e12
         recs[w.name] = {
             "B": w.B, "H": w.H, "N": w.N, "mask_heads": Hm,
@@ -517,10 +512,10 @@ def configs_leg(bs, W, torch, dev, calls: int, planned: bool = True):
             "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
             "ms_at_half_peak": round(flops / (0.5 * PEAK_BF16_TFLOPS * 1e12) * 1e3, 3),
             "us_per_active_tile_head": round(f_ms * 1e3 / tiles, 5),
-            ("fwd_unplanned_ms_median" if planned else "fwd_planned_ms_median"):
-                round(o_ms, 4),
-            ("fwd_unplanned_tflops" if planned else "fwd_planned_tflops"):
-                round(flops / (o_ms * 1e-3) / 1e12, 1),
+            "interleaved": {"fwd_ms_median": round(u_ms, 4),
+                            "planned_fwd_ms_median": round(p_ms, 4),
+                            "fwd_tflops": round(flops / (u_ms * 1e-3) / 1e12, 1),
+                            "planned_fwd_tflops": round(flops / (p_ms * 1e-3) / 1e12, 1)},
         }
         del q, k, v, o, mask, row_ptr, col_idx
         torch.cuda.empty_cache()
@@ -700,19 +695,14 @@ def main():
 
     # the other forward on the lists of the last step: without a plan (one
     # workgroup per query-tile pair) or through one (built once here)
-    other_ms = None
+    ab = None
     if args.other_calls > 0:
-        run = forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, w.tile, Hm,
-                         not args.planned, stream)
-        run()
-        ue = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.other_calls)]
-        for a_, b_ in ue:
-            a_.record(stream)
-            run()
-            b_.record(stream)
-        torch.cuda.synchronize()
-        other_ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in ue]))
+        run_u = forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, w.tile, Hm, False, stream)
+        run_p = forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, w.tile, Hm, True, stream)
+        u_ms, p_ms = time_interleaved(torch, stream, [run_u, run_p], args.other_calls)
+        ab = {"lists": "the last step's (rotation %d)" % ((args.warmup + args.steps - 1) % T),
+              "fwd_ms_median": round(u_ms, 4), "planned_fwd_ms_median": round(p_ms, 4),
+              "planned_speedup": round(u_ms / p_ms, 4)}
     ms_per_step = elapsed * 1e3 / args.steps
     value = total_flops / elapsed / 1e12
     fwd_flops_mean = total_flops / args.steps
@@ -754,7 +744,7 @@ def main():
         torch.cuda.synchronize()
         dense_ms = float(np.median([a.elapsed_time(b) for a, b in dev_ev]))
 
-    sweep = density_sweep(bs, W, torch, dev, q, k, v, o, planned=True) \
+    sweep = density_sweep(bs, W, torch, dev, q, k, v, o, planned=False) \
         if args.sweep else None
 
     expanded = expanded_windows(bs, W, torch, dev, args.expanded) \
@@ -841,8 +831,7 @@ def main():
         "build_mask_us": round(float(np.median(mask_ms)) * 1e3, 2),
         "compact_us": round(float(np.median(compact_ms)) * 1e3, 2),
         "plan_us": round(float(np.median(plan_ms)) * 1e3, 2) if args.planned else None,
-        ("fwd_unplanned_ms_median" if args.planned else "fwd_planned_ms_median"):
-            None if other_ms is None else round(other_ms, 4),
+        "planned_vs_unplanned_interleaved": ab,
         "density": None if dense_flops is None else round(fwd_flops_mean / dense_flops, 4),
         "dense_fwd_ms": None if dense_ms is None else round(dense_ms, 4),
         "dense_tflops": None if dense_ms is None else

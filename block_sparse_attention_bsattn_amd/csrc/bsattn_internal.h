@@ -26,12 +26,15 @@ struct PlanLayout {
   int32_t B, H, N, tiles, mask_heads, workers, pairs;
   int64_t items;      // B * H * pairs
   int64_t step_cap;   // capacity of the step array (8-byte entries)
-  int64_t off_wstep;  // int32 [workers + 1]: each worker's range of the step array
+  int64_t off_wstep;  // int32 [4 * workers]: each worker's pair stream, group 0's and
+                      // group 1's single-tile streams: first step of each, then the end
   int64_t off_witem;  // int32 [2 * workers]: each worker's (first, count) in witems
-  int64_t off_wcnt;   // int32 [workers]: steps of each worker's pair stream
+  int64_t off_wcnt;   // int32 [3 * workers]: steps of each worker's three streams
   int64_t off_witems; // int32 [items]: item words in each worker's order (bit 31: split mode)
-  int64_t off_pinfo;  // int32x4 [mask_heads * pairs]: union, common, n0, n1 per list pair
-  int64_t off_itmp;   // int32x4 [items]: worker, step offset, sequence number
+  int64_t off_pinfo;  // int32x8 [mask_heads * pairs]: union, common, raw lengths n0 and
+                      // n1, valid lengths a and b, per list pair
+  int64_t off_itmp;   // int32x4 [items]: worker, sequence number, step offset(s) (the
+                      // last with bit 30 set when tile 2p + 1 goes to group 0)
   int64_t off_steps;  // int32x2 [step_cap]: (entry word, item word)
   int64_t bytes;
 };
@@ -43,8 +46,10 @@ constexpr int kPlanHeaderInts = 16;
 constexpr int kPlanXcds = 8;
 constexpr int kPlanMaxTiles = 4096;
 constexpr int kPlanMaxWorkersPerXcd = 64;
-// Item words: (b * H + h) << 15 | pair, pair = query-tile pair index.
+// Item words: in a pair stream (b * H + h) << 15 | pair, pair = query-tile
+// pair index; in a single-tile stream (b * H + h) << 13 | query tile.
 constexpr int kPlanPairBits = 15;
+constexpr int kPlanTileBits = 13;
 
 PlanLayout plan_layout(int32_t B, int32_t H, int32_t N, int32_t tile, int32_t mask_heads,
                        int64_t nnz_bound, int32_t workers);
@@ -53,7 +58,7 @@ int device_compute_units();
 // The allocation-free forward's plan: a static device array of this many
 // bytes per GPU; noalloc_scratch gives the current device's address (a
 // hipError_t value, 0 = success).
-constexpr int64_t kNoAllocScratchBytes = (int64_t)64 << 20;
+constexpr int64_t kNoAllocScratchBytes = (int64_t)96 << 20;
 int noalloc_scratch(char** ptr);
 
 struct FwdLaunch {

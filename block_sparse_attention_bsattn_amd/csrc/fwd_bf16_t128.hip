@@ -989,12 +989,15 @@ fwd_bf16_t128_d128(FwdLaunch a) {
         hdr[4] != a.tiles || hdr[5] != a.mask_heads || hdr[6] != (int)gridDim.x ||
         hdr[7] != (int)pairs)
       return;  // a plan made for other arguments (uniform: nothing ran yet)
-    const int64_t cap = a.pl.step_cap;
+    // this worker's streams: [w0, w1) pair-mode steps, [w1, w2) group 0's
+    // single-tile steps, [w2, w3) group 1's (clamped into the step array)
+    const int cap = (int)min(a.pl.step_cap, (int64_t)0x7FFFFFFF);
     const sconst_i32 wstep = (sconst_i32)(uintptr_t)(a.plan + a.pl.off_wstep);
-    int sb = wstep[wk], se = wstep[wk + 1];
-    sb = max(sb, 0);
-    se = (int)min((int64_t)se, cap);
-    if (se < sb) se = sb;
+    const int w0 = min(max(wstep[4 * wk], 0), cap);
+    const int w1 = min(max(wstep[4 * wk + 1], w0), cap);
+    const int w2 = min(max(wstep[4 * wk + 2], w1), cap);
+    const int w3 = min(max(wstep[4 * wk + 3], w2), cap);
+    const int sb = w0, se = w1;
     typedef const __attribute__((address_space(4))) uint64_t* sconst_u64;
     const sconst_u64 steps = (sconst_u64)(uintptr_t)(a.plan + a.pl.off_steps);
     // item word -> the head's first row, and this group's query tile
@@ -1101,6 +1104,105 @@ fwd_bf16_t128_d128(FwdLaunch a) {
       store_o(cur_hr, cur_qt, l > 0.f ? 1.f / l : 0.f, 0, 4);
       store_lse(cur_hr, cur_qt, m, l);
     }
+
+    // ---- the split-mode items: each group walks its own stream of single
+    // query tiles (tile 2p of an item in group 0's, 2p + 1 in group 1's),
+    // with its own K slot and V slot, item after item with no drain.  As in
+    // split mode, group g's matrix phase i runs P V of its entry i-1 and S
+    // of entry i; its vector phase i the softmax of entry i and the fetches
+    // of K of entry i+1 and V of entry i, awaited before the phase ends.
+    // Both groups run n = 1 + (the longer stream's length) matrix phases
+    // and pass the same barriers; a group whose stream is done idles.
+    if (w3 > w1) {
+      reset_state();
+      const int gb = grp ? w2 : w1, ge = grp ? w3 : w2;
+      const int niter = max(w2 - w1, w3 - w2) + 1;
+      auto tile_hr = [&](int iw) INLINE {
+        return (int64_t)min((int)((uint32_t)iw >> kPlanTileBits), BH - 1) * N;
+      };
+      auto tile_qt = [&](int iw) INLINE {
+        return min(iw & ((1 << kPlanTileBits) - 1), a.tiles - 1);
+      };
+      int sidx = gb;
+      const int slast = max(ge - 1, gb);
+      uint64_t look = gb < ge ? steps[gb] : 0;
+      auto next_step = [&](int& iw) INLINE {
+        const bool have = sidx < ge;
+        const uint64_t cur = look;
+        ++sidx;
+        look = steps[min(sidx, slast)];
+        iw = have ? (int)(uint32_t)(cur >> 32) : -1;
+        return have ? (int)((uint32_t)cur & 0x1FFFFFFFu) : NONE;
+      };
+      e_m1 = NONE;
+      i_m1 = -1;
+      e_0 = next_step(i_0);
+      e_1 = next_step(i_1);
+      int cur = i_0;  // -1: this group's stream is empty
+      int64_t cur_hr = cur >= 0 ? tile_hr(cur) : 0;
+      int cur_qt = cur >= 0 ? tile_qt(cur) : 0;
+      if (cur >= 0) load_q(cur_hr, cur_qt);
+      kr = kr_slot0 ^ (uint32_t)(grp * TILE_BYTES);
+      vr[0] = vr0_slot0 ^ (uint32_t)(grp * TILE_BYTES);
+      vr[1] = vr1_slot0 ^ (uint32_t)(grp * TILE_BYTES);
+      const uint32_t kown = kl32 + (uint32_t)(grp * TILE_BYTES);
+      const uint32_t vown = vl32 + (uint32_t)(grp * TILE_BYTES);
+      // prologue: each group fetches the K tile of its first entry
+      vector_phase(false, -1, ent_tile(e_0), -1, kown, vown, 0u,
+                   k_rsrc(cur >= 0 ? cur_hr : 0), v_rsrc(0));
+      __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+      BARRIER();
+      auto ind_vector = [&]() INLINE {
+        const bool bnd = e_0 != NONE && e_m1 != NONE && i_0 != i_m1;
+        const bool nxt = e_1 != NONE && i_1 != i_0;
+        if (bnd) {
+          l_over_halves();
+          store_o(cur_hr, cur_qt, l > 0.f ? 1.f / l : 0.f, 0, 4);
+          store_lse(cur_hr, cur_qt, m, l);
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+          m = -INFINITY;
+          l = 0.f;
+          cur = i_0;
+          cur_hr = tile_hr(cur);
+          cur_qt = tile_qt(cur);
+        }
+        // (the softmax always runs: with no entry every score is masked, so
+        // P = 0 and m, l and O stay as they are)
+        vector_phase(true, ent_tile(e_0), ent_tile(e_1), ent_tile(e_0), kown, vown, 0u,
+                     k_rsrc(e_1 != NONE ? tile_hr(i_1) : 0),
+                     v_rsrc(e_0 != NONE ? tile_hr(i_0) : 0));
+        if (nxt) {
+          load_q(tile_hr(i_1), tile_qt(i_1));
+#pragma unroll
+          for (int e = 0; e < 16; ++e) nm[e] = 0.f;
+        }
+        // this phase's fetches (and the new Q) have landed; as a builtin, so
+        // the compiler keeps no wait of its own in the matrix phases
+        __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+        BARRIER();
+        e_m1 = e_0;
+        i_m1 = i_0;
+        e_0 = e_1;
+        i_0 = i_1;
+        e_1 = next_step(i_1);
+      };
+      if (grp == 1) BARRIER();  // phase 0: group 0's first matrix phase
+#pragma unroll 1
+      for (int it = 0; it < niter; ++it) {
+        matrix_phase(e_m1 != NONE, e_0 != NONE);
+        BARRIER();
+        if (grp == 1 && it + 1 == niter) break;
+        ind_vector();
+      }
+      if (cur >= 0) {
+        l_over_halves();
+        store_o(cur_hr, cur_qt, l > 0.f ? 1.f / l : 0.f, 0, 4);
+        store_lse(cur_hr, cur_qt, m, l);
+      }
+    }
   }
 
   // ================= split-mode items =================
@@ -1108,30 +1210,9 @@ fwd_bf16_t128_d128(FwdLaunch a) {
   // the worker's split-mode items, one after the other (both groups have
   // passed the same barriers in the stream, and no LDS read or tile fetch
   // is in flight).
-  int ib = 0, ic = split ? 1 : 0;
-  if constexpr (PLANNED) {
-    const sconst_i32 witem = (sconst_i32)(uintptr_t)(a.plan + a.pl.off_witem);
-    const int64_t items = a.pl.items;
-    ib = (int)min(max((int64_t)witem[2 * blockIdx.x], (int64_t)0), items);
-    ic = (int)min(max((int64_t)witem[2 * blockIdx.x + 1], (int64_t)0), items - ib);
-  }
+  const int ic = PLANNED ? 0 : (split ? 1 : 0);
 #pragma unroll 1
   for (int t = 0; t < ic; ++t) {
-    if constexpr (PLANNED) {
-      const sconst_i32 witems = (sconst_i32)(uintptr_t)(a.plan + a.pl.off_witems);
-      const int iw = witems[ib + t];
-      if (iw >= 0) continue;  // a pair-mode item: done in the stream
-      const int BH = a.B * a.H;
-      const int wd = iw & 0x7FFFFFFF;
-      bh = min(wd >> kPlanPairBits, BH - 1);
-      qt0 = 2 * min(wd & ((1 << kPlanPairBits) - 1), (int)pairs - 1);
-      h = bh % a.H;
-      head_row = (int64_t)bh * N;
-      krs4 = k_rsrc(head_row);
-      vrs4 = v_rsrc(head_row);
-      item_lists();
-      reset_state();
-    }
     // ================= split mode =================
     // Both groups work on one query tile (the same 128 rows, the same Q),
     // entry e of its list going to group e % 2.  Phase p: group p % 2 runs

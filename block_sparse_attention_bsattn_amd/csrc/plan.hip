@@ -8,11 +8,14 @@
 // compute unit), in which order, and the merged key-tile list of every pair.
 //
 // A work item is one (batch, head, query-tile pair p) -- query tiles 2p and
-// 2p + 1.  Its two groups of four waves own one query tile each and walk the
-// union of the two active lists (pair mode), or, when the lists have little
-// in common, the two tiles are processed one after the other (split mode):
-// split mode when 5 I < n0 + n1 (I common tiles of lists of n0 and n1
-// entries), and always when one list is empty.
+// 2p + 1.  When the two active lists largely coincide (pair mode), the
+// worker's two groups of four waves own one query tile each and walk the
+// union of the two lists, so every staged key tile serves both.  When they
+// have little in common (split mode: 5 I < n0 + n1, I common tiles of lists
+// of n0 and n1 entries, and always when one list is empty), tile 2p goes to
+// group 0 and tile 2p + 1 to group 1, each walking its own list.  A worker
+// thus has three streams of steps: its pair-mode items (one step per union
+// tile) and one single-tile stream per group.
 //
 // Three launches:
 //   1. pairs:  one wave per (mask slice, pair): the two lists become bitmaps
@@ -26,10 +29,12 @@
 //              worker.  Records each item's worker, its place in the
 //              worker's order and the offset of its steps in the worker's
 //              pair-mode stream.
-//   3. steps:  one wave per item: the worker's item list, and for a pair-mode
+//   3. steps:  one wave per item: the worker's item list; for a pair-mode
 //              item its union list in ascending key-tile order, one step per
 //              tile, (tile | group 0 needs it << 30 | group 1 needs it << 29,
-//              item word).  An empty union is one step with no tile.
+//              item word); for a split-mode item each tile's own list into
+//              its group's stream, (tile, tile's item word).  An empty list
+//              is one step with no tile (its rows are still written).
 //
 // Outputs depend only on the lists: the forward computes every item the same
 // way whichever worker runs it.  Every read of the CSR is clamped to its
@@ -145,35 +150,41 @@ __global__ void __launch_bounds__(256) plan_pairs_kernel(PlanArgs a) {
   lane_words(bms[wv], lane, wa, wb);
   const int u = wave_sum(__popcll(wa | wb));
   const int common = wave_sum(__popcll(wa & wb));
+  const int va = wave_sum(__popcll(wa));
+  const int vb = wave_sum(__popcll(wb));
   if (use && lane == 0) {
-    int32_t* pi = P32(a, L.off_pinfo) + 4 * sp;
+    int32_t* pi = P32(a, L.off_pinfo) + 8 * sp;
     pi[0] = u;
     pi[1] = common;
     pi[2] = n0;
     pi[3] = n1;
+    pi[4] = va;
+    pi[5] = vb;
   }
 }
 
 struct ItemCost {
   int cost;   // estimated work, in fifths of a pair-mode step
   int steps;  // steps in the worker's pair-mode stream (0 in split mode)
+  int sa, sb; // steps in the groups' single-tile streams (0 in pair mode)
   int split;
 };
 
 // cost of the item of (mask slice s, pair p)
 __device__ __forceinline__ ItemCost item_cost_sp(const PlanArgs& a, int s, int p) {
   const PlanLayout& L = a.L;
-  const int32_t* pi = P32(a, L.off_pinfo) + 4 * ((int64_t)s * L.pairs + p);
-  const int u = pi[0], common = pi[1], n0 = pi[2], n1 = pi[3];
+  const int32_t* pi = P32(a, L.off_pinfo) + 8 * ((int64_t)s * L.pairs + p);
+  const int u = pi[0], common = pi[1], n0 = pi[2], n1 = pi[3], va = pi[4], vb = pi[5];
   ItemCost c;
-  // the forward's own rule: split mode unless the lists largely coincide
+  // the rule of bsattn_fwd: split mode unless the lists largely coincide
   c.split = (n0 == 0 || n1 == 0 || 5 * common < n0 + n1) ? 1 : 0;
-  // a split-mode step serves half the rows of a pair-mode one and runs
-  // about 0.8 as long; each item also pays a fixed set-up (pair mode: the
-  // hand-over to the next item; split mode: a drained start and the
-  // combine of the two groups)
   c.steps = c.split ? 0 : max(u, 1);
-  c.cost = c.split ? 4 * (n0 + n1) + 30 : 5 * (c.steps + 1);
+  c.sa = c.split ? max(va, 1) : 0;
+  c.sb = c.split && 2 * p + 1 < L.tiles ? max(vb, 1) : 0;
+  // a single-tile step serves half the rows of a pair-mode step and its
+  // fetch has one phase to land instead of two: about 0.8 of a pair-mode
+  // step each (two run side by side); every item also pays a hand-over
+  c.cost = c.split ? 4 * (c.sa + c.sb) + 5 : 5 * (c.steps + 1);
   return c;
 }
 
@@ -183,14 +194,17 @@ constexpr int kLdsPairs = 4096;
 
 struct CostTable {
   const int* cost;   // LDS, or null
-  const int* steps;
+  const int* steps;  // steps | split << 30, or sa | sb << 15 | split << 30
   __device__ __forceinline__ ItemCost get(const PlanArgs& a, int s, int p) const {
     if (cost == nullptr) return item_cost_sp(a, s, p);
     const int sp = s * a.L.pairs + p;
     ItemCost c;
+    const int st = steps[sp];
     c.cost = cost[sp];
-    c.steps = steps[sp] & 0x3FFFFFFF;
-    c.split = steps[sp] >> 30;
+    c.split = st >> 30;
+    c.steps = c.split ? 0 : st & 0x3FFFFFFF;
+    c.sa = c.split ? st & 0x7FFF : 0;
+    c.sb = c.split ? (st >> 15) & 0x7FFF : 0;
     return c;
   }
   __device__ __forceinline__ ItemCost item(const PlanArgs& a, int i) const {
@@ -222,7 +236,7 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
     for (int sp = tid; sp < nsp; sp += kAssignThreads) {
       const ItemCost c = item_cost_sp(a, sp / L.pairs, sp % L.pairs);
       t_cost[sp] = c.cost;
-      t_steps[sp] = c.steps | (c.split << 30);
+      t_steps[sp] = (c.split ? c.sa | (c.sb << 15) : c.steps) | (c.split << 30);
     }
     __syncthreads();
     tab.cost = t_cost;
@@ -286,8 +300,9 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
   if (tid < R) s_load[tid] = 0;
 
   // deal [lo, hi) over the R workers, 64 items at a time; thread j < R
-  // keeps worker j's item count and pair-mode steps (its load in LDS)
-  int cnt = 0, nsteps = 0;
+  // keeps worker j's item count and the lengths of its three streams (its
+  // load in LDS)
+  int cnt = 0, nsteps = 0, na = 0, nb = 0;
   for (int b0 = lo; b0 < hi; b0 += kWave) {
     const int nvalid = min(kWave, hi - b0);
     uint32_t key = 0;
@@ -296,7 +311,7 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
       // longest first, ties by position; 0 marks an empty slot
       key = ((uint32_t)min(ic.cost, (1 << 25) - 1) << 6 | (uint32_t)(kWave - 1 - tid)) + 1;
       s_cost[tid] = ic.cost;
-      s_steps[tid] = ic.steps + (ic.split << 30);
+      s_steps[tid] = (ic.split ? ic.sa | (ic.sb << 15) : ic.steps) | (ic.split << 30);
     }
     if (tid < kWave) keys[tid] = key;
     __syncthreads();
@@ -329,13 +344,25 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
         const int src = sorted[r0 + wr];
         const int item = b0 + src;
         const int st = s_steps[src];
+        const int split = st >> 30;
         int32_t* it = P32(a, L.off_itmp) + 4 * (int64_t)item;
         it[0] = x + kPlanXcds * tid;
-        it[1] = nsteps;
-        it[2] = cnt;
-        it[3] = st >> 30;  // split
+        it[1] = cnt;
         s_load[tid] = mine + s_cost[src];
-        nsteps += st & 0x3FFFFFFF;
+        if (split) {
+          // the two tiles go to the two groups' streams, the longer list to
+          // the shorter stream (orient 1: tile 2p + 1 to group 0's)
+          const int sa = st & 0x7FFF, sb = (st >> 15) & 0x7FFF;
+          const int orient = max(na + sb, nb + sa) < max(na + sa, nb + sb) ? 1 : 0;
+          it[2] = na;
+          it[3] = nb | (orient << 30);
+          na += orient ? sb : sa;
+          nb += orient ? sa : sb;
+        } else {
+          it[2] = nsteps;
+          it[3] = 0;
+          nsteps += st & 0x3FFFFFFF;
+        }
         cnt += 1;
       }
       __syncthreads();
@@ -352,12 +379,40 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
       const int w = x + kPlanXcds * tid;
       P32(a, L.off_witem)[2 * w] = lo + pc - cnt;
       P32(a, L.off_witem)[2 * w + 1] = cnt;
-      P32(a, L.off_wcnt)[w] = nsteps;
+      P32(a, L.off_wcnt)[3 * w] = nsteps;
+      P32(a, L.off_wcnt)[3 * w + 1] = na;
+      P32(a, L.off_wcnt)[3 * w + 2] = nb;
     }
   }
 }
 
-// ---- 3. per item: the worker's item list and the pair's merged steps
+// one list of a split-mode item into its group's stream at `base`, item
+// word `word`; an empty list is one step with no tile
+__device__ void write_list(int2* steps, int64_t cap, int64_t base, uint64_t bits, int lane,
+                           int word) {
+  const int mine = __popcll(bits);
+  int pos = mine;  // inclusive scan over lanes, then exclusive
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(pos, o, kWave);
+    if (lane >= o) pos += t;
+  }
+  const int n = __shfl(pos, kWave - 1, kWave);
+  pos -= mine;
+  if (n == 0) {
+    if (lane == 0 && base < cap) steps[base] = make_int2(kBadTile, word);
+    return;
+  }
+  uint64_t m = bits;
+  while (m) {
+    const int b = __builtin_ctzll(m);
+    m &= m - 1;
+    const int64_t at = base + pos;
+    if (at < cap) steps[at] = make_int2(64 * lane + b, word);
+    ++pos;
+  }
+}
+
+// ---- 3. per item: the worker's item list and the item's steps
 __global__ void __launch_bounds__(256) plan_steps_kernel(PlanArgs a) {
   __shared__ uint32_t bms[4][2 * kWords];
   __shared__ int64_t wbase[kPlanXcds * kPlanMaxWorkersPerXcd + 1];
@@ -365,11 +420,15 @@ __global__ void __launch_bounds__(256) plan_steps_kernel(PlanArgs a) {
   const PlanLayout& L = a.L;
   const int W = L.workers;  // at most 512: two per thread
   const int tid = threadIdx.x;
-  // every workgroup scans the workers' stream lengths
+  const int32_t* wc = P32(a, L.off_wcnt);
+  // every workgroup scans the workers' total stream lengths
   {
-    const int32_t* wc = P32(a, L.off_wcnt);
-    const int64_t v0 = 2 * tid < W ? wc[2 * tid] : 0;
-    const int64_t v1 = 2 * tid + 1 < W ? wc[2 * tid + 1] : 0;
+    const int64_t v0 = 2 * tid < W
+                           ? (int64_t)wc[6 * tid] + wc[6 * tid + 1] + wc[6 * tid + 2]
+                           : 0;
+    const int64_t v1 = 2 * tid + 1 < W
+                           ? (int64_t)wc[6 * tid + 3] + wc[6 * tid + 4] + wc[6 * tid + 5]
+                           : 0;
     part[tid] = v0 + v1;
     __syncthreads();
     for (int o = 1; o < 256; o <<= 1) {
@@ -385,8 +444,14 @@ __global__ void __launch_bounds__(256) plan_steps_kernel(PlanArgs a) {
     __syncthreads();
   }
   if (blockIdx.x == 0) {
-    for (int w = tid; w <= W; w += blockDim.x)
-      P32(a, L.off_wstep)[w] = (int32_t)min(wbase[w], L.step_cap);
+    for (int w = tid; w < W; w += blockDim.x) {
+      int32_t* ws = P32(a, L.off_wstep) + 4 * w;
+      const int64_t b = wbase[w];
+      ws[0] = (int32_t)min(b, L.step_cap);
+      ws[1] = (int32_t)min(b + wc[3 * w], L.step_cap);
+      ws[2] = (int32_t)min(b + wc[3 * w] + wc[3 * w + 1], L.step_cap);
+      ws[3] = (int32_t)min(wbase[w + 1], L.step_cap);
+    }
   }
   const int lane = tid % kWave;
   const int wv = tid / kWave;
@@ -394,29 +459,39 @@ __global__ void __launch_bounds__(256) plan_steps_kernel(PlanArgs a) {
   for (int64_t i0 = (int64_t)blockIdx.x * 4; i0 < L.items; i0 += (int64_t)gridDim.x * 4) {
     const int64_t i = i0 + wv;
     bool use = i < L.items;
-    int w = 0, off = 0, seq = 0, split = 1;
+    int w = 0, seq = 0, offa = 0, offb = 0, orient = 0;
     if (use) {
       const int32_t* it = P32(a, L.off_itmp) + 4 * i;
       w = it[0];
-      off = it[1];
-      seq = it[2];
-      split = it[3];
+      seq = it[1];
+      offa = it[2];
+      offb = it[3] & 0x3FFFFFFF;
+      orient = (it[3] >> 30) & 1;
       use = w >= 0 && w < W;  // every item is dealt; kept as a guard
     }
     const int64_t bh = use ? i / L.pairs : 0;
     const int p = use ? (int)(i - bh * L.pairs) : 0;
+    const int s = L.mask_heads == 1 ? 0 : (int)(bh % L.H);
+    const ItemCost ic = item_cost_sp(a, s, p);
     const int word = (int)((bh << kPlanPairBits) | p);
     if (use && lane == 0) {
       const int32_t* wi = P32(a, L.off_witem) + 2 * w;
-      if (seq < wi[1]) P32(a, L.off_witems)[wi[0] + seq] = word | (split << 31);
+      if (seq < wi[1]) P32(a, L.off_witems)[wi[0] + seq] = word | (ic.split << 31);
     }
-    const bool merge = use && !split;
-    const int s = L.mask_heads == 1 ? 0 : (int)(bh % L.H);
     int n0, n1;
-    lists_to_bitmaps(a, merge, s, p, bms[wv], lane, n0, n1);
-    if (!merge) continue;  // (no barrier below)
+    lists_to_bitmaps(a, use, s, p, bms[wv], lane, n0, n1);
+    if (!use) continue;  // (no barrier below)
     uint64_t wa, wb;
     lane_words(bms[wv], lane, wa, wb);
+    const int64_t b = wbase[w];
+    if (ic.split) {
+      const int64_t ba = b + wc[3 * w] + offa;                   // group 0's stream
+      const int64_t bb = b + wc[3 * w] + wc[3 * w + 1] + offb;   // group 1's stream
+      const int wda = (int)((bh << kPlanTileBits) | (2 * p));
+      write_list(steps, L.step_cap, orient ? bb : ba, wa, lane, wda);
+      if (2 * p + 1 < L.tiles) write_list(steps, L.step_cap, orient ? ba : bb, wb, lane, wda + 1);
+      continue;
+    }
     const uint64_t un = wa | wb;
     const int mine = __popcll(un);
     int pos = mine;  // inclusive scan over lanes, then exclusive
@@ -426,17 +501,17 @@ __global__ void __launch_bounds__(256) plan_steps_kernel(PlanArgs a) {
     }
     const int u = __shfl(pos, kWave - 1, kWave);
     pos -= mine;
-    const int64_t base = wbase[w] + off;
+    const int64_t base = b + offa;
     if (u == 0) {
       if (lane == 0 && base < L.step_cap) steps[base] = make_int2(kBadTile, word);
       continue;
     }
     uint64_t m = un;
     while (m) {
-      const int b = __builtin_ctzll(m);
+      const int bt = __builtin_ctzll(m);
       m &= m - 1;
-      const int t = 64 * lane + b;
-      const int e = t | (int)(((wa >> b) & 1) << 30) | (int)(((wb >> b) & 1) << 29);
+      const int t = 64 * lane + bt;
+      const int e = t | (int)(((wa >> bt) & 1) << 30) | (int)(((wb >> bt) & 1) << 29);
       const int64_t at = base + pos;
       if (at < L.step_cap) steps[at] = make_int2(e, word);
       ++pos;
@@ -457,25 +532,29 @@ PlanLayout plan_layout(int32_t B, int32_t H, int32_t N, int32_t tile, int32_t ma
   L.workers = workers;
   L.pairs = (L.tiles + 1) / 2;
   L.items = (int64_t)B * H * L.pairs;
-  // each pair's steps number at most n0 + n1 and at most Tk (at least 1);
-  // per head, the lists of a mask slice are used once per batch entry and
-  // per head that shares the slice
+  // An item's steps number at most n0 + n1 + 2 (an empty list is one
+  // step).  A pair-mode item has at most Tk; a split-mode one a + b = union
+  // + common < Tk + (n0 + n1) / 5 + 2, under 7 Tk / 5 + 2 for lists of
+  // distinct tiles.  Per head, the lists of a mask slice are used once per
+  // batch entry and per head that shares the slice.
   const int64_t share = mask_heads > 0 ? (int64_t)H / mask_heads : 0;
-  const int64_t by_lists = (int64_t)B * share * (nnz_bound + (int64_t)mask_heads * L.pairs);
-  const int64_t by_tiles = L.items * (int64_t)(L.tiles > 1 ? L.tiles : 1);
+  const int64_t by_lists =
+      (int64_t)B * share * (nnz_bound + 2 * (int64_t)mask_heads * L.pairs);
+  const int64_t tk = L.tiles > 1 ? L.tiles : 1;
+  const int64_t by_tiles = L.items * ((7 * tk + 4) / 5 + 2);
   L.step_cap = by_lists < by_tiles ? by_lists : by_tiles;
   auto up16 = [](int64_t v) { return (v + 15) & ~(int64_t)15; };
   int64_t off = up16(kPlanHeaderInts * 4);
   L.off_wstep = off;
-  off = up16(off + 4 * ((int64_t)workers + 1));
+  off = up16(off + 16 * (int64_t)workers);
   L.off_witem = off;
   off = up16(off + 8 * (int64_t)workers);
   L.off_wcnt = off;
-  off = up16(off + 4 * (int64_t)workers);
+  off = up16(off + 12 * (int64_t)workers);
   L.off_witems = off;
   off = up16(off + 4 * L.items);
   L.off_pinfo = off;
-  off = up16(off + 16 * (int64_t)mask_heads * L.pairs);
+  off = up16(off + 32 * (int64_t)mask_heads * L.pairs);
   L.off_itmp = off;
   off = up16(off + 16 * L.items);
   L.off_steps = off;

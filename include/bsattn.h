@@ -219,9 +219,14 @@ BSATTN_API int bsattn_fwd_grouped(int32_t B, int32_t H, int32_t N, int32_t d, in
  * the work schedule is worked out once per list set too: which query-tile
  * pairs each worker (one persistent workgroup per compute unit) computes, in
  * which order, and every pair's merged key-tile list.  The planned forward
- * then moves from one pair to the next without draining its pipeline: the
- * same arithmetic, item by item, as bsattn_fwd (bitwise-identical O and
- * LSE), with the per-workgroup set-up of bsattn_fwd gone.
+ * then moves from one pair to the next without draining its pipeline, the
+ * per-workgroup set-up of bsattn_fwd gone.  A pair whose two lists largely
+ * coincide is computed as bsattn_fwd computes it (bitwise-identical O and
+ * LSE); a pair that bsattn_fwd splits (5 I < n0 + n1, I common key tiles of
+ * lists of n0 and n1 entries, or an empty list) becomes two single tiles,
+ * each walked by one group of waves over its own list, item after item:
+ * the same softmax arithmetic as a tile in pair mode, different from
+ * bsattn_fwd's split mode only by rounding (both within the output bar).
  *
  * Supported: bf16, d = 128, tile = 128, Tq <= 4096, B*H <= 65535.  Workers
  * is a multiple of 8 in [8, 512] (worker w is taken to run on XCD w % 8);
@@ -270,15 +275,16 @@ BSATTN_API int bsattn_fwd_planned(int32_t B, int32_t H, int32_t N, int32_t d, in
                                   int32_t window, float scale, void* stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
- * capture, tight serving loops, harnesses that forbid hipMalloc): the same
- * result as bsattn_fwd, bitwise, with arguments as bsattn_fwd.  For bf16,
- * d = 128, tile = 128 (Tq <= 4096, B*H <= 65535) it plans the lists
- * (bsattn_fwd_plan, three launches) into a static device array of the
- * library's own and runs bsattn_fwd_planned from it; every other supported
- * shape runs bsattn_fwd's kernels, which need no memory beyond the
- * arguments.  It calls no allocator.  The array holds 64 MiB per GPU, kept
- * until the process ends (the plan for B = 1, H = 12, 131 072 tokens needs
- * about 50 MiB); a plan larger than that is rejected with INVALID_ARG
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * forward of bsattn_fwd, with its arguments.  For bf16, d = 128, tile = 128
+ * (Tq <= 4096, B*H <= 65535) it plans the lists (bsattn_fwd_plan, three
+ * launches) into a static device array of the library's own and runs
+ * bsattn_fwd_planned from it (the same output, bit for bit, as those two
+ * calls with a buffer of the caller's); every other supported shape runs
+ * bsattn_fwd's kernels, which need no memory beyond the arguments.  It
+ * calls no allocator.  The array holds 96 MiB per GPU, kept until the
+ * process ends (the worst-case plan for B = 1, H = 12, 131 072 tokens needs
+ * about 68 MiB); a plan larger than that is rejected with INVALID_ARG
  * before anything is enqueued.  Every call on a GPU shares that GPU's
  * array: calls that overlap in time on one GPU (on different streams) race,
  * so order them on one stream.  Errors: as bsattn_fwd; INVALID_ARG for a

@@ -283,9 +283,10 @@ def test_fwd_plan_bytes():
     assert _plan_bytes(nnz=1002, mask_heads=12) - _plan_bytes(nnz=1000, mask_heads=12) == 16
     assert _plan_bytes(nnz=10**12) == full             # clamped to Hm * Tq * Tk
     assert _plan_bytes(nnz=256 * 256) == full
-    # at most Tk steps per query-tile pair: 12 heads x 128 pairs x 256 tiles
-    assert _plan_bytes(nnz=200 * 256) == full
-    assert full - _plan_bytes(nnz=0) == 8 * (12 * 128 * 256 - 12 * 128)
+    # at most ceil(7 Tk / 5) + 2 steps per query-tile pair: 12 heads x 128
+    # pairs x 361; the list bound for nnz = 0 is 2 steps per pair
+    assert full - _plan_bytes(nnz=0) == 8 * (12 * 128 * 361 - 12 * 2 * 128)
+    assert _plan_bytes(nnz=361 * 128 - 256) == full
     assert _plan_bytes(tile=64) == bs.ERR_UNSUPPORTED
     assert _plan_bytes(N=4097 * 128) == bs.ERR_UNSUPPORTED   # Tq > 4096
     assert _plan_bytes(mask_heads=5) == bs.ERR_INVALID_ARG

@@ -1,12 +1,15 @@
 """The planned forward (bsattn_fwd_plan + bsattn_fwd_planned).
 
 The plan is integer work and is compared bit for bit with what the CSR
-fixes: every query-tile pair dealt to exactly one worker, its mode by the
-forward's own rule, and for a pair-mode item its merged key-tile list in
-ascending order with the right group flags.  The planned forward computes
-every item with the same arithmetic as bsattn_fwd, so its O and LSE must be
-bitwise equal to bsattn_fwd's; at full size it is also compared with the
-float64 oracle."""
+fixes: every query-tile pair dealt to exactly one worker, its mode by
+bsattn_fwd's rule, for a pair-mode item its merged key-tile list in
+ascending order with the right group flags, for a split-mode item each
+tile's own list in its group's stream.  The planned forward computes a
+pair-mode pair as bsattn_fwd does, and each tile of a split-mode pair as
+bsattn_fwd computes a tile in pair mode, so its O and LSE must be bitwise
+equal to bsattn_fwd's for pair-mode pairs and to bsattn_fwd's on a CSR whose
+pairs hold twin lists for split-mode pairs; at full size it is also
+compared with the float64 oracle."""
 import numpy as np
 import pytest
 import torch
@@ -20,6 +23,7 @@ from parity_util import (assert_close, check_mask_csr, gpu_mask_csr,
 pytestmark = pytest.mark.gpu
 
 PAIR_BITS = 15
+TILE_BITS = 13
 BAD_TILE = 0x0FFFFFFE
 
 
@@ -33,50 +37,60 @@ def read_plan(plan, items):
     return dict(
         header=h,
         workers=W_,
-        wstep=a[sec["wstep"]:sec["wstep"] + W_ + 1],
+        wstep=a[sec["wstep"]:sec["wstep"] + 4 * W_].reshape(W_, 4),
         witem=a[sec["witem"]:sec["witem"] + 2 * W_].reshape(W_, 2),
         witems=a[sec["witems"]:sec["witems"] + items],
+        itmp=a[sec["itmp"]:sec["itmp"] + 4 * items].reshape(items, 4),
         steps=a[sec["steps"]:sec["steps"] + 2 * cap].reshape(cap, 2),
     )
 
 
+def _lists(rp, ci, tiles, s, p):
+    r0 = s * tiles + 2 * p
+    la = ci[rp[r0]:rp[r0 + 1]].tolist()
+    lb = ci[rp[r0 + 1]:rp[r0 + 2]].tolist() if 2 * p + 1 < tiles else []
+    return la, lb
+
+
 def expected_items(rp, ci, B, H, N, Hm):
-    """Per item (b*H + h) * pairs + p: (split, list of (tile, need0, need1))
-    from the CSR, by the rule the forward uses."""
+    """Per item (b*H + h) * pairs + p: (split, union steps, list A, list B)
+    from the CSR, by the rule bsattn_fwd uses (split mode when 5 I < n0 + n1
+    or a list is empty; I common valid tiles, n raw lengths)."""
     tiles = -(-N // 128)
     pairs = (tiles + 1) // 2
     out = {}
     cache = {}
     for s in range(Hm):
         for p in range(pairs):
-            r0 = s * tiles + 2 * p
-            la = ci[rp[r0]:rp[r0 + 1]].tolist()
-            lb = ci[rp[r0 + 1]:rp[r0 + 2]].tolist() if 2 * p + 1 < tiles else []
+            la, lb = _lists(rp, ci, tiles, s, p)
             a = {t for t in la if 0 <= t < tiles}
             b = {t for t in lb if 0 <= t < tiles}
             n0, n1 = len(la), len(lb)
             split = n0 == 0 or n1 == 0 or 5 * len(a & b) < n0 + n1
-            cache[s, p] = (split, [(t, t in a, t in b) for t in sorted(a | b)])
+            cache[s, p] = (split, [(t, t in a, t in b) for t in sorted(a | b)],
+                           sorted(a), sorted(b))
     for bh in range(B * H):
         s = 0 if Hm == 1 else bh % H
         for p in range(pairs):
             out[bh * pairs + p] = cache[s, p]
-    return out, pairs
+    return out, pairs, tiles
 
 
 def check_plan(plan, rp, ci, B, H, N, Hm):
+    """The plan against the CSR, bit for bit; returns (plan fields, number
+    of split-mode items)."""
     rp = rp.cpu().numpy()
     ci = ci.cpu().numpy()
-    exp, pairs = expected_items(rp, ci, B, H, N, Hm)
+    exp, pairs, tiles = expected_items(rp, ci, B, H, N, Hm)
     P = read_plan(plan, len(exp))
     h = P["header"]
     assert (h[0], h[1], h[2], h[3], h[5], h[7]) == (0x42535031, B, H, N, Hm, pairs)
     seen = np.zeros(len(exp), dtype=np.int64)
     pos = 0
+    nsplit = 0
     for w in range(P["workers"]):
         first, cnt = P["witem"][w]
-        assert P["wstep"][w] == pos, f"worker {w}: stream not contiguous"
-        stream = []
+        streams = ([], [], [])
         for t in range(cnt):
             iw = int(P["witems"][first + t])
             split = iw < 0
@@ -84,19 +98,97 @@ def check_plan(plan, rp, ci, B, H, N, Hm):
             bh, p = iw >> PAIR_BITS, iw & ((1 << PAIR_BITS) - 1)
             i = bh * pairs + p
             seen[i] += 1
-            esplit, union = exp[i]
+            esplit, union, la, lb = exp[i]
             assert split == esplit, f"item {i}: mode"
             if not split:
-                if union:
-                    stream += [(t_ | (n0 << 30) | (n1 << 29), iw) for t_, n0, n1 in union]
-                else:
-                    stream.append((BAD_TILE, iw))
-        got = P["steps"][pos:pos + len(stream)]
-        assert [tuple(x) for x in got.tolist()] == stream, f"worker {w}: steps"
-        pos += len(stream)
-        assert P["wstep"][w + 1] == pos
+                streams[0].extend([(t_ | (n0 << 30) | (n1 << 29), iw) for t_, n0, n1 in union]
+                                  or [(BAD_TILE, iw)])
+                continue
+            nsplit += 1
+            wd = (bh << TILE_BITS) | (2 * p)
+            ga, gb = (2, 1) if (P["itmp"][i][3] >> 30) & 1 else (1, 2)   # orientation
+            streams[ga].extend([(t_, wd) for t_ in la] or [(BAD_TILE, wd)])
+            if 2 * p + 1 < tiles:
+                streams[gb].extend([(t_, wd + 1) for t_ in lb] or [(BAD_TILE, wd + 1)])
+        for g in range(3):
+            assert P["wstep"][w][g] == pos, f"worker {w}: stream {g} not contiguous"
+            got = P["steps"][pos:pos + len(streams[g])]
+            assert [tuple(x) for x in got.tolist()] == streams[g], f"worker {w}: stream {g}"
+            pos += len(streams[g])
+        assert P["wstep"][w][3] == pos
     assert (seen == 1).all(), "every item exactly once"
-    return P
+    return P, nsplit
+
+
+def _twin_csr(rp, ci, tiles, Hm, keep_even):
+    """The CSR with each query-tile pair's two rows both holding one tile's
+    list (tile 2p's when keep_even, else tile 2p + 1's)."""
+    rp = rp.cpu().numpy()
+    ci = ci.cpu().numpy()
+    rows, cols = [0], []
+    for s in range(Hm):
+        for r in range(tiles):
+            src = (r & ~1) if keep_even else min(r | 1, tiles - 1)
+            r0 = s * tiles + src
+            cols += ci[rp[r0]:rp[r0 + 1]].tolist()
+            rows.append(len(cols))
+    return (torch.tensor(rows, dtype=torch.int32, device="cuda"),
+            torch.tensor(cols + [0], dtype=torch.int32, device="cuda"))
+
+
+def reference_of_plan(q, k, v, rp, ci, Hm, window=0):
+    """What the planned forward must give bit for bit: bsattn_fwd's output
+    for pair-mode pairs; for split-mode pairs, each tile as bsattn_fwd
+    computes a tile in pair mode (its group walking its own list), taken
+    from bsattn_fwd on a CSR whose pairs both hold that tile's list.  With
+    an odd number of tiles the last one has no partner, so bsattn_fwd can
+    compute it in split mode only: its rows are NaN here (not compared; the
+    oracle checks them)."""
+    B, H, N, _ = q.shape
+    tiles = -(-N // 128)
+
+    def run(rp_, ci_):
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        if window:
+            bs.fwd_grouped(q, k, v, o, rp_, ci_, window, mask_heads=Hm, lse=lse)
+        else:
+            bs.fwd(q, k, v, o, rp_, ci_, 128, mask_heads=Hm, lse=lse)
+        return o, lse
+
+    o, lse = run(rp, ci)
+    exp, pairs, _ = expected_items(rp.cpu().numpy(), ci.cpu().numpy(), B, H, N, Hm)
+    split_pairs = [(bh, p) for bh in range(B * H) for p in range(pairs)
+                   if exp[bh * pairs + p][0]]
+    if split_pairs:
+        oa, la = run(*_twin_csr(rp, ci, tiles, Hm, True))
+        ob, lb = run(*_twin_csr(rp, ci, tiles, Hm, False))
+        o = o.view(B * H, N, -1)
+        lse = lse.view(B * H, N)
+        for src_o, src_l, odd in ((oa, la, 0), (ob, lb, 1)):
+            so = src_o.view(B * H, N, -1)
+            sl = src_l.view(B * H, N)
+            for bh, p in split_pairs:
+                t = 2 * p + odd
+                if t == tiles - 1 and tiles % 2 == 1:
+                    so = so.clone()
+                    sl = sl.clone()
+                    so[bh, t * 128:N] = float("nan")
+                    sl[bh, t * 128:N] = float("nan")
+                if t < tiles:
+                    r0, r1 = t * 128, min(t * 128 + 128, N)
+                    if window:   # rows of position-major tile t in the window-major buffer
+                        G = N // window
+                        idx = torch.tensor([(pp % G) * window + pp // G for pp in range(r0, r1)],
+                                           device=q.device)
+                        o[bh, idx] = so[bh, idx]
+                        lse[bh, idx] = sl[bh, idx]
+                    else:
+                        o[bh, r0:r1] = so[bh, r0:r1]
+                        lse[bh, r0:r1] = sl[bh, r0:r1]
+        o = o.view(q.shape)
+        lse = lse.view(q.shape[:3])
+    return o, lse, len(split_pairs)
 
 
 def run_both(q, k, v, rp, ci, Hm, workers=0, window=0):
@@ -104,19 +196,15 @@ def run_both(q, k, v, rp, ci, Hm, workers=0, window=0):
     plan = bs.make_plan(rp, ci, B, H, N, 128, Hm, workers)
     o_p, l_p = bs.attention_planned(q, k, v, rp, ci, plan, mask_heads=Hm, want_lse=True,
                                     workers=workers, window=window)
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    if window:
-        bs.fwd_grouped(q, k, v, o, rp, ci, window, mask_heads=Hm, lse=lse)
-    else:
-        bs.fwd(q, k, v, o, rp, ci, 128, mask_heads=Hm, lse=lse)
+    o, lse, _ = reference_of_plan(q, k, v, rp, ci, Hm, window)
     torch.cuda.synchronize()
     return plan, o_p, l_p, o, lse
 
 
 def assert_bitwise(name, o_p, l_p, o, lse):
-    same_o = torch.equal(o_p, o)
-    same_l = torch.equal(l_p.view(torch.int32), lse.view(torch.int32))
+    keep = ~torch.isnan(lse)          # rows the reference leaves out (NaN)
+    same_o = torch.equal(o_p[keep], o[keep])
+    same_l = torch.equal(l_p[keep].view(torch.int32), lse[keep].view(torch.int32))
     if not (same_o and same_l):
         d = (o_p.float() - o.float()).abs().max().item()
         pytest.fail(f"{name}: planned differs from bsattn_fwd (max |dO| {d:.3e}, "
@@ -155,7 +243,8 @@ def test_small_plan_and_bitwise(name, w, workers):
     q, k, v = W.make_qkv(w, device="cuda")
     Hm = w.mask.mask_heads
     plan, o_p, l_p, o, lse = run_both(q, k, v, rp, ci, Hm, workers)
-    check_plan(plan, rp, ci, w.B, w.H, w.N, Hm)
+    _, nsplit = check_plan(plan, rp, ci, w.B, w.H, w.N, Hm)
+    print(f"{name}: {nsplit} split-mode pairs", flush=True)
     assert_bitwise(f"{name} workers={workers}", o_p, l_p, o, lse)
     if workers == 0:
         o_ref, l_ref, tol = oracle_rows_and_lse_tol(q, k, v, m_ref, 128, workers=8)

@@ -1,9 +1,10 @@
 """bsattn_fwd_noalloc (the forward that allocates nothing: its plan lives in
 the library's own device array) against bsattn_fwd, through the C ABI: two
 calls in a row, the second on a smaller input, each compared with
-bsattn_fwd's output element by element (the planned path's arithmetic is
-bsattn_fwd's, so they must agree bit for bit, inside the output bar a
-fortiori); sizes beyond the array are refused before anything runs."""
+bsattn_fwd's output element by element within the output bar (max |err| <=
+1e-2, mean |err| <= 1e-3), and bit for bit with bsattn_fwd_planned through
+a plan of the caller's (the same kernels); sizes beyond the array are
+refused before anything runs."""
 import ctypes
 
 import numpy as np
@@ -34,12 +35,21 @@ def _compare(name, w):
     lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
     assert _noalloc(q, k, v, o, lse, rp, ci, w.tile, Hm) == bs.OK, bs.lib().bsattn_last_error()
     o_ref, lse_ref = bs.attention(q, k, v, rp, ci, w.tile, mask_heads=Hm, want_lse=True)
+    planned = w.d == 128 and w.tile == 128 and w.dtype == W.DTYPE_BF16
+    if planned:
+        o_pl, lse_pl = bs.attention_planned(q, k, v, rp, ci, mask_heads=Hm, want_lse=True)
     torch.cuda.synchronize()
     d = (o.double() - o_ref.double()).abs()
-    print(f"{name}: max|dO| {d.max().item():.3e}", flush=True)
+    print(f"{name}: max|dO| {d.max().item():.3e} mean {d.mean().item():.3e}", flush=True)
     assert d.max().item() <= MAX_ABS and d.mean().item() <= MEAN_ABS
-    assert torch.equal(o, o_ref)
-    assert torch.equal(lse.view(torch.int32), lse_ref.view(torch.int32))
+    fin = torch.isfinite(lse_ref)
+    assert torch.equal(torch.isfinite(lse), fin)
+    assert (lse[fin] - lse_ref[fin]).abs().max().item() <= 2e-2
+    if planned:
+        assert torch.equal(o, o_pl)
+        assert torch.equal(lse.view(torch.int32), lse_pl.view(torch.int32))
+    else:
+        assert torch.equal(o, o_ref)
 
 
 def test_two_calls_in_a_row_the_second_smaller():
