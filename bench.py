@@ -373,13 +373,17 @@ def squad_leg(bs, W, torch, dev, calls: int):
 
 
 def repetition_leg(bs, W, torch, dev, calls: int):
-    """Spatial repetition at the video shape (21 x 30 x 52, 12 heads, six of
-    them with repeating rows): row cosines and the head decision at stride
-    2, gamma 0.9; then attention of all heads computed on anchor rows only
-    against dense attention of the same shape."""
+    """CalibAtt's spatial repetition at the video shape (21 x 30 x 52, 12
+    heads; in six of them the rows of a frame repeat, the other six attend
+    frame-locally): calibration (row cosines and the head decision at stride
+    2, gamma 0.9; block energies, selection and agreement for the block
+    lists), then the inference layer itself -- repetitive heads on anchor
+    rows copied, the others on their calibrated lists, one forward for all
+    heads (gather, forward, broadcast) -- against dense attention of the
+    same shape."""
     w = W.WORKLOADS[2]
     stride, gamma = 2, 0.9
-    q, k = W.make_qk_row_repetitive(w, rep_heads=6, device=dev)
+    q, k = W.make_qk_row_repetitive(w, rep_heads=6, local_strength=0.7, device=dev)
     v = torch.randn(q.shape, generator=torch.Generator().manual_seed(9)).to(
         torch.bfloat16).to(dev)
     stream = torch.cuda.current_stream()
@@ -399,42 +403,46 @@ def repetition_leg(bs, W, torch, dev, calls: int):
     nonanchor = w.grid_h - (-(-w.grid_h // stride))
     # one sweep x two queries x (non-anchor rows x grid_w) x N keys x 2d
     cos_flops = 2 * w.B * w.H * w.frames * nonanchor * w.grid_w * w.N * 2.0 * w.d
-    bs.repeated_attention(q, k, v, w.frames, w.grid_h, w.grid_w, stride, w.tile)
-    re = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(calls)]
-    for a, b in re:
-        a.record(stream)
-        bs.repeated_attention(q, k, v, w.frames, w.grid_h, w.grid_w, stride, w.tile,
-                              stream=stream)
-        b.record(stream)
+    # block lists of every head from this prompt (used by the others)
+    cal_mask, _, _ = bs.calibrate(q, k, w.tile, W.CALIB_EPS, W.CALIB_RHO)
+    rp, ci, mixed = bs.mixed_layer_csr(flags, cal_mask, w.frames, w.grid_h, w.grid_w, stride,
+                                       w.tile)
     torch.cuda.synchronize()
-    rep_ms = float(np.median([a.elapsed_time(b) for a, b in re]))
+    qb, ob, out = torch.zeros_like(q), torch.empty_like(q), torch.empty_like(q)
+
+    def layer():
+        bs.mixed_attention(q, k, v, flags, rp, ci, w.frames, w.grid_h, w.grid_w, stride,
+                           w.tile, qbuf=qb, obuf=ob, out=out, stream=stream)
+
     dm = bs.make_mask(w.frames, w.grid_h, w.grid_w, w.tile, device=dev, kind=W.MASK_DENSE)
     drp, dci = bs.make_csr(dm)
     o = torch.empty_like(q)
-    bs.fwd(q, k, v, o, drp, dci, w.tile)
-    de = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(calls)]
-    for a, b in de:
-        a.record(stream)
+
+    def dense():
         bs.fwd(q, k, v, o, drp, dci, w.tile, stream=stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    dense_ms = float(np.median([a.elapsed_time(b) for a, b in de]))
+
+    layer_ms, dense_ms = time_interleaved(torch, stream, [layer, dense], calls)
     c = cos.cpu().numpy()
-    na = w.frames * (-(-w.grid_h // stride)) * w.grid_w
-    return {"workload": w.name + "_rows_repeat_in_6_of_12_heads", "stride": stride,
+    fl = flags.cpu().numpy()
+    cm = cal_mask.cpu().numpy()
+    mm = mixed.cpu().numpy()
+    act = active_flops(mm, w)
+    return {"workload": w.name + "_calibatt_layer_6_repetitive_heads", "stride": stride,
             "gamma": gamma,
             "row_cosines_ms": round(cos_ms, 3),
             "row_cosines_tflops": round(cos_flops / (cos_ms * 1e-3) / 1e12, 1),
             "heads_ms": round(heads_ms, 4),
-            "flags": flags.cpu().tolist(),
+            "flags": fl.tolist(),
             "mean_cos_repeating_heads": round(float(c[:, :6, :, 1::2].mean()), 4),
             "mean_cos_other_heads": round(float(c[:, 6:, :, 1::2].mean()), 4),
-            "anchor_fraction": round(na / w.N, 4),
-            "repeated_attention_ms": round(rep_ms, 4),
+            "calibrated_density_other_heads":
+                round(float(cm[fl == 0].mean()) if (fl == 0).any() else 0.0, 4),
+            "layer": "flagged heads: anchor rows (half the rows) copied; others: calibrated "
+                     "lists; gather + one forward + broadcast",
+            "layer_ms": round(layer_ms, 4),
+            "layer_forward_active_tflop": round(act / 1e12, 4),
             "dense_ms": round(dense_ms, 4),
-            "speedup_vs_dense": round(dense_ms / rep_ms, 2)}
+            "speedup_vs_dense": round(dense_ms / layer_ms, 2)}
 
 
 # Time at half the bf16 dense peak for each workload's active-block work: the

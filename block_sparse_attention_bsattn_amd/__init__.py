@@ -19,9 +19,12 @@ The calls mirror include/bsattn.h:
     row_cosines(q, k, ..., cos)                         -> bsattn_row_cosines
     repetitive_heads(cos, stride, gamma, flags)         -> bsattn_repetitive_heads
     anchor_rows(src, dst, ..., broadcast, block_rows)   -> bsattn_anchor_rows
+    anchor_rows(..., flags=f)                           -> bsattn_anchor_rows_heads
+    mask_select(flags, set_mask, clear_mask, out)       -> bsattn_mask_select
 
 plus small helpers that allocate the outputs with torch (make_mask,
-make_csr, make_plan, attention, calibrate, squad, repeated_attention).  There is no fallback: if libbsattn.so is missing or a
+make_csr, make_plan, attention, calibrate, squad, repeated_attention,
+mixed_layer_csr, mixed_attention).  There is no fallback: if libbsattn.so is missing or a
 call fails, an exception is raised.
 """
 from __future__ import annotations
@@ -56,7 +59,8 @@ EXPORTS = ("bsattn_version", "bsattn_status_string", "bsattn_last_error",
            "bsattn_fwd", "bsattn_fwd_grouped", "bsattn_fwd_plan_bytes", "bsattn_fwd_plan",
            "bsattn_fwd_planned", "bsattn_fwd_noalloc", "bsattn_window_reorder",
            "bsattn_row_cosines",
-           "bsattn_repetitive_heads", "bsattn_anchor_rows", "bsattn_block_energy",
+           "bsattn_repetitive_heads", "bsattn_anchor_rows", "bsattn_anchor_rows_heads",
+           "bsattn_mask_select", "bsattn_block_energy",
            "bsattn_select_blocks",
            "bsattn_aggregate_masks", "bsattn_mfma_ceiling")
 
@@ -136,6 +140,11 @@ def lib() -> ctypes.CDLL:
     L.bsattn_repetitive_heads.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.c_double, u8p, vp]
     L.bsattn_anchor_rows.restype = ctypes.c_int
     L.bsattn_anchor_rows.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, i32, i32, vp]
+    L.bsattn_anchor_rows_heads.restype = ctypes.c_int
+    L.bsattn_anchor_rows_heads.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, i32,
+                                           i32, u8p, vp]
+    L.bsattn_mask_select.restype = ctypes.c_int
+    L.bsattn_mask_select.argtypes = [i32, i32, i32, u8p, u8p, i32, u8p, i32, u8p, vp]
     L.bsattn_block_energy.restype = ctypes.c_int
     L.bsattn_block_energy.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp,
                                       ctypes.c_float, vp]
@@ -421,20 +430,50 @@ def repetitive_heads(cos, stride, gamma, flags, stream=None):
 
 
 def anchor_rows(src, dst, frames, grid_h, grid_w, stride, broadcast=False, block_rows=0,
-                stream=None):
+                flags=None, stream=None):
     """bsattn_anchor_rows between [B, H, N, d] buffers (gather, or broadcast
     with broadcast=True); block_rows > 0 spreads the packed anchor rows in
-    blocks of that many rows."""
+    blocks of that many rows.  With flags (uint8 [H] on the device),
+    bsattn_anchor_rows_heads: only the flagged heads are gathered or
+    broadcast, the others copied row for row."""
+    import torch
     if src.dim() != 4 or tuple(dst.shape) != tuple(src.shape) or dst.dtype != src.dtype:
         raise ValueError("src and dst must share shape [B, H, N, d] and dtype")
     B, H, N, d = src.shape
     if N != frames * grid_h * grid_w:
         raise ValueError("N must equal frames * grid_h * grid_w")
-    st = lib().bsattn_anchor_rows(B, H, frames, grid_h, grid_w, d, stride, _dtype_code(src),
-                                  _ptr(src, "src", src.dtype), _ptr(dst, "dst", src.dtype),
-                                  int(bool(broadcast)), int(block_rows), _stream(stream))
-    _check(st, "bsattn_anchor_rows")
+    if flags is None:
+        st = lib().bsattn_anchor_rows(B, H, frames, grid_h, grid_w, d, stride, _dtype_code(src),
+                                      _ptr(src, "src", src.dtype), _ptr(dst, "dst", src.dtype),
+                                      int(bool(broadcast)), int(block_rows), _stream(stream))
+        _check(st, "bsattn_anchor_rows")
+        return dst
+    if tuple(flags.shape) != (H,):
+        raise ValueError("flags must have shape [H]")
+    st = lib().bsattn_anchor_rows_heads(B, H, frames, grid_h, grid_w, d, stride,
+                                        _dtype_code(src), _ptr(src, "src", src.dtype),
+                                        _ptr(dst, "dst", src.dtype), int(bool(broadcast)),
+                                        int(block_rows), _ptr(flags, "flags", torch.uint8),
+                                        _stream(stream))
+    _check(st, "bsattn_anchor_rows_heads")
     return dst
+
+
+def mask_select(flags, set_mask, clear_mask, out, stream=None):
+    """bsattn_mask_select: out[h] = set_mask[h or 0] if flags[h] else
+    clear_mask[h or 0], masks uint8 [heads, Tq, Tk]."""
+    import torch
+    H, Tq, Tk = out.shape
+    for name, m in (("set_mask", set_mask), ("clear_mask", clear_mask)):
+        if m.dim() != 3 or tuple(m.shape[1:]) != (Tq, Tk) or m.shape[0] not in (1, H):
+            raise ValueError(f"{name} must have shape [1 or H, Tq, Tk]")
+    st = lib().bsattn_mask_select(H, Tq, Tk, _ptr(flags, "flags", torch.uint8),
+                                  _ptr(set_mask, "set_mask", torch.uint8), set_mask.shape[0],
+                                  _ptr(clear_mask, "clear_mask", torch.uint8),
+                                  clear_mask.shape[0], _ptr(out, "out", torch.uint8),
+                                  _stream(stream))
+    _check(st, "bsattn_mask_select")
+    return out
 
 
 def block_energy(q, k, energy, tile: int, scale: float = 0.0, stream=None):
@@ -627,6 +666,47 @@ def repeated_attention(q, k, v, frames, grid_h, grid_w, stride, tile, scale=0.0,
     out = torch.empty_like(q)
     anchor_rows(oa, out, frames, grid_h, grid_w, stride, broadcast=True, block_rows=block_rows,
                 stream=stream)
+    return out
+
+
+def mixed_layer_csr(flags, calibrated_mask, frames, grid_h, grid_w, stride, tile,
+                    stream=None):
+    """The block lists of CalibAtt's mixed inference layer (set up once per
+    layer: flags and calibrated masks are static): per head, the spread
+    anchor-row mask (DENSE_ROWS_SPREAD, blocks of two query tiles) when the
+    head is repetitive, else its calibrated mask [H or 1, Tq, Tk].
+    Returns (row_ptr, col_idx, mask) for mask_heads = H."""
+    import torch
+    H = flags.shape[0]
+    na = frames * (-(-grid_h // stride)) * grid_w
+    ta = -(-na // tile)
+    rows = make_mask(frames, grid_h, grid_w, tile, device=flags.device, stream=stream,
+                     kind=MASK_DENSE_ROWS_SPREAD, query_tiles=ta, block_tiles=2)
+    out = torch.empty((H,) + tuple(rows.shape[1:]), dtype=torch.uint8, device=flags.device)
+    mask_select(flags, rows, calibrated_mask, out, stream=stream)
+    rp, ci = make_csr(out, stream=stream)
+    return rp, ci, out
+
+
+def mixed_attention(q, k, v, flags, row_ptr, col_idx, frames, grid_h, grid_w, stride, tile,
+                    qbuf=None, obuf=None, out=None, scale=0.0, stream=None):
+    """CalibAtt's inference layer with the lists of mixed_layer_csr: the
+    repetitive heads' anchor-row queries are gathered into blocks spread over
+    their rows (the other heads' queries copied), one forward runs every
+    head on its own lists, and the repetitive heads' outputs are broadcast
+    from their anchor rows (the other heads' copied).  qbuf, obuf and out
+    are optional preallocated [B, H, N, d] buffers."""
+    import torch
+    block_rows = 2 * tile
+    qbuf = torch.zeros_like(q) if qbuf is None else qbuf
+    obuf = torch.empty_like(q) if obuf is None else obuf
+    out = torch.empty_like(q) if out is None else out
+    anchor_rows(q, qbuf, frames, grid_h, grid_w, stride, block_rows=block_rows, flags=flags,
+                stream=stream)
+    fwd(qbuf, k, v, obuf, row_ptr, col_idx, tile, mask_heads=q.shape[1], scale=scale,
+        stream=stream)
+    anchor_rows(obuf, out, frames, grid_h, grid_w, stride, broadcast=True,
+                block_rows=block_rows, flags=flags, stream=stream)
     return out
 
 

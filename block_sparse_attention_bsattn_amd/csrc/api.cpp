@@ -487,34 +487,76 @@ BSATTN_API int bsattn_repetitive_heads(int32_t B, int32_t H, int32_t T, int32_t 
                     "repetitive_heads");
 }
 
+static int anchor_rows_call(const char* who, int32_t B, int32_t H, int32_t T, int32_t grid_h,
+                            int32_t grid_w, int32_t d, int32_t stride, int32_t dtype,
+                            const void* src, void* dst, int32_t broadcast, int32_t block_rows,
+                            const uint8_t* flags, bool need_flags, void* stream);
+
 BSATTN_API int bsattn_anchor_rows(int32_t B, int32_t H, int32_t T, int32_t grid_h,
                                   int32_t grid_w, int32_t d, int32_t stride, int32_t dtype,
                                   const void* src, void* dst, int32_t broadcast,
                                   int32_t block_rows, void* stream) {
-  const int st = check_grid("anchor_rows", B, H, T, grid_h, grid_w, d, stride, dtype, false);
+  return anchor_rows_call("anchor_rows", B, H, T, grid_h, grid_w, d, stride, dtype, src, dst,
+                          broadcast, block_rows, nullptr, false, stream);
+}
+
+BSATTN_API int bsattn_anchor_rows_heads(int32_t B, int32_t H, int32_t T, int32_t grid_h,
+                                        int32_t grid_w, int32_t d, int32_t stride,
+                                        int32_t dtype, const void* src, void* dst,
+                                        int32_t broadcast, int32_t block_rows,
+                                        const uint8_t* flags, void* stream) {
+  return anchor_rows_call("anchor_rows_heads", B, H, T, grid_h, grid_w, d, stride, dtype, src,
+                          dst, broadcast, block_rows, flags, true, stream);
+}
+
+BSATTN_API int bsattn_mask_select(int32_t H, int32_t Tq, int32_t Tk, const uint8_t* flags,
+                                  const uint8_t* set_mask, int32_t set_heads,
+                                  const uint8_t* clear_mask, int32_t clear_heads,
+                                  uint8_t* out, void* stream) {
+  if (H < 0 || Tq < 0 || Tk < 0)
+    return fail(BSATTN_ERR_INVALID_ARG, "mask_select: H, Tq and Tk must be >= 0");
+  if ((set_heads != 1 && set_heads != H) || (clear_heads != 1 && clear_heads != H))
+    return fail(BSATTN_ERR_INVALID_ARG, "mask_select: mask heads must be 1 or H=%d", H);
+  const int64_t cells = (int64_t)Tq * Tk;
+  if ((int64_t)H * cells >= kMaxCells)
+    return fail(BSATTN_ERR_INVALID_ARG, "mask_select: mask has >= 2^31 cells");
+  if ((int64_t)H * cells == 0) return ok();
+  if (!flags || !set_mask || !clear_mask || !out)
+    return fail(BSATTN_ERR_INVALID_ARG, "mask_select: null pointer");
+  return hip_status(bsattn::launch_mask_select(H, cells, flags, set_mask, set_heads, clear_mask,
+                                               clear_heads, out, stream),
+                    "mask_select");
+}
+
+static int anchor_rows_call(const char* who, int32_t B, int32_t H, int32_t T, int32_t grid_h,
+                            int32_t grid_w, int32_t d, int32_t stride, int32_t dtype,
+                            const void* src, void* dst, int32_t broadcast, int32_t block_rows,
+                            const uint8_t* flags, bool need_flags, void* stream) {
+  const int st = check_grid(who, B, H, T, grid_h, grid_w, d, stride, dtype, false);
   if (st != BSATTN_OK) return st;
   if ((d * (dtype == BSATTN_DTYPE_BF16 ? 2 : 4)) % 16 != 0)
-    return fail(BSATTN_ERR_INVALID_ARG, "anchor_rows: rows must be 16-byte multiples");
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: rows must be 16-byte multiples", who);
   if (block_rows < 0)
-    return fail(BSATTN_ERR_INVALID_ARG, "anchor_rows: block_rows must be >= 0");
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: block_rows must be >= 0", who);
   if (block_rows > 0) {
     const int64_t n = (int64_t)T * grid_h * grid_w;
     const int64_t packed = (int64_t)T * ((grid_h + stride - 1) / stride) * grid_w;
     if ((packed + block_rows - 1) / block_rows > (n + block_rows - 1) / block_rows)
       return fail(BSATTN_ERR_INVALID_ARG,
-                  "anchor_rows: %lld anchor rows in blocks of %d do not fit %lld block slots",
+                  "%s: %lld anchor rows in blocks of %d do not fit %lld block slots", who,
                   (long long)packed, block_rows, (long long)((n + block_rows - 1) / block_rows));
   }
   if ((int64_t)B * H * T == 0) return ok();
   if (!src || !dst || src == dst)
-    return fail(BSATTN_ERR_INVALID_ARG, "anchor_rows: null or aliased buffers");
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: null or aliased buffers", who);
   if (!aligned16(src) || !aligned16(dst))
-    return fail(BSATTN_ERR_INVALID_ARG, "anchor_rows: buffers must be 16-byte aligned");
+    return fail(BSATTN_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", who);
+  if (need_flags && !flags) return fail(BSATTN_ERR_INVALID_ARG, "%s: null flags", who);
   const int32_t row_bytes = d * (dtype == BSATTN_DTYPE_BF16 ? 2 : 4);
   return hip_status(bsattn::launch_anchor_rows((int64_t)B * H, T * grid_h * grid_w, row_bytes,
                                                grid_h, grid_w, stride, broadcast != 0,
-                                               block_rows, src, dst, stream),
-                    "anchor_rows");
+                                               block_rows, src, dst, flags, H, stream),
+                    who);
 }
 
 BSATTN_API int bsattn_block_energy(int32_t B, int32_t H, int32_t N, int32_t d, int32_t tile,

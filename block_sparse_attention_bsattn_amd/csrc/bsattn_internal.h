@@ -115,9 +115,15 @@ struct RowCosLaunch {
 int launch_row_cosines(const RowCosLaunch& a, void* stream);
 int launch_repetitive_heads(int32_t B, int32_t H, int32_t T, int32_t gh, int32_t stride,
                             const float* cos, double gamma, uint8_t* flags, void* stream);
+// flags: null, or uint8 [H]: heads with flag 0 are copied row for row
 int launch_anchor_rows(int64_t BH, int32_t N, int32_t row_bytes, int32_t gh, int32_t gw,
                        int32_t stride, int broadcast, int32_t block_rows, const void* src,
-                       void* dst, void* stream);
+                       void* dst, const uint8_t* flags, int32_t H, void* stream);
+// out[h] = flags[h] ? set[set_heads == 1 ? 0 : h] : clear[clear_heads == 1 ? 0 : h],
+// each a [cells] byte slice
+int launch_mask_select(int32_t H, int64_t cells, const uint8_t* flags, const uint8_t* set,
+                       int32_t set_heads, const uint8_t* clear, int32_t clear_heads,
+                       uint8_t* out, void* stream);
 
 // static-mask calibration
 int launch_block_energy(const EnergyLaunch& a, void* stream);

@@ -166,4 +166,32 @@ int launch_build_mask(const MaskLaunch& a, uint8_t* mask, void* stream) {
   return hipGetLastError();
 }
 
+__global__ void __launch_bounds__(256)
+mask_select_kernel(int32_t H, int64_t cells, const uint8_t* __restrict__ flags,
+                   const uint8_t* __restrict__ set, int32_t set_heads,
+                   const uint8_t* __restrict__ clear, int32_t clear_heads,
+                   uint8_t* __restrict__ out) {
+  const int64_t total = (int64_t)H * cells;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int h = (int)(i / cells);
+    const int64_t c = i - (int64_t)h * cells;
+    out[i] = flags[h] ? set[(set_heads == 1 ? 0 : (int64_t)h) * cells + c]
+                      : clear[(clear_heads == 1 ? 0 : (int64_t)h) * cells + c];
+  }
+}
+
+int launch_mask_select(int32_t H, int64_t cells, const uint8_t* flags, const uint8_t* set,
+                       int32_t set_heads, const uint8_t* clear, int32_t clear_heads,
+                       uint8_t* out, void* stream) {
+  const int64_t total = (int64_t)H * cells;
+  if (total == 0) return hipSuccess;
+  int64_t grid = (total + 255) / 256;
+  if (grid > 1 << 16) grid = 1 << 16;
+  hipLaunchKernelGGL(mask_select_kernel, dim3((unsigned)grid), dim3(256), 0,
+                     (hipStream_t)stream, H, cells, flags, set, set_heads, clear, clear_heads,
+                     out);
+  return hipGetLastError();
+}
+
 }  // namespace bsattn

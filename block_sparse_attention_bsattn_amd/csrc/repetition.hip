@@ -29,7 +29,10 @@
 //
 // anchor_rows_kernel: an HBM-bound row copy.  Gather packs the anchor rows'
 // tokens (frame by frame, row by row) into Na rows of a buffer; broadcast
-// gives every token its anchor row's value from such a buffer.  The packed
+// gives every token its anchor row's value from such a buffer.  With
+// per-head flags, only the heads whose flag is set are gathered or
+// broadcast; the others are copied row for row (CalibAtt's inference runs
+// repetitive and other heads in one layer).  The packed
 // index a sits at buffer row a, or, spread in blocks of block_rows rows, at
 // row floor(g * Pg / Rg) * block_rows + a mod block_rows with g = a /
 // block_rows, Rg = ceil(Na / block_rows) and Pg = ceil(N / block_rows).  With
@@ -298,7 +301,8 @@ __global__ void repetitive_heads_kernel(int32_t B, int32_t H, int32_t T, int32_t
 __global__ void __launch_bounds__(256)
 anchor_rows_kernel(int64_t BH, int32_t N, int32_t cpr, int32_t gh, int32_t gw, int32_t stride,
                    int32_t na, int broadcast, int32_t block_rows, int32_t rg, int32_t pg,
-                   const i32x4* __restrict__ src, i32x4* __restrict__ dst) {
+                   const i32x4* __restrict__ src, i32x4* __restrict__ dst,
+                   const uint8_t* __restrict__ flags, int32_t H) {
   // buffer row of packed index p
   auto place = [&](int p) {
     if (block_rows == 0) return p;
@@ -308,7 +312,10 @@ anchor_rows_kernel(int64_t BH, int32_t N, int32_t cpr, int32_t gh, int32_t gw, i
   const int P = gh * gw;
   const int T = N / P;
   const int per_frame_a = na * gw;
-  const int rows = broadcast ? N : T * per_frame_a;  // destination rows per head
+  const int packed = T * per_frame_a;
+  // destination rows per head: with per-head flags every row (a head whose
+  // flag is 0 is copied row for row)
+  const int rows = (broadcast || flags != nullptr) ? N : packed;
   const int64_t total = BH * rows * cpr;
   const int64_t stride_g = (int64_t)gridDim.x * blockDim.x;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
@@ -317,6 +324,11 @@ anchor_rows_kernel(int64_t BH, int32_t N, int32_t cpr, int32_t gh, int32_t gw, i
     const int c = (int)(idx - r * cpr);
     const int64_t bh = r / rows;
     const int dn = (int)(r - bh * rows);
+    if (flags != nullptr && flags[bh % H] == 0) {
+      dst[(bh * N + dn) * cpr + c] = src[(bh * N + dn) * cpr + c];
+      continue;
+    }
+    if (!broadcast && dn >= packed) continue;  // not an anchor token's row
     int sn;
     if (!broadcast) {  // dst row dn = compact index: (frame, anchor number, x)
       const int f = dn / per_frame_a, rem = dn - f * per_frame_a;
@@ -367,21 +379,22 @@ int launch_repetitive_heads(int32_t B, int32_t H, int32_t T, int32_t gh, int32_t
 
 int launch_anchor_rows(int64_t BH, int32_t N, int32_t row_bytes, int32_t gh, int32_t gw,
                        int32_t stride, int broadcast, int32_t block_rows, const void* src,
-                       void* dst, void* stream) {
+                       void* dst, const uint8_t* flags, int32_t H, void* stream) {
   const int32_t cpr = row_bytes / 16;
   const int32_t na = (gh + stride - 1) / stride;
   const int32_t T = N / (gh * gw);
   const int32_t packed = T * na * gw;
   const int32_t rg = block_rows > 0 ? (packed + block_rows - 1) / block_rows : 1;
   const int32_t pg = block_rows > 0 ? (N + block_rows - 1) / block_rows : 1;
-  const int64_t rows = broadcast ? (int64_t)N : (int64_t)T * na * gw;
+  const int64_t rows = (broadcast || flags != nullptr) ? (int64_t)N : (int64_t)T * na * gw;
   const int64_t total = BH * rows * cpr;
   if (total == 0) return hipSuccess;
   int64_t grid = (total + 255) / 256;
   if (grid > 1 << 20) grid = 1 << 20;
   hipLaunchKernelGGL(anchor_rows_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
                      BH, N, cpr, gh, gw, stride, na, broadcast, block_rows, rg, pg,
-                     reinterpret_cast<const i32x4*>(src), reinterpret_cast<i32x4*>(dst));
+                     reinterpret_cast<const i32x4*>(src), reinterpret_cast<i32x4*>(dst), flags,
+                     H > 0 ? H : 1);
   return hipGetLastError();
 }
 

@@ -369,6 +369,38 @@ BSATTN_API int bsattn_anchor_rows(int32_t B, int32_t H, int32_t T, int32_t grid_
                                   const void* src, void* dst, int32_t broadcast,
                                   int32_t block_rows, void* stream);
 
+/* As bsattn_anchor_rows, head by head (CalibAtt page, "B. Fase di
+ * Inferenza": in one layer the repetitive heads compute their anchor rows
+ * and copy them, the other heads follow their block lists): heads with
+ * flags[h] != 0 are gathered (broadcast == 0) or broadcast as
+ * bsattn_anchor_rows does; heads with flags[h] == 0 are copied row for row
+ * (dst row n = src row n, every row).  In a gathered head the rows that do
+ * not hold an anchor token are not written.
+ *   flags: device uint8 [H] (as written by bsattn_repetitive_heads).
+ * Other arguments and errors as bsattn_anchor_rows; INVALID_ARG for null
+ * flags. */
+BSATTN_API int bsattn_anchor_rows_heads(int32_t B, int32_t H, int32_t T, int32_t grid_h,
+                                        int32_t grid_w, int32_t d, int32_t stride,
+                                        int32_t dtype, const void* src, void* dst,
+                                        int32_t broadcast, int32_t block_rows,
+                                        const uint8_t* flags, void* stream);
+
+/* Per-head choice between two tile masks (the mask of CalibAtt's mixed
+ * inference layer: the anchor-row mask for the repetitive heads, the
+ * calibrated block list for the others):
+ *   out[h] = flags[h] != 0 ? set_mask[set_heads == 1 ? 0 : h]
+ *                          : clear_mask[clear_heads == 1 ? 0 : h],
+ * each slice uint8 [Tq, Tk].
+ *   flags: device uint8 [H]; set_mask: device uint8 [set_heads, Tq, Tk];
+ *   clear_mask: device uint8 [clear_heads, Tq, Tk]; out: device uint8
+ *   [H, Tq, Tk], written (not aliasing the inputs).
+ * Errors: INVALID_ARG (negative sizes, mask heads not in {1, H}, null
+ * pointers, H*Tq*Tk >= 2^31), HIP.  H*Tq*Tk == 0 is a no-op. */
+BSATTN_API int bsattn_mask_select(int32_t H, int32_t Tq, int32_t Tk, const uint8_t* flags,
+                                  const uint8_t* set_mask, int32_t set_heads,
+                                  const uint8_t* clear_mask, int32_t clear_heads,
+                                  uint8_t* out, void* stream);
+
 /* ---- Static-mask calibration (CalibAtt page, "A. Fase di Calibrazione").
  * The calibration runs full attention on a few prompts, measures how much
  * attention every block receives, keeps per query block the fewest key

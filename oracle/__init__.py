@@ -31,7 +31,8 @@ Modules:
   squad      two-pass local/global attention (local output as the global
              pass's values)
   repetition spatial-row similarity, repetitive heads, attention on anchor
-             rows copied to the other rows
+             rows copied to the other rows, and the inference layer that
+             mixes such heads with block-list heads
 
 Every function here is pinned by tests/test_oracle_*.py against values and
 properties fixed by the pages or by mathematics (hand-enumerated masks,
@@ -51,7 +52,8 @@ from .calibration import (block_energy, block_energy_rows, select_row,
                           select_mask, aggregate)
 from .repetition import (anchor_row, row_cosines, repetitive_heads,
                          anchor_count, gather_anchor_rows,
-                         broadcast_anchor_rows, repeated_attention)
+                         broadcast_anchor_rows, repeated_attention,
+                         mixed_heads_attention, mixed_heads_attention_rows)
 from .squad import (squad_local, squad_attention, squad_attention_rows,
                     window_major_to_position_major,
                     position_major_to_window_major)
@@ -69,4 +71,5 @@ __all__ = [
     "window_major_to_position_major", "position_major_to_window_major",
     "anchor_row", "row_cosines", "repetitive_heads", "anchor_count",
     "gather_anchor_rows", "broadcast_anchor_rows", "repeated_attention",
+    "mixed_heads_attention", "mixed_heads_attention_rows",
 ]

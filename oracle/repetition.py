@@ -25,7 +25,10 @@ Readings taken where the page leaves a step open:
     is >= gamma; a head whose frames have no non-anchor row is repetitive;
   * a repetitive head computes full softmax attention (all keys) for the
     anchor-row queries, the repetition taking the place of block skipping
-    for that head, and o(f, y, x) = o(f, a(y), x).
+    for that head, and o(f, y, x) = o(f, a(y), x);
+  * in one layer (the inference of "B. Fase di Inferenza") the repetitive
+    heads do that and every other head computes attention over its static
+    block list.
 """
 from __future__ import annotations
 
@@ -33,7 +36,7 @@ import math
 
 import numpy as np
 
-from .attention import _as_f64
+from .attention import _as_f64, block_sparse_attention_rows
 
 
 def anchor_row(y: int, stride: int) -> int:
@@ -133,3 +136,47 @@ def repeated_attention(q, k, v, frames: int, grid_h: int, grid_w: int,
         for h in range(H):
             oa[b, h] = _probabilities(qa[b, h], k[b, h], scale) @ v[b, h]
     return broadcast_anchor_rows(oa, frames, grid_h, grid_w, stride)
+
+
+def mixed_heads_attention_rows(q, k, v, flags, mask, tile: int, frames: int,
+                               grid_h: int, grid_w: int, stride: int, rows,
+                               scale: float | None = None, workers: int = 1):
+    """One inference layer, for the query rows `rows` of every head: a head
+    with flags[h] set takes, for token (f, y, x), the full-attention output
+    of its anchor token (f, a(y), x); every other head takes attention over
+    its block list (mask [Hm, Tq, Tk], Hm in {1, H}).  Returns o
+    [B, H, len(rows), d] (float64)."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, N, d = q.shape
+    P = grid_h * grid_w
+    if N != frames * P:
+        raise ValueError("N must equal frames * grid_h * grid_w")
+    flags = np.asarray(flags)
+    mask = np.asarray(mask)
+    if flags.shape != (H,) or mask.shape[0] not in (1, H):
+        raise ValueError("flags must be [H] and mask [1 or H, Tq, Tk]")
+    rows = np.asarray(rows, dtype=np.int64)
+    f, rem = rows // P, rows % P
+    y, x = rem // grid_w, rem % grid_w
+    anchors = f * P + stride * (y // stride) * grid_w + x
+    dense = np.ones((1,) + mask.shape[1:], dtype=np.uint8)
+    o = np.zeros((B, H, len(rows), v.shape[3]))
+    for h in range(H):
+        sl = slice(h, h + 1)
+        if flags[h]:
+            o[:, sl], _ = block_sparse_attention_rows(q[:, sl], k[:, sl], v[:, sl], dense, tile,
+                                                      anchors, scale=scale, workers=workers)
+        else:
+            mh = mask[h if mask.shape[0] == H else 0][None]
+            o[:, sl], _ = block_sparse_attention_rows(q[:, sl], k[:, sl], v[:, sl], mh, tile,
+                                                      rows, scale=scale, workers=workers)
+    return o
+
+
+def mixed_heads_attention(q, k, v, flags, mask, tile: int, frames: int, grid_h: int,
+                          grid_w: int, stride: int, scale: float | None = None,
+                          workers: int = 1):
+    """mixed_heads_attention_rows for every row."""
+    N = np.asarray(q.shape)[2]
+    return mixed_heads_attention_rows(q, k, v, flags, mask, tile, frames, grid_h, grid_w,
+                                      stride, np.arange(N), scale=scale, workers=workers)

@@ -200,3 +200,104 @@ def test_repeated_attention_video_shape():
     dense = np.ones((1, w.num_tiles, w.num_tiles), dtype=np.uint8)
     want, _ = oracle.block_sparse_attention_rows(q, k, v, dense, w.tile, rows, workers=16)
     assert_close("repeated 21x30x52 anchor rows", to64(o[:, :, rows]), want)
+
+
+@pytest.mark.parametrize("T,gh,gw,d,s,dt", [(2, 5, 3, 128, 2, torch.bfloat16),
+                                            (3, 7, 4, 64, 3, torch.float32)])
+def test_anchor_rows_heads_bit_exact(T, gh, gw, d, s, dt):
+    """Per-head gather and broadcast: flagged heads as bsattn_anchor_rows
+    (spread layout), the others copied row for row."""
+    from layout_contract import anchor_buffer_rows
+    N = T * gh * gw
+    H = 4
+    x = torch.randn(2, H, N, d, generator=torch.Generator().manual_seed(N)).to(dt)
+    flags = torch.tensor([1, 0, 0, 1], dtype=torch.uint8, device="cuda")
+    br = 4
+    ga = torch.full_like(x, -7.0).cuda()
+    bs.anchor_rows(x.cuda(), ga, T, gh, gw, s, block_rows=br, flags=flags)
+    bc = torch.empty_like(ga)
+    bs.anchor_rows(ga, bc, T, gh, gw, s, broadcast=True, block_rows=br, flags=flags)
+    torch.cuda.synchronize()
+    na = T * oracle.anchor_count(gh, s) * gw
+    rows = anchor_buffer_rows(na, N, br)
+    xf = x.float().numpy()
+    got = ga.cpu().float().numpy()
+    for h in range(H):
+        if flags[h]:
+            want = oracle.gather_anchor_rows(xf[:, h], T, gh, gw, s)
+            assert np.array_equal(got[:, h][:, rows], want)
+            rest = np.setdiff1d(np.arange(N), rows)
+            assert (got[:, h][:, rest] == -7.0).all()          # not written
+            wb = oracle.broadcast_anchor_rows(want, T, gh, gw, s)
+            assert np.array_equal(bc.cpu().float().numpy()[:, h], wb)
+        else:
+            assert np.array_equal(got[:, h], xf[:, h])
+            assert np.array_equal(bc.cpu().float().numpy()[:, h], xf[:, h])
+
+
+def test_mask_select_bit_exact():
+    g = torch.Generator().manual_seed(4)
+    H, Tq, Tk = 5, 9, 11
+    a = (torch.rand(1, Tq, Tk, generator=g) < 0.5).to(torch.uint8)
+    b = (torch.rand(H, Tq, Tk, generator=g) < 0.5).to(torch.uint8)
+    f = torch.tensor([0, 1, 1, 0, 1], dtype=torch.uint8)
+    out = torch.empty(H, Tq, Tk, dtype=torch.uint8, device="cuda")
+    bs.mask_select(f.cuda(), a.cuda(), b.cuda(), out)
+    torch.cuda.synchronize()
+    want = np.where(f.numpy()[:, None, None] != 0, a.numpy(), b.numpy())
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
+def _mixed_case(T, gh, gw, H, s, flags, p, seed, tile=128):
+    N = T * gh * gw
+    g = torch.Generator().manual_seed(seed)
+    q, k, v = (torch.randn(1, H, N, 128, generator=g).to(torch.bfloat16) for _ in range(3))
+    Tn = -(-N // tile)
+    cal = oracle.tile_mask_static(H, Tn, Tn, seed, W.thresh24_for_density(p), True)
+    f = torch.tensor(flags, dtype=torch.uint8, device="cuda")
+    rp, ci, mm = bs.mixed_layer_csr(f, torch.from_numpy(cal).cuda(), T, gh, gw, s, tile)
+    o = bs.mixed_attention(q.cuda(), k.cuda(), v.cuda(), f, rp, ci, T, gh, gw, s, tile)
+    torch.cuda.synchronize()
+    return q, k, v, cal, o, mm
+
+
+@pytest.mark.parametrize("T,gh,gw,H,s,flags,p", [
+    (3, 9, 16, 4, 2, [1, 0, 1, 0], 0.4),
+    (2, 12, 20, 3, 3, [0, 1, 1], 0.3),
+    (4, 6, 30, 2, 2, [0, 0], 0.5),
+    (2, 7, 18, 2, 2, [1, 1], 0.5),
+])
+def test_mixed_layer_against_the_oracle(T, gh, gw, H, s, flags, p):
+    """CalibAtt's inference layer (CalibAtt page, "B. Fase di Inferenza"):
+    flagged heads on anchor rows, copied; the others on their block lists;
+    one forward for all heads.  Against the oracle's composition, every
+    element; the mixed mask bit-exact."""
+    from layout_contract import spread_dense_rows_mask
+    q, k, v, cal, o, mm = _mixed_case(T, gh, gw, H, s, flags, p, seed=T * gh + H)
+    N = T * gh * gw
+    na = T * oracle.anchor_count(gh, s) * gw
+    rows_mask = spread_dense_rows_mask(1, N, 128, -(-na // 128), 2)
+    want_mask = np.where(np.array(flags)[:, None, None] != 0, rows_mask, cal)
+    assert np.array_equal(mm.cpu().numpy(), want_mask)
+    want = oracle.mixed_heads_attention(q, k, v, flags, cal, 128, T, gh, gw, s)
+    assert_close(f"mixed layer {T}x{gh}x{gw} flags {flags}", to64(o), want)
+
+
+@pytest.mark.timeout(600)
+def test_mixed_layer_video_shape():
+    """21 x 30 x 52 latents, 12 heads, stride 2, flags on six heads, a
+    per-head static mask (p = 0.3) for the others: sampled rows of every
+    query tile against the oracle; flagged heads' rows copy their anchors
+    bitwise."""
+    flags = [1, 0] * 6
+    q, k, v, cal, o, _ = _mixed_case(21, 30, 52, 12, 2, flags, 0.3, seed=21)
+    N = q.shape[2]
+    ov = o.view(1, 12, 21, 30, 52, 128)
+    for h in range(0, 12, 2):
+        assert torch.equal(ov[:, h, :, 1::2], ov[:, h, :, 0:-1:2])
+    rows = np.concatenate([np.arange(t * 128, min(t * 128 + 128, N))[[0, 57, -1]]
+                           for t in range(-(-N // 128))])
+    want = oracle.mixed_heads_attention_rows(q, k, v, flags, cal, 128, 21, 30, 52, 2, rows,
+                                             workers=16)
+    assert_close("mixed layer 21x30x52 (3 rows of every tile, 12 heads)",
+                 to64(o[:, :, torch.from_numpy(rows).cuda()]), want)

@@ -112,3 +112,37 @@ def test_repeated_attention():
     for y in range(gh):
         np.testing.assert_allclose(o[:, :, :, y], f[:, :, :, 2 * (y // 2)], rtol=1e-12,
                                    atol=1e-13)
+
+
+def test_mixed_heads_reduce_to_each_kind():
+    """The mixed inference layer: no head flagged = block-sparse attention on
+    the lists; every head flagged = attention on anchor rows copied; a mix
+    gives each head its own kind; a flagged head's rows repeat their
+    anchor's and a dense list equals textbook attention."""
+    T, gh, gw, d, s, tile = 2, 6, 8, 8, 2, 16
+    N = T * gh * gw
+    q, k, v = _qkv(1, 3, N, d, 12)
+    Tq = -(-N // tile)
+    g = np.random.default_rng(3)
+    mask = (g.random((3, Tq, Tq)) < 0.5).astype(np.uint8)
+    mask[:, np.arange(Tq), np.arange(Tq)] = 1
+    sparse, _ = oracle.block_sparse_attention(q, k, v, mask, tile)
+    rep = oracle.repeated_attention(q, k, v, T, gh, gw, s)
+    none = oracle.mixed_heads_attention(q, k, v, [0, 0, 0], mask, tile, T, gh, gw, s)
+    np.testing.assert_allclose(none, sparse, rtol=0, atol=1e-14)
+    allf = oracle.mixed_heads_attention(q, k, v, [1, 1, 1], mask, tile, T, gh, gw, s)
+    np.testing.assert_allclose(allf, rep, rtol=0, atol=1e-14)
+    mix = oracle.mixed_heads_attention(q, k, v, [1, 0, 1], mask, tile, T, gh, gw, s)
+    np.testing.assert_allclose(mix[:, [0, 2]], rep[:, [0, 2]], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(mix[:, 1], sparse[:, 1], rtol=0, atol=1e-14)
+    m4 = mix.reshape(1, 3, T, gh, gw, d)
+    for y in range(gh):
+        assert np.array_equal(m4[:, 0, :, y], m4[:, 0, :, s * (y // s)])
+    dense = np.ones((1, Tq, Tq), dtype=np.uint8)
+    full = torch.nn.functional.scaled_dot_product_attention(q, k, v).numpy()
+    d0 = oracle.mixed_heads_attention(q, k, v, [0, 0, 0], dense, tile, T, gh, gw, s)
+    np.testing.assert_allclose(d0, full, rtol=1e-12, atol=1e-13)
+    # the rows variant on a sample equals the full one
+    rows = np.array([0, 5, 47, 48, 95])
+    r = oracle.mixed_heads_attention_rows(q, k, v, [1, 0, 1], mask, tile, T, gh, gw, s, rows)
+    np.testing.assert_allclose(r, mix[:, :, rows], rtol=0, atol=1e-14)

@@ -167,11 +167,15 @@ def make_qk_frame_local(w: Workload, strength: float = 1.0,
 
 
 def make_qk_row_repetitive(w: Workload, rep_heads: int, noise: float = 0.1,
-                           seed: Optional[int] = None, device: str = "cpu"):
+                           seed: Optional[int] = None, device: str = "cpu",
+                           local_strength: float = 0.0):
     """Q and K where, in heads 0 .. rep_heads-1, every spatial row of a frame
     repeats one per-frame row of queries plus N(0, noise^2) noise (the rows
-    of a frame then attend alike); the other heads are i.i.d. N(0, 1).  K is
-    i.i.d. N(0, 1).  Rounded to the workload's dtype."""
+    of a frame then attend alike); the other heads are i.i.d. N(0, 1), plus,
+    when local_strength > 0, a shared per-(head, frame) component of that
+    strength in both Q and K (their attention then concentrates on the
+    query's own frame, as make_qk_frame_local).  K is otherwise i.i.d.
+    N(0, 1).  Rounded to the workload's dtype."""
     g = torch.Generator(device="cpu")
     g.manual_seed(w.seed if seed is None else seed)
     q = torch.randn((w.B, w.H, w.N, w.d), generator=g, dtype=torch.float32)
@@ -181,6 +185,11 @@ def make_qk_row_repetitive(w: Workload, rep_heads: int, noise: float = 0.1,
         jit = noise * torch.randn((w.B, rep_heads, w.frames, w.grid_h, w.grid_w, w.d),
                                   generator=g)
         q[:, :rep_heads] = (row + jit).reshape(w.B, rep_heads, w.N, w.d)
+    if local_strength > 0 and rep_heads < w.H:
+        c = torch.randn((1, w.H - rep_heads, w.frames, w.d), generator=g)
+        cf = c.repeat_interleave(w.P, dim=2)
+        q[:, rep_heads:] += local_strength * cf
+        k[:, rep_heads:] += local_strength * cf
     return (q.to(w.torch_dtype()).to(device), k.to(w.torch_dtype()).to(device))
 
 
