@@ -389,11 +389,14 @@ def repetition_leg(bs, W, torch, dev, calls: int):
     stream = torch.cuda.current_stream()
     cos = torch.empty((w.B, w.H, w.frames, w.grid_h), dtype=torch.float32, device=dev)
     flags = torch.empty(w.H, dtype=torch.uint8, device=dev)
-    bs.row_cosines(q, k, w.frames, w.grid_h, w.grid_w, stride, cos)
+    ws = torch.empty(bs.row_cosines_workspace_bytes(w.B, w.H, w.frames, w.grid_h, w.grid_w,
+                                                    stride), dtype=torch.uint8, device=dev)
+    bs.row_cosines(q, k, w.frames, w.grid_h, w.grid_w, stride, cos, workspace=ws)
     cev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(calls)]
     for ev in cev:
         ev[0].record(stream)
-        bs.row_cosines(q, k, w.frames, w.grid_h, w.grid_w, stride, cos, stream=stream)
+        bs.row_cosines(q, k, w.frames, w.grid_h, w.grid_w, stride, cos, stream=stream,
+                       workspace=ws)
         ev[1].record(stream)
         bs.repetitive_heads(cos, stride, gamma, flags, stream=stream)
         ev[2].record(stream)

@@ -17,6 +17,7 @@ The calls mirror include/bsattn.h:
     aggregate_masks(masks, rho, out)                    -> bsattn_aggregate_masks
     window_reorder(src, dst, w, inverse)                -> bsattn_window_reorder
     row_cosines(q, k, ..., cos)                         -> bsattn_row_cosines
+    row_cosines_workspace_bytes(...)                    -> bsattn_row_cosines_workspace_bytes
     repetitive_heads(cos, stride, gamma, flags)         -> bsattn_repetitive_heads
     anchor_rows(src, dst, ..., broadcast, block_rows)   -> bsattn_anchor_rows
     anchor_rows(..., flags=f)                           -> bsattn_anchor_rows_heads
@@ -58,7 +59,7 @@ EXPORTS = ("bsattn_version", "bsattn_status_string", "bsattn_last_error",
            "bsattn_num_tiles", "bsattn_build_mask", "bsattn_compact",
            "bsattn_fwd", "bsattn_fwd_grouped", "bsattn_fwd_plan_bytes", "bsattn_fwd_plan",
            "bsattn_fwd_planned", "bsattn_fwd_noalloc", "bsattn_window_reorder",
-           "bsattn_row_cosines",
+           "bsattn_row_cosines", "bsattn_row_cosines_workspace_bytes",
            "bsattn_repetitive_heads", "bsattn_anchor_rows", "bsattn_anchor_rows_heads",
            "bsattn_mask_select", "bsattn_block_energy",
            "bsattn_select_blocks",
@@ -135,7 +136,9 @@ def lib() -> ctypes.CDLL:
     L.bsattn_window_reorder.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i32, vp]
     L.bsattn_row_cosines.restype = ctypes.c_int
     L.bsattn_row_cosines.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp,
-                                     ctypes.c_float, vp]
+                                     ctypes.c_float, vp, ctypes.c_int64, vp]
+    L.bsattn_row_cosines_workspace_bytes.restype = ctypes.c_int64
+    L.bsattn_row_cosines_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     L.bsattn_repetitive_heads.restype = ctypes.c_int
     L.bsattn_repetitive_heads.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.c_double, u8p, vp]
     L.bsattn_anchor_rows.restype = ctypes.c_int
@@ -400,18 +403,37 @@ def window_reorder(src, dst, w: int, inverse: bool = False, stream=None):
     return dst
 
 
-def row_cosines(q, k, frames, grid_h, grid_w, stride, cos, scale=0.0, stream=None):
-    """bsattn_row_cosines into cos [B, H, frames, grid_h] (float32)."""
+def row_cosines_workspace_bytes(B, H, frames, grid_h, grid_w, stride):
+    """bsattn_row_cosines_workspace_bytes."""
+    n = lib().bsattn_row_cosines_workspace_bytes(B, H, frames, grid_h, grid_w, stride)
+    if n < 0:
+        raise ValueError("row_cosines_workspace_bytes: invalid sizes")
+    return n
+
+
+def row_cosines(q, k, frames, grid_h, grid_w, stride, cos, scale=0.0, stream=None,
+                workspace=None, packed=True):
+    """bsattn_row_cosines into cos [B, H, frames, grid_h] (float32).  With
+    packed (the default) a workspace of row_cosines_workspace_bytes bytes is
+    passed (`workspace`, a device uint8 tensor, or one allocated here);
+    packed=False passes none (the row-aligned schedule)."""
     import torch
     B, H, N, d = q.shape
     if N != frames * grid_h * grid_w or tuple(k.shape) != tuple(q.shape):
         raise ValueError("q, k must be [B, H, frames*grid_h*grid_w, d]")
     if tuple(cos.shape) != (B, H, frames, grid_h):
         raise ValueError("cos must have shape [B, H, frames, grid_h]")
+    ws_ptr, ws_bytes = None, 0
+    if packed:
+        need = row_cosines_workspace_bytes(B, H, frames, grid_h, grid_w, stride)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace is not None:
+            ws_ptr, ws_bytes = _ptr(workspace, "workspace", torch.uint8), workspace.numel()
     st = lib().bsattn_row_cosines(B, H, frames, grid_h, grid_w, d, stride, _dtype_code(q),
                                   _ptr(q, "q", q.dtype), _ptr(k, "k", q.dtype),
                                   _ptr(cos, "cos", torch.float32), float(scale),
-                                  _stream(stream))
+                                  ws_ptr, ws_bytes, _stream(stream))
     _check(st, "bsattn_row_cosines")
     return cos
 

@@ -438,10 +438,17 @@ static int check_grid(const char* who, int32_t B, int32_t H, int32_t T, int32_t 
   return BSATTN_OK;
 }
 
+BSATTN_API int64_t bsattn_row_cosines_workspace_bytes(int32_t B, int32_t H, int32_t T,
+                                                      int32_t grid_h, int32_t grid_w,
+                                                      int32_t stride) {
+  if (B < 0 || H < 0 || T < 0 || grid_h < 1 || grid_w < 1 || stride < 1) return -1;
+  return bsattn::row_cos_workspace_bytes(B, H, T, grid_h, grid_w, stride);
+}
+
 BSATTN_API int bsattn_row_cosines(int32_t B, int32_t H, int32_t T, int32_t grid_h,
                                   int32_t grid_w, int32_t d, int32_t stride, int32_t dtype,
                                   const void* q, const void* k, float* cos, float scale,
-                                  void* stream) {
+                                  void* workspace, int64_t workspace_bytes, void* stream) {
   const int st = check_grid("row_cosines", B, H, T, grid_h, grid_w, d, stride, dtype, true);
   if (st != BSATTN_OK) return st;
   if (grid_w > 256) return fail(BSATTN_ERR_UNSUPPORTED, "row_cosines: grid_w %d > 256", grid_w);
@@ -453,6 +460,14 @@ BSATTN_API int bsattn_row_cosines(int32_t B, int32_t H, int32_t T, int32_t grid_
     return fail(BSATTN_ERR_INVALID_ARG, "row_cosines: scale must be finite");
   if ((int64_t)T * grid_h > INT32_MAX / 2)
     return fail(BSATTN_ERR_INVALID_ARG, "row_cosines: too many rows");
+  if (workspace != nullptr) {
+    const int64_t need = bsattn::row_cos_workspace_bytes(B, H, T, grid_h, grid_w, stride);
+    if (workspace_bytes < need)
+      return fail(BSATTN_ERR_INVALID_ARG, "row_cosines: workspace of %lld bytes, %lld needed",
+                  (long long)workspace_bytes, (long long)need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 3) != 0)
+      return fail(BSATTN_ERR_INVALID_ARG, "row_cosines: workspace must be 4-byte aligned");
+  }
   bsattn::RowCosLaunch a;
   a.B = B;
   a.H = H;
@@ -468,6 +483,7 @@ BSATTN_API int bsattn_row_cosines(int32_t B, int32_t H, int32_t T, int32_t grid_
   a.cos = cos;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
   a.scale_log2 = sc * 1.4426950408889634f;
+  a.ws = static_cast<float*>(workspace);
   return hip_status(bsattn::launch_row_cosines(a, stream), "row_cosines");
 }
 

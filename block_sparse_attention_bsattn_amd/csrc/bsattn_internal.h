@@ -111,8 +111,14 @@ struct RowCosLaunch {
   const void* k;
   float* cos;         // [B, H, T, gh]
   float scale_log2;   // softmax scale * log2(e)
+  float* ws;          // null, or per-column sums [B, H, T * nna * gw, 3] (tuned, packed)
 };
 int launch_row_cosines(const RowCosLaunch& a, void* stream);
+// tuned instance (bf16, d = 128; without a workspace grid_w <= 128): non-anchor rows only
+bool row_cos_tuned_fits(const RowCosLaunch& a);
+int64_t row_cos_workspace_bytes(int64_t B, int64_t H, int64_t T, int32_t gh, int32_t gw,
+                                int32_t stride);
+int launch_row_cos_tuned(const RowCosLaunch& a, void* stream);
 int launch_repetitive_heads(int32_t B, int32_t H, int32_t T, int32_t gh, int32_t stride,
                             const float* cos, double gamma, uint8_t* flags, void* stream);
 // flags: null, or uint8 [H]: heads with flag 0 are copied row for row

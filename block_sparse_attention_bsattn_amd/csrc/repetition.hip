@@ -354,6 +354,10 @@ int launch_cos(const RowCosLaunch& a, hipStream_t s) {
                      a.stride, a.cos);
   const int nna = a.gh - (a.gh + a.stride - 1) / a.stride;
   if (nna == 0) return hipGetLastError();
+  if (row_cos_tuned_fits(a)) {
+    const int e = hipGetLastError();
+    return e != hipSuccess ? e : launch_row_cos_tuned(a, s);
+  }
   const int wpr = (a.gw + 31) / 32;      // waves per row, <= 8
   const int rows_per_wg = 8 / wpr;       // up to 8 waves per workgroup
   const int rows = a.T * nna;

@@ -326,13 +326,27 @@ BSATTN_API int bsattn_window_reorder(int32_t B, int32_t H, int32_t N, int32_t d,
  * (scale <= 0 selects 1/sqrt(d)); anchor rows get 1.
  *   q, k: device [B, H, N, d], dtype BF16 (or F32 rounded to bf16).
  *   cos:  device float [B, H, T, grid_h], written.
+ *   workspace: null, or device memory of at least
+ *              bsattn_row_cosines_workspace_bytes(...) bytes, 4-byte
+ *              aligned, owned by the caller and overwritten.  With bf16 and
+ *              d = 128 it lets the kernel pack the columns of all rows into
+ *              full waves (per-column sums go there, a second kernel adds
+ *              them per row); otherwise, or when null, it is not used.
  * Supported: d in {64, 128}, grid_w <= 256.  B*H*T == 0 is a no-op.
  * Errors: INVALID_ARG (null pointers, sizes, B or H > 65535, unaligned q or
- * k, non-finite scale), UNSUPPORTED (d, dtype, grid_w), HIP. */
+ * k, non-finite scale, workspace_bytes below the size asked for),
+ * UNSUPPORTED (d, dtype, grid_w), HIP. */
 BSATTN_API int bsattn_row_cosines(int32_t B, int32_t H, int32_t T, int32_t grid_h,
                                   int32_t grid_w, int32_t d, int32_t stride, int32_t dtype,
                                   const void* q, const void* k, float* cos, float scale,
-                                  void* stream);
+                                  void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of the workspace bsattn_row_cosines packs with: 12 * B * H * T *
+ * (non-anchor rows per frame) * grid_w; 0 when there is no non-anchor row.
+ * Negative on invalid sizes (B, H, T < 0, grid_h, grid_w, stride < 1). */
+BSATTN_API int64_t bsattn_row_cosines_workspace_bytes(int32_t B, int32_t H, int32_t T,
+                                                      int32_t grid_h, int32_t grid_w,
+                                                      int32_t stride);
 
 /* Repetitive heads (calibration): flags[h] = 1 when the mean of cos over the
  * prompts b, frames f and non-anchor rows y (float64, summed in that

@@ -50,7 +50,7 @@ from .masks import (anchor_frames, window_frames, frame_set, frame_mask,
 from .csr import tile_csr
 from .calibration import (block_energy, block_energy_rows, select_row,
                           select_mask, aggregate)
-from .repetition import (anchor_row, row_cosines, repetitive_heads,
+from .repetition import (anchor_row, row_cosines, row_cosines_at, repetitive_heads,
                          anchor_count, gather_anchor_rows,
                          broadcast_anchor_rows, repeated_attention,
                          mixed_heads_attention, mixed_heads_attention_rows)
@@ -69,7 +69,7 @@ __all__ = [
     "block_energy", "block_energy_rows", "select_row", "select_mask",
     "aggregate", "squad_local", "squad_attention", "squad_attention_rows",
     "window_major_to_position_major", "position_major_to_window_major",
-    "anchor_row", "row_cosines", "repetitive_heads", "anchor_count",
+    "anchor_row", "row_cosines", "row_cosines_at", "repetitive_heads", "anchor_count",
     "gather_anchor_rows", "broadcast_anchor_rows", "repeated_attention",
     "mixed_heads_attention", "mixed_heads_attention_rows",
 ]

@@ -50,31 +50,60 @@ def _probabilities(q_rows, k, scale):
     return p / p.sum(axis=1, keepdims=True)
 
 
-def row_cosines(q, k, frames: int, grid_h: int, grid_w: int, stride: int,
-                scale: float | None = None) -> np.ndarray:
-    """cos[b, h, f, y] as defined above (float64)."""
-    q, k = _as_f64(q), _as_f64(k)
-    B, H, N, d = q.shape
+def _row_cosine(qbh, kbh, f: int, y: int, grid_h: int, grid_w: int, stride: int,
+                scale: float) -> float:
+    """cos(y) of frame f for one (prompt, head) slice ([N, d] float64)."""
+    a = anchor_row(y, stride)
+    if a == y:
+        return 1.0
     P = grid_h * grid_w
-    if N != frames * P:
+    r0 = f * P + y * grid_w
+    a0 = f * P + a * grid_w
+    p1 = _probabilities(qbh[r0:r0 + grid_w], kbh, scale)
+    p2 = _probabilities(qbh[a0:a0 + grid_w], kbh, scale)
+    return float((p1 * p2).sum() / math.sqrt((p1 * p1).sum() * (p2 * p2).sum()))
+
+
+def _check_grid(q, frames, grid_h, grid_w, stride, scale):
+    B, H, N, d = q.shape
+    if N != frames * grid_h * grid_w:
         raise ValueError("N must equal frames * grid_h * grid_w")
     if stride < 1:
         raise ValueError("stride must be >= 1")
     if scale is None or scale <= 0:
         scale = 1.0 / math.sqrt(d)
+    return scale
+
+
+def row_cosines(q, k, frames: int, grid_h: int, grid_w: int, stride: int,
+                scale: float | None = None) -> np.ndarray:
+    """cos[b, h, f, y] as defined above (float64)."""
+    q, k = _as_f64(q), _as_f64(k)
+    B, H = q.shape[:2]
+    scale = _check_grid(q, frames, grid_h, grid_w, stride, scale)
     out = np.ones((B, H, frames, grid_h))
     for b in range(B):
         for h in range(H):
             for f in range(frames):
                 for y in range(grid_h):
-                    a = anchor_row(y, stride)
-                    if a == y:
-                        continue
-                    r0 = f * P + y * grid_w
-                    a0 = f * P + a * grid_w
-                    p1 = _probabilities(q[b, h, r0:r0 + grid_w], k[b, h], scale)
-                    p2 = _probabilities(q[b, h, a0:a0 + grid_w], k[b, h], scale)
-                    out[b, h, f, y] = (p1 * p2).sum() / math.sqrt((p1 * p1).sum() * (p2 * p2).sum())
+                    out[b, h, f, y] = _row_cosine(q[b, h], k[b, h], f, y, grid_h, grid_w,
+                                                  stride, scale)
+    return out
+
+
+def row_cosines_at(q, k, frames: int, grid_h: int, grid_w: int, stride: int, cells,
+                   scale: float | None = None) -> np.ndarray:
+    """cos at the listed cells (b, h, f, y) only, in their order (float64):
+    the same per-row arithmetic as row_cosines, for shapes whose every row
+    would take too long."""
+    scale = _check_grid(q, frames, grid_h, grid_w, stride, scale)
+    out = np.empty(len(cells))
+    cache = {}
+    for i, (b, h, f, y) in enumerate(cells):
+        if (b, h) not in cache:  # one float64 copy per slice
+            cache = {(b, h): (_as_f64(q[b, h]), _as_f64(k[b, h]))}
+        qbh, kbh = cache[(b, h)]
+        out[i] = _row_cosine(qbh, kbh, f, y, grid_h, grid_w, stride, scale)
     return out
 
 

@@ -247,12 +247,22 @@ def test_repetition_calls_reject_bad_arguments():
     L = bs.lib()
     p, p2 = ctypes.c_void_p(64), ctypes.c_void_p(128)
     C = L.bsattn_row_cosines
-    assert C(1, 1, 2, 4, 8, 128, 0, 0, p, p, p, 0.0, None) == bs.ERR_INVALID_ARG   # stride 0
-    assert C(1, 1, 2, 4, 300, 128, 2, 0, p, p, p, 0.0, None) == bs.ERR_UNSUPPORTED  # grid_w
-    assert C(1, 1, 2, 4, 8, 96, 2, 0, p, p, p, 0.0, None) == bs.ERR_UNSUPPORTED
-    assert C(1, 1, 2, 4, 8, 128, 2, 0, p, p, None, 0.0, None) == bs.ERR_INVALID_ARG
-    assert C(1, 1, 2, 4, 8, 128, 2, 0, p, p, p, float("nan"), None) == bs.ERR_INVALID_ARG
-    assert C(0, 1, 2, 4, 8, 128, 2, 0, None, None, None, 0.0, None) == bs.OK
+    assert C(1, 1, 2, 4, 8, 128, 0, 0, p, p, p, 0.0, None, 0, None) == bs.ERR_INVALID_ARG
+    assert C(1, 1, 2, 4, 300, 128, 2, 0, p, p, p, 0.0, None, 0, None) == bs.ERR_UNSUPPORTED
+    assert C(1, 1, 2, 4, 8, 96, 2, 0, p, p, p, 0.0, None, 0, None) == bs.ERR_UNSUPPORTED
+    assert C(1, 1, 2, 4, 8, 128, 2, 0, p, p, None, 0.0, None, 0, None) == bs.ERR_INVALID_ARG
+    assert C(1, 1, 2, 4, 8, 128, 2, 0, p, p, p, float("nan"), None, 0, None) == \
+        bs.ERR_INVALID_ARG
+    assert C(0, 1, 2, 4, 8, 128, 2, 0, None, None, None, 0.0, None, 0, None) == bs.OK
+    # workspace: 12 B per column of the non-anchor rows (2 of 4 at stride 2)
+    WB = L.bsattn_row_cosines_workspace_bytes
+    assert WB(2, 3, 5, 4, 8, 2) == 12 * 2 * 3 * 5 * 2 * 8
+    assert WB(1, 1, 2, 4, 8, 1) == 0
+    assert WB(1, 1, 2, 4, 8, 0) < 0 and WB(-1, 1, 2, 4, 8, 2) < 0
+    need = WB(1, 1, 2, 4, 8, 2)
+    assert C(1, 1, 2, 4, 8, 128, 2, 0, p, p, p, 0.0, p2, need - 1, None) == bs.ERR_INVALID_ARG
+    assert C(1, 1, 2, 4, 8, 128, 2, 0, p, p, p, 0.0, ctypes.c_void_p(130), need, None) == \
+        bs.ERR_INVALID_ARG                                              # unaligned workspace
     R = L.bsattn_repetitive_heads
     assert R(1, 2, 3, 4, 0, p, 0.9, p, None) == bs.ERR_INVALID_ARG
     assert R(1, 2, 3, 4, 2, None, 0.9, p, None) == bs.ERR_INVALID_ARG

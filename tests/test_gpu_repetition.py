@@ -33,17 +33,27 @@ def _qk(B, H, T, gh, gw, d, seed, dt=torch.bfloat16):
     (1, 2, 3, 4, 40, 64, 2, torch.float32),      # fp32 inputs, d 64
     (1, 1, 1, 3, 200, 64, 2, torch.bfloat16),    # seven waves
     (1, 1, 2, 4, 8, 128, 1, torch.bfloat16),     # stride 1: all anchors
+    (1, 1, 2, 3, 96, 128, 2, torch.bfloat16),    # three waves a row, one idle a group
+    (1, 2, 2, 3, 128, 128, 2, torch.bfloat16),   # four waves a row
+    (1, 1, 1, 3, 13, 128, 2, torch.bfloat16),    # N = 39: one partial key tile
+    (2, 1, 3, 5, 33, 128, 2, torch.bfloat16),    # 31 idle columns in every second wave
+    (1, 1, 2, 5, 160, 128, 2, torch.bfloat16),   # grid_w > 128: the generic kernel
+    (1, 1, 2, 5, 20, 128, 2, torch.float32),     # fp32 inputs, d 128: the generic kernel
 ])
-def test_row_cosines(B, H, T, gh, gw, d, s, dt):
+@pytest.mark.parametrize("packed", [True, False])
+def test_row_cosines(B, H, T, gh, gw, d, s, dt, packed):
+    """Both schedules of the tuned kernel (packed columns with a workspace,
+    row-aligned without) and the generic kernel against the oracle."""
     q, k = _qk(B, H, T, gh, gw, d, 100 + gh * gw + s, dt)
     cos = torch.empty(B, H, T, gh, dtype=torch.float32, device="cuda")
-    bs.row_cosines(q.cuda(), k.cuda(), T, gh, gw, s, cos)
+    bs.row_cosines(q.cuda(), k.cuda(), T, gh, gw, s, cos, packed=packed)
     torch.cuda.synchronize()
     qo, ko = (q, k) if dt == torch.bfloat16 else (q.to(torch.bfloat16), k.to(torch.bfloat16))
     want = oracle.row_cosines(qo, ko, T, gh, gw, s)
     got = cos.cpu().numpy()
     err = float(np.abs(got - want).max())
-    print(f"cos B{B} H{H} T{T} {gh}x{gw} d{d} s{s}: max|dcos| {err:.2e}", flush=True)
+    print(f"cos B{B} H{H} T{T} {gh}x{gw} d{d} s{s} packed {packed}: max|dcos| {err:.2e}",
+          flush=True)
     assert err <= COS_TOL
     anchors = [y for y in range(gh) if s * (y // s) == y]
     assert (got[:, :, :, anchors] == 1.0).all()
@@ -73,6 +83,66 @@ def test_row_cosines_rising_scores(scale):
     print(f"cos rising scores scale {scale}: max|dcos| {err:.2e} "
           f"range [{float(want.min()):.3f}, {float(want.max()):.3f}]", flush=True)
     assert err <= COS_TOL
+
+
+@pytest.mark.parametrize("jump", [20.0, 60.0, 200.0])
+def test_row_cosines_score_jumps(jump):
+    """Every query's scores jump by `jump` (log2 units) at one late key tile
+    and fall back after it: the running max then grows long after the first
+    tile, by less (20: exponentials up to 2^20 against the old max) or more
+    (60, 200: the tile is redone against its exact max, and at 200 all
+    earlier sums vanish) than the kernel's rescaling limit."""
+    B, H, T, gh, gw, d, s = 1, 2, 2, 6, 40, 128, 2
+    N = T * gh * gw
+    g = torch.Generator().manual_seed(77)
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    q = torch.randn(B, H, N, d, generator=g) * 0.3 + 1.0 * u
+    k = torch.randn(B, H, N, d, generator=g) * 0.3
+    # scale 1: score ~ 1.0 * c for a key c * u; jump in natural units
+    c = jump / 1.4426950408889634
+    k[:, :, 5 * 64 + 3:5 * 64 + 40] += c * u
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    cos = torch.empty(B, H, T, gh, dtype=torch.float32, device="cuda")
+    bs.row_cosines(q.cuda(), k.cuda(), T, gh, gw, s, cos, scale=1.0)
+    torch.cuda.synchronize()
+    want = oracle.row_cosines(q, k, T, gh, gw, s, scale=1.0)
+    got = cos.cpu().numpy()
+    err = float(np.abs(got - want).max())
+    print(f"cos score jump {jump}: max|dcos| {err:.2e} "
+          f"range [{float(want.min()):.4f}, {float(want.max()):.4f}]", flush=True)
+    assert np.isfinite(got).all()
+    assert err <= COS_TOL
+
+
+def test_row_cosines_video_shape_sampled():
+    """The benchmark's calibration shape and inputs (21 x 30 x 52, 12 heads,
+    stride 2; six heads with repeating rows, six frame-local), sampled: the
+    oracle's cosine for three non-anchor rows of every head (first, last
+    and one random frame), every anchor row exactly 1, every value
+    finite."""
+    w = W.WORKLOADS[2]
+    s = 2
+    q, k = W.make_qk_row_repetitive(w, rep_heads=6, local_strength=0.7)
+    qc, kc = q.cuda(), k.cuda()
+    rng = np.random.default_rng(5)
+    cells = []
+    for h in range(w.H):
+        for f in (0, w.frames - 1, int(rng.integers(1, w.frames - 1))):
+            cells.append((0, h, f, 1 + s * int(rng.integers(0, w.grid_h // s))))
+    want = oracle.row_cosines_at(q, k, w.frames, w.grid_h, w.grid_w, s, cells)
+    for packed in (True, False):
+        cos = torch.empty(w.B, w.H, w.frames, w.grid_h, dtype=torch.float32, device="cuda")
+        bs.row_cosines(qc, kc, w.frames, w.grid_h, w.grid_w, s, cos, packed=packed)
+        torch.cuda.synchronize()
+        got = cos.cpu().numpy()
+        assert np.isfinite(got).all()
+        assert (got[:, :, :, 0::s] == 1.0).all()
+        g = np.array([got[c] for c in cells])
+        err = float(np.abs(g - want).max())
+        print(f"cos video shape, packed {packed}, {len(cells)} sampled rows: "
+              f"max|dcos| {err:.2e}", flush=True)
+        assert err <= COS_TOL
 
 
 def test_row_cosines_of_repeated_rows_are_one():

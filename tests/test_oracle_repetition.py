@@ -76,6 +76,17 @@ def test_cosine_brute_force():
     assert abs(got[0, 0, 0, 1] - d12 / math.sqrt(d11 * d22)) < 1e-13
 
 
+def test_sampled_cosines_are_the_full_ones():
+    """row_cosines_at (the sampled form the full-size GPU checks use) gives,
+    cell for cell, what the pinned row_cosines gives, anchors included."""
+    B, H, T, gh, gw, d, s = 2, 2, 2, 5, 3, 8, 2
+    q, k, _ = _qkv(B, H, T * gh * gw, d, 5)
+    full = oracle.row_cosines(q, k, T, gh, gw, s, scale=0.3)
+    cells = [(1, 0, 1, 3), (0, 1, 0, 1), (0, 1, 0, 2), (1, 1, 1, 4), (0, 0, 1, 1)]
+    got = oracle.row_cosines_at(q, k, T, gh, gw, s, cells, scale=0.3)
+    assert np.array_equal(got, np.array([full[c] for c in cells]))
+
+
 def test_repetitive_heads_by_hand():
     cos = np.ones((2, 3, 1, 4), dtype=np.float32)    # stride 2: rows 1, 3 count
     cos[:, 0, 0, 1] = 0.8
