@@ -13,6 +13,7 @@ The calls mirror include/bsattn.h:
     fwd_planned(q, k, v, o, row_ptr, col_idx, plan, ..) -> bsattn_fwd_planned
     fwd_noalloc(q, k, v, o, row_ptr, col_idx, tile, ...) -> bsattn_fwd_noalloc
     block_energy(q, k, energy, tile, ...)               -> bsattn_block_energy
+    block_energy_workspace_bytes(...)                   -> bsattn_block_energy_workspace_bytes
     select_blocks(energy, eps, mask)                    -> bsattn_select_blocks
     aggregate_masks(masks, rho, out)                    -> bsattn_aggregate_masks
     window_reorder(src, dst, w, inverse)                -> bsattn_window_reorder
@@ -61,7 +62,7 @@ EXPORTS = ("bsattn_version", "bsattn_status_string", "bsattn_last_error",
            "bsattn_fwd_planned", "bsattn_fwd_noalloc", "bsattn_window_reorder",
            "bsattn_row_cosines", "bsattn_row_cosines_workspace_bytes",
            "bsattn_repetitive_heads", "bsattn_anchor_rows", "bsattn_anchor_rows_heads",
-           "bsattn_mask_select", "bsattn_block_energy",
+           "bsattn_mask_select", "bsattn_block_energy", "bsattn_block_energy_workspace_bytes",
            "bsattn_select_blocks",
            "bsattn_aggregate_masks", "bsattn_mfma_ceiling")
 
@@ -150,7 +151,9 @@ def lib() -> ctypes.CDLL:
     L.bsattn_mask_select.argtypes = [i32, i32, i32, u8p, u8p, i32, u8p, i32, u8p, vp]
     L.bsattn_block_energy.restype = ctypes.c_int
     L.bsattn_block_energy.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp,
-                                      ctypes.c_float, vp]
+                                      ctypes.c_float, vp, ctypes.c_int64, vp]
+    L.bsattn_block_energy_workspace_bytes.restype = ctypes.c_int64
+    L.bsattn_block_energy_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.bsattn_select_blocks.restype = ctypes.c_int
     L.bsattn_select_blocks.argtypes = [i32, i32, vp, ctypes.c_double, u8p, vp]
     L.bsattn_aggregate_masks.restype = ctypes.c_int
@@ -498,9 +501,21 @@ def mask_select(flags, set_mask, clear_mask, out, stream=None):
     return out
 
 
-def block_energy(q, k, energy, tile: int, scale: float = 0.0, stream=None):
+def block_energy_workspace_bytes(B, H, N, tile):
+    """bsattn_block_energy_workspace_bytes."""
+    n = lib().bsattn_block_energy_workspace_bytes(B, H, N, tile)
+    if n < 0:
+        raise ValueError("block_energy_workspace_bytes: invalid sizes")
+    return n
+
+
+def block_energy(q, k, energy, tile: int, scale: float = 0.0, stream=None, workspace=None,
+                 one_sweep=True):
     """bsattn_block_energy: energy [B, H, T, T] (float32) = block sums of the
-    full softmax attention probabilities of q, k ([B, H, N, d])."""
+    full softmax attention probabilities of q, k ([B, H, N, d]).  With
+    one_sweep (the default) a workspace of block_energy_workspace_bytes
+    bytes is passed (`workspace`, a device uint8 tensor, or one allocated
+    here); one_sweep=False passes none (the two-sweep kernel)."""
     import torch
     if q.dim() != 4 or tuple(k.shape) != tuple(q.shape):
         raise ValueError("q and k must share the shape [B, H, N, d]")
@@ -508,10 +523,17 @@ def block_energy(q, k, energy, tile: int, scale: float = 0.0, stream=None):
     t = num_tiles(N, tile) if N > 0 else 0
     if tuple(energy.shape) != (B, H, t, t):
         raise ValueError(f"energy must have shape {(B, H, t, t)}")
+    ws_ptr, ws_bytes = None, 0
+    if one_sweep and B * H * N > 0:
+        need = block_energy_workspace_bytes(B, H, N, tile)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace is not None:
+            ws_ptr, ws_bytes = _ptr(workspace, "workspace", torch.uint8), workspace.numel()
     st = lib().bsattn_block_energy(B, H, N, d, tile, _dtype_code(q),
                                    _ptr(q, "q", q.dtype), _ptr(k, "k", q.dtype),
                                    _ptr(energy, "energy", torch.float32),
-                                   float(scale), _stream(stream))
+                                   float(scale), ws_ptr, ws_bytes, _stream(stream))
     _check(st, "bsattn_block_energy")
     return energy
 
@@ -607,15 +629,16 @@ def attention_planned(q, k, v, row_ptr, col_idx, plan=None, mask_heads=1, want_l
     return (o, lse) if want_lse else o
 
 
-def calibrate(q, k, tile, eps, rho, scale=0.0, stream=None):
+def calibrate(q, k, tile, eps, rho, scale=0.0, stream=None, workspace=None):
     """The static mask [H, T, T] (uint8) from the prompts along q's and k's
-    batch axis: block energies, per-prompt selection at eps, agreement at
-    rho.  Returns (mask, energy, per_prompt_masks)."""
+    batch axis: block energies (one sweep, with `workspace` or one allocated
+    here), per-prompt selection at eps, agreement at rho.  Returns (mask,
+    energy, per_prompt_masks)."""
     import torch
     B, H, N, d = q.shape
     t = num_tiles(N, tile)
     energy = torch.empty((B, H, t, t), dtype=torch.float32, device=q.device)
-    block_energy(q, k, energy, tile, scale=scale, stream=stream)
+    block_energy(q, k, energy, tile, scale=scale, stream=stream, workspace=workspace)
     sel = torch.empty((B, H, t, t), dtype=torch.uint8, device=q.device)
     select_blocks(energy, eps, sel, stream=stream)
     mask = torch.empty((H, t, t), dtype=torch.uint8, device=q.device)

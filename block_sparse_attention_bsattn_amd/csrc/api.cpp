@@ -575,9 +575,16 @@ static int anchor_rows_call(const char* who, int32_t B, int32_t H, int32_t T, in
                     who);
 }
 
+BSATTN_API int64_t bsattn_block_energy_workspace_bytes(int32_t B, int32_t H, int32_t N,
+                                                       int32_t tile) {
+  if (B < 0 || H < 0 || N < 0 || (tile != 64 && tile != 128)) return -1;
+  return bsattn::energy_workspace_bytes(B, H, N, tile);
+}
+
 BSATTN_API int bsattn_block_energy(int32_t B, int32_t H, int32_t N, int32_t d, int32_t tile,
                                    int32_t dtype, const void* q, const void* k, float* energy,
-                                   float scale, void* stream) {
+                                   float scale, void* workspace, int64_t workspace_bytes,
+                                   void* stream) {
   if (B < 0 || H < 0 || N < 0 || d < 0)
     return fail(BSATTN_ERR_INVALID_ARG, "block_energy: B, H, N and d must be >= 0");
   if (d != 64 && d != 128)
@@ -597,6 +604,14 @@ BSATTN_API int bsattn_block_energy(int32_t B, int32_t H, int32_t N, int32_t d, i
   const int32_t tiles = bsattn_num_tiles(N, tile);
   if ((int64_t)B * H * tiles * tiles >= kMaxCells)
     return fail(BSATTN_ERR_INVALID_ARG, "block_energy: energy tensor has >= 2^31 cells");
+  if (workspace != nullptr) {
+    const int64_t need = bsattn::energy_workspace_bytes(B, H, N, tile);
+    if (workspace_bytes < need)
+      return fail(BSATTN_ERR_INVALID_ARG, "block_energy: workspace of %lld bytes, %lld needed",
+                  (long long)workspace_bytes, (long long)need);
+    if (!aligned16(workspace))
+      return fail(BSATTN_ERR_INVALID_ARG, "block_energy: workspace must be 16-byte aligned");
+  }
   bsattn::EnergyLaunch a;
   a.B = B;
   a.H = H;
@@ -610,6 +625,7 @@ BSATTN_API int bsattn_block_energy(int32_t B, int32_t H, int32_t N, int32_t d, i
   a.tiles = tiles;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
   a.scale_log2 = sc * 1.4426950408889634f;
+  a.ws = static_cast<float*>(workspace);
   return hip_status(bsattn::launch_block_energy(a, stream), "block_energy");
 }
 

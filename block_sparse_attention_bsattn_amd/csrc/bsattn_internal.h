@@ -88,7 +88,13 @@ struct EnergyLaunch {
   float* energy;      // [B, H, tiles, tiles]
   int32_t tiles;
   float scale_log2;   // softmax scale * log2(e)
+  float* ws;          // null, or the one-sweep workspace (tuned instance)
 };
+
+// tuned block energies (bf16, d = 128, tile = 128)
+bool energy_tuned_fits(const EnergyLaunch& a);
+int64_t energy_workspace_bytes(int64_t B, int64_t H, int64_t N, int32_t tile);
+int launch_energy_tuned(const EnergyLaunch& a, void* stream);
 
 int launch_build_mask(const MaskLaunch& a, uint8_t* mask, void* stream);
 int launch_compact(int32_t rows, int32_t tk, const uint8_t* mask,

@@ -314,6 +314,7 @@ __global__ void aggregate_kernel(int32_t P, int64_t cells, const uint8_t* __rest
 }  // namespace
 
 int launch_block_energy(const EnergyLaunch& a, void* stream) {
+  if (energy_tuned_fits(a)) return launch_energy_tuned(a, stream);
   hipStream_t s = (hipStream_t)stream;
   return a.tile == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
 }

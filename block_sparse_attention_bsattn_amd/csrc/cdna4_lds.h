@@ -51,6 +51,12 @@ __device__ __forceinline__ float max_across_halves(float x) {
                                                   false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// sum over the two lanes (l, l ^ 32); both lanes get the same value
+__device__ __forceinline__ float sum_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Direct-to-LDS tile fetches written as inline asm.  buffer_load_dwordx4
 // ... lds moves 16 bytes per lane from global memory to LDS address

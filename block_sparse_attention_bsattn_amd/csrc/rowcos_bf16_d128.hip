@@ -286,10 +286,12 @@ row_cos_bf16_d128(RowCosLaunch a) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            if (u * 32 + 8 * i + e >= lim) {
-              a1[u][4 * i + e] = -INFINITY;
-              a2[u][4 * i + e] = -INFINITY;
-            }
+            // an integer select: no per-element compare masks
+            const uint32_t keep = (uint32_t)(((u * 32 + 8 * i + e) - lim) >> 31);
+            a1[u][4 * i + e] = __uint_as_float((__float_as_uint(a1[u][4 * i + e]) & keep) |
+                                               (0xff800000u & ~keep));
+            a2[u][4 * i + e] = __uint_as_float((__float_as_uint(a2[u][4 * i + e]) & keep) |
+                                               (0xff800000u & ~keep));
           }
     }
     float t1, t2, t12, t11, t22;

@@ -430,14 +430,30 @@ BSATTN_API int bsattn_mask_select(int32_t H, int32_t Tq, int32_t Tk, const uint8
  *            F32 rounded to bf16 for the products, which accumulate in fp32).
  *   energy:  device float [B, H, T, T], T = ceil(N / tile), written.
  *   scale:   softmax scale; <= 0 selects 1/sqrt(d).
+ *   workspace: null, or device memory of at least
+ *            bsattn_block_energy_workspace_bytes(...) bytes, 16-byte aligned,
+ *            owned by the caller and overwritten.  With bf16, d = 128 and
+ *            tile = 128 it lets the kernel make one sweep over the keys
+ *            instead of two (every row's per-tile sums wait there until the
+ *            row's normaliser is known); otherwise, or when null, it is not
+ *            used.
  * The batch index plays the role of the calibration prompt.  Supported:
  * d in {64, 128}, tile in {64, 128}.  B*H*N == 0 is a no-op.
  * Errors: INVALID_ARG (null pointers, negative sizes, B or H > 65535,
- * unaligned q or k, non-finite scale, B*H*T*T >= 2^31), UNSUPPORTED (d,
- * tile, dtype), HIP. */
+ * unaligned q, k or workspace, non-finite scale, B*H*T*T >= 2^31,
+ * workspace_bytes below the size asked for), UNSUPPORTED (d, tile, dtype),
+ * HIP. */
 BSATTN_API int bsattn_block_energy(int32_t B, int32_t H, int32_t N, int32_t d, int32_t tile,
                                    int32_t dtype, const void* q, const void* k, float* energy,
-                                   float scale, void* stream);
+                                   float scale, void* workspace, int64_t workspace_bytes,
+                                   void* stream);
+
+/* Bytes of the workspace of bsattn_block_energy's one-sweep kernel:
+ * 1024 * min(512, B * H * ceil(T / 2)) * T for tile 128 (512 persistent
+ * workgroups at most, each with 2 query tiles x 128 rows x T floats), 0 for
+ * other tiles.  Negative on invalid sizes. */
+BSATTN_API int64_t bsattn_block_energy_workspace_bytes(int32_t B, int32_t H, int32_t N,
+                                                       int32_t tile);
 
 /* Energy-based block selection (step 1), one row at a time:
  *   energy: device float [rows, Tk], finite and >= 0 (as written by

@@ -206,16 +206,27 @@ def test_calibration_calls_reject_bad_arguments():
     L = bs.lib()
     p = ctypes.c_void_p(64)
     E = L.bsattn_block_energy
-    assert E(1, 1, 256, 128, 128, 0, p, p, None, 0.0, None) == bs.ERR_INVALID_ARG
-    assert E(1, 1, 256, 96, 128, 0, p, p, p, 0.0, None) == bs.ERR_UNSUPPORTED
-    assert E(1, 1, 256, 128, 32, 0, p, p, p, 0.0, None) == bs.ERR_UNSUPPORTED
-    assert E(1, 1, 256, 128, 128, 7, p, p, p, 0.0, None) == bs.ERR_UNSUPPORTED
-    assert E(-1, 1, 256, 128, 128, 0, p, p, p, 0.0, None) == bs.ERR_INVALID_ARG
-    assert E(1, 1, 256, 128, 128, 0, ctypes.c_void_p(65), p, p, 0.0, None) == \
+    n = (None, 0, None)  # no workspace, stream
+    assert E(1, 1, 256, 128, 128, 0, p, p, None, 0.0, *n) == bs.ERR_INVALID_ARG
+    assert E(1, 1, 256, 96, 128, 0, p, p, p, 0.0, *n) == bs.ERR_UNSUPPORTED
+    assert E(1, 1, 256, 128, 32, 0, p, p, p, 0.0, *n) == bs.ERR_UNSUPPORTED
+    assert E(1, 1, 256, 128, 128, 7, p, p, p, 0.0, *n) == bs.ERR_UNSUPPORTED
+    assert E(-1, 1, 256, 128, 128, 0, p, p, p, 0.0, *n) == bs.ERR_INVALID_ARG
+    assert E(1, 1, 256, 128, 128, 0, ctypes.c_void_p(65), p, p, 0.0, *n) == \
         bs.ERR_INVALID_ARG
-    assert E(1, 1, 256, 128, 128, 0, p, p, p, float("nan"), None) == bs.ERR_INVALID_ARG
-    assert E(70000, 1, 256, 128, 128, 0, p, p, p, 0.0, None) == bs.ERR_INVALID_ARG
-    assert E(0, 1, 256, 128, 128, 0, None, None, None, 0.0, None) == bs.OK
+    assert E(1, 1, 256, 128, 128, 0, p, p, p, float("nan"), *n) == bs.ERR_INVALID_ARG
+    assert E(70000, 1, 256, 128, 128, 0, p, p, p, 0.0, *n) == bs.ERR_INVALID_ARG
+    assert E(0, 1, 256, 128, 128, 0, None, None, None, 0.0, *n) == bs.OK
+    # one-sweep workspace: 1024 * min(512, B * H * ceil(T / 2)) * T bytes at tile 128
+    WB = L.bsattn_block_energy_workspace_bytes
+    assert WB(1, 1, 256, 128) == 1024 * 1 * 2
+    assert WB(4, 12, 32760, 128) == 1024 * 512 * 256
+    assert WB(2, 3, 1000, 128) == 1024 * (2 * 3 * 4) * 8
+    assert WB(1, 1, 256, 64) == 0 and WB(-1, 1, 256, 128) < 0 and WB(1, 1, 256, 32) < 0
+    need = WB(1, 1, 256, 128)
+    assert E(1, 1, 256, 128, 128, 0, p, p, p, 0.0, p, need - 1, None) == bs.ERR_INVALID_ARG
+    assert E(1, 1, 256, 128, 128, 0, p, p, p, 0.0, ctypes.c_void_p(72), need, None) == \
+        bs.ERR_INVALID_ARG                                              # unaligned workspace
     S = L.bsattn_select_blocks
     assert S(-1, 4, p, 0.5, p, None) == bs.ERR_INVALID_ARG
     assert S(4, 4097, p, 0.5, p, None) == bs.ERR_UNSUPPORTED

@@ -24,11 +24,11 @@ E_RTOL = 1e-4
 E_ATOL = 1e-5
 
 
-def _gpu_energy(q, k, tile):
+def _gpu_energy(q, k, tile, one_sweep=True):
     B, H, N, d = q.shape
     t = bs.num_tiles(N, tile)
     e = torch.empty((B, H, t, t), dtype=torch.float32, device="cuda")
-    bs.block_energy(q, k, e, tile)
+    bs.block_energy(q, k, e, tile, one_sweep=one_sweep)
     torch.cuda.synchronize()
     return e
 
@@ -49,19 +49,49 @@ def _check_energy(name, got, want, rows_per_tile=None):
     (384, 128, 64, W.DTYPE_BF16, 1, 1),    # exact tiles
     (300, 64, 128, W.DTYPE_F32, 2, 1),     # fp32 inputs
     (1, 128, 128, W.DTYPE_BF16, 1, 1),     # one token
+    (640, 128, 128, W.DTYPE_BF16, 1, 3),   # odd tile count: the last pair's second tile is absent
+    (1100, 128, 128, W.DTYPE_BF16, 2, 1),  # odd and ragged
+    (700, 128, 128, W.DTYPE_F32, 1, 1),    # fp32 inputs, d 128: the generic kernel
 ])
-def test_block_energy_small(N, d, tile, dtype, B, H):
+@pytest.mark.parametrize("one_sweep", [True, False])
+def test_block_energy_small(N, d, tile, dtype, B, H, one_sweep):
+    """Both kernels of the tuned instance (one sweep with a workspace, two
+    without) and the generic kernel against the oracle."""
     w = W.small_workload(frames=1, grid_h=1, grid_w=N, tile=tile, d=d, H=H, B=B,
                          dtype=dtype, seed=zlib.crc32(f"{N}{d}{tile}".encode()) & 0xFFFF)
     q, k = W.make_qk_frame_local(w, strength=1.0)
-    e = _gpu_energy(q.cuda(), k.cuda(), tile).cpu().numpy()
+    e = _gpu_energy(q.cuda(), k.cuda(), tile, one_sweep).cpu().numpy()
     # the library rounds fp32 inputs to bf16 for the products (its contract);
     # the oracle gets those rounded values
     qo, ko = (q, k) if dtype == W.DTYPE_BF16 else (q.to(torch.bfloat16), k.to(torch.bfloat16))
     want = oracle.block_energy(qo, ko, tile)
-    _check_energy(f"N={N} d={d} tile={tile}", e, want)
+    _check_energy(f"N={N} d={d} tile={tile} one sweep {one_sweep}", e, want)
     rows = np.minimum(tile, N - np.arange(e.shape[-1]) * tile)
     np.testing.assert_allclose(e.sum(-1), np.broadcast_to(rows, e.shape[:-1]), rtol=2e-5)
+
+
+@pytest.mark.parametrize("one_sweep", [True, False])
+@pytest.mark.parametrize("jump", [20.0, 60.0, 200.0])
+def test_block_energy_score_jumps(jump, one_sweep):
+    """Scores jump by `jump` (log2 units) at a late key tile: the running
+    max of the first sweep grows long after the first tile, by less (20) or
+    more (60, 200: the tile is redone against its exact max) than the
+    rescaling limit; the energy moves onto that tile.  In one sweep the
+    redo also rescales the tile sums already in the workspace."""
+    B, H, N, d, tile = 1, 2, 1000, 128, 128
+    g = torch.Generator().manual_seed(78)
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    q = torch.randn(B, H, N, d, generator=g) * 0.3 + 1.0 * u
+    k = torch.randn(B, H, N, d, generator=g) * 0.3
+    k[:, :, 5 * 128 + 3:5 * 128 + 40] += (jump / 1.4426950408889634) * u
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    t = bs.num_tiles(N, tile)
+    e = torch.empty((B, H, t, t), dtype=torch.float32, device="cuda")
+    bs.block_energy(q.cuda(), k.cuda(), e, tile, scale=1.0, one_sweep=one_sweep)
+    torch.cuda.synchronize()
+    want = oracle.block_energy(q, k, tile, scale=1.0)
+    _check_energy(f"score jump {jump} one sweep {one_sweep}", e.cpu().numpy(), want)
 
 
 def test_block_energy_full_size_sampled_rows():
@@ -69,14 +99,17 @@ def test_block_energy_full_size_sampled_rows():
     sampled query tiles (first, last, and spread) against the oracle."""
     w = W.CALIB
     q, k = W.make_qk_frame_local(w, strength=1.0)
-    e = _gpu_energy(q.cuda(), k.cuda(), w.tile).cpu().numpy()
     T = w.num_tiles
     rows = np.minimum(w.tile, w.N - np.arange(T) * w.tile)
-    np.testing.assert_allclose(e.sum(-1), np.broadcast_to(rows, e.shape[:-1]), rtol=E_RTOL)
     pick = [0, 1, 97, 128, 200, T - 1]
     want = oracle.block_energy_rows(q[:2, :3], k[:2, :3], w.tile, pick)
-    _check_energy("video shape, 6 query tiles x 2 prompts x 3 heads",
-                  e[:2, :3][:, :, pick], want)
+    qc, kc = q.cuda(), k.cuda()
+    for one_sweep in (True, False):   # 6144 pairs over 512 persistent workgroups; one each
+        e = _gpu_energy(qc, kc, w.tile, one_sweep).cpu().numpy()
+        np.testing.assert_allclose(e.sum(-1), np.broadcast_to(rows, e.shape[:-1]),
+                                   rtol=E_RTOL)
+        _check_energy(f"video shape, one sweep {one_sweep}, 6 query tiles x 2 prompts x "
+                      "3 heads", e[:2, :3][:, :, pick], want)
 
 
 @pytest.mark.parametrize("rows,tk,eps,seed", [
