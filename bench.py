@@ -190,6 +190,56 @@ def expanded_windows(bs, W, torch, dev, calls: int):
             "step_tflops": round(float(np.sum(flops) / (step_ms.sum() * 1e-3)) / 1e12, 1)}
 
 
+def d64_leg(bs, W, torch, dev, calls: int):
+    """The 32 760-token video shape at head dim 64 and 64 x 64 tiles (24
+    heads, window +-1 frame + 2 anchors): `calls` steps at rotations 0, 1,
+    ..., each timed in its three parts with events on the launch stream."""
+    w = W.VIDEO_D64
+    q, k, v = W.make_qkv(w, device=dev)
+    o = torch.empty_like(q)
+    Tn = w.num_tiles
+    mask = torch.empty((1, Tn, Tn), dtype=torch.uint8, device=dev)
+    row_ptr = torch.empty(Tn + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(Tn * Tn, dtype=torch.int32, device=dev)
+    layout = (w.frames, w.grid_h, w.grid_w, w.tile)
+    stream = torch.cuda.current_stream()
+
+    def run(r, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        bs.build_mask(layout, mask, stream=stream,
+                      **bs.mask_params_of(w.with_rotation(r).mask))
+        if ev is not None:
+            ev[1].record(stream)
+        bs.compact(mask, row_ptr, col_idx, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    flops, dens = [], []
+    for r in range(calls):
+        run(r)
+        m_np = mask.cpu().numpy()
+        flops.append(active_flops(m_np, w))
+        dens.append(float(m_np.mean()))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+           for _ in range(calls)]
+    for r in range(calls):
+        run(r, evs[r])
+    torch.cuda.synchronize()
+    part = lambda a, b: np.array([e[a].elapsed_time(e[b]) for e in evs])
+    fwd_ms = part(2, 3)
+    tf = float(np.sum(flops) / (fwd_ms.sum() * 1e-3)) / 1e12
+    return {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "tile": w.tile,
+            "mask": "window +-1 frame + 2 anchors, rotation 0.." + str(calls - 1),
+            "density_mean": round(float(np.mean(dens)), 4),
+            "fwd_ms_median": round(float(np.median(fwd_ms)), 4),
+            "fwd_tflops": round(tf, 1),
+            "fwd_frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def calibration(bs, W, torch, dev, calls: int):
     """Static-mask calibration at the video shape (4 prompts x 12 heads x
     32 760 tokens, frame-local Q/K): block energies, per-prompt selection at
@@ -607,6 +657,8 @@ def main():
     ap.add_argument("--expanded", type=int, default=6,
                     help="steps of the expanded-window long-video path "
                          "(0 = skip)")
+    ap.add_argument("--d64", type=int, default=6,
+                    help="steps of the d 64 / tile 64 video leg (0: skip)")
     ap.add_argument("--calib", type=int, default=3,
                     help="timed calls of the static-mask calibration leg "
                          "(0 = skip)")
@@ -765,6 +817,8 @@ def main():
     expanded = expanded_windows(bs, W, torch, dev, args.expanded) \
         if args.expanded > 0 else None
 
+    d64 = d64_leg(bs, W, torch, dev, args.d64) if args.d64 > 0 else None
+
     calib = calibration(bs, W, torch, dev, args.calib) if args.calib > 0 else None
 
     squad = squad_leg(bs, W, torch, dev, args.squad) if args.squad > 0 else None
@@ -856,6 +910,7 @@ def main():
         "configs": configs,
         "density_sweep": sweep,
         "expanded_windows": expanded,
+        "d64_t64": d64,
         "calibration": calib,
         "squad": squad,
         "repetition": repetition,

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsattn.so")
 
-SOURCES = ["mask.hip", "compact.hip", "plan.hip", "fwd.hip", "fwd_bf16_t128.hip",
+SOURCES = ["mask.hip", "compact.hip", "plan.hip", "fwd.hip", "fwd_bf16_t128.hip", "fwd_bf16_d64_t64.hip",
            "calib.hip", "energy_bf16_d128.hip", "reorder.hip", "repetition.hip", "rowcos_bf16_d128.hip", "mfma_ceiling.hip",
            "api.cpp"]
 ARCH = "gfx950"

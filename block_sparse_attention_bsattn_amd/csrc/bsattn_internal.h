@@ -91,6 +91,10 @@ struct EnergyLaunch {
   float* ws;          // null, or the one-sweep workspace (tuned instance)
 };
 
+// tuned forward for bf16, d = 64, tile = 64 (contiguous rows, no plan)
+bool fwd_d64_t64_fits(const FwdLaunch& a);
+int launch_fwd_d64_t64(const FwdLaunch& a, void* stream);
+
 // tuned block energies (bf16, d = 128, tile = 128)
 bool energy_tuned_fits(const EnergyLaunch& a);
 int64_t energy_workspace_bytes(int64_t B, int64_t H, int64_t N, int32_t tile);

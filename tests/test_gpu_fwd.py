@@ -199,12 +199,14 @@ def sample_rows(w, per_tile, seed=0):
 # checked, with its first and last row.
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg,per_tile,rotation", [(4, 16, 0), (4, 4, 37),
-                                                   ("expanded", 8, 0)])
+                                                   ("expanded", 8, 0), ("video_d64", 8, 0),
+                                                   ("video_d64", 4, 9)])
 def test_full_size_sampled_rows(cfg, per_tile, rotation):
-    """Full-size 131 040-token workload on the GPU (launch configuration of
-    the benchmark); the oracle computes `per_tile` rows of every query tile
+    """Full-size workloads on the GPU (launch configuration of the
+    benchmark): the 131 040-token shapes and the 32 760-token d = 64 /
+    tile 64 shape; the oracle computes `per_tile` rows of every query tile
     for every head."""
-    w = W.EXPANDED if cfg == "expanded" else W.WORKLOADS[cfg]
+    w = {"expanded": W.EXPANDED, "video_d64": W.VIDEO_D64}.get(cfg) or W.WORKLOADS[cfg]
     w = w.with_rotation(rotation)
     q, k, v, mask, rp, ci, o, lse = run_gpu(w)
     m_ref = check_mask_csr(w, mask, rp, ci)
@@ -288,6 +290,58 @@ def test_tuned_kernel_pair_and_split_lists_and_bad_indices():
     torch.cuda.synchronize()
     assert_close("out-of-range entries skipped", to64(o2), o_ref, to64(lse2),
                  lse_ref, tol)
+
+
+def test_d64_t64_kernel_quad_lists_and_bad_indices():
+    """bf16 / d 64 / tile 64 (its tuned kernel: four query tiles walk the
+    union of their lists) on hand-built lists: quads with identical,
+    disjoint, partly empty, all empty and random lists, and a last quad of
+    two tiles; then the same lists with out-of-range key-tile indices mixed
+    in, which must be skipped."""
+    w = W.small_workload(frames=18, grid_h=8, grid_w=8, tile=64, d=64, H=2)
+    Tn = w.num_tiles
+    assert Tn == 18
+    g = np.random.default_rng(78)
+    m = np.zeros((2, Tn, Tn), dtype=np.uint8)
+    for h in range(2):
+        lists = {
+            0: [0, 3, 5, 9, 17], 1: [0, 3, 5, 9, 17], 2: [0, 3, 5, 9, 17],
+            3: [0, 3, 5, 9, 17],                                 # identical
+            4: [0, 4], 5: [1, 5, 8], 6: [2, 6, 10, 14], 7: [3, 16],  # disjoint
+            8: [], 9: [7, 8, 9], 10: [], 11: [1],                # partly empty
+            12: [], 13: [], 14: [], 15: [],                      # all empty
+        }
+        for i in (16, 17):                                        # a quad of two
+            lists[i] = sorted(g.choice(Tn, size=int(g.integers(1, 10)),
+                                       replace=False).tolist())
+        if h == 1:
+            lists = {i: lists[(i + 6) % 18] for i in range(18)}
+        for i, js in lists.items():
+            m[h, i, js] = 1
+    q, k, v = W.make_qkv(w, device="cuda")
+    rp, ci = bs.make_csr(torch.from_numpy(m).cuda())
+    o, lse = bs.attention(q, k, v, rp, ci, w.tile, mask_heads=2, want_lse=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.block_sparse_attention(q.cpu(), k.cpu(), v.cpu(), m, w.tile)
+    tol = lse_tolerance(q, k, m, w.tile)
+    assert_close("d64 quad lists", to64(o), o_ref, to64(lse), lse_ref, tol)
+    rows, cols = [0], []
+    for r in range(2 * Tn):
+        js = np.nonzero(m.reshape(2 * Tn, Tn)[r])[0].tolist()
+        if r % 3 == 0:
+            js = js + [Tn]
+        if r % 4 == 1:
+            js = [-1] + js
+        if r % 5 == 2:
+            js = js + [1 << 20]
+        cols += js
+        rows.append(len(cols))
+    rp2 = torch.tensor(rows, dtype=torch.int32, device="cuda")
+    ci2 = torch.tensor(cols + [0], dtype=torch.int32, device="cuda")
+    o2, lse2 = bs.attention(q, k, v, rp2, ci2, w.tile, mask_heads=2, want_lse=True)
+    torch.cuda.synchronize()
+    assert_close("d64 out-of-range entries skipped", to64(o2), o_ref, to64(lse2), lse_ref,
+                 tol)
 
 
 @pytest.mark.parametrize("mode", ["pair", "split"])

@@ -122,6 +122,15 @@ WORKLOADS = {
 }
 
 
+# The 32 760-token video shape at head dim 64 and 64 x 64 tiles (24 heads of
+# 64: the same width as 12 of 128), window/anchor mask as index 2: the
+# measurement and parity case of the d = 64 / tile 64 kernel.
+VIDEO_D64 = Workload("video_21x30x52_d64_t64_window_anchor", B=1, H=24, d=64, frames=21,
+                     grid_h=30, grid_w=52, tile=64, dtype=DTYPE_BF16,
+                     mask=MaskSpec(MASK_WINDOW_ANCHOR, window=1, num_anchors=2),
+                     seed=1007, rotations=tuple(range(21)))
+
+
 # The long-video shape with the LVSA expanded adaptive windows: every query
 # frame attends to a budget of C = 21 frames (the 21-frame training horizon),
 # made of 4 rotating anchors and a window grown from +/-2 frames.  A parity and
