@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 
 METRIC = "block-sparse attn fwd TFLOP/s (active blocks) + ms/call at 32760 tokens"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (no sparsity)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 HEADLINE = 2                # the 32 760-token video workload
 TRAFFIC_SUMMARY = "fwd_bf16_t128_d128.video_21x30x52_window_anchor.traffic.txt"
 MFMA_SUMMARY = "fwd_bf16_t128_d128.video_21x30x52_window_anchor.mfma.txt"
@@ -407,12 +408,25 @@ def squad_leg(bs, W, torch, dev, calls: int):
     dense_ms = float(np.median([a.elapsed_time(b) for a, b in de]))
     dense_flops = 4.0 * w.d * w.N * w.N * w.B * w.H
     p_l, p_g, p_t = part(evp, 0, 1), part(evp, 1, 2), part(evp, 0, 2)
+    # compulsory HBM bytes of one pass: Q, K and V (the local output in the
+    # global pass) read once, O written once.  At w = 256 a pass does 4 d w
+    # FLOPs per query row against 8 d bytes: 128 FLOP/B, under the MI355X
+    # ridge (2 500 TFLOP/s / 8 TB/s = 312 FLOP/B), so HBM bounds the passes.
+    pass_bytes = 4.0 * w.B * w.H * w.N * w.d * 2
+    gbs = lambda ms: pass_bytes / (ms * 1e-3) / 1e9
     return {"workload": w.name, "window": win, "groups": G,
             "planned_path": {"ms_total": round(p_t, 4), "local_ms": round(p_l, 4),
                              "local_tflops": round(flops_local / (p_l * 1e-3) / 1e12, 1),
+                             "local_hbm_gbs": round(gbs(p_l), 1),
                              "global_grouped_ms": round(p_g, 4),
                              "global_grouped_tflops":
-                                 round(flops_global / (p_g * 1e-3) / 1e12, 1)},
+                                 round(flops_global / (p_g * 1e-3) / 1e12, 1),
+                             "global_hbm_gbs": round(gbs(p_g), 1),
+                             "hbm_frac_of_peak": round(2 * pass_bytes / (p_t * 1e-3) / 1e9
+                                                       / PEAK_HBM_GBS, 4),
+                             "speedup_vs_dense": round(dense_ms / p_t, 2)},
+            "pass_bytes": int(pass_bytes),
+            "flop_per_byte": round(flops_local / pass_bytes, 1),
             "ms_total": round(total, 4),
             "local_ms": round(l_ms, 4), "local_tflops": round(flops_local / (l_ms * 1e-3) / 1e12, 1),
             "global_grouped_ms": round(g_ms, 4),
