@@ -856,8 +856,8 @@ def main():
     if args.cpu_tiles > 0:
         bs.build_mask(layout, mask, **bs.mask_params_of(w.with_rotation(0).mask))
         torch.cuda.synchronize()
-        # the pool takes every core this process may run on, up to the 16
-        # threads a one-GPU machine grants a job
+        # the pool takes every core this process may run on, up to 16 (the
+        # host share that goes with one GPU); both counts are reported
         host = len(os.sched_getaffinity(0))
         workers = max(1, min(16, host))
         cpu = cpu_baseline(w, q, k, v, mask.cpu().numpy(), args.cpu_tiles, workers)

@@ -8,7 +8,7 @@ import torch
 import block_sparse_attention_bsattn_amd as bs
 import oracle
 
-# spec gates for the output (bf16 I/O, fp32 accumulation)
+# the output bar (bf16 I/O, fp32 accumulation)
 MAX_ABS = 1e-2
 MEAN_ABS = 1e-3
 
