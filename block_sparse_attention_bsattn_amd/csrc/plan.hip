@@ -24,9 +24,9 @@
 //              of equal estimated cost (neighbouring pairs of a head share
 //              key tiles, which the XCD's L2 then serves), and each range is
 //              spread over the XCD's workers (worker w runs on XCD w % 8):
-//              64 items at a time are ranked by cost, longest first, and
-//              dealt a round at a time, the longest to the least-loaded
-//              worker.  Records each item's worker, its place in the
+//              256 items at a time (a whole range at most shapes) are ranked
+//              by cost, longest first, and dealt a round at a time, the
+//              longest to the least-loaded worker.  Records each item's worker, its place in the
 //              worker's order and the offset of its steps in the worker's
 //              pair-mode stream.
 //   3. steps:  one wave per item: the worker's item list; for a pair-mode
@@ -215,12 +215,17 @@ struct CostTable {
 
 // ---- 2. per XCD: the item range and its deal over the XCD's workers
 constexpr int kAssignThreads = 256;
+// items ranked together: the deal balances the workers only as well as the
+// longest items of a range are seen before the short ones, and ranges of a
+// few hundred lumpy items (lists of 12 to 180 tiles in one calibrated mask)
+// need the whole range at once
+constexpr int kBatch = kAssignThreads;
 
 __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a) {
   __shared__ int64_t part[kAssignThreads];
-  __shared__ __attribute__((aligned(16))) uint32_t keys[kWave];
-  __shared__ int sorted[kWave];
-  __shared__ int s_cost[kWave], s_steps[kWave];
+  __shared__ __attribute__((aligned(16))) uint32_t keys[kBatch];
+  __shared__ int sorted[kBatch];
+  __shared__ int s_cost[kBatch], s_steps[kBatch];
   __shared__ __attribute__((aligned(16))) int64_t s_load[kPlanMaxWorkersPerXcd];
   __shared__ int t_cost[kLdsPairs], t_steps[kLdsPairs];
   const int tid = threadIdx.x;
@@ -299,27 +304,27 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
   const int lo = (int)(part[0] >> 32), hi = (int)(part[0] & 0xFFFFFFFF);
   if (tid < R) s_load[tid] = 0;
 
-  // deal [lo, hi) over the R workers, 64 items at a time; thread j < R
+  // deal [lo, hi) over the R workers, kBatch items at a time; thread j < R
   // keeps worker j's item count and the lengths of its three streams (its
   // load in LDS)
   int cnt = 0, nsteps = 0, na = 0, nb = 0;
-  for (int b0 = lo; b0 < hi; b0 += kWave) {
-    const int nvalid = min(kWave, hi - b0);
+  for (int b0 = lo; b0 < hi; b0 += kBatch) {
+    const int nvalid = min(kBatch, hi - b0);
     uint32_t key = 0;
     if (tid < nvalid) {
       const ItemCost ic = tab.item(a, b0 + tid);
       // longest first, ties by position; 0 marks an empty slot
-      key = ((uint32_t)min(ic.cost, (1 << 25) - 1) << 6 | (uint32_t)(kWave - 1 - tid)) + 1;
+      key = ((uint32_t)min(ic.cost, (1 << 23) - 1) << 8 | (uint32_t)(kBatch - 1 - tid)) + 1;
       s_cost[tid] = ic.cost;
       s_steps[tid] = (ic.split ? ic.sa | (ic.sb << 15) : ic.steps) | (ic.split << 30);
     }
-    if (tid < kWave) keys[tid] = key;
+    keys[tid] = key;
     __syncthreads();
     if (tid < nvalid) {
       int rank = 0;
       const uint4* k4 = reinterpret_cast<const uint4*>(keys);
 #pragma unroll
-      for (int j = 0; j < kWave / 4; ++j) {
+      for (int j = 0; j < kBatch / 4; ++j) {
         const uint4 kv = k4[j];
         rank += (kv.x > key) + (kv.y > key) + (kv.z > key) + (kv.w > key);
       }
