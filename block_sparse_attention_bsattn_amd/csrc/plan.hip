@@ -25,8 +25,9 @@
 //              key tiles, which the XCD's L2 then serves), and each range is
 //              spread over the XCD's workers (worker w runs on XCD w % 8):
 //              256 items at a time (a whole range at most shapes) are ranked
-//              by cost, longest first, and dealt a round at a time, the
-//              longest to the least-loaded worker.  Records each item's worker, its place in the
+//              by cost, longest first, and dealt in rounds of half the
+//              XCD's workers, the longest of a round to the least-loaded
+//              worker.  Records each item's worker, its place in the
 //              worker's order and the offset of its steps in the worker's
 //              pair-mode stream.
 //   3. steps:  one wave per item: the worker's item list; for a pair-mode
@@ -331,8 +332,12 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
       sorted[rank] = tid;
     }
     __syncthreads();
-    for (int r0 = 0; r0 < nvalid; r0 += R) {
-      const int k = min(R, nvalid - r0);
+    // half the workers per round: a round hands one item to each of its
+    // least-loaded workers, so a worker already holding the range's longest
+    // items sits rounds out instead of taking one item every round
+    const int per_round = max(1, R / 2);
+    for (int r0 = 0; r0 < nvalid; r0 += per_round) {
+      const int k = min(per_round, nvalid - r0);
       int wr = R;
       int64_t mine = 0;
       if (tid < R) {

@@ -364,6 +364,56 @@ def test_never_read_tiles_are_never_fetched():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def _lumpy_masks(H, T, seed):
+    """Per-head masks whose lists are mostly short (12 to 41 tiles) with a
+    few long ones (about 8 % of even query tiles get 170 more); each odd
+    tile repeats its even neighbour's list plus two tiles, so pairs run in
+    pair mode."""
+    rng = np.random.default_rng(seed)
+    m = np.zeros((H, T, T), dtype=np.uint8)
+    for h in range(H):
+        for i in range(T):
+            if i % 2 == 1:
+                m[h, i] = m[h, i - 1]
+                m[h, i, rng.choice(T, size=2, replace=False)] = 1
+                continue
+            n = min(T, 12 + (170 if rng.random() < 0.08 else 0) + int(rng.integers(0, 30)))
+            m[h, i, rng.choice(T, size=n, replace=False)] = 1
+    return m
+
+
+def test_plan_deals_lumpy_lists_evenly():
+    """A few very long items among many short ones: the deal must leave no
+    worker far above the mean load, counted with the plan's own cost
+    estimate (pair mode 5 (union + 1), split mode 4 (n0 + n1) + 5).  Dealing
+    one item to every worker in each round left the worst worker at about
+    1.6x the mean here; rounds of half the workers, after ranking a whole
+    XCD range, about 1.04x."""
+    H, T = 12, 256
+    N = T * 128
+    m = _lumpy_masks(H, T, 11)
+    rp, ci = bs.make_csr(torch.from_numpy(m).cuda())
+    plan = bs.make_plan(rp, ci, 1, H, N, 128, H)
+    torch.cuda.synchronize()
+    P, _ = check_plan(plan, rp, ci, 1, H, N, H)
+    exp, pairs, tiles = expected_items(rp.cpu().numpy(), ci.cpu().numpy(), 1, H, N, H)
+    load = np.zeros(P["workers"], dtype=np.int64)
+    for w in range(P["workers"]):
+        first, cnt = P["witem"][w]
+        for t in range(cnt):
+            iw = int(P["witems"][first + t]) & 0x7FFFFFFF
+            bh, p = iw >> PAIR_BITS, iw & ((1 << PAIR_BITS) - 1)
+            split, union, la, lb = exp[bh * pairs + p]
+            if split:
+                sb = max(len(lb), 1) if 2 * p + 1 < tiles else 0
+                load[w] += 4 * (max(len(la), 1) + sb) + 5
+            else:
+                load[w] += 5 * (max(len(union), 1) + 1)
+    ratio = float(load.max() / load.mean())
+    print(f"lumpy lists: worst worker {ratio:.3f}x the mean load", flush=True)
+    assert ratio < 1.15
+
+
 def test_plan_for_other_sizes_writes_nothing():
     w = W.small_workload(frames=4, grid_h=8, grid_w=16, tile=128, d=128, H=2)
     mask, rp, ci = gpu_mask_csr(w)
