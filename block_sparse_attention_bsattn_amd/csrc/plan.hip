@@ -227,6 +227,9 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
   __shared__ __attribute__((aligned(16))) uint32_t keys[kBatch];
   __shared__ int sorted[kBatch];
   __shared__ int s_cost[kBatch], s_steps[kBatch];
+  // each dealt item's record, kept here until its batch is dealt: a global
+  // store before every round's barrier would make each barrier wait for it
+  __shared__ __attribute__((aligned(16))) int s_it[kBatch][4];
   __shared__ __attribute__((aligned(16))) int64_t s_load[kPlanMaxWorkersPerXcd];
   __shared__ int t_cost[kLdsPairs], t_steps[kLdsPairs];
   const int tid = threadIdx.x;
@@ -303,7 +306,10 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
     __syncthreads();
   }
   const int lo = (int)(part[0] >> 32), hi = (int)(part[0] & 0xFFFFFFFF);
-  if (tid < R) s_load[tid] = 0;
+  // worker j's key: its load * 512 + j, so one comparison orders by load
+  // and then by index; slots past R hold 2^62 and never come first (loads
+  // stay far below 2^53)
+  if (tid < kPlanMaxWorkersPerXcd) s_load[tid] = tid < R ? (int64_t)tid : ((int64_t)1 << 62);
 
   // deal [lo, hi) over the R workers, kBatch items at a time; thread j < R
   // keeps worker j's item count and the lengths of its three streams (its
@@ -341,24 +347,24 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
       int wr = R;
       int64_t mine = 0;
       if (tid < R) {
-        // rank of worker j by load (ties by index)
+        // rank of worker tid by load (ties by index): the keys below mine,
+        // counted by the sign of the difference over every slot, so the
+        // reads issue back to back with no compare per slot
         mine = s_load[tid];
         wr = 0;
-        for (int j2 = 0; j2 < R; ++j2) {
-          const int64_t l2 = s_load[j2];
-          wr += (l2 < mine || (l2 == mine && j2 < tid)) ? 1 : 0;
-        }
+#pragma unroll
+        for (int j2 = 0; j2 < kPlanMaxWorkersPerXcd; ++j2)
+          wr += (int)((uint64_t)(s_load[j2] - mine) >> 63);
       }
       __syncthreads();
       if (tid < R && wr < k) {
         const int src = sorted[r0 + wr];
-        const int item = b0 + src;
         const int st = s_steps[src];
         const int split = st >> 30;
-        int32_t* it = P32(a, L.off_itmp) + 4 * (int64_t)item;
+        int* it = s_it[src];
         it[0] = x + kPlanXcds * tid;
         it[1] = cnt;
-        s_load[tid] = mine + s_cost[src];
+        s_load[tid] = mine + ((int64_t)s_cost[src] << 9);
         if (split) {
           // the two tiles go to the two groups' streams, the longer list to
           // the shorter stream (orient 1: tile 2p + 1 to group 0's)
@@ -377,6 +383,9 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
       }
       __syncthreads();
     }
+    for (int i = tid; i < nvalid; i += kAssignThreads)
+      *reinterpret_cast<int4*>(P32(a, L.off_itmp) + 4 * (int64_t)(b0 + i)) =
+          *reinterpret_cast<const int4*>(s_it[i]);
   }
   // worker j's items take witems[lo + (items of workers < j), ...)
   if (tid < kWave) {
