@@ -90,10 +90,12 @@ def time_interleaved(torch, stream, fns, calls: int):
 SWEEP_P = (0.05, 0.1, 0.2, 0.3, 0.5, 0.7, 1.0)
 
 
-def density_sweep(bs, W, torch, dev, q, k, v, o, calls: int = 5, planned: bool = True):
+def density_sweep(bs, W, torch, dev, q, k, v, o, calls: int = 5):
     """The forward on the 32 760-token shape with per-head static random
     masks (seed 3, diagonal forced) at several densities: median ms per call
-    against active TFLOP, and a least-squares line through them."""
+    against active TFLOP, and a least-squares line through them, for
+    bsattn_fwd and for the planned forward (a static mask's plan is built
+    once, outside the timed calls), the two timed interleaved."""
     base = W.WORKLOADS[3]
     Tn = base.num_tiles
     Hm = base.H
@@ -112,30 +114,33 @@ def density_sweep(bs, W, torch, dev, q, k, v, o, calls: int = 5, planned: bool =
         bs.compact(mask, row_ptr, col_idx)
         m_np = mask.cpu().numpy()
         flops = active_flops(m_np, base)
-        run = forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, base.tile, Hm, planned,
-                         stream)
-        run()
-        evs = [(torch.cuda.Event(enable_timing=True),
-                torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
-        for a, b in evs:
-            a.record(stream)
-            run()
-            b.record(stream)
-        torch.cuda.synchronize()
-        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        runs = [forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, base.tile, Hm, pl, stream)
+                for pl in (False, True)]
+        ms, pms = time_interleaved(torch, stream, runs, calls)
         pts.append({"p": p, "density": round(float(m_np.mean()), 4),
                     "ms": round(ms, 4), "active_tflop": round(flops / 1e12, 4),
-                    "tflops": round(flops / (ms * 1e-3) / 1e12, 1)})
-    x = np.array([pt["active_tflop"] for pt in pts])
-    y = np.array([pt["ms"] for pt in pts])
-    slope, icpt = np.polyfit(x, y, 1)
-    r2 = 1.0 - ((y - (slope * x + icpt)) ** 2).sum() / ((y - y.mean()) ** 2).sum()
+                    "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                    "planned_ms": round(pms, 4),
+                    "planned_tflops": round(flops / (pms * 1e-3) / 1e12, 1)})
+
+    def fit(key):
+        x = np.array([pt["active_tflop"] for pt in pts])
+        y = np.array([pt[key] for pt in pts])
+        slope, icpt = np.polyfit(x, y, 1)
+        r2 = 1.0 - ((y - (slope * x + icpt)) ** 2).sum() / ((y - y.mean()) ** 2).sum()
+        return round(float(slope), 4), round(float(icpt), 4), round(float(r2), 5)
+
+    slope, icpt, r2 = fit("ms")
+    pslope, picpt, pr2 = fit("planned_ms")
     return {"mask": "static random per head (seed 3, diagonal forced), "
                     "B=1 H=12 N=32760 d=128 tile 128",
             "points": pts,
-            "fit_ms_per_active_tflop": round(float(slope), 4),
-            "fit_intercept_ms": round(float(icpt), 4),
-            "fit_r2": round(float(r2), 5)}
+            "fit_ms_per_active_tflop": slope,
+            "fit_intercept_ms": icpt,
+            "fit_r2": r2,
+            "planned_fit_ms_per_active_tflop": pslope,
+            "planned_fit_intercept_ms": picpt,
+            "planned_fit_r2": pr2}
 
 
 def expanded_windows(bs, W, torch, dev, calls: int):
@@ -825,7 +830,7 @@ def main():
         torch.cuda.synchronize()
         dense_ms = float(np.median([a.elapsed_time(b) for a, b in dev_ev]))
 
-    sweep = density_sweep(bs, W, torch, dev, q, k, v, o, planned=False) \
+    sweep = density_sweep(bs, W, torch, dev, q, k, v, o) \
         if args.sweep else None
 
     expanded = expanded_windows(bs, W, torch, dev, args.expanded) \
