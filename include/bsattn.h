@@ -125,19 +125,24 @@ typedef struct {
   int32_t query_tiles;    /* DENSE_ROWS(_SPREAD): >= 0 query tiles with every key tile */
 } bsattn_mask_params;
 
-/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH (a library utility,
+ * not a step of the method). */
 BSATTN_API int bsattn_version(void);
 
-/* Short static text for a status code. */
+/* Short static text for a status code (library utility). */
 BSATTN_API const char* bsattn_status_string(int status);
 
-/* Detail of the last error on the calling thread ("" if none). */
+/* Detail of the last error on the calling thread ("" if none; library
+ * utility). */
 BSATTN_API const char* bsattn_last_error(void);
 
-/* Number of tiles along one side: ceil(tokens / tile); -1 on bad input. */
+/* Number of tiles along one side: ceil(tokens / tile); -1 on bad input (the
+ * 128x128 blocks of CalibAtt page, "A. Fase di Calibrazione"). */
 BSATTN_API int32_t bsattn_num_tiles(int64_t tokens, int32_t tile);
 
-/* Build the tile mask.
+/* Build the tile mask of one of the kinds above, each defined by the passage
+ * cited on it (LVSA page, "Meccanismo Core"; CalibAtt page, "B. Fase di
+ * Inferenza"; SQuad page, "1. Operatore di Attenzione SQuad").
  *   layout, params: host structs (read during the call only).
  *   mask: device uint8 [Hm, Tq, Tk], row-major, Hm = params->mask_heads;
  *         every byte is written (0 or 1).
@@ -232,7 +237,9 @@ BSATTN_API int bsattn_fwd_grouped(int32_t B, int32_t H, int32_t N, int32_t d, in
  * is a multiple of 8 in [8, 512] (worker w is taken to run on XCD w % 8);
  * 0 selects the current device's compute units (256 on MI355X). */
 
-/* Bytes of a plan buffer for these sizes: a fixed part, plus 8 bytes per
+/* Bytes of a plan buffer (the plan of bsattn_fwd_plan, for block lists fixed
+ * before inference: CalibAtt page, "B. Fase di Inferenza") for these sizes:
+ * a fixed part, plus 8 bytes per
  * step; the steps number at most the smaller of B * (H / mask_heads) *
  * (nnz_bound + mask_heads * ceil(Tq / 2)) and B * H * ceil(Tq / 2) * Tk,
  * nnz_bound an upper bound on the CSR's entries (< 0 or above
@@ -242,7 +249,9 @@ BSATTN_API int64_t bsattn_fwd_plan_bytes(int32_t B, int32_t H, int32_t N, int32_
                                          int32_t mask_heads, int64_t nnz_bound,
                                          int32_t workers);
 
-/* Build the plan of a CSR (as written by bsattn_compact for rows =
+/* Build the plan of a CSR (CalibAtt page, "B. Fase di Inferenza": the block
+ * lists are fixed before inference, so the forward's scheduling can be
+ * worked out once per list set) (as written by bsattn_compact for rows =
  * mask_heads*Tq, Tk = Tq = ceil(N / tile)) into `plan`: device memory of
  * plan_bytes bytes, 16-byte aligned, owned by the caller; its contents are
  * the library's own (three launches on `stream`).  Key-tile indices outside
@@ -258,7 +267,9 @@ BSATTN_API int bsattn_fwd_plan(int32_t B, int32_t H, int32_t N, int32_t tile,
                                const int32_t* col_idx, int32_t workers, void* plan,
                                int64_t plan_bytes, void* stream);
 
-/* The forward through a plan: arguments as bsattn_fwd, plus the plan buffer
+/* The forward through a plan: the attention bsattn_fwd computes (CalibAtt
+ * page, "B. Fase di Inferenza"; LVSA page, "Meccanismo Core"), with
+ * arguments as bsattn_fwd, plus the plan buffer
  * (plan, plan_bytes and workers as given to bsattn_fwd_plan, whose CSR must
  * be row_ptr / col_idx) and window: 0 for contiguous tokens, w > 0 for the
  * grouped view of bsattn_fwd_grouped.  Launches `workers` workgroups.  The
@@ -319,7 +330,7 @@ BSATTN_API int bsattn_window_reorder(int32_t B, int32_t H, int32_t N, int32_t d,
  * Tokens are frame-major, n = f*P + y*grid_w + x, N = T*grid_h*grid_w; row
  * y copies from its anchor a(y) = s*floor(y/s). */
 
-/* Row similarity (calibration):
+/* Row similarity (CalibAtt page, "A. Fase di Calibrazione", step 3):
  *   cos[b, h, f, y] = sum_x <p_(y,x), p_(a,x)> /
  *                     sqrt(sum_x |p_(y,x)|^2 * sum_x |p_(a,x)|^2),
  * p_n the full-attention softmax probabilities of query n over all N keys
@@ -341,14 +352,16 @@ BSATTN_API int bsattn_row_cosines(int32_t B, int32_t H, int32_t T, int32_t grid_
                                   const void* q, const void* k, float* cos, float scale,
                                   void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Bytes of the workspace bsattn_row_cosines packs with: 12 * B * H * T *
+/* Bytes of the workspace bsattn_row_cosines packs with (row similarity:
+ * CalibAtt page, "A. Fase di Calibrazione", step 3): 12 * B * H * T *
  * (non-anchor rows per frame) * grid_w; 0 when there is no non-anchor row.
  * Negative on invalid sizes (B, H, T < 0, grid_h, grid_w, stride < 1). */
 BSATTN_API int64_t bsattn_row_cosines_workspace_bytes(int32_t B, int32_t H, int32_t T,
                                                       int32_t grid_h, int32_t grid_w,
                                                       int32_t stride);
 
-/* Repetitive heads (calibration): flags[h] = 1 when the mean of cos over the
+/* Repetitive heads (CalibAtt page, "A. Fase di Calibrazione", step 3):
+ * flags[h] = 1 when the mean of cos over the
  * prompts b, frames f and non-anchor rows y (float64, summed in that
  * order) is >= gamma, or when no row is a non-anchor row.
  *   cos:   device float [B, H, T, grid_h] (as written by bsattn_row_cosines).
@@ -359,7 +372,9 @@ BSATTN_API int bsattn_repetitive_heads(int32_t B, int32_t H, int32_t T, int32_t 
                                        int32_t stride, const float* cos, double gamma,
                                        uint8_t* flags, void* stream);
 
-/* Anchor-row gather and broadcast (inference), on [B, H, N, d] buffers.
+/* Anchor-row gather and broadcast (CalibAtt page, "B. Fase di Inferenza": a
+ * repetitive head computes its anchor rows and copies them to the rows
+ * between), on [B, H, N, d] buffers.
  * The anchor rows' tokens, frame by frame, row by row, have packed indices
  * a = 0 .. Na-1 (Na = T * ceil(grid_h/stride) * grid_w); packed index a is
  * stored at buffer row a when block_rows == 0, else at row
@@ -399,9 +414,9 @@ BSATTN_API int bsattn_anchor_rows_heads(int32_t B, int32_t H, int32_t T, int32_t
                                         int32_t broadcast, int32_t block_rows,
                                         const uint8_t* flags, void* stream);
 
-/* Per-head choice between two tile masks (the mask of CalibAtt's mixed
- * inference layer: the anchor-row mask for the repetitive heads, the
- * calibrated block list for the others):
+/* Per-head choice between two tile masks (CalibAtt page, "B. Fase di
+ * Inferenza": in its inference layer the repetitive heads take the
+ * anchor-row mask, the others their calibrated block lists):
  *   out[h] = flags[h] != 0 ? set_mask[set_heads == 1 ? 0 : h]
  *                          : clear_mask[clear_heads == 1 ? 0 : h],
  * each slice uint8 [Tq, Tk].
@@ -422,7 +437,8 @@ BSATTN_API int bsattn_mask_select(int32_t H, int32_t Tq, int32_t Tk, const uint8
  * static mask when enough prompts agree.  The result feeds bsattn_compact and
  * bsattn_fwd like any other tile mask. */
 
-/* Block energies of full softmax attention (step 1):
+/* Block energies of full softmax attention (CalibAtt page, "A. Fase di
+ * Calibrazione", step 1):
  *   E[b, h, i, j] = sum over query rows n of tile i and key columns m of
  *   tile j of softmax_m(scale * q_n . k_m), the softmax over all N keys.
  * Each row of E sums to the number of query rows in tile i.
@@ -448,14 +464,16 @@ BSATTN_API int bsattn_block_energy(int32_t B, int32_t H, int32_t N, int32_t d, i
                                    float scale, void* workspace, int64_t workspace_bytes,
                                    void* stream);
 
-/* Bytes of the workspace of bsattn_block_energy's one-sweep kernel:
+/* Bytes of the workspace of bsattn_block_energy's one-sweep kernel (block
+ * energies: CalibAtt page, "A. Fase di Calibrazione", step 1):
  * 1024 * min(512, B * H * ceil(T / 2)) * T for tile 128 (512 persistent
  * workgroups at most, each with 2 query tiles x 128 rows x T floats), 0 for
  * other tiles.  Negative on invalid sizes. */
 BSATTN_API int64_t bsattn_block_energy_workspace_bytes(int32_t B, int32_t H, int32_t N,
                                                        int32_t tile);
 
-/* Energy-based block selection (step 1), one row at a time:
+/* Energy-based block selection (CalibAtt page, "A. Fase di Calibrazione",
+ * step 1), one row at a time:
  *   energy: device float [rows, Tk], finite and >= 0 (as written by
  *           bsattn_block_energy, viewed as [B*H*T, T]).
  *   mask:   device uint8 [rows, Tk], written: 1 for the kept key blocks.
@@ -470,7 +488,7 @@ BSATTN_API int64_t bsattn_block_energy_workspace_bytes(int32_t B, int32_t H, int
 BSATTN_API int bsattn_select_blocks(int32_t rows, int32_t Tk, const float* energy, double eps,
                                     uint8_t* mask, void* stream);
 
-/* Cross-prompt agreement (step 2):
+/* Cross-prompt agreement (CalibAtt page, "A. Fase di Calibrazione", step 2):
  *   masks: device uint8 [P, cells] (P prompt masks, any nonzero = selected).
  *   out:   device uint8 [cells], written: 1 where the number of prompts that
  *          selected the cell is >= rho * P (float64), else 0.
@@ -479,7 +497,8 @@ BSATTN_API int bsattn_select_blocks(int32_t rows, int32_t Tk, const float* energ
 BSATTN_API int bsattn_aggregate_masks(int32_t P, int64_t cells, const uint8_t* masks, double rho,
                                       uint8_t* out, void* stream);
 
-/* Diagnostic: the achievable bf16 matrix-core rate of the device, against
+/* Diagnostic, not a step of any page's method: the achievable bf16
+ * matrix-core rate of the device, against
  * which the forward's throughput is read (next to the vendor's dense peak).
  * Enqueues `blocks` workgroups of 512 threads that each run `iters` loop
  * trips of 16 register-only v_mfma_f32_32x32x16_bf16 per wave (four
