@@ -338,10 +338,14 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
       sorted[rank] = tid;
     }
     __syncthreads();
-    // half the workers per round: a round hands one item to each of its
-    // least-loaded workers, so a worker already holding the range's longest
-    // items sits rounds out instead of taking one item every round
-    const int per_round = max(1, R / 2);
+    // A round hands one item to each of its least-loaded workers.  When the
+    // batch's items are uneven (its longest more than twice the median),
+    // rounds of half the workers let a worker already holding some of the
+    // longest sit rounds out instead of taking one item every round; when
+    // they are even, rounds of all the workers deal the same way in half
+    // the rounds.
+    const int c_max = s_cost[sorted[0]], c_mid = s_cost[sorted[nvalid / 2]];
+    const int per_round = c_max <= 2 * c_mid ? R : max(1, R / 2);
     for (int r0 = 0; r0 < nvalid; r0 += per_round) {
       const int k = min(per_round, nvalid - r0);
       int wr = R;
@@ -405,30 +409,32 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
   }
 }
 
-// one list of a split-mode item into its group's stream at `base`, item
-// word `word`; an empty list is one step with no tile
-__device__ void write_list(int2* steps, int64_t cap, int64_t base, uint64_t bits, int lane,
-                           int word) {
-  const int mine = __popcll(bits);
-  int pos = mine;  // inclusive scan over lanes, then exclusive
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(pos, o, kWave);
-    if (lane >= o) pos += t;
+// The tiles set in list A's bitmap (and, with B, in either list's) in
+// ascending order into the steps at `base`, item word `word`: 64 tiles at a
+// time, each lane testing one and a ballot giving its place, so the whole
+// wave stores at once.  With B each step carries the group flags (tile |
+// group 0 needs it << 30 | group 1 needs it << 29).  An empty result is one
+// step with no tile.
+__device__ void write_tiles(int2* steps, int64_t cap, int64_t base, const uint32_t* bma,
+                            const uint32_t* bmb, int tiles, int lane, int word) {
+  int n = 0;
+  for (int c0 = 0; c0 < tiles; c0 += kWave) {
+    const int t = c0 + lane;
+    uint32_t fa = 0, fb = 0;
+    if (t < tiles) {
+      fa = (bma[t >> 5] >> (t & 31)) & 1u;
+      if (bmb != nullptr) fb = (bmb[t >> 5] >> (t & 31)) & 1u;
+    }
+    const bool on = (fa | fb) != 0u;
+    const uint64_t m = __ballot(on);
+    if (on) {
+      const int64_t at = base + n + __popcll(m & ((1ull << lane) - 1ull));
+      const int e = bmb != nullptr ? (t | (int)(fa << 30) | (int)(fb << 29)) : t;
+      if (at < cap) steps[at] = make_int2(e, word);
+    }
+    n += __popcll(m);
   }
-  const int n = __shfl(pos, kWave - 1, kWave);
-  pos -= mine;
-  if (n == 0) {
-    if (lane == 0 && base < cap) steps[base] = make_int2(kBadTile, word);
-    return;
-  }
-  uint64_t m = bits;
-  while (m) {
-    const int b = __builtin_ctzll(m);
-    m &= m - 1;
-    const int64_t at = base + pos;
-    if (at < cap) steps[at] = make_int2(64 * lane + b, word);
-    ++pos;
-  }
+  if (n == 0 && lane == 0 && base < cap) steps[base] = make_int2(kBadTile, word);
 }
 
 // ---- 3. per item: the worker's item list and the item's steps
@@ -500,41 +506,18 @@ __global__ void __launch_bounds__(256) plan_steps_kernel(PlanArgs a) {
     int n0, n1;
     lists_to_bitmaps(a, use, s, p, bms[wv], lane, n0, n1);
     if (!use) continue;  // (no barrier below)
-    uint64_t wa, wb;
-    lane_words(bms[wv], lane, wa, wb);
     const int64_t b = wbase[w];
     if (ic.split) {
       const int64_t ba = b + wc[3 * w] + offa;                   // group 0's stream
       const int64_t bb = b + wc[3 * w] + wc[3 * w + 1] + offb;   // group 1's stream
       const int wda = (int)((bh << kPlanTileBits) | (2 * p));
-      write_list(steps, L.step_cap, orient ? bb : ba, wa, lane, wda);
-      if (2 * p + 1 < L.tiles) write_list(steps, L.step_cap, orient ? ba : bb, wb, lane, wda + 1);
+      write_tiles(steps, L.step_cap, orient ? bb : ba, bms[wv], nullptr, L.tiles, lane, wda);
+      if (2 * p + 1 < L.tiles)
+        write_tiles(steps, L.step_cap, orient ? ba : bb, bms[wv] + kWords, nullptr, L.tiles,
+                    lane, wda + 1);
       continue;
     }
-    const uint64_t un = wa | wb;
-    const int mine = __popcll(un);
-    int pos = mine;  // inclusive scan over lanes, then exclusive
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int t = __shfl_up(pos, o, kWave);
-      if (lane >= o) pos += t;
-    }
-    const int u = __shfl(pos, kWave - 1, kWave);
-    pos -= mine;
-    const int64_t base = b + offa;
-    if (u == 0) {
-      if (lane == 0 && base < L.step_cap) steps[base] = make_int2(kBadTile, word);
-      continue;
-    }
-    uint64_t m = un;
-    while (m) {
-      const int bt = __builtin_ctzll(m);
-      m &= m - 1;
-      const int t = 64 * lane + bt;
-      const int e = t | (int)(((wa >> bt) & 1) << 30) | (int)(((wb >> bt) & 1) << 29);
-      const int64_t at = base + pos;
-      if (at < L.step_cap) steps[at] = make_int2(e, word);
-      ++pos;
-    }
+    write_tiles(steps, L.step_cap, b + offa, bms[wv], bms[wv] + kWords, L.tiles, lane, word);
   }
 }
 
