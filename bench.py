@@ -4,9 +4,10 @@ One step = one pass of the whole path over one synthetic batch at the
 32 760-token video shape (B=1, H=12, d=128, 21 frames of 30x52 latents, bf16,
 128x128 tiles): build the window(+-1 frame) + 2 rotating-anchor mask for
 rotation r = (layer + step) mod 21 (layer 0), compact it into active-tile
-lists, run the fused forward (--planned 1: build the forward's work plan
-from the lists every step and run the forward through it).  Inputs are
-resident in HBM before timing.  SQuad's passes (two key tiles per query
+lists, build the forward's work plan from the lists (the mask changes every
+step, so the plan is rebuilt every step) and run the fused forward through
+it (--planned 0: bsattn_fwd, one workgroup per query-tile pair, no plan).
+Inputs are resident in HBM before timing.  SQuad's passes (two key tiles per query
 tile, where the per-workgroup set-up of bsattn_fwd dominates) run through
 work plans built once; elsewhere both forwards are reported, timed
 interleaved call by call.
@@ -685,7 +686,7 @@ def main():
                     help="timed calls of the SQuad two-pass leg (0 = skip)")
     ap.add_argument("--repetition", type=int, default=5,
                     help="timed calls of the spatial-repetition leg (0 = skip)")
-    ap.add_argument("--planned", type=int, default=0,
+    ap.add_argument("--planned", type=int, default=1,
                     help="headline step: forward through a work plan rebuilt every "
                          "step (bsattn_fwd_plan + bsattn_fwd_planned); 0 = bsattn_fwd")
     ap.add_argument("--other-calls", type=int, default=10,
