@@ -271,26 +271,35 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
       }
     }
   }
-  part[tid] = sum;
-  __syncthreads();
-  for (int o = 1; o < kAssignThreads; o <<= 1) {
-    const int64_t t = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += t;
-    __syncthreads();
+  // prefix of the chunk sums over the threads: within each wave by
+  // shuffles, then across the four waves
+  const int lane = tid & (kWave - 1), wv = tid / kWave;
+  int64_t incl = sum;
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int64_t t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
   }
-  const int64_t total = part[kAssignThreads - 1];
-  int64_t run = part[tid] - sum;
+  if (lane == kWave - 1) part[wv] = incl;
+  __syncthreads();
+  int64_t total = 0, before = 0;
+  for (int w2 = 0; w2 < kAssignThreads / kWave; ++w2) {
+    const int64_t t = part[w2];
+    before += w2 < wv ? t : 0;
+    total += t;
+  }
+  int64_t run = before + incl - sum;
+  // item i lies on XCD floor(A / B), A = 8 (2 prefix(i) + cost(i)),
+  // B = 2 total (clamped to 7): below x when A < x B, at most x when
+  // A < (x + 1) B or x = 7
   int below = 0, upto = 0;  // items of this chunk on XCDs < x, <= x
   {
+    const int64_t B2 = 2 * total;
     int p = p0, h = h0;
     for (int i = c0; i < c1; ++i) {
       const int c = tab.get(a, L.mask_heads == 1 ? 0 : h, p).cost;
-      const int64_t xi = total > 0 ? min((int64_t)kPlanXcds - 1,
-                                         (kPlanXcds * (2 * run + c)) / (2 * total))
-                                   : 0;
-      below += xi < x ? 1 : 0;
-      upto += xi <= x ? 1 : 0;
+      const int64_t A = (int64_t)kPlanXcds * (2 * run + c);
+      below += (total > 0 ? A < (int64_t)x * B2 : x > 0) ? 1 : 0;
+      upto += (total <= 0 || x == kPlanXcds - 1 || A < (int64_t)(x + 1) * B2) ? 1 : 0;
       run += c;
       if (++p == L.pairs) {
         p = 0;
@@ -298,14 +307,15 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
       }
     }
   }
+  // the counts summed over the workgroup: within each wave, then across
+  int64_t bu = ((int64_t)below << 32) | (uint32_t)upto;
+  for (int o = kWave / 2; o > 0; o >>= 1) bu += __shfl_xor(bu, o, kWave);
+  __syncthreads();  // every wave has read part[] above
+  if (lane == 0) part[wv] = bu;
   __syncthreads();
-  part[tid] = ((int64_t)below << 32) | (uint32_t)upto;
-  __syncthreads();
-  for (int o = kAssignThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) part[tid] += part[tid + o];
-    __syncthreads();
-  }
-  const int lo = (int)(part[0] >> 32), hi = (int)(part[0] & 0xFFFFFFFF);
+  bu = 0;
+  for (int w2 = 0; w2 < kAssignThreads / kWave; ++w2) bu += part[w2];
+  const int lo = (int)(bu >> 32), hi = (int)(bu & 0xFFFFFFFF);
   // worker j's key: its load * 512 + j, so one comparison orders by load
   // and then by index; slots past R hold 2^62 and never come first (loads
   // stay far below 2^53)
@@ -356,9 +366,14 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
         // reads issue back to back with no compare per slot
         mine = s_load[tid];
         wr = 0;
+        if (R <= 32) {
 #pragma unroll
-        for (int j2 = 0; j2 < kPlanMaxWorkersPerXcd; ++j2)
-          wr += (int)((uint64_t)(s_load[j2] - mine) >> 63);
+          for (int j2 = 0; j2 < 32; ++j2) wr += (int)((uint64_t)(s_load[j2] - mine) >> 63);
+        } else {
+#pragma unroll
+          for (int j2 = 0; j2 < kPlanMaxWorkersPerXcd; ++j2)
+            wr += (int)((uint64_t)(s_load[j2] - mine) >> 63);
+        }
       }
       __syncthreads();
       if (tid < R && wr < k) {
