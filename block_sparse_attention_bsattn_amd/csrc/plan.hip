@@ -27,9 +27,12 @@
 //              256 items at a time (a whole range at most shapes) are ranked
 //              by cost, longest first, and dealt in rounds of half the
 //              XCD's workers, the longest of a round to the least-loaded
-//              worker.  Records each item's worker, its place in the
-//              worker's order and the offset of its steps in the worker's
-//              pair-mode stream.
+//              worker.  Ranges of up to 1024 items are then refined: in
+//              rounds, the k-th most loaded worker and the k-th least loaded
+//              exchange the item (or pair of items) that best evens them
+//              out, and each worker runs its items in item order.  Records
+//              each item's worker, its place in the worker's order and the
+//              offsets of its steps in the worker's streams.
 //   3. steps:  one wave per item: the worker's item list; for a pair-mode
 //              item its union list in ascending key-tile order, one step per
 //              tile, (tile | group 0 needs it << 30 | group 1 needs it << 29,
@@ -221,6 +224,11 @@ constexpr int kAssignThreads = 256;
 // few hundred lumpy items (lists of 12 to 180 tiles in one calibrated mask)
 // need the whole range at once
 constexpr int kBatch = kAssignThreads;
+// XCD ranges of at most this many items are refined after the deal (below)
+constexpr int kRefineItems = 1024;
+constexpr int kRefineWords = kRefineItems / 32;
+constexpr int kRefineRounds = 8;
+constexpr int kListCap = 32;  // items per worker the refinement searches
 
 __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a) {
   __shared__ int64_t part[kAssignThreads];
@@ -232,6 +240,16 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
   __shared__ __attribute__((aligned(16))) int s_it[kBatch][4];
   __shared__ __attribute__((aligned(16))) int64_t s_load[kPlanMaxWorkersPerXcd];
   __shared__ int t_cost[kLdsPairs], t_steps[kLdsPairs];
+  // refinement: each item's cost and steps, each worker's items as a bitmap
+  // (for the records) and as a list (for the search), the workers by load,
+  // whether a round moved anything, and whether a list overflowed
+  __shared__ int s_ic[kRefineItems], s_ist[kRefineItems];
+  __shared__ uint32_t s_wbm[kPlanMaxWorkersPerXcd][kRefineWords];
+  __shared__ int16_t s_list[kPlanMaxWorkersPerXcd][kListCap];
+  __shared__ __attribute__((aligned(16))) int s_lc[kPlanMaxWorkersPerXcd][kListCap];
+  __shared__ int s_lcnt[kPlanMaxWorkersPerXcd];
+  __shared__ int s_order[kPlanMaxWorkersPerXcd];
+  __shared__ int s_lover;
   const int tid = threadIdx.x;
   const int x = blockIdx.x;  // XCD
   const PlanLayout& L = a.L;
@@ -324,6 +342,15 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
   // deal [lo, hi) over the R workers, kBatch items at a time; thread j < R
   // keeps worker j's item count and the lengths of its three streams (its
   // load in LDS)
+  // Ranges of at most kRefineItems items keep only each item's worker in
+  // the deal; the refinement below then evens the workers out and writes
+  // the records.
+  const bool refine = hi - lo <= kRefineItems && R >= 2;
+  if (refine) {
+    for (int k = tid; k < kPlanMaxWorkersPerXcd * kRefineWords; k += kAssignThreads)
+      s_wbm[k / kRefineWords][k % kRefineWords] = 0u;
+    if (tid == 0) s_lover = 0;
+  }
   int cnt = 0, nsteps = 0, na = 0, nb = 0;
   for (int b0 = lo; b0 < hi; b0 += kBatch) {
     const int nvalid = min(kBatch, hi - b0);
@@ -334,6 +361,10 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
       key = ((uint32_t)min(ic.cost, (1 << 23) - 1) << 8 | (uint32_t)(kBatch - 1 - tid)) + 1;
       s_cost[tid] = ic.cost;
       s_steps[tid] = (ic.split ? ic.sa | (ic.sb << 15) : ic.steps) | (ic.split << 30);
+      if (refine) {
+        s_ic[b0 - lo + tid] = ic.cost;
+        s_ist[b0 - lo + tid] = s_steps[tid];
+      }
     }
     keys[tid] = key;
     __syncthreads();
@@ -355,7 +386,41 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
     // they are even, rounds of all the workers deal the same way in half
     // the rounds.
     const int c_max = s_cost[sorted[0]], c_mid = s_cost[sorted[nvalid / 2]];
-    const int per_round = c_max <= 2 * c_mid ? R : max(1, R / 2);
+    const bool even = c_max <= 2 * c_mid;
+    // an item of the refined path: its worker's bitmap bit, list entry and
+    // cost (list overflow switches the refinement off)
+    auto note = [&](int src, int n) {
+      const int j = b0 - lo + src;
+      s_wbm[tid][j >> 5] |= 1u << (j & 31);
+      if (n < kListCap) {
+        s_list[tid][n] = (int16_t)j;
+        s_lc[tid][n] = s_cost[src];
+      } else {
+        s_lover = 1;
+      }
+    };
+    if (refine && even) {
+      // Even batches of a refined range are dealt in a snake, with no
+      // ranking of the workers: rank r goes to worker r mod R on even
+      // sweeps and R - 1 - (r mod R) on odd ones (the refinement evens out
+      // what is left).
+      if (tid < R) {
+        int64_t ld = s_load[tid];
+        bool odd = false;
+        for (int r0 = 0; r0 < nvalid; r0 += R, odd = !odd) {
+          const int r = r0 + (odd ? R - 1 - tid : tid);
+          if (r < nvalid) {
+            const int src = sorted[r];
+            note(src, cnt);
+            ld += (int64_t)s_cost[src] << 9;
+            cnt += 1;
+          }
+        }
+        s_load[tid] = ld;
+      }
+      __syncthreads();
+    } else {
+    const int per_round = even ? R : max(1, R / 2);
     for (int r0 = 0; r0 < nvalid; r0 += per_round) {
       const int k = min(per_round, nvalid - r0);
       int wr = R;
@@ -384,7 +449,9 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
         it[0] = x + kPlanXcds * tid;
         it[1] = cnt;
         s_load[tid] = mine + ((int64_t)s_cost[src] << 9);
-        if (split) {
+        if (refine) {
+          note(src, cnt);
+        } else if (split) {
           // the two tiles go to the two groups' streams, the longer list to
           // the shorter stream (orient 1: tile 2p + 1 to group 0's)
           const int sa = st & 0x7FFF, sb = (st >> 15) & 0x7FFF;
@@ -402,9 +469,142 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
       }
       __syncthreads();
     }
-    for (int i = tid; i < nvalid; i += kAssignThreads)
-      *reinterpret_cast<int4*>(P32(a, L.off_itmp) + 4 * (int64_t)(b0 + i)) =
-          *reinterpret_cast<const int4*>(s_it[i]);
+    }
+    if (!refine)
+      for (int i = tid; i < nvalid; i += kAssignThreads)
+        *reinterpret_cast<int4*>(P32(a, L.off_itmp) + 4 * (int64_t)(b0 + i)) =
+            *reinterpret_cast<const int4*>(s_it[i]);
+  }
+  if (refine) {
+    // With a few items per worker the deal leaves some workers an item more
+    // than others (a range of 194 items on 32 workers: two hold seven), up
+    // to 8 % above the mean load.  Each round ranks the workers by load and
+    // pairs the k-th least loaded with the k-th most loaded; every pair
+    // makes its best single move (an item of the heavier to the lighter)
+    // or swap (an item each way), the one that brings their difference d
+    // closest to zero, if it lowers the heavier's load.  Both new loads lie
+    // between the old two, so no worker ever exceeds the old maximum.
+    // Sixteen lanes search a pair, each taking every sixteenth word of the
+    // heavier worker's bitmap; pairs are disjoint, so they move at once.
+    const int nwd = (hi - lo + 31) >> 5;
+    if (tid < R) s_lcnt[tid] = cnt;
+    // (also when the range is empty and the deal passed no barrier: every
+    // thread must read the same s_lover)
+    __syncthreads();
+    const int rounds = s_lover ? 0 : kRefineRounds;
+    int64_t prev_max = INT64_MAX;
+    for (int round = 0; round < rounds; ++round) {
+      if (tid < R) {
+        const int64_t mine = s_load[tid];
+        int wr = 0;
+        if (R <= 32) {
+#pragma unroll
+          for (int j2 = 0; j2 < 32; ++j2) wr += (int)((uint64_t)(s_load[j2] - mine) >> 63);
+        } else {
+#pragma unroll
+          for (int j2 = 0; j2 < kPlanMaxWorkersPerXcd; ++j2)
+            wr += (int)((uint64_t)(s_load[j2] - mine) >> 63);
+        }
+        s_order[wr] = tid;
+      }
+      __syncthreads();
+      // stop once a round has not lowered the heaviest load
+      const int64_t cur_max = s_load[s_order[R - 1]] >> 9;
+      if (cur_max >= prev_max) break;
+      prev_max = cur_max;
+      const int grp16 = tid >> 4, gl = tid & 15;
+      for (int k = grp16; k < R / 2; k += kAssignThreads / 16) {
+        const int lw = s_order[k], hw = s_order[R - 1 - k];
+        const int gap = (int)min((s_load[hw] >> 9) - (s_load[lw] >> 9), (int64_t)(1 << 24));
+        const int nh = s_lcnt[hw], nl = s_lcnt[lw];
+        // Lane gl tries the items at positions gl, gl + 16 of the heavier
+        // list against every item of the lighter one and against none (a
+        // move, while the lighter list has room); a candidate with
+        // difference d, 0 < d < gap, scores |gap - 2 d|.  Key: score << 12 |
+        // position of a << 6 | position of b (nl: a move).
+        int64_t best = INT64_MAX;
+        if (gap > 0) {
+          const int nb1 = nl < kListCap ? nl + 1 : nl;
+          for (int ai = gl; ai < nh; ai += 16) {
+            const int ca = s_lc[hw][ai];
+            int bl = INT32_MAX;  // score << 6 | b
+            for (int b4 = 0; b4 < nb1; b4 += 4) {
+              const int4 c4 = *reinterpret_cast<const int4*>(&s_lc[lw][b4]);
+              const int cb[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int bi = b4 + e;
+                const int d = ca - (bi < nl ? cb[e] : 0);
+                const int v = abs(gap - 2 * d);
+                if (bi < nb1 && d > 0 && d < gap) bl = min(bl, (v << 6) | bi);
+              }
+            }
+            if (bl != INT32_MAX)
+              best = min(best, ((int64_t)(bl >> 6) << 12) | (ai << 6) | (bl & 63));
+          }
+        }
+        for (int o = 8; o > 0; o >>= 1) best = min(best, (int64_t)__shfl_xor(best, o, 16));
+        if (gl == 0 && best != INT64_MAX) {
+          const int ai = (int)((best >> 6) & 63), bi = (int)(best & 63);
+          const int ia = s_list[hw][ai];
+          int64_t d = s_lc[hw][ai];
+          s_wbm[hw][ia >> 5] &= ~(1u << (ia & 31));
+          s_wbm[lw][ia >> 5] |= 1u << (ia & 31);
+          if (bi < nl) {
+            const int ib = s_list[lw][bi];
+            const int cb = s_lc[lw][bi];
+            d -= cb;
+            s_wbm[lw][ib >> 5] &= ~(1u << (ib & 31));
+            s_wbm[hw][ib >> 5] |= 1u << (ib & 31);
+            s_lc[lw][bi] = s_lc[hw][ai];
+            s_list[lw][bi] = (int16_t)ia;
+            s_list[hw][ai] = (int16_t)ib;
+            s_lc[hw][ai] = cb;
+          } else {
+            s_list[lw][nl] = (int16_t)ia;
+            s_lc[lw][nl] = s_lc[hw][ai];
+            s_lcnt[lw] = nl + 1;
+            s_list[hw][ai] = s_list[hw][nh - 1];
+            s_lc[hw][ai] = s_lc[hw][nh - 1];
+            s_lcnt[hw] = nh - 1;
+          }
+          s_load[hw] -= d << 9;
+          s_load[lw] += d << 9;
+        }
+      }
+      __syncthreads();
+    }
+    // each worker's records, its items in item order: its place, and the
+    // offsets of its steps in its three streams
+    cnt = nsteps = na = nb = 0;
+    if (tid < R) {
+      for (int wd = 0; wd < nwd; ++wd) {
+        uint32_t bits = s_wbm[tid][wd];
+        while (bits != 0u) {
+          const int j = 32 * wd + __ffs(bits) - 1;
+          bits &= bits - 1u;
+          const int st = s_ist[j];
+          int4 rec;
+          rec.x = x + kPlanXcds * tid;
+          rec.y = cnt;
+          if (st >> 30) {
+            // the longer list to the shorter stream, as in the deal
+            const int sa = st & 0x7FFF, sb = (st >> 15) & 0x7FFF;
+            const int orient = max(na + sb, nb + sa) < max(na + sa, nb + sb) ? 1 : 0;
+            rec.z = na;
+            rec.w = nb | (orient << 30);
+            na += orient ? sb : sa;
+            nb += orient ? sa : sb;
+          } else {
+            rec.z = nsteps;
+            rec.w = 0;
+            nsteps += st & 0x3FFFFFFF;
+          }
+          *reinterpret_cast<int4*>(P32(a, L.off_itmp) + 4 * (int64_t)(lo + j)) = rec;
+          cnt += 1;
+        }
+      }
+    }
   }
   // worker j's items take witems[lo + (items of workers < j), ...)
   if (tid < kWave) {

@@ -299,19 +299,22 @@ def test_uneven_per_head_masks(N, H, B, seed):
     assert_bitwise(f"uneven heads N={N}", o_p, l_p, o, lse)
 
 
-@pytest.mark.parametrize("cfg,rotation", [(2, 0), (2, 5), (3, 0), (4, 0), (5, 0),
-                                          ("expanded", 2)])
-def test_full_size_plan_and_bitwise(cfg, rotation):
+@pytest.mark.parametrize("cfg,rotation,workers", [
+    (2, 0, 0), (2, 5, 0), (3, 0, 0), (4, 0, 0), (5, 0, 0), ("expanded", 2, 0),
+    # two workers per XCD (each holds about 96 items, too many for the
+    # refinement's lists: the deal stands as dealt), six and eight per XCD
+    (2, 10, 16), (3, 0, 48), (2, 0, 64)])
+def test_full_size_plan_and_bitwise(cfg, rotation, workers):
     """Every full-size workload in the launch configuration the bench
-    times: the plan against the CSR, and the planned forward bitwise equal
-    to bsattn_fwd."""
+    times (and a few other worker counts): the plan against the CSR, and
+    the planned forward bitwise equal to bsattn_fwd."""
     w = (W.EXPANDED if cfg == "expanded" else W.WORKLOADS[cfg]).with_rotation(rotation)
     mask, rp, ci = gpu_mask_csr(w)
     q, k, v = W.make_qkv(w, device="cuda")
     Hm = w.mask.mask_heads
-    plan, o_p, l_p, o, lse = run_both(q, k, v, rp, ci, Hm)
+    plan, o_p, l_p, o, lse = run_both(q, k, v, rp, ci, Hm, workers)
     check_plan(plan, rp, ci, w.B, w.H, w.N, Hm)
-    assert_bitwise(f"{w.name} r{rotation}", o_p, l_p, o, lse)
+    assert_bitwise(f"{w.name} r{rotation} workers={workers}", o_p, l_p, o, lse)
 
 
 @pytest.mark.timeout(900)
@@ -382,21 +385,11 @@ def _lumpy_masks(H, T, seed):
     return m
 
 
-def test_plan_deals_lumpy_lists_evenly():
-    """A few very long items among many short ones: the deal must leave no
-    worker far above the mean load, counted with the plan's own cost
-    estimate (pair mode 5 (union + 1), split mode 4 (n0 + n1) + 5).  Dealing
-    one item to every worker in each round left the worst worker at about
-    1.6x the mean here; rounds of half the workers, after ranking a whole
-    XCD range, about 1.04x."""
-    H, T = 12, 256
-    N = T * 128
-    m = _lumpy_masks(H, T, 11)
-    rp, ci = bs.make_csr(torch.from_numpy(m).cuda())
-    plan = bs.make_plan(rp, ci, 1, H, N, 128, H)
-    torch.cuda.synchronize()
-    P, _ = check_plan(plan, rp, ci, 1, H, N, H)
-    exp, pairs, tiles = expected_items(rp.cpu().numpy(), ci.cpu().numpy(), 1, H, N, H)
+def _worker_loads(plan, rp, ci, B, H, N, Hm):
+    """Each worker's load by the plan's own cost estimate (pair mode
+    5 (union + 1), split mode 4 (n0 + n1) + 5), from its item list."""
+    P, _ = check_plan(plan, rp, ci, B, H, N, Hm)
+    exp, pairs, tiles = expected_items(rp.cpu().numpy(), ci.cpu().numpy(), B, H, N, Hm)
     load = np.zeros(P["workers"], dtype=np.int64)
     for w in range(P["workers"]):
         first, cnt = P["witem"][w]
@@ -409,9 +402,40 @@ def test_plan_deals_lumpy_lists_evenly():
                 load[w] += 4 * (max(len(la), 1) + sb) + 5
             else:
                 load[w] += 5 * (max(len(union), 1) + 1)
+    return load
+
+
+def test_plan_deals_lumpy_lists_evenly():
+    """A few very long items among many short ones: the deal must leave no
+    worker far above the mean load.  Dealing one item to every worker in
+    each round left the worst worker at about 1.6x the mean here; rounds of
+    half the workers, after ranking a whole XCD range, about 1.04x."""
+    H, T = 12, 256
+    N = T * 128
+    m = _lumpy_masks(H, T, 11)
+    rp, ci = bs.make_csr(torch.from_numpy(m).cuda())
+    plan = bs.make_plan(rp, ci, 1, H, N, 128, H)
+    torch.cuda.synchronize()
+    load = _worker_loads(plan, rp, ci, 1, H, N, H)
     ratio = float(load.max() / load.mean())
     print(f"lumpy lists: worst worker {ratio:.3f}x the mean load", flush=True)
     assert ratio < 1.15
+
+
+@pytest.mark.parametrize("rotation", [0, 10])
+def test_plan_evens_out_the_window_mask(rotation):
+    """The 32 760-token window mask has about six pairs per worker and XCD
+    ranges of 190 or 194 of them, so the deal alone leaves two workers of
+    an XCD holding seven (about 1.08x the mean load); the refinement after
+    it brings the worst worker to within 3 % of the mean."""
+    w = W.WORKLOADS[2].with_rotation(rotation)
+    mask, rp, ci = gpu_mask_csr(w)
+    plan = bs.make_plan(rp, ci, w.B, w.H, w.N, 128, w.mask.mask_heads)
+    torch.cuda.synchronize()
+    load = _worker_loads(plan, rp, ci, w.B, w.H, w.N, w.mask.mask_heads)
+    ratio = float(load.max() / load.mean())
+    print(f"window mask r{rotation}: worst worker {ratio:.3f}x the mean load", flush=True)
+    assert ratio < 1.03
 
 
 def test_plan_for_other_sizes_writes_nothing():
