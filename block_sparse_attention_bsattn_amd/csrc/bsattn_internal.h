@@ -26,6 +26,7 @@ struct PlanLayout {
   int32_t B, H, N, tiles, mask_heads, workers, pairs;
   int64_t items;      // B * H * pairs
   int64_t step_cap;   // capacity of the step array (8-byte entries)
+  int64_t off_xw;     // int32 [8]: the XCD weights the ranges were cut by (byte 64)
   int64_t off_wstep;  // int32 [4 * workers]: each worker's pair stream, group 0's and
                       // group 1's single-tile streams: first step of each, then the end
   int64_t off_witem;  // int32 [2 * workers]: each worker's (first, count) in witems
@@ -39,6 +40,8 @@ struct PlanLayout {
   int64_t bytes;
 };
 constexpr int32_t kPlanMagic = 0x42535031;
+// XCD weights are in units of 1/4096 of the mean XCD speed
+constexpr int kPlanWeightOne = 4096;
 // header: magic, B, H, N, tiles, Hm, workers, pairs, then the section
 // offsets / 16 (wstep, witem, wcnt, witems, pinfo, itmp, steps) and the step
 // capacity (clamped to 2^31 - 1)
@@ -60,6 +63,10 @@ int device_compute_units();
 // hipError_t value, 0 = success).
 constexpr int64_t kNoAllocScratchBytes = (int64_t)96 << 20;
 int noalloc_scratch(char** ptr);
+// The current device's XCD feedback table: one (busy ticks, planned load)
+// pair of int32 per worker of the last planned forward on the device, written by
+// that forward and read by the next plan (a hipError_t value, 0 = success).
+int xcd_feedback(int32_t** ptr);
 
 struct FwdLaunch {
   int32_t B, H, N, d, tile, dtype;
@@ -78,6 +85,7 @@ struct FwdLaunch {
   // planned forward only (plan == nullptr otherwise)
   const char* plan;
   PlanLayout pl;
+  int32_t* xfb = nullptr;  // the device's XCD feedback table: int32 pairs (planned only)
 };
 
 // Each returns a hipError_t value (0 = success).

@@ -895,6 +895,14 @@ fwd_bf16_t128_d128(FwdLaunch a) {
     const int w2 = min(max(wstep[4 * wk + 2], w1), cap);
     const int w3 = min(max(wstep[4 * wk + 3], w2), cap);
     const int sb = w0, se = w1;
+    // For the XCD feedback table: the workgroup's start and the load its
+    // plan gave it (the plan's cost units: 5 per pair-mode step and per
+    // item, 4 per single-tile step), kept in VGPRs (scalar registers are
+    // scarce in the stream loop).
+    uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+    int fb_load = 5 * (w1 - w0) + 4 * (w3 - w1) +
+                  5 * max(((sconst_i32)(uintptr_t)(a.plan + a.pl.off_witem))[2 * wk + 1], 0);
+    asm volatile("" : "+v"(t_start), "+v"(fb_load));
     typedef const __attribute__((address_space(4))) uint64_t* sconst_u64;
     const sconst_u64 steps = (sconst_u64)(uintptr_t)(a.plan + a.pl.off_steps);
     // item word -> the head's first row, and this group's query tile
@@ -1100,6 +1108,13 @@ fwd_bf16_t128_d128(FwdLaunch a) {
         store_lse(cur_hr, cur_qt, m, l);
       }
     }
+    // XCD feedback: how long this workgroup ran and its load, read by the
+    // next plan on this device
+    if (tid == 0) {
+      const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+      reinterpret_cast<int2*>(a.xfb)[wk] =
+          make_int2((int)min(t_end - t_start, (uint64_t)0x7FFFFFFF), fb_load);
+    }
   }
 
   // ================= split-mode items =================
@@ -1241,10 +1256,13 @@ int launch_fwd_bf16_t128_d128(const FwdLaunch& a, void* stream) {
   if (a.plan != nullptr) {
     // one persistent workgroup per worker of the plan
     const dim3 grid((unsigned)a.pl.workers);
+    FwdLaunch b = a;
+    const int fe = xcd_feedback(&b.xfb);
+    if (fe != hipSuccess) return fe;
     if (a.window > 0)
-      hipLaunchKernelGGL((fwd_bf16_t128_d128<true, true>), grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL((fwd_bf16_t128_d128<true, true>), grid, dim3(512), 0, s, b);
     else
-      hipLaunchKernelGGL((fwd_bf16_t128_d128<false, true>), grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL((fwd_bf16_t128_d128<false, true>), grid, dim3(512), 0, s, b);
     return hipGetLastError();
   }
   // one workgroup per (batch*head, query-tile pair), in either mode

@@ -62,6 +62,7 @@ struct PlanArgs {
   const int32_t* col_idx;
   int64_t col_cap;
   char* plan;
+  const int32_t* xfb;  // the device's XCD feedback table (int32 pairs)
 };
 
 __device__ __forceinline__ int32_t* P32(const PlanArgs& a, int64_t off) {
@@ -118,6 +119,61 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
+// The XCDs of one GPU run at different speeds (up to a tenth apart, in the
+// same order whatever the work), and a launch lasts as long as its slowest
+// XCD.  Every planned forward leaves, per worker, how long its workgroup
+// ran (s_memrealtime ticks) and the load the plan gave it (the cost units
+// of item_cost_sp); worker w ran on XCD w mod 8.  Each XCD's speed is its
+// summed load over its summed time, and the XCD ranges of the next plan
+// are cut in proportion to the speeds, relative to their mean and clamped
+// to [0.8, 1.25].  With no usable record (no planned forward yet on this
+// device, or one too short to time: under 100 us summed over an XCD's
+// workers) every weight is 1.  The weights go
+// into the plan, so that the eight workgroups of the assign kernel cut by
+// the same ones even while another launch writes the table.  Workers with
+// no load are left out.  Run by one workgroup of 256 threads.
+__device__ void xcd_weights(const PlanArgs& a) {
+  __shared__ int64_t xs[4][2 * kPlanXcds];
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  int64_t ld = 0, bz = 0;  // this thread's workers: tid, tid + 256 (XCD tid % 8)
+  for (int w = tid; w < a.L.workers; w += 256) {
+    const int2 r = reinterpret_cast<const int2*>(a.xfb)[w];
+    if (r.x > 0 && r.y > 0) {
+      bz += r.x;
+      ld += r.y;
+    }
+  }
+  // lanes l, l + 8, ..., l + 56 share an XCD
+  for (int o = 8; o < kWave; o <<= 1) {
+    ld += __shfl_xor(ld, o, kWave);
+    bz += __shfl_xor(bz, o, kWave);
+  }
+  if (lane < kPlanXcds) {
+    xs[wv][lane] = ld;
+    xs[wv][kPlanXcds + lane] = bz;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double sp[kPlanXcds], mean = 0.0;
+    bool ok = true;
+    for (int x = 0; x < kPlanXcds; ++x) {
+      const int64_t l = xs[0][x] + xs[1][x] + xs[2][x] + xs[3][x];
+      const int64_t b = xs[0][kPlanXcds + x] + xs[1][kPlanXcds + x] + xs[2][kPlanXcds + x] +
+                        xs[3][kPlanXcds + x];
+      // at least 100 us of summed busy time (100 MHz ticks)
+      ok = ok && l > 0 && b >= 10000;
+      sp[x] = ok ? (double)l / (double)b : 0.0;
+      mean += sp[x];
+    }
+    mean /= kPlanXcds;
+    int32_t* xw = P32(a, a.L.off_xw);
+    for (int x = 0; x < kPlanXcds; ++x) {
+      const double r = ok && mean > 0.0 ? fmin(fmax(sp[x] / mean, 0.8), 1.25) : 1.0;
+      xw[x] = (int32_t)(r * kPlanWeightOne + 0.5);
+    }
+  }
+}
+
 // ---- 1. per (mask slice, pair): union and common tile counts
 __global__ void __launch_bounds__(256) plan_pairs_kernel(PlanArgs a) {
   __shared__ uint32_t bms[4][2 * kWords];
@@ -146,6 +202,7 @@ __global__ void __launch_bounds__(256) plan_pairs_kernel(PlanArgs a) {
     h[14] = (int32_t)(L.off_steps / 16);
     h[15] = (int32_t)min(L.step_cap, (int64_t)0x7FFFFFFF);
   }
+  if (blockIdx.x == 0) xcd_weights(a);
   const bool use = sp < (int64_t)L.mask_heads * L.pairs;
   const int s = use ? (int)(sp / L.pairs) : 0, p = use ? (int)(sp % L.pairs) : 0;
   int n0, n1;
@@ -306,18 +363,30 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
     total += t;
   }
   int64_t run = before + incl - sum;
-  // item i lies on XCD floor(A / B), A = 8 (2 prefix(i) + cost(i)),
-  // B = 2 total (clamped to 7): below x when A < x B, at most x when
-  // A < (x + 1) B or x = 7
+  // XCD x takes the items whose cost midpoint falls in its share of the
+  // total, shares in proportion to the weights wt (XCD speeds, from the
+  // pairs kernel): item i lies below x when A < B C(x), A = (2 prefix(i) +
+  // cost(i)) C(8), B = 2 total, C(x) = wt(0) + ... + wt(x - 1); at most x
+  // when A < B C(x + 1) or x = 7
+  int64_t cw_lo = 0, cw_hi = 0, cw_all = 0;
+  {
+    const int32_t* xw = P32(a, L.off_xw);
+    for (int x2 = 0; x2 < kPlanXcds; ++x2) {
+      const int64_t wt = min(max(xw[x2], 1), 4 * kPlanWeightOne);
+      cw_lo += x2 < x ? wt : 0;
+      cw_hi += x2 <= x ? wt : 0;
+      cw_all += wt;
+    }
+  }
   int below = 0, upto = 0;  // items of this chunk on XCDs < x, <= x
   {
     const int64_t B2 = 2 * total;
     int p = p0, h = h0;
     for (int i = c0; i < c1; ++i) {
       const int c = tab.get(a, L.mask_heads == 1 ? 0 : h, p).cost;
-      const int64_t A = (int64_t)kPlanXcds * (2 * run + c);
-      below += (total > 0 ? A < (int64_t)x * B2 : x > 0) ? 1 : 0;
-      upto += (total <= 0 || x == kPlanXcds - 1 || A < (int64_t)(x + 1) * B2) ? 1 : 0;
+      const int64_t A = cw_all * (2 * run + c);
+      below += (total > 0 ? A < cw_lo * B2 : x > 0) ? 1 : 0;
+      upto += (total <= 0 || x == kPlanXcds - 1 || A < cw_hi * B2) ? 1 : 0;
       run += c;
       if (++p == L.pairs) {
         p = 0;
@@ -762,6 +831,8 @@ PlanLayout plan_layout(int32_t B, int32_t H, int32_t N, int32_t tile, int32_t ma
   L.step_cap = by_lists < by_tiles ? by_lists : by_tiles;
   auto up16 = [](int64_t v) { return (v + 15) & ~(int64_t)15; };
   int64_t off = up16(kPlanHeaderInts * 4);
+  L.off_xw = off;
+  off = up16(off + 4 * kPlanXcds);
   L.off_wstep = off;
   off = up16(off + 16 * (int64_t)workers);
   L.off_witem = off;
@@ -787,6 +858,10 @@ PlanLayout plan_layout(int32_t B, int32_t H, int32_t N, int32_t tile, int32_t ma
 // device with that device current, on the first call there.
 static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
 
+// The XCD feedback table (one per GPU, zero until a planned forward runs):
+// (busy ticks, planned load) per worker.
+static __device__ __align__(16) int2 xcd_table[kPlanXcds * kPlanMaxWorkersPerXcd];
+
 namespace {
 constexpr int kMaxDevices = 64;
 std::once_flag g_scratch_once[kMaxDevices];
@@ -809,6 +884,27 @@ int noalloc_scratch(char** ptr) {
   return hipSuccess;
 }
 
+namespace {
+std::once_flag g_xfb_once[kMaxDevices];
+int32_t* g_xfb_ptr[kMaxDevices];
+hipError_t g_xfb_err[kMaxDevices];
+}  // namespace
+
+int xcd_feedback(int32_t** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_xfb_once[dev], [dev]() {
+    void* p = nullptr;
+    g_xfb_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(xcd_table));
+    g_xfb_ptr[dev] = static_cast<int32_t*>(p);
+  });
+  if (g_xfb_err[dev] != hipSuccess) return g_xfb_err[dev];
+  *ptr = g_xfb_ptr[dev];
+  return hipSuccess;
+}
+
 int device_compute_units() {
   int dev = 0, cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -826,6 +922,10 @@ int launch_fwd_plan(const PlanLayout& L, const int32_t* row_ptr, const int32_t* 
   a.col_idx = col_idx;
   a.col_cap = col_cap;
   a.plan = plan;
+  int32_t* xfb = nullptr;
+  const int fe = xcd_feedback(&xfb);
+  if (fe != hipSuccess) return fe;
+  a.xfb = xfb;
   const int64_t sp = (int64_t)L.mask_heads * L.pairs;
   hipLaunchKernelGGL(plan_pairs_kernel, dim3((unsigned)((sp + 3) / 4 > 0 ? (sp + 3) / 4 : 1)),
                      dim3(256), 0, s, a);

@@ -258,7 +258,12 @@ BSATTN_API int64_t bsattn_fwd_plan_bytes(int32_t B, int32_t H, int32_t N, int32_
  * [0, Tk) are left out; entries beyond the plan's step capacity (a
  * plan_bytes below what bsattn_fwd_plan_bytes gives for the CSR's entry
  * count) are dropped, and the forward then misses them.  The plan stays
- * valid as long as the CSR does not change.
+ * valid as long as the CSR does not change.  How the work is shared out
+ * follows the speeds of the GPU's eight XCDs as the last planned forward on
+ * the current device measured them (a small table of the library's, one
+ * per GPU): ranges of work go to the XCDs in proportion to their measured
+ * speeds, or evenly before any planned forward has run.  That moves work
+ * between compute units only: the outputs never depend on it.
  * Errors: INVALID_ARG (sizes, mask_heads not in {1, H}, null or unaligned
  * pointers, plan_bytes below the fixed part, bad workers), UNSUPPORTED
  * (tile, Tq, B*H), HIP.  B*H*N == 0 is a no-op. */
@@ -274,7 +279,11 @@ BSATTN_API int bsattn_fwd_plan(int32_t B, int32_t H, int32_t N, int32_t tile,
  * be row_ptr / col_idx) and window: 0 for contiguous tokens, w > 0 for the
  * grouped view of bsattn_fwd_grouped.  Launches `workers` workgroups.  The
  * kernel checks the plan's header (B, H, N, Tq, mask_heads, workers); a
- * plan built for other sizes makes it return without writing O or LSE.
+ * plan built for other sizes makes it return without writing O or LSE.  The
+ * plan is only read; each workgroup also records how long it ran, with its
+ * share of the work, in the library's per-GPU table that the next
+ * bsattn_fwd_plan on the device reads (calls racing on one GPU write the
+ * same entries; either record serves).
  * Errors: as bsattn_fwd and bsattn_fwd_plan; UNSUPPORTED for other dtypes,
  * head dims or tiles; INVALID_ARG for window < 0 or N not of the grouped
  * form. */

@@ -438,6 +438,43 @@ def test_plan_evens_out_the_window_mask(rotation):
     assert ratio < 1.03
 
 
+def test_plan_cuts_xcd_ranges_by_measured_speed():
+    """A planned forward leaves each workgroup's run time and load in the
+    library's per-GPU table; the next plan weights the eight XCD ranges by
+    the speeds measured there (relative to their mean, clamped to
+    [0.8, 1.25]) and keeps the weights at byte 64.  Each XCD's share of the
+    total estimated cost must follow its weight to within one item's cost."""
+    w = W.WORKLOADS[2]
+    mask, rp, ci = gpu_mask_csr(w)
+    q, k, v = W.make_qkv(w, device="cuda")
+    o = torch.empty_like(q)
+    plan = bs.make_plan(rp, ci, w.B, w.H, w.N, 128, 1)
+    for _ in range(3):
+        bs.fwd_planned(q, k, v, o, rp, ci, plan)
+    bs.fwd_plan(rp, ci, w.B, w.H, w.N, plan, 128, 1)
+    torch.cuda.synchronize()
+    wt = plan[64:96].cpu().numpy().view(np.int32).astype(np.float64) / 4096.0
+    print("XCD weights:", np.round(wt, 3), flush=True)
+    assert ((wt >= 0.8 - 1e-3) & (wt <= 1.25 + 1e-3)).all()
+    P, _ = check_plan(plan, rp, ci, w.B, w.H, w.N, 1)
+    exp, pairs, tiles = expected_items(rp.cpu().numpy(), ci.cpu().numpy(), w.B, w.H, w.N, 1)
+    cost = np.zeros(8)
+    biggest = 0
+    for wk in range(P["workers"]):
+        first, cnt = P["witem"][wk]
+        for t in range(cnt):
+            iw = int(P["witems"][first + t]) & 0x7FFFFFFF
+            bh, p = iw >> PAIR_BITS, iw & ((1 << PAIR_BITS) - 1)
+            split, union, la, lb = exp[bh * pairs + p]
+            c = (4 * (max(len(la), 1) + (max(len(lb), 1) if 2 * p + 1 < tiles else 0)) + 5
+                 if split else 5 * (max(len(union), 1) + 1))
+            cost[wk % 8] += c
+            biggest = max(biggest, c)
+    share, want = cost / cost.sum(), wt / wt.sum()
+    print("cost shares:", np.round(share, 4), "weights:", np.round(want, 4), flush=True)
+    assert np.abs(share - want).max() <= biggest / cost.sum() + 1e-9
+
+
 def test_plan_for_other_sizes_writes_nothing():
     w = W.small_workload(frames=4, grid_h=8, grid_w=16, tile=128, d=128, H=2)
     mask, rp, ci = gpu_mask_csr(w)
