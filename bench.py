@@ -71,14 +71,29 @@ def forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, tile, Hm, planned, strea
                                   stream=stream)
 
 
+def settle(torch, fn, ms: float = 50.0, cap: int = 500):
+    """Run fn untimed until about `ms` of wall time has passed.  After the
+    GPU sits idle (host work between legs), its clock takes several
+    milliseconds to come back up: timed calls issued straight away run up to
+    15 % slower for the first few."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for n in range(1, cap + 1):
+        fn()
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= ms:
+                break
+    torch.cuda.synchronize()
+
+
 def time_interleaved(torch, stream, fns, calls: int):
     """Median event time (ms) of each callable, the callables run in turn
     call after call, so that all see the same clock (the chip's clock
     drifts by several per cent as a run heats it)."""
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(calls)] for _ in fns]
-    for f in fns:
-        f()
+    settle(torch, lambda: [f() for f in fns])
     for c in range(calls):
         for f, ev in zip(fns, evs):
             ev[c][0].record(stream)
@@ -181,6 +196,7 @@ def expanded_windows(bs, W, torch, dev, calls: int):
         dens.append(float(m_np.mean()))
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
            for _ in range(calls)]
+    settle(torch, lambda: run(0))
     for r in range(calls):
         run(r, evs[r])
     torch.cuda.synchronize()
@@ -233,6 +249,7 @@ def d64_leg(bs, W, torch, dev, calls: int):
         dens.append(float(m_np.mean()))
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
            for _ in range(calls)]
+    settle(torch, lambda: run(0))
     for r in range(calls):
         run(r, evs[r])
     torch.cuda.synchronize()
@@ -275,7 +292,7 @@ def calibration(bs, W, torch, dev, calls: int):
         if ev is not None:
             ev[3].record(stream)
 
-    run()
+    settle(torch, run)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(calls)]
     for e in evs:
         run(e)
@@ -381,9 +398,7 @@ def squad_leg(bs, W, torch, dev, calls: int):
         bs.fwd_planned(q, k, o_l, out, rp, ci, pl, window=win, stream=stream)
         mark(2)
 
-    run()
-    run_reordered()
-    run_planned()
+    settle(torch, lambda: (run(), run_reordered(), run_planned()))
     evp = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(calls)]
     for e in evp:
         run_planned(e)
@@ -403,7 +418,7 @@ def squad_leg(bs, W, torch, dev, calls: int):
     # dense attention of the same shape with the same kernel
     dm = bs.make_mask(*layout, device=dev, kind=W.MASK_DENSE)
     drp, dci = bs.make_csr(dm)
-    bs.fwd(q, k, v, og, drp, dci, w.tile)
+    settle(torch, lambda: bs.fwd(q, k, v, og, drp, dci, w.tile))
     de = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(max(1, calls // 2))]
     for a, b in de:
@@ -465,7 +480,8 @@ def repetition_leg(bs, W, torch, dev, calls: int):
     flags = torch.empty(w.H, dtype=torch.uint8, device=dev)
     ws = torch.empty(bs.row_cosines_workspace_bytes(w.B, w.H, w.frames, w.grid_h, w.grid_w,
                                                     stride), dtype=torch.uint8, device=dev)
-    bs.row_cosines(q, k, w.frames, w.grid_h, w.grid_w, stride, cos, workspace=ws)
+    settle(torch, lambda: bs.row_cosines(q, k, w.frames, w.grid_h, w.grid_w, stride, cos,
+                                         workspace=ws))
     cev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(calls)]
     for ev in cev:
         ev[0].record(stream)
@@ -573,6 +589,7 @@ def configs_leg(bs, W, torch, dev, calls: int, planned: bool = True):
         m_np = mask.cpu().numpy()
         flops = active_flops(m_np, w)
         tiles = int(m_np.sum()) * (w.H if Hm == 1 else 1) * w.B
+        settle(torch, run)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(calls)]
         for e in evs:
             run(e)
@@ -664,7 +681,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--cpu-tiles", type=int, default=256,
                     help="query tiles in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--dense-calls", type=int, default=5,
@@ -820,7 +837,7 @@ def main():
         dense_flops = active_flops(mask.cpu().numpy(), w)
         run = forward_fn(bs, torch, q, k, v, o, row_ptr, col_idx, w.tile, Hm,
                          bool(args.planned), stream)
-        run()
+        settle(torch, run)
         dev_ev = [(torch.cuda.Event(enable_timing=True),
                    torch.cuda.Event(enable_timing=True))
                   for _ in range(args.dense_calls)]

@@ -126,49 +126,60 @@ __device__ __forceinline__ int wave_sum(int v) {
 // of item_cost_sp); worker w ran on XCD w mod 8.  Each XCD's speed is its
 // summed load over its summed time, and the XCD ranges of the next plan
 // are cut in proportion to the speeds, relative to their mean and clamped
-// to [0.8, 1.25].  With no usable record (no planned forward yet on this
-// device, or one too short to time: under 100 us summed over an XCD's
-// workers) every weight is 1.  The weights go
+// to [0.9, 1.1].  Only long launches are trusted: when the loaded
+// workgroups ran under 400 us on average (short lists, such as SQuad's
+// passes, where fetch latency and the launch's own start and end dominate)
+// the speeds mislead (measured: 8 % slower than equal weights there), and
+// every weight is 1, as with no record at all.  The weights go
 // into the plan, so that the eight workgroups of the assign kernel cut by
 // the same ones even while another launch writes the table.  Workers with
 // no load are left out.  Run by one workgroup of 256 threads.
 __device__ void xcd_weights(const PlanArgs& a) {
-  __shared__ int64_t xs[4][2 * kPlanXcds];
+  __shared__ int64_t xs[4][3 * kPlanXcds];
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
-  int64_t ld = 0, bz = 0;  // this thread's workers: tid, tid + 256 (XCD tid % 8)
+  int64_t ld = 0, bz = 0, nw = 0;  // this thread's workers: tid, tid + 256 (XCD tid % 8)
   for (int w = tid; w < a.L.workers; w += 256) {
     const int2 r = reinterpret_cast<const int2*>(a.xfb)[w];
     if (r.x > 0 && r.y > 0) {
       bz += r.x;
       ld += r.y;
+      nw += 1;
     }
   }
   // lanes l, l + 8, ..., l + 56 share an XCD
   for (int o = 8; o < kWave; o <<= 1) {
     ld += __shfl_xor(ld, o, kWave);
     bz += __shfl_xor(bz, o, kWave);
+    nw += __shfl_xor(nw, o, kWave);
   }
   if (lane < kPlanXcds) {
     xs[wv][lane] = ld;
     xs[wv][kPlanXcds + lane] = bz;
+    xs[wv][2 * kPlanXcds + lane] = nw;
   }
   __syncthreads();
   if (tid == 0) {
     double sp[kPlanXcds], mean = 0.0;
+    int64_t btot = 0, ntot = 0;
     bool ok = true;
     for (int x = 0; x < kPlanXcds; ++x) {
       const int64_t l = xs[0][x] + xs[1][x] + xs[2][x] + xs[3][x];
       const int64_t b = xs[0][kPlanXcds + x] + xs[1][kPlanXcds + x] + xs[2][kPlanXcds + x] +
                         xs[3][kPlanXcds + x];
-      // at least 100 us of summed busy time (100 MHz ticks)
-      ok = ok && l > 0 && b >= 10000;
+      const int64_t n = xs[0][2 * kPlanXcds + x] + xs[1][2 * kPlanXcds + x] +
+                        xs[2][2 * kPlanXcds + x] + xs[3][2 * kPlanXcds + x];
+      ok = ok && l > 0 && b > 0;
       sp[x] = ok ? (double)l / (double)b : 0.0;
       mean += sp[x];
+      btot += b;
+      ntot += n;
     }
+    // 400 us (100 MHz ticks) per loaded workgroup on average
+    ok = ok && ntot > 0 && btot >= 40000 * ntot;
     mean /= kPlanXcds;
     int32_t* xw = P32(a, a.L.off_xw);
     for (int x = 0; x < kPlanXcds; ++x) {
-      const double r = ok && mean > 0.0 ? fmin(fmax(sp[x] / mean, 0.8), 1.25) : 1.0;
+      const double r = ok && mean > 0.0 ? fmin(fmax(sp[x] / mean, 0.9), 1.1) : 1.0;
       xw[x] = (int32_t)(r * kPlanWeightOne + 0.5);
     }
   }

@@ -5,7 +5,8 @@ Three summaries:
   stats    per-kernel call count and durations from a ``--kernel-trace
            --stats`` run (the ``*_kernel_stats.csv`` file), with the mean and
            median over every launch after a kernel's first from the
-           per-dispatch trace (``*_kernel_trace.csv``);
+           per-dispatch trace (``*_kernel_trace.csv``), and with ``--tail N``
+           over each kernel's last N launches;
   mfma     the matrix-core busy fraction and executed bf16 MFMA work of one
            kernel from one ``--pmc`` run (SQ_VALU_MFMA_BUSY_CYCLES,
            GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_BF16);
@@ -50,11 +51,9 @@ def source_sha256(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def _warm_durations(csv_dir: str):
-    """{kernel name: [duration ns of each dispatch after the first]} from the
-    per-dispatch kernel trace, or {} when the trace is missing.  The first
-    launch of a kernel in a process pays one-time costs (code object load,
-    cold caches) that the steady state does not."""
+def _dispatch_durations(csv_dir: str):
+    """{kernel name: [duration ns of each dispatch, in launch order]} from the
+    per-dispatch kernel trace, or {} when the trace is missing."""
     try:
         path = _one(os.path.join(csv_dir, "**", "*kernel_trace.csv"))
     except FileNotFoundError:
@@ -68,29 +67,40 @@ def _warm_durations(csv_dir: str):
     out = {}
     for name, lst in per.items():
         lst.sort()
-        out[name] = [d for _, d in lst[1:]]
+        out[name] = [d for _, d in lst]
     return out
 
 
-def stats_summary(csv_dir: str, command: str, top: int = 12) -> str:
+def stats_summary(csv_dir: str, command: str, top: int = 12, tail: int = 0) -> str:
+    """The kernel statistics, with the mean and median over every launch
+    after a kernel's first (the first pays one-time costs: code object load,
+    cold caches) and, with tail > 0, over each kernel's last `tail` launches
+    (a benchmark's timed steps, when its warm-up steps come first)."""
     path = _one(os.path.join(csv_dir, "**", "*kernel_stats.csv"))
     rows = list(csv.DictReader(open(path)))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    warm = _warm_durations(csv_dir)
+    disp = _dispatch_durations(csv_dir)
     lines = ["# rocprofv3 kernel-trace statistics", "",
              f"command: {command}", "",
              "warm_avg_us / warm_med_us: every launch after a kernel's first "
-             "(from the per-dispatch trace)", "",
-             f"{'calls':>6} {'avg_us':>10} {'warm_avg_us':>12} {'warm_med_us':>12} "
-             f"{'min_us':>10} {'max_us':>10} {'total_ms':>10} {'pct':>6}  kernel"]
+             "(from the per-dispatch trace)"]
+    if tail > 0:
+        lines.append(f"tail_avg_us / tail_med_us: each kernel's last {tail} launches "
+                     "(the timed steps)")
+    lines += ["", f"{'calls':>6} {'avg_us':>10} {'warm_avg_us':>12} {'warm_med_us':>12} "
+              + (f"{'tail_avg_us':>12} {'tail_med_us':>12} " if tail > 0 else "")
+              + f"{'min_us':>10} {'max_us':>10} {'total_ms':>10} {'pct':>6}  kernel"]
+    fmt = lambda f, xs: f"{f(xs) / 1e3:12.2f}" if xs else f"{'n/a':>12}"
     for r in rows[:top]:
         name = r["Name"]
-        wd = warm.get(name, [])
-        wa = f"{statistics.mean(wd) / 1e3:12.2f}" if wd else f"{'n/a':>12}"
-        wm = f"{statistics.median(wd) / 1e3:12.2f}" if wd else f"{'n/a':>12}"
+        d = disp.get(name, [])
+        wd, td = d[1:], d[-tail:] if tail > 0 else []
+        extra = (fmt(statistics.mean, td) + " " + fmt(statistics.median, td) + " "
+                 if tail > 0 else "")
+        wa, wm = fmt(statistics.mean, wd), fmt(statistics.median, wd)
         if len(name) > 90:
             name = name[:87] + "..."
-        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {wa} {wm} "
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {wa} {wm} {extra}"
                      f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
                      f"{float(r['TotalDurationNs']) / 1e6:10.3f} "
                      f"{float(r['Percentage']):6.2f}  {name}")
@@ -237,6 +247,7 @@ def main(argv=None):
     s.add_argument("--csv-dir", required=True)
     s.add_argument("--command", required=True)
     s.add_argument("--out", required=True)
+    s.add_argument("--tail", type=int, default=0)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch-dir", required=True)
     t.add_argument("--write-dir", required=True)
@@ -256,7 +267,7 @@ def main(argv=None):
     m.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
-        text = stats_summary(a.csv_dir, a.command)
+        text = stats_summary(a.csv_dir, a.command, tail=a.tail)
     elif a.cmd == "mfma":
         text = mfma_summary(a.pmc_dir, a.kernel, a.simds, a.xcds, a.source, a.command)
     else:

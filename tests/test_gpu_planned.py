@@ -442,7 +442,7 @@ def test_plan_cuts_xcd_ranges_by_measured_speed():
     """A planned forward leaves each workgroup's run time and load in the
     library's per-GPU table; the next plan weights the eight XCD ranges by
     the speeds measured there (relative to their mean, clamped to
-    [0.8, 1.25]) and keeps the weights at byte 64.  Each XCD's share of the
+    [0.9, 1.1]) and keeps the weights at byte 64.  Each XCD's share of the
     total estimated cost must follow its weight to within one item's cost."""
     w = W.WORKLOADS[2]
     mask, rp, ci = gpu_mask_csr(w)
@@ -455,7 +455,7 @@ def test_plan_cuts_xcd_ranges_by_measured_speed():
     torch.cuda.synchronize()
     wt = plan[64:96].cpu().numpy().view(np.int32).astype(np.float64) / 4096.0
     print("XCD weights:", np.round(wt, 3), flush=True)
-    assert ((wt >= 0.8 - 1e-3) & (wt <= 1.25 + 1e-3)).all()
+    assert ((wt >= 0.9 - 1e-3) & (wt <= 1.1 + 1e-3)).all()
     P, _ = check_plan(plan, rp, ci, w.B, w.H, w.N, 1)
     exp, pairs, tiles = expected_items(rp.cpu().numpy(), ci.cpu().numpy(), w.B, w.H, w.N, 1)
     cost = np.zeros(8)
@@ -473,6 +473,29 @@ def test_plan_cuts_xcd_ranges_by_measured_speed():
     share, want = cost / cost.sum(), wt / wt.sum()
     print("cost shares:", np.round(share, 4), "weights:", np.round(want, 4), flush=True)
     assert np.abs(share - want).max() <= biggest / cost.sum() + 1e-9
+
+
+def test_short_launches_leave_equal_xcd_weights():
+    """Speeds measured on short launches (workgroups busy under 400 us on
+    average) are not trusted: after a planned forward on a small shape the
+    next plan weights every XCD alike."""
+    w = W.WORKLOADS[2]
+    mask, rp, ci = gpu_mask_csr(w)
+    q, k, v = W.make_qkv(w, device="cuda")
+    o = torch.empty_like(q)
+    plan = bs.make_plan(rp, ci, w.B, w.H, w.N, 128, 1)
+    for _ in range(2):
+        bs.fwd_planned(q, k, v, o, rp, ci, plan)
+    ws = W.small_workload(frames=8, grid_h=8, grid_w=16, tile=128, d=128, H=2)
+    _, rps, cis = gpu_mask_csr(ws)
+    qs, ks, vs = W.make_qkv(ws, device="cuda")
+    plan_s = bs.make_plan(rps, cis, ws.B, ws.H, ws.N, 128, ws.mask.mask_heads)
+    bs.fwd_planned(qs, ks, vs, torch.empty_like(qs), rps, cis, plan_s,
+                   mask_heads=ws.mask.mask_heads)
+    bs.fwd_plan(rp, ci, w.B, w.H, w.N, plan, 128, 1)
+    torch.cuda.synchronize()
+    wt = plan[64:96].cpu().numpy().view(np.int32)
+    assert (wt == 4096).all(), wt
 
 
 def test_plan_for_other_sizes_writes_nothing():
