@@ -379,11 +379,45 @@ __global__ void __launch_bounds__(kAssignThreads) plan_assign_kernel(PlanArgs a)
   // pairs kernel): item i lies below x when A < B C(x), A = (2 prefix(i) +
   // cost(i)) C(8), B = 2 total, C(x) = wt(0) + ... + wt(x - 1); at most x
   // when A < B C(x + 1) or x = 7
+  //
+  // The weights are used only when the items' costs vary (coefficient of
+  // variation at least 0.1, as on window masks): a range then takes a
+  // slightly larger or smaller share and the refinement spreads the
+  // difference over its workers by exchanging items of different cost.
+  // With items of one cost (a dense mask: six per worker) a few per cent
+  // more work on an XCD is a seventh item on some of its workers, 17 %
+  // more for them, and nothing can even that out (measured: 6 % slower
+  // than equal weights).  Integer sums over the cost table, so every
+  // workgroup decides the same.
+  int64_t cs = 0, cs2 = 0;
+  for (int sp = tid; sp < nsp; sp += kAssignThreads) {
+    const int64_t c = tab.get(a, sp / L.pairs, sp % L.pairs).cost;
+    cs += c;
+    cs2 += c * c;
+  }
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    cs += __shfl_xor(cs, o, kWave);
+    cs2 += __shfl_xor(cs2, o, kWave);
+  }
+  __syncthreads();  // every wave has read part[] above
+  if (lane == 0) {
+    part[wv] = cs;
+    part[kAssignThreads / kWave + wv] = cs2;
+  }
+  __syncthreads();
+  cs = 0;
+  cs2 = 0;
+  for (int w2 = 0; w2 < kAssignThreads / kWave; ++w2) {
+    cs += part[w2];
+    cs2 += part[kAssignThreads / kWave + w2];
+  }
+  const double csd = (double)cs;
+  const bool use_w = cs > 0 && 100.0 * ((double)nsp * (double)cs2 - csd * csd) >= csd * csd;
   int64_t cw_lo = 0, cw_hi = 0, cw_all = 0;
   {
     const int32_t* xw = P32(a, L.off_xw);
     for (int x2 = 0; x2 < kPlanXcds; ++x2) {
-      const int64_t wt = min(max(xw[x2], 1), 4 * kPlanWeightOne);
+      const int64_t wt = use_w ? min(max(xw[x2], 1), 4 * kPlanWeightOne) : kPlanWeightOne;
       cw_lo += x2 < x ? wt : 0;
       cw_hi += x2 <= x ? wt : 0;
       cw_all += wt;

@@ -475,6 +475,30 @@ def test_plan_cuts_xcd_ranges_by_measured_speed():
     assert np.abs(share - want).max() <= biggest / cost.sum() + 1e-9
 
 
+def test_uniform_items_ignore_xcd_weights():
+    """With items of one cost (a dense mask: 1 536 pairs of 256 key tiles,
+    six per worker) a weighted cut would put a seventh item on some workers
+    of a faster XCD; the plan then cuts the ranges evenly whatever the
+    weights: 192 pairs per XCD."""
+    w = W.WORKLOADS[2]
+    m = bs.make_mask(w.frames, w.grid_h, w.grid_w, w.tile, device="cuda", kind=W.MASK_DENSE)
+    rp, ci = bs.make_csr(m)
+    q, k, v = W.make_qkv(w, device="cuda")
+    o = torch.empty_like(q)
+    plan = bs.make_plan(rp, ci, w.B, w.H, w.N, 128, 1)
+    for _ in range(2):
+        bs.fwd_planned(q, k, v, o, rp, ci, plan)
+    bs.fwd_plan(rp, ci, w.B, w.H, w.N, plan, 128, 1)
+    torch.cuda.synchronize()
+    P, _ = check_plan(plan, rp, ci, w.B, w.H, w.N, 1)
+    per_xcd = np.zeros(8, dtype=np.int64)
+    for wk in range(P["workers"]):
+        per_xcd[wk % 8] += P["witem"][wk][1]
+    print("weights", plan[64:96].cpu().numpy().view(np.int32) / 4096.0, "pairs per XCD", per_xcd,
+          flush=True)
+    assert (per_xcd == 192).all()
+
+
 def test_short_launches_leave_equal_xcd_weights():
     """Speeds measured on short launches (workgroups busy under 400 us on
     average) are not trusted: after a planned forward on a small shape the
