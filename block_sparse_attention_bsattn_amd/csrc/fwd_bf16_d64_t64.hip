@@ -88,6 +88,8 @@ fwd_bf16_d64_t64(FwdLaunch a) {
   __shared__ uint32_t ulist[Q_MAXT];           // union list: tile | need bits << 27
   __shared__ uint32_t bmap[4 * (Q_MAXT / 32)];  // the four lists as bitmaps
   __shared__ int wcount[8];
+  __shared__ uint32_t okeys[32];
+  __shared__ int oitem[32];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -99,14 +101,43 @@ fwd_bf16_d64_t64(FwdLaunch a) {
   const uint32_t kl32 = (uint32_t)(uintptr_t)uniform_lds((lds_char_t*)kslots);
   const uint32_t vl32 = (uint32_t)(uintptr_t)uniform_lds((lds_char_t*)vslots);
 
-  // ---- workgroup -> (batch * head, quad of query tiles), XCD-contiguous
+  // ---- workgroup -> (batch * head, quad of query tiles), XCD-contiguous.
+  // Each XCD's range is cut into chunks of 32 quads (about one per compute
+  // unit of the XCD), and the k-th workgroup of a chunk to be dispatched
+  // takes its k-th longest quad (by the four lists' summed length, ties by
+  // position), so long quads start first and short ones fill the end.
   const int quads = (a.tiles + 3) >> 2;
   uint32_t logical;
   {
     const uint32_t G = gridDim.x, hw = blockIdx.x;
     const uint32_t q8 = G / Q_NXCD, r8 = G % Q_NXCD, xcd = hw % Q_NXCD, slot = hw / Q_NXCD;
     const uint32_t lo = xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8;
-    logical = lo + slot;
+    const uint32_t len = q8 + (xcd < r8 ? 1u : 0u);
+    const uint32_t c0 = lo + (slot & ~31u);
+    const int nchunk = (int)min(32u, lo + len - c0);
+    if (tid < 32) {
+      uint32_t key = 0;
+      if (tid < nchunk) {
+        const uint32_t it = c0 + (uint32_t)tid;
+        const int qd = (int)(it % (uint32_t)quads);
+        const int hh = (int)(it / (uint32_t)quads) % a.H;
+        const int r0 = (a.mask_heads == 1 ? 0 : hh) * a.tiles + 4 * qd;
+        const int r1 = min(r0 + 4, (a.mask_heads == 1 ? 0 : hh) * a.tiles + a.tiles);
+        const int64_t n = (int64_t)a.row_ptr[r1] - a.row_ptr[r0];
+        key = ((uint32_t)min(max(n, (int64_t)0), (int64_t)0xFFFFFF) << 8 | (uint32_t)(31 - tid)) + 1;
+      }
+      okeys[tid] = key;
+    }
+    __syncthreads();
+    if (tid < nchunk) {
+      const uint32_t mine = okeys[tid];
+      int rank = 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) rank += okeys[j] > mine ? 1 : 0;
+      oitem[rank] = tid;
+    }
+    __syncthreads();
+    logical = c0 + (uint32_t)oitem[slot & 31u];
   }
   const int quad = (int)(logical % (uint32_t)quads);
   const int bh = (int)(logical / (uint32_t)quads);
