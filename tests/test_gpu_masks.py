@@ -68,10 +68,12 @@ def test_static_masks(hm, seed, p, diag):
 
 def test_compact_on_arbitrary_masks():
     """Compaction of masks the builder cannot produce (any nonzero byte is
-    active; wide rows spanning several 64-column chunks; empty rows)."""
+    active; wide rows spanning several 64-column chunks; empty rows; more
+    than 4096 rows; rows of an odd width)."""
     g = torch.Generator().manual_seed(5)
     for rows, tk in [(1, 1), (3, 63), (5, 64), (7, 65), (130, 200), (2, 1024),
-                     (1025, 3), (4000, 17)]:
+                     (1025, 3), (4000, 17), (4096, 16), (256, 256), (4097, 5), (300, 1000),
+                     (256, 257)]:
         m = (torch.randint(0, 4, (rows, tk), generator=g) *
              torch.randint(0, 2, (rows, tk), generator=g)).to(torch.uint8)
         m[rows // 2] = 0
