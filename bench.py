@@ -264,6 +264,45 @@ def d64_leg(bs, W, torch, dev, calls: int):
             "fwd_frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
+def generic_leg(bs, W, torch, dev, calls: int):
+    """The generic forward (the shapes no tuned kernel takes) on the
+    32 760-token video shape with the window/anchor mask at rotation 0:
+    fp32 I/O at d 128 / tile 128, bf16 at d 128 / tile 64 and at d 64 /
+    tile 128 (24 heads); median of `calls` event-timed calls each."""
+    from dataclasses import replace
+    base = W.WORKLOADS[HEADLINE]
+    stream = torch.cuda.current_stream()
+    recs = {}
+    for dt, d, tile, H in ((W.DTYPE_F32, 128, 128, 12), (W.DTYPE_BF16, 128, 64, 12),
+                           (W.DTYPE_BF16, 64, 128, 24)):
+        w = replace(base, name=f"video_21x30x52_{'f32' if dt == W.DTYPE_F32 else 'bf16'}"
+                    f"_d{d}_t{tile}", dtype=dt, d=d, tile=tile, H=H)
+        q, k, v = W.make_qkv(w, device=dev)
+        o = torch.empty_like(q)
+        mask = bs.make_mask(w.frames, w.grid_h, w.grid_w, w.tile, device=dev,
+                            **bs.mask_params_of(w.mask))
+        row_ptr, col_idx = bs.make_csr(mask)
+        flops = active_flops(mask.cpu().numpy(), w)
+        run = lambda: bs.fwd(q, k, v, o, row_ptr, col_idx, w.tile, stream=stream)
+        settle(torch, run)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(calls)]
+        for a, b in evs:
+            a.record(stream)
+            run()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        tf = flops / (ms * 1e-3) / 1e12
+        recs[w.name] = {"H": H, "d": d, "tile": tile,
+                        "io": "fp32" if dt == W.DTYPE_F32 else "bf16",
+                        "fwd_ms_median": round(ms, 4), "fwd_tflops": round(tf, 1),
+                        "fwd_frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del q, k, v, o
+        torch.cuda.empty_cache()
+    return recs
+
+
 def calibration(bs, W, torch, dev, calls: int):
     """Static-mask calibration at the video shape (4 prompts x 12 heads x
     32 760 tokens, frame-local Q/K): block energies, per-prompt selection at
@@ -696,6 +735,8 @@ def main():
                          "(0 = skip)")
     ap.add_argument("--d64", type=int, default=6,
                     help="steps of the d 64 / tile 64 video leg (0: skip)")
+    ap.add_argument("--generic", type=int, default=5,
+                    help="calls per shape of the generic-forward leg (0 = skip)")
     ap.add_argument("--calib", type=int, default=3,
                     help="timed calls of the static-mask calibration leg "
                          "(0 = skip)")
@@ -856,6 +897,8 @@ def main():
 
     d64 = d64_leg(bs, W, torch, dev, args.d64) if args.d64 > 0 else None
 
+    generic = generic_leg(bs, W, torch, dev, args.generic) if args.generic > 0 else None
+
     calib = calibration(bs, W, torch, dev, args.calib) if args.calib > 0 else None
 
     squad = squad_leg(bs, W, torch, dev, args.squad) if args.squad > 0 else None
@@ -948,6 +991,7 @@ def main():
         "density_sweep": sweep,
         "expanded_windows": expanded,
         "d64_t64": d64,
+        "generic_fwd": generic,
         "calibration": calib,
         "squad": squad,
         "repetition": repetition,

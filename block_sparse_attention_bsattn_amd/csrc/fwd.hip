@@ -9,9 +9,16 @@
 // Work decomposition: one workgroup per (batch, head, query tile) with
 // tile/32 waves; each wave owns 32 query rows.
 //
+// Staging: K/V tiles are double-buffered in LDS.  While the waves compute on
+// the tile in one buffer, the next listed tile's rows are already loading
+// into registers (issued before the tile's matrix products); after the
+// tile's last LDS read they are written into the other buffer, and one
+// barrier per tile separates the two uses of each buffer.
+//
 // Per active key tile j:
 //   * K_j is staged in LDS row-major and V_j transposed (V^T, keys
-//     contiguous), so both matrix products read MFMA operands as short runs.
+//     contiguous; each thread writes two consecutive keys at once), so both
+//     matrix products read MFMA operands as short runs.
 //   * S^T = K_j Q^T on v_mfma_f32_32x32x16_bf16: A = K rows (32 keys x 16 d),
 //     B = Q^T (16 d x 32 queries).  Lane l then holds query (l % 32) and, per
 //     32-key block, keys 8*i + 4*(l/32) + e (i, e in 0..3), so every lane sees
@@ -31,25 +38,62 @@
 namespace bsattn {
 namespace {
 
+#define INLINE_FN __attribute__((always_inline))
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// 8 consecutive elements of a row as loaded from memory: bf16, or fp32
+// rounded to bf16 only when written to LDS (so the load stays in flight).
+template <bool F32IN> struct Raw8;
+template <> struct Raw8<false> { bf16x8 v; };
+template <> struct Raw8<true> { f32x4 lo, hi; };
+
+template <bool F32IN>
+__device__ __forceinline__ void load_raw(Raw8<F32IN>& r, const void* base, int64_t off) {
+  if constexpr (F32IN) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + off);
+    r.lo = p[0];
+    r.hi = p[1];
+  } else {
+    r.v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(base) + off);
+  }
+}
+
+template <bool F32IN>
+__device__ __forceinline__ void zero_raw(Raw8<F32IN>& r) {
+  if constexpr (F32IN) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r.lo[e] = r.hi[e] = 0.f;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r.v[e] = (__bf16)0.f;
+  }
+}
+
+template <bool F32IN>
+__device__ __forceinline__ bf16x8 to_bf16(const Raw8<F32IN>& r) {
+  if constexpr (F32IN) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[e] = (__bf16)r.lo[e];
+      o[e + 4] = (__bf16)r.hi[e];
+    }
+    return o;
+  } else {
+    return r.v;
+  }
+}
+
 template <bool F32IN>
 __device__ __forceinline__ bf16x8 load8(const void* base, int64_t off) {
-  if constexpr (F32IN) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(
-        reinterpret_cast<const float*>(base) + off);
-    const f32x4 x = p[0], y = p[1];
-    bf16x8 r;
-    r[0] = (__bf16)x[0]; r[1] = (__bf16)x[1]; r[2] = (__bf16)x[2]; r[3] = (__bf16)x[3];
-    r[4] = (__bf16)y[0]; r[5] = (__bf16)y[1]; r[6] = (__bf16)y[2]; r[7] = (__bf16)y[3];
-    return r;
-  } else {
-    return *reinterpret_cast<const bf16x8*>(
-        reinterpret_cast<const __bf16*>(base) + off);
-  }
+  Raw8<F32IN> r;
+  load_raw<F32IN>(r, base, off);
+  return to_bf16<F32IN>(r);
 }
 
 template <bool F32IN>
@@ -65,8 +109,15 @@ __device__ __forceinline__ void store4(void* base, int64_t off, float a, float b
   }
 }
 
+// Waves per SIMD the register allocation must leave room for: at d = 64 the
+// tile is small enough that more resident workgroups hide latency better
+// than a deeper prefetch would.
+template <int BT, int D>
+constexpr int kMinWaves = D == 64 ? (BT == 64 ? 3 : 2) : 1;
+
 template <int BT, int D, bool F32IN>
 __global__ void __launch_bounds__(BT * 2)
+__attribute__((amdgpu_waves_per_eu(kMinWaves<BT, D>, 8)))
 fwd_kernel(FwdLaunch a) {
   constexpr int NT = BT * 2;         // threads: BT/32 waves of 64
   constexpr int KB = BT / 32;        // 32-key blocks per tile
@@ -74,8 +125,12 @@ fwd_kernel(FwdLaunch a) {
   constexpr int DB = D / 32;         // 32-row blocks of O^T
   constexpr int KP = D + 8;          // K row pitch in LDS (bf16 elements)
   constexpr int VP = BT + 8;         // V^T row pitch in LDS
-  __shared__ __bf16 Ks[BT * KP];
-  __shared__ __bf16 Vt[D * VP];
+  constexpr int CPR = D / 8;         // 8-element chunks per row
+  // staging items per thread: (pair of consecutive rows, chunk) of K and V
+  constexpr int ITEMS = (BT / 2) * CPR / NT;
+  static_assert((BT / 2) * CPR == ITEMS * NT, "tile rows must split evenly over the threads");
+  __shared__ __bf16 Ks[2][BT * KP];
+  __shared__ __bf16 Vt[2][D * VP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -108,31 +163,73 @@ fwd_kernel(FwdLaunch a) {
 
   const int mrow = (a.mask_heads == 1 ? 0 : h) * a.tiles + qt;
   int jb = a.row_ptr[mrow];
-  int64_t je = a.row_ptr[mrow + 1];
+  int64_t je64 = a.row_ptr[mrow + 1];
   if (jb < 0) jb = 0;
-  if (je > a.col_cap) je = a.col_cap;
+  if (je64 > a.col_cap) je64 = a.col_cap;
+  const int je = (int)je64;  // row_ptr entries are int32
 
-  for (int jj = jb; jj < je; ++jj) {
-    const int j = a.col_idx[jj];
-    if (j < 0 || j >= a.tiles) continue;  // uniform across the workgroup
-    __syncthreads();                      // previous tile's LDS reads done
-    for (int c = tid; c < BT * D / 8; c += NT) {
-      const int r = c / (D / 8);
-      const int cc = (c % (D / 8)) * 8;
-      const int tok = j * BT + r;
-      bf16x8 kv, vv;
-      if (tok < N) {
-        kv = load8<F32IN>(a.k, (head_row + tok) * D + cc);
-        vv = load8<F32IN>(a.v, (head_row + tok) * D + cc);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { kv[e] = (__bf16)0.f; vv[e] = (__bf16)0.f; }
-      }
-      *reinterpret_cast<bf16x8*>(&Ks[r * KP + cc]) = kv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[(cc + e) * VP + r] = vv[e];
+  // first entry at or after jj naming a key tile in [0, tiles); je if none.
+  // Every thread reads the same list entries, so the result is uniform.
+  auto next_valid = [&](int jj) INLINE_FN {
+    for (; jj < je; ++jj) {
+      const int j = a.col_idx[jj];
+      if (j >= 0 && j < a.tiles) break;
     }
-    __syncthreads();
+    return jj;
+  };
+
+  // the next tile's rows, held in registers while the current one is computed
+  Raw8<F32IN> kr[ITEMS][2], vr[ITEMS][2];
+  auto fetch = [&](int j) INLINE_FN {
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int c = tid + it * NT;
+      const int r = 2 * (c / CPR);
+      const int cc = (c % CPR) * 8;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int tok = j * BT + r + e;
+        if (tok < N) {
+          load_raw<F32IN>(kr[it][e], a.k, (head_row + tok) * D + cc);
+          load_raw<F32IN>(vr[it][e], a.v, (head_row + tok) * D + cc);
+        } else {
+          zero_raw<F32IN>(kr[it][e]);
+          zero_raw<F32IN>(vr[it][e]);
+        }
+      }
+    }
+  };
+  auto stage = [&](int st) INLINE_FN {
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int c = tid + it * NT;
+      const int r = 2 * (c / CPR);
+      const int cc = (c % CPR) * 8;
+      *reinterpret_cast<bf16x8*>(&Ks[st][r * KP + cc]) = to_bf16<F32IN>(kr[it][0]);
+      *reinterpret_cast<bf16x8*>(&Ks[st][(r + 1) * KP + cc]) = to_bf16<F32IN>(kr[it][1]);
+      const bf16x8 v0 = to_bf16<F32IN>(vr[it][0]), v1 = to_bf16<F32IN>(vr[it][1]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16x2 pr;
+        pr[0] = v0[e];
+        pr[1] = v1[e];
+        *reinterpret_cast<bf16x2*>(&Vt[st][(cc + e) * VP + r]) = pr;
+      }
+    }
+  };
+
+  int jj = next_valid(jb);
+  if (jj < je) {
+    fetch(a.col_idx[jj]);
+    stage(0);
+  }
+  __syncthreads();
+  int st = 0;
+  while (jj < je) {
+    const int j = a.col_idx[jj];
+    const int jn = next_valid(jj + 1);
+    const bool more = jn < je;  // uniform
+    if (more) fetch(a.col_idx[jn]);
 
     // S^T = K_j Q^T
     f32x16 s[KB];
@@ -143,7 +240,7 @@ fwd_kernel(FwdLaunch a) {
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-            &Ks[(kb * 32 + l32) * KP + c * 16 + half * 8]);
+            &Ks[st][(kb * 32 + l32) * KP + c * 16 + half * 8]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[c], s[kb], 0, 0, 0);
       }
     }
@@ -196,14 +293,20 @@ fwd_kernel(FwdLaunch a) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int dd = db * 32 + l32;
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&Vt[dd * VP + key0]);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&Vt[dd * VP + key0 + 8]);
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&Vt[st][dd * VP + key0]);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&Vt[st][dd * VP + key0 + 8]);
         bf16x8 va;
         va[0] = lo[0]; va[1] = lo[1]; va[2] = lo[2]; va[3] = lo[3];
         va[4] = hi[0]; va[5] = hi[1]; va[6] = hi[2]; va[7] = hi[3];
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
       }
     }
+
+    // buffer st ^ 1 was last read before the previous barrier
+    if (more) stage(st ^ 1);
+    __syncthreads();
+    st ^= 1;
+    jj = jn;
   }
 
   l += __shfl_xor(l, 32);
