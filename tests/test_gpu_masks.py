@@ -84,6 +84,25 @@ def test_compact_on_arbitrary_masks():
         assert np.array_equal(ci[:int(rp_ref[-1])].cpu().numpy(), ci_ref)
 
 
+def test_compact_any_byte_values_and_unaligned_masks():
+    """Masks of up to 128 KiB are compacted in one launch that counts the
+    cells before each workgroup's rows four bytes at a time: bytes of every
+    value (0x80 and above included) must count as active, and a mask that
+    starts at an odd address must give the same lists."""
+    g = torch.Generator().manual_seed(11)
+    for rows, tk, offset in [(100, 100, 0), (256, 256, 0), (512, 256, 0), (33, 31, 1),
+                             (256, 256, 3), (17, 7, 2), (513, 255, 1)]:
+        vals = torch.randint(0, 256, (rows * tk + offset,), generator=g).to(torch.uint8)
+        vals[torch.randint(0, 2, (rows * tk + offset,), generator=g).bool()] = 0
+        buf = vals.cuda()
+        dev = buf[offset:].reshape(1, rows, tk)
+        rp, ci = bs.make_csr(dev)
+        m = vals[offset:].numpy().reshape(1, rows, tk)
+        rp_ref, ci_ref = oracle.tile_csr(m)
+        assert np.array_equal(rp.cpu().numpy(), rp_ref), (rows, tk, offset)
+        assert np.array_equal(ci[:int(rp_ref[-1])].cpu().numpy(), ci_ref), (rows, tk, offset)
+
+
 def test_mask_and_csr_repeatable():
     w = W.WORKLOADS[3]
     m1, rp1, ci1 = gpu_mask_csr(w)
