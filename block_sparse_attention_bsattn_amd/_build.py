@@ -83,5 +83,29 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+CAPI_SRC = os.path.join(ROOT, "tests", "capi", "fwd_driver.c")
+CAPI_EXE = os.path.join(ROOT, "tests", "capi", "fwd_driver")
+
+
+def build_capi_driver(verbose: bool = False) -> str:
+    """Compile the plain-C consumer of the library that the C-ABI test runs
+    (C11, gcc, the HIP runtime's C API; no HIP device code)."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler for tests/capi/fwd_driver.c")
+    rocm_lib = "/opt/rocm/lib"
+    cmd = [cc, "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           f"-I{INCLUDE}", CAPI_SRC, "-o", CAPI_EXE + ".tmp", f"-L{PKG}", "-lbsattn",
+           f"-L{rocm_lib}", "-lamdhip64", f"-Wl,-rpath,{rocm_lib}",
+           "-Wl,-rpath,$ORIGIN/../../block_sparse_attention_bsattn_amd"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("C driver build failed:\n" + r.stdout + r.stderr)
+    os.replace(CAPI_EXE + ".tmp", CAPI_EXE)
+    return CAPI_EXE
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
