@@ -222,6 +222,38 @@ def mfma_summary(pmc_dir, kernel, simds, xcds, source, command):
     return "\n".join(lines) + "\n"
 
 
+def l2_summary(pmc_dir, kernel, source, command):
+    """L2 hit rate per launch of one kernel: TCC_HIT_sum / (TCC_HIT_sum +
+    TCC_MISS_sum), both summed over the L2 channels of every XCD."""
+    hit = dict(_counter_by_dispatch(pmc_dir, "TCC_HIT_sum"))
+    miss = dict(_counter_by_dispatch(pmc_dir, "TCC_MISS_sum"))
+    rates, reqs = [], []
+    for name, dv in hit.items():
+        if kernel not in name:
+            continue
+        m = {d: v for d, v in miss.get(name, [])}
+        for d, h in dv:
+            if d in m and h + m[d] > 0:
+                rates.append(h / (h + m[d]))
+                reqs.append(h + m[d])
+    if not rates:
+        raise KeyError(f"no dispatch of a kernel matching {kernel!r}")
+    lines = [
+        "# L2 hit rate from rocprofv3 PMC counters", "",
+        f"kernel: {kernel}",
+        f"source: {os.path.relpath(source)}",
+        f"source_sha256: {source_sha256(source)}",
+        f"command: {command}",
+        "counters: TCC_HIT_sum, TCC_MISS_sum (all L2 channels of all XCDs)",
+        f"launches: {len(rates)}",
+        f"l2_hit_rate_mean: {statistics.mean(rates):.4f}",
+        f"l2_hit_rate_min: {min(rates):.4f}",
+        f"l2_hit_rate_max: {max(rates):.4f}",
+        f"l2_requests_per_launch: {statistics.mean(reqs):.4e}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
 def read_mfma(path: str, source: str):
     """The MFMA summary as a dict, or None when missing or taken on another
     version of the kernel source."""
@@ -265,9 +297,17 @@ def main(argv=None):
     m.add_argument("--source", required=True)
     m.add_argument("--command", required=True)
     m.add_argument("--out", required=True)
+    c = sub.add_parser("l2")
+    c.add_argument("--pmc-dir", required=True)
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--source", required=True)
+    c.add_argument("--command", required=True)
+    c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         text = stats_summary(a.csv_dir, a.command, tail=a.tail)
+    elif a.cmd == "l2":
+        text = l2_summary(a.pmc_dir, a.kernel, a.source, a.command)
     elif a.cmd == "mfma":
         text = mfma_summary(a.pmc_dir, a.kernel, a.simds, a.xcds, a.source, a.command)
     else:

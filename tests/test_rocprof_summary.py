@@ -64,3 +64,22 @@ def test_traffic_scales_by_the_copy(tmp_path):
     assert rs.read_traffic(str(out), str(src)) is not None
     src.write_text("// changed\n")
     assert rs.read_traffic(str(out), str(src)) is None
+
+
+def test_l2_hit_rate(tmp_path):
+    d = tmp_path / "l2"
+    d.mkdir()
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    # two launches: 75 % and 50 % hits; another kernel is ignored
+    _write(d / "l2_counter_collection.csv", hdr,
+           [(1, "kern<x>", "TCC_HIT_sum", 300.0), (1, "kern<x>", "TCC_MISS_sum", 100.0),
+            (2, "kern<x>", "TCC_HIT_sum", 50.0), (2, "kern<x>", "TCC_MISS_sum", 50.0),
+            (3, "other", "TCC_HIT_sum", 0.0), (3, "other", "TCC_MISS_sum", 10.0)])
+    src = tmp_path / "k.hip"
+    src.write_text("// kernel\n")
+    text = rs.l2_summary(str(d), "kern", str(src), "cmd")
+    kv = dict(ln.split(": ", 1) for ln in text.splitlines() if ": " in ln)
+    assert kv["launches"] == "2"
+    assert float(kv["l2_hit_rate_mean"]) == 0.625
+    assert float(kv["l2_hit_rate_min"]) == 0.5 and float(kv["l2_hit_rate_max"]) == 0.75
+    assert float(kv["l2_requests_per_launch"]) == 250.0
