@@ -269,14 +269,10 @@ def generic_leg(bs, W, torch, dev, calls: int):
     32 760-token video shape with the window/anchor mask at rotation 0:
     fp32 I/O at d 128 / tile 128, bf16 at d 128 / tile 64 and at d 64 /
     tile 128 (24 heads); median of `calls` event-timed calls each."""
-    from dataclasses import replace
-    base = W.WORKLOADS[HEADLINE]
     stream = torch.cuda.current_stream()
     recs = {}
-    for dt, d, tile, H in ((W.DTYPE_F32, 128, 128, 12), (W.DTYPE_BF16, 128, 64, 12),
-                           (W.DTYPE_BF16, 64, 128, 24)):
-        w = replace(base, name=f"video_21x30x52_{'f32' if dt == W.DTYPE_F32 else 'bf16'}"
-                    f"_d{d}_t{tile}", dtype=dt, d=d, tile=tile, H=H)
+    for w in W.GENERIC:
+        dt, d, tile, H = w.dtype, w.d, w.tile, w.H
         q, k, v = W.make_qkv(w, device=dev)
         o = torch.empty_like(q)
         mask = bs.make_mask(w.frames, w.grid_h, w.grid_w, w.tile, device=dev,

@@ -142,6 +142,16 @@ EXPANDED = Workload("long_84x30x52_expanded_c21", B=1, H=12, d=128, frames=84,
                     seed=1006, rotations=tuple(range(84)))
 
 
+# The shapes only the generic forward takes, at the 32 760-token video size
+# with the window/anchor mask: fp32 I/O at d 128 / tile 128, bf16 at d 128 /
+# tile 64, bf16 at d 64 / tile 128 (24 heads).
+GENERIC = tuple(
+    replace(WORKLOADS[2], name=f"video_21x30x52_{'f32' if dt == DTYPE_F32 else 'bf16'}_d{d}_t{t}",
+            dtype=dt, d=d, tile=t, H=h)
+    for dt, d, t, h in ((DTYPE_F32, 128, 128, 12), (DTYPE_BF16, 128, 64, 12),
+                        (DTYPE_BF16, 64, 128, 24)))
+
+
 def make_qkv(w: Workload, seed: Optional[int] = None, device: str = "cpu"):
     """Q, K, V of shape [B, H, N, d] drawn i.i.d. N(0, 1) in float32 from a CPU
     generator (seeded, in the order Q, K, V), then rounded to the workload's
