@@ -71,11 +71,28 @@ def _dispatch_durations(csv_dir: str):
     return out
 
 
-def stats_summary(csv_dir: str, command: str, top: int = 12, tail: int = 0) -> str:
+def _bench_line(path: str):
+    """The last JSON line a benchmark run printed (None if there is none)."""
+    import json
+    last = None
+    for line in open(path, errors="replace"):
+        line = line.strip()
+        if line.startswith("{") and line.endswith("}"):
+            try:
+                last = json.loads(line)
+            except ValueError:
+                pass
+    return last
+
+
+def stats_summary(csv_dir: str, command: str, top: int = 12, tail: int = 0,
+                  bench_log: str = "") -> str:
     """The kernel statistics, with the mean and median over every launch
     after a kernel's first (the first pays one-time costs: code object load,
     cold caches) and, with tail > 0, over each kernel's last `tail` launches
-    (a benchmark's timed steps, when its warm-up steps come first)."""
+    (a benchmark's timed steps, when its warm-up steps come first).  With
+    bench_log, the forward time the same run's benchmark line reports from
+    its own events, to compare with the traced durations."""
     path = _one(os.path.join(csv_dir, "**", "*kernel_stats.csv"))
     rows = list(csv.DictReader(open(path)))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
@@ -104,6 +121,16 @@ def stats_summary(csv_dir: str, command: str, top: int = 12, tail: int = 0) -> s
                      f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
                      f"{float(r['TotalDurationNs']) / 1e6:10.3f} "
                      f"{float(r['Percentage']):6.2f}  {name}")
+    if bench_log:
+        b = _bench_line(bench_log)
+        if b is not None and b.get("roofline"):
+            rf = b["roofline"]
+            lines += ["", "same run, benchmark line (HIP events on the launch stream):",
+                      f"  kernel: {rf.get('kernel')}",
+                      f"  fwd_ms_mean: {rf.get('fwd_ms_mean')}",
+                      f"  roofline_frac: {rf.get('frac')}",
+                      f"  ms_per_step: {b.get('ms_per_step')}",
+                      f"  value: {b.get('value')} {b.get('unit')}"]
     return "\n".join(lines) + "\n"
 
 
@@ -280,6 +307,7 @@ def main(argv=None):
     s.add_argument("--command", required=True)
     s.add_argument("--out", required=True)
     s.add_argument("--tail", type=int, default=0)
+    s.add_argument("--bench-log", default="")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch-dir", required=True)
     t.add_argument("--write-dir", required=True)
@@ -305,7 +333,7 @@ def main(argv=None):
     c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
-        text = stats_summary(a.csv_dir, a.command, tail=a.tail)
+        text = stats_summary(a.csv_dir, a.command, tail=a.tail, bench_log=a.bench_log)
     elif a.cmd == "l2":
         text = l2_summary(a.pmc_dir, a.kernel, a.source, a.command)
     elif a.cmd == "mfma":

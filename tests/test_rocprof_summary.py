@@ -83,3 +83,20 @@ def test_l2_hit_rate(tmp_path):
     assert float(kv["l2_hit_rate_mean"]) == 0.625
     assert float(kv["l2_hit_rate_min"]) == 0.5 and float(kv["l2_hit_rate_max"]) == 0.75
     assert float(kv["l2_requests_per_launch"]) == 250.0
+
+
+def test_stats_reports_the_same_runs_bench_line(tmp_path):
+    d = tmp_path / "run"
+    d.mkdir()
+    _write(d / "x_kernel_trace.csv", ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+           [("A", 0, 1000), ("A", 2000, 3000)])
+    _write(d / "x_kernel_stats.csv",
+           ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"],
+           [("A", 2, 2000, 1000, 100.0, 1000, 1000)])
+    log = tmp_path / "bench.log"
+    log.write_text("profiler noise\n{not json}\n"
+                   '{"value": 5.0, "unit": "TFLOP/s", "ms_per_step": 1.1, '
+                   '"roofline": {"kernel": "A", "fwd_ms_mean": 1.0, "frac": 0.5}}\n')
+    text = rs.stats_summary(str(d), "cmd", bench_log=str(log))
+    assert "fwd_ms_mean: 1.0" in text and "roofline_frac: 0.5" in text
+    assert "ms_per_step: 1.1" in text
