@@ -717,6 +717,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="untimed steps for about this long before the warm-up steps "
+                         "(the clock's return after the host-side setup)")
     ap.add_argument("--cpu-tiles", type=int, default=256,
                     help="query tiles in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--dense-calls", type=int, default=5,
@@ -816,6 +819,15 @@ def main():
             ev[4].record(stream)
         return flops_by_r[r]
 
+    # After the host-side setup above the GPU's clock takes several
+    # milliseconds of work to come back up (timed calls issued straight away
+    # ran up to 15 % slower for the first few, and the rate still crept up
+    # by about 1 % over the next few hundred milliseconds): the step runs
+    # untimed for about --settle-ms first, so that the W warm-up steps and the
+    # K timed ones start from a running clock whatever W is.
+    if args.settle_ms > 0:
+        n_settle = iter(range(1 << 30))
+        settle(torch, lambda: step(next(n_settle)), ms=args.settle_ms, cap=10000)
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
@@ -939,6 +951,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms_before_warmup": args.settle_ms,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
